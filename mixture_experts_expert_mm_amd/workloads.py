@@ -1,0 +1,218 @@
+"""Seeded synthetic inputs for the routed-expert path.
+
+This module only draws and stores inputs; it holds none of the expert path's
+arithmetic (no dispatch, no GEMM, no SwiGLU, no activation quantisation, no
+combine).  Both the CPU oracle and the GPU path are fed from here.
+
+Recipe (all draws are numpy PCG64, float32):
+
+* Expert weights, one stream per expert ``default_rng([seed, 0, e])``:
+  ``W1[e] ~ N(0,1)/sqrt(hidden)`` of shape ``[hidden, 2*intermediate]`` then
+  ``W2[e] ~ N(0,1)/sqrt(intermediate)`` of shape ``[intermediate, hidden]``,
+  both rounded to bf16 (the model weights).  The layout is the one of the
+  Formula paragraph of the Ascend ``mega_moe`` operator page
+  (``W1 in R^{E x hidden x 2I}``, ``W2 in R^{E x I x hidden}``).
+* Per-expert routing bias ``default_rng([seed, 2]) ~ N(0,1) * bias_std``
+  (``bias_std = 0.5`` for the skewed DeepSeek-V3-like shapes, 0 otherwise).
+* Router scores ``default_rng([seed, 1, T]) ~ N(0,1)`` of shape ``[T, E]``
+  plus the bias; ``topk_ids`` are the K largest (descending, ties to the
+  lower expert id), ``topk_weights`` the float32 softmax over the K selected
+  scores.  The pages' own examples draw top-k of randn scores the same way
+  (Ascend page, Example; DeepEP metadata notes, section 4.1).
+* Tokens ``X ~ N(0,1)`` rounded to bf16, drawn in row chunks of 1024 with
+  stream ``default_rng([seed, 3, T, chunk])``.
+* Optional masked routes (DeepEP metadata notes, section 5.2): each route is
+  set to id -1 with probability ``masked_ratio`` (stream
+  ``default_rng([seed, 4, T])``) and its weight to 0.
+
+Quantised use cases take the weights offline to the use case's dtype, as the
+Ascend page's A2/A3 example does before calling the operator: per output
+channel (amax over the input dimension), ``scale = max(amax / Qmax, 1e-8)``
+in float32, ``q = w / scale`` in float32, then round-half-even and clamp to
++-127 (int8, Qmax 127) or saturate to +-448 and round to OCP e4m3fn (fp8,
+Qmax 448).  This is input preparation outside the operator, not part of the
+path under test.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import torch
+
+USECASES = ("bf16", "fp8", "int8")
+QMAX = {"fp8": 448.0, "int8": 127.0}
+
+
+@dataclasses.dataclass(frozen=True)
+class Config:
+    name: str
+    usecase: str
+    T: int
+    H: int
+    I: int
+    E: int
+    K: int
+    bias_std: float
+    seed: int
+    masked_ratio: float = 0.0
+
+    @property
+    def routes(self) -> int:
+        return self.T * self.K
+
+    def with_(self, **kw) -> "Config":
+        return dataclasses.replace(self, **kw)
+
+
+# The five workloads (names say what they are).  The fp8 shape is swept over
+# two token counts that share one weight set (same seed).
+CONFIGS = {
+    "tiny_bf16": Config("tiny_bf16", "bf16", 64, 256, 128, 8, 2, 0.0, 1000),
+    "mid_bf16": Config("mid_bf16", "bf16", 2048, 4096, 1408, 16, 4, 0.0, 1001),
+    "dsv3_bf16": Config("dsv3_bf16", "bf16", 4096, 7168, 2048, 32, 8, 0.5, 1002),
+    "dsv3_fp8_t128": Config("dsv3_fp8_t128", "fp8", 128, 7168, 2048, 32, 8, 0.5, 1003),
+    "dsv3_fp8_t16384": Config("dsv3_fp8_t16384", "fp8", 16384, 7168, 2048, 32, 8, 0.5, 1003),
+    "dsv3_int8": Config("dsv3_int8", "int8", 8192, 7168, 2048, 32, 8, 0.0, 1004),
+}
+
+
+def _threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+# --------------------------------------------------------------------------
+# routing + tokens
+# --------------------------------------------------------------------------
+
+def routing(cfg: Config):
+    """Return ``(topk_ids int32 [T,K], topk_weights float32 [T,K])`` as torch CPU tensors."""
+    rng = np.random.default_rng([cfg.seed, 1, cfg.T])
+    scores = rng.standard_normal((cfg.T, cfg.E), dtype=np.float32)
+    if cfg.bias_std > 0:
+        bias = np.random.default_rng([cfg.seed, 2]).standard_normal(cfg.E, dtype=np.float32)
+        scores = scores + (bias * np.float32(cfg.bias_std))[None, :]
+    order = np.argsort(-scores, axis=1, kind="stable")[:, : cfg.K]
+    sel = np.take_along_axis(scores, order, axis=1).astype(np.float64)
+    ex = np.exp(sel - sel.max(axis=1, keepdims=True))
+    wts = (ex / ex.sum(axis=1, keepdims=True)).astype(np.float32)
+    ids = order.astype(np.int32)
+    if cfg.masked_ratio > 0:
+        m = np.random.default_rng([cfg.seed, 4, cfg.T]).random((cfg.T, cfg.K)) < cfg.masked_ratio
+        ids = np.where(m, np.int32(-1), ids)
+        wts = np.where(m, np.float32(0.0), wts)
+    return torch.from_numpy(np.ascontiguousarray(ids)), torch.from_numpy(np.ascontiguousarray(wts))
+
+
+def tokens(cfg: Config) -> torch.Tensor:
+    """Return X as a bf16 torch CPU tensor ``[T, H]``."""
+    chunk = 1024
+    n_chunks = (cfg.T + chunk - 1) // chunk
+    out = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16)
+
+    def one(c):
+        r0, r1 = c * chunk, min(cfg.T, (c + 1) * chunk)
+        a = np.random.default_rng([cfg.seed, 3, cfg.T, c]).standard_normal((r1 - r0, cfg.H), dtype=np.float32)
+        out[r0:r1] = torch.from_numpy(a).to(torch.bfloat16)
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(one, range(n_chunks)))
+    return out
+
+
+# --------------------------------------------------------------------------
+# expert weights
+# --------------------------------------------------------------------------
+
+def expert_weights_f32(cfg: Config, e: int):
+    """bf16-rounded model weights of expert ``e`` as float32 ``(W1[H,2I], W2[I,H])``."""
+    rng = np.random.default_rng([cfg.seed, 0, e])
+    w1 = rng.standard_normal((cfg.H, 2 * cfg.I), dtype=np.float32)
+    w1 *= np.float32(1.0 / np.sqrt(cfg.H))
+    w2 = rng.standard_normal((cfg.I, cfg.H), dtype=np.float32)
+    w2 *= np.float32(1.0 / np.sqrt(cfg.I))
+    w1 = torch.from_numpy(w1).to(torch.bfloat16).float()
+    w2 = torch.from_numpy(w2).to(torch.bfloat16).float()
+    return w1, w2
+
+
+def quantize_weight_per_channel(w: torch.Tensor, usecase: str):
+    """Offline per-output-channel weight quantisation (input preparation).
+
+    ``w`` is float32 ``[K_in, N]``; returns ``(q, scale[N] float32)`` with ``q``
+    int8 or float8_e4m3fn.  Follows the per-channel recipe of the Ascend
+    page's A2/A3 example (amax over dim 0, clamp 1e-8, round, clamp).
+    """
+    qmax = QMAX[usecase]
+    amax = w.abs().amax(dim=0)
+    sf = torch.clamp(amax / qmax, min=1e-8).to(torch.float32)
+    v = w / sf[None, :]
+    if usecase == "int8":
+        q = torch.round(v).clamp_(-127, 127).to(torch.int8)
+    else:
+        q = v.clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
+    return q, sf
+
+
+def expert_weights(cfg: Config, e: int):
+    """Weights of expert ``e`` in the use case's dtype.
+
+    Returns ``(w1, w2, s1, s2)``: ``w1 [H,2I]``, ``w2 [I,H]`` in bf16 / fp8 /
+    int8; ``s1 [2I]``, ``s2 [H]`` float32 per-channel scales (``None`` for bf16).
+    """
+    w1, w2 = expert_weights_f32(cfg, e)
+    if cfg.usecase == "bf16":
+        return w1.to(torch.bfloat16), w2.to(torch.bfloat16), None, None
+    q1, s1 = quantize_weight_per_channel(w1, cfg.usecase)
+    q2, s2 = quantize_weight_per_channel(w2, cfg.usecase)
+    return q1, q2, s1, s2
+
+
+@dataclasses.dataclass
+class Weights:
+    w1: torch.Tensor            # [E, H, 2I]
+    w2: torch.Tensor            # [E, I, H]
+    s1: torch.Tensor | None     # [E, 2I] float32
+    s2: torch.Tensor | None     # [E, H] float32
+
+
+def all_weights(cfg: Config) -> Weights:
+    dt = {"bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn, "int8": torch.int8}[cfg.usecase]
+    w1 = torch.empty((cfg.E, cfg.H, 2 * cfg.I), dtype=dt)
+    w2 = torch.empty((cfg.E, cfg.I, cfg.H), dtype=dt)
+    q = cfg.usecase != "bf16"
+    s1 = torch.empty((cfg.E, 2 * cfg.I), dtype=torch.float32) if q else None
+    s2 = torch.empty((cfg.E, cfg.H), dtype=torch.float32) if q else None
+
+    def one(e):
+        a, b, c, d = expert_weights(cfg, e)
+        w1[e] = a
+        w2[e] = b
+        if q:
+            s1[e] = c
+            s2[e] = d
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(one, range(cfg.E)))
+    return Weights(w1, w2, s1, s2)
+
+
+@dataclasses.dataclass
+class Inputs:
+    cfg: Config
+    x: torch.Tensor
+    topk_ids: torch.Tensor
+    topk_weights: torch.Tensor
+    weights: Weights
+
+
+def make_inputs(cfg: Config) -> Inputs:
+    ids, wts = routing(cfg)
+    return Inputs(cfg, tokens(cfg), ids, wts, all_weights(cfg))

@@ -1,0 +1,359 @@
+"""Plain float64 oracle of the routed-expert path (test infrastructure only).
+
+Sources, cited by page title and section:
+
+* [ASC] "mega_moe" -- Ascend CANN ops-transformer operator page.
+  Formula, Conventions, Computation Process (A16W16 non-quantized use case;
+  A8W8-INT Quantization Use Case), Parameters table, Deterministic
+  Computation.
+* [MD]  "05_05 Metadata System" -- DeepEP-v2 notes on DeepGEMM Mega MoE.
+  Section 1 (Count -> Prefix Sum -> Scatter), section 3.5 (pool block
+  offset), section 5.2 (masked routes).
+* [DG]  "DeepGEMM MegaMoE: Fused Communication and Expert Compute".
+  Section 2 (token identities).
+
+Readings taken where the pages are silent or ambiguous (each one is listed
+with its reason in the design notes of the repository):
+
+* rounding ``round-to-nearest`` of [ASC] Conventions is ties-to-even;
+* a zero row gets the 1e-8 scale floor the page's weight example uses, so
+  its codes are 0;
+* the fp8 (OCP e4m3fn) variant of the A8W8 formulas uses Qmax = 448 and
+  saturates to +-448 before rounding, per-row scales over the full row;
+* the activation quantisation before Dispatch is evaluated in IEEE float32
+  (the precision the kernels use), so the integer / e4m3 codes it decides
+  are the same on both sides;
+* the Linear2 operand A is rounded to the Linear's activation dtype of the
+  use case table (bf16 for A16W16);
+* route ids < 0 are masked: skipped, counted nowhere, contribute 0 ([MD] 5.2).
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+# --------------------------------------------------------------------------
+# number formats
+# --------------------------------------------------------------------------
+
+_BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127
+_E4M3_MAX = 448.0
+
+
+def _round_to_significand(a: np.ndarray, sig_bits: int, min_exp: int) -> np.ndarray:
+    """Round float64 ``a`` to ``sig_bits`` significant bits, ties to even.
+
+    Numbers below ``2**min_exp`` (the smallest normal) share the subnormal
+    quantum ``2**(min_exp - sig_bits + 1)``.  Division by a power of two is
+    exact in float64, so the only rounding is the one ``np.rint`` does.
+    """
+    a = np.asarray(a, dtype=np.float64)
+    _, ex = np.frexp(a)                      # a = m * 2**ex, 0.5 <= |m| < 1
+    e = np.maximum(ex - 1, min_exp)          # |a| in [2**e, 2**(e+1))
+    quantum = np.ldexp(1.0, e - (sig_bits - 1))
+    return np.rint(a / quantum) * quantum
+
+
+def bf16_round(a) -> np.ndarray:
+    """Value of ``a`` rounded to bfloat16 (8 significant bits, ties to even)."""
+    r = _round_to_significand(a, 8, -126)
+    return np.where(np.abs(r) > _BF16_MAX, np.copysign(np.inf, r), r)
+
+
+def e4m3_round(a) -> np.ndarray:
+    """Value of ``a`` in OCP float8 e4m3fn: saturate to +-448, round half-even.
+
+    e4m3fn has 4 significant bits, exponent bias 7, smallest normal 2**-6,
+    subnormal quantum 2**-9, no infinity, largest finite 448.
+    """
+    a = np.clip(np.asarray(a, dtype=np.float64), -_E4M3_MAX, _E4M3_MAX)
+    return _round_to_significand(a, 4, -6)
+
+
+def e4m3_encode(a) -> np.ndarray:
+    """Bit pattern (uint8) of ``e4m3_round(a)``; sign bit kept for -0."""
+    a = np.asarray(a, dtype=np.float64)
+    r = e4m3_round(a)
+    sign = np.signbit(a).astype(np.uint8) << 7
+    mag = np.abs(r)
+    _, ex = np.frexp(mag)
+    e = ex - 1
+    normal = mag >= 2.0 ** -6
+    ebits = np.where(normal, e + 7, 0)
+    mant = np.where(normal, mag / np.ldexp(1.0, e) - 1.0, mag / 2.0 ** -9) * np.where(normal, 8.0, 1.0)
+    mant = np.rint(mant).astype(np.int64)
+    code = (ebits.astype(np.int64) << 3) | mant
+    code = np.where(mag == 0, 0, code)
+    return (code.astype(np.uint8) | sign).astype(np.uint8)
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """float64 value of e4m3fn bit patterns (0x7f / 0xff are NaN)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    s = np.where(c & 0x80, -1.0, 1.0)
+    eb = (c >> 3) & 0xF
+    m = c & 0x7
+    val = np.where(eb == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.ldexp(1.0, eb - 7))
+    val = np.where((eb == 0xF) & (m == 0x7), np.nan, val)
+    return s * val
+
+
+# --------------------------------------------------------------------------
+# activation
+# --------------------------------------------------------------------------
+
+def silu(z):
+    """SiLU(z) = z / (1 + e^{-z})  ([ASC] Conventions)."""
+    z = np.asarray(z, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def swiglu(h: np.ndarray) -> np.ndarray:
+    """[ASC] Computation Process, Expert Compute step 2 (SwiGLU activation).
+
+    The first ``intermediate_hidden`` columns of the Linear1 output are the
+    gate part, the last ``intermediate_hidden`` the up part;
+    ``A = SiLU(H_gate) * H_up``.
+    """
+    n2 = h.shape[-1]
+    assert n2 % 2 == 0
+    inter = n2 // 2
+    return silu(h[..., :inter]) * h[..., inter:]
+
+
+# --------------------------------------------------------------------------
+# quantisation ([ASC] A8W8-INT use case; fp8 variant by the same formulas)
+# --------------------------------------------------------------------------
+
+QMAX = {"int8": 127, "fp8": 448}
+
+
+def quantize_tokens(x_f32: np.ndarray, usecase: str):
+    """Per-token activation quantisation done before Dispatch.
+
+    [ASC] A8W8-INT Quantization Use Case, EP Dispatch: ``s_i = max|X[i,:]|/Qmax``,
+    ``q_i = round(X[i,:] / s_i)`` in the symmetric range.  Evaluated in IEEE
+    float32 (amax exact, one correctly rounded division for the scale, one per
+    element for the quotient); scale floored at 1e-8.
+
+    Returns ``(codes, scale float32 [T], values float64)`` where ``codes`` is
+    int8 (int8 use case) or the uint8 e4m3 bit patterns (fp8), and ``values``
+    are the integer / e4m3 values the codes stand for.
+    """
+    x = np.asarray(x_f32, dtype=np.float32)
+    qmax = np.float32(QMAX[usecase])
+    amax = np.max(np.abs(x), axis=1)
+    s = np.maximum(amax / qmax, np.float32(1e-8)).astype(np.float32)
+    v = (x / s[:, None]).astype(np.float32)
+    if usecase == "int8":
+        q = np.clip(np.rint(v), -127, 127).astype(np.int8)
+        return q, s, q.astype(np.float64)
+    codes = e4m3_encode(v)
+    return codes, s, e4m3_decode(codes)
+
+
+def requantize_rows(a: np.ndarray, usecase: str, emulate_fp32: bool = False):
+    """Per-row requantisation of the SwiGLU output before Linear2.
+
+    [ASC] A8W8-INT use case, Expert Compute step 3: ``s^A_i = max|A[i,:]|/Qmax``,
+    ``A^q[i,:] = round(A[i,:] / s^A_i)``.  float64 by default; with
+    ``emulate_fp32`` the row is first rounded to float32 and the scale and
+    quotients are float32 operations.  Returns ``(values float64, scale float64)``.
+    """
+    qmax = QMAX[usecase]
+    if emulate_fp32:
+        af = np.asarray(a, dtype=np.float32)
+        s = np.maximum(np.max(np.abs(af), axis=1) / np.float32(qmax), np.float32(1e-8)).astype(np.float32)
+        v = (af / s[:, None]).astype(np.float32).astype(np.float64)
+        s = s.astype(np.float64)
+    else:
+        a = np.asarray(a, dtype=np.float64)
+        s = np.maximum(np.max(np.abs(a), axis=1) / qmax, 1e-8)
+        v = a / s[:, None]
+    if usecase == "int8":
+        q = np.clip(np.rint(v), -127, 127)
+    else:
+        q = e4m3_round(v)
+    return q, s
+
+
+# --------------------------------------------------------------------------
+# dispatch layout ([MD] sections 1, 3.5; [ASC] EP Dispatch)
+# --------------------------------------------------------------------------
+
+def dispatch_layout(topk_ids: np.ndarray, num_experts: int, block_m: int):
+    """Count -> Prefix Sum -> Scatter, with a BLOCK_M-padded pool.
+
+    * ``counts[e] = N_e`` = number of valid routes with id ``e`` ([ASC] EP
+      Dispatch defines ``N_e = |I_e|``; ids are distinct per token, so this is
+      also the route count).  Masked routes (id < 0) are not counted.
+    * ``offsets[e+1] = offsets[e] + BLOCK_M * ceil(N_e / BLOCK_M)`` -- each
+      expert owns a contiguous, block-aligned pool range ([MD] 3.5).
+    * ``routes[e]`` = the sorted flat route ids ``i*K + k`` with
+      ``E[i,k] == e`` -- the (token, top-k slot) identity multiset of the
+      expert ([DG] section 2; [MD] 4.2).  Their order inside the pool is any
+      fixed order ([ASC] EP Dispatch), so only the multiset is defined.
+    """
+    ids = np.asarray(topk_ids).reshape(-1).astype(np.int64)
+    if np.any(ids >= num_experts):
+        raise ValueError("expert id out of range")
+    valid = ids >= 0
+    counts = np.bincount(ids[valid], minlength=num_experts).astype(np.int64)
+    blocks = (counts + block_m - 1) // block_m
+    offsets = np.zeros(num_experts + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(blocks * block_m)
+    routes = [np.nonzero(ids == e)[0] for e in range(num_experts)]
+    return {"counts": counts, "offsets": offsets, "routes": routes}
+
+
+# --------------------------------------------------------------------------
+# forward
+# --------------------------------------------------------------------------
+
+def _expert_f64(expert, e, usecase):
+    """Decode expert ``e`` to float64 ``(W1 [H,2I], W2 [I,H], s1, s2)``."""
+    w1, w2, s1, s2 = expert(e)
+    w1 = np.asarray(w1)
+    w2 = np.asarray(w2)
+    if usecase == "fp8":
+        w1 = e4m3_decode(w1.view(np.uint8))
+        w2 = e4m3_decode(w2.view(np.uint8))
+    else:
+        w1 = w1.astype(np.float64)
+        w2 = w2.astype(np.float64)
+    if usecase != "bf16":
+        s1 = np.asarray(s1, dtype=np.float64)
+        s2 = np.asarray(s2, dtype=np.float64)
+    return w1, w2, s1, s2
+
+
+def moe_forward(x_f32, topk_ids, topk_weights, expert, usecase: str,
+                tokens=None, requant_fp32: bool = False):
+    """y_i = sum_k G[i,k] * SwiGLU-FFN_{E[i,k]}(x_i), float64.
+
+    [ASC] Computation Process: EP Dispatch groups the tokens per expert,
+    Linear1 ``H_e = X_e W1[e]``, SwiGLU, Linear2 ``Y_e = A_e W2[e]``, Token
+    Combine ``y_i = sum_k w_k Y_{e_ik}[row(i,k)]``.  For A8W8 the Linear1
+    result is dequantised ``(C * s^W1) * s^X``, A is requantised per row, and
+    the Linear2 result is dequantised ``(D * s^W2) * s^A``.
+
+    Inputs: ``x_f32`` [T,H] float32 holding the bf16 token values; ``topk_ids``
+    [T,K] int; ``topk_weights`` [T,K] float32; ``expert(e)`` returns expert
+    ``e``'s weights (bf16 values as float32, int8, or e4m3 bit patterns as
+    uint8) and per-channel scales.  ``tokens`` optionally restricts the
+    result to those token indices (rows are independent, so each is the same
+    as in the full computation).  Returns ``(y float64 [T or len(tokens), H],
+    counts)``.
+
+    Rows are grouped per expert and multiplied with float64 BLAS, which
+    changes no definition: every GEMM row is independent of the others.
+    The float64 sum over the top-k slots is independent of order at the
+    tolerances used.
+    """
+    x = np.asarray(x_f32, dtype=np.float32)
+    ids = np.asarray(topk_ids).astype(np.int64)
+    g = np.asarray(topk_weights, dtype=np.float64)
+    T, K = ids.shape
+    if tokens is None:
+        tok = np.arange(T)
+    else:
+        tok = np.asarray(tokens, dtype=np.int64)
+    pos = np.full(T, -1, dtype=np.int64)
+    pos[tok] = np.arange(len(tok))
+
+    if usecase != "bf16":
+        _, sx_sub, xin_sub = quantize_tokens(x[tok], usecase)
+
+    H = x.shape[1]
+    y = np.zeros((len(tok), H), dtype=np.float64)
+    flat = ids.reshape(-1)
+    sub_mask = np.zeros(T, dtype=bool)
+    sub_mask[tok] = True
+    e_max = int(flat.max()) if flat.size else -1
+    counts = np.bincount(flat[flat >= 0], minlength=max(e_max + 1, 0))
+    for e in range(e_max + 1):
+        r = np.nonzero(flat == e)[0]
+        r = r[sub_mask[r // K]]
+        if r.size == 0:
+            continue
+        i = r // K
+        rows = pos[i]
+        w1, w2, s1, s2 = _expert_f64(expert, e, usecase)
+        if usecase == "bf16":
+            xe = x[i].astype(np.float64)
+            h = xe @ w1
+            a = bf16_round(swiglu(h))
+            o = a @ w2
+        else:
+            c = xin_sub[rows] @ w1
+            h = (c * s1[None, :]) * sx_sub[rows].astype(np.float64)[:, None]
+            a = swiglu(h)
+            aq, sa = requantize_rows(a, usecase, emulate_fp32=requant_fp32)
+            d = aq @ w2
+            o = (d * s2[None, :]) * sa[:, None]
+        np.add.at(y, rows, g.reshape(-1)[r][:, None] * o)
+    return y, counts
+
+
+def moe_forward_bruteforce(x_f32, topk_ids, topk_weights, expert, usecase: str):
+    """Literal per-token, per-slot scalar loops (tiny inputs only).
+
+    Follows [ASC] Computation Process one scalar at a time: for token i and
+    slot k with e = E[i,k] >= 0, h_c = sum_j x_ij W1[e][j,c]; a_c =
+    SiLU(h_c) * h_{I+c}; o_n = sum_c a_c W2[e][c,n]; y_in += G[i,k] o_n.
+    Quantised use cases take the quantised tokens, dequantise h per element,
+    requantise a per route with its own amax, and dequantise o per element.
+    """
+    x = np.asarray(x_f32, dtype=np.float32)
+    ids = np.asarray(topk_ids).astype(np.int64)
+    g = np.asarray(topk_weights, dtype=np.float64)
+    T, K = ids.shape
+    H = x.shape[1]
+    if usecase != "bf16":
+        _, sx, xq = quantize_tokens(x, usecase)
+    y = [[0.0] * H for _ in range(T)]
+    cache = {}
+    for i in range(T):
+        for k in range(K):
+            e = int(ids[i, k])
+            if e < 0:
+                continue
+            if e not in cache:
+                cache[e] = _expert_f64(expert, e, usecase)
+            w1, w2, s1, s2 = cache[e]
+            n2 = w1.shape[1]
+            inter = n2 // 2
+            h = []
+            for c in range(n2):
+                acc = 0.0
+                for j in range(H):
+                    xv = float(x[i, j]) if usecase == "bf16" else float(xq[i, j])
+                    acc += xv * float(w1[j, c])
+                if usecase != "bf16":
+                    acc = acc * float(s1[c]) * float(sx[i])
+                h.append(acc)
+            a = []
+            for c in range(inter):
+                z = h[c]
+                a.append((z / (1.0 + math.exp(-z))) * h[inter + c])
+            if usecase == "bf16":
+                a = [float(bf16_round(v)) for v in a]
+                sa = 1.0
+            else:
+                qmax = QMAX[usecase]
+                sa = max(max(abs(v) for v in a) / qmax, 1e-8)
+                if usecase == "int8":
+                    a = [float(min(127.0, max(-127.0, round(v / sa)))) for v in a]
+                else:
+                    a = [float(e4m3_round(v / sa)) for v in a]
+            for n in range(H):
+                acc = 0.0
+                for c in range(inter):
+                    acc += a[c] * float(w2[c, n])
+                if usecase != "bf16":
+                    acc = acc * float(s2[n]) * sa
+                y[i][n] += float(g[i, k]) * acc
+    return np.array(y, dtype=np.float64)

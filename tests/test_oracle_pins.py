@@ -1,0 +1,360 @@
+"""Pins of the CPU oracle to something other than itself (no GPU needed).
+
+Each test names what fixes the expected value: a hand-derived fixture under
+tests/golden (with its citation), a library routine that the oracle's own
+code does not call (torch casts, scipy's logistic, torch's SiLU), a closed
+form, an invariant of the definition, or the literal brute-force loops on a
+tiny input.
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+from scipy.special import expit
+
+import oracle
+from oracle import moe_oracle as om
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# --------------------------------------------------------------------------
+# number formats, pinned to torch's own casts
+# --------------------------------------------------------------------------
+
+def test_bf16_round_matches_torch_cast_random():
+    rng = np.random.default_rng(0)
+    mant = rng.standard_normal(200_000).astype(np.float32)
+    expo = rng.integers(-130, 120, 200_000)
+    x = (mant * np.ldexp(np.float32(1.0), expo)).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    got = oracle.bf16_round(x.astype(np.float64))
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_bf16_round_ties_to_even_at_midpoints():
+    # every midpoint between two adjacent bf16 values of [1, 2) and [2^-20, 2^-19)
+    for base in (1.0, 2.0 ** -20):
+        lo = base * (1.0 + np.arange(128) / 128.0)
+        mid = (lo + base / 128.0 / 2.0).astype(np.float32)      # exact in fp32
+        ref = torch.from_numpy(mid).to(torch.bfloat16).double().numpy()
+        np.testing.assert_array_equal(oracle.bf16_round(mid.astype(np.float64)), ref)
+
+
+def test_e4m3_decode_all_codes_match_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = oracle.e4m3_decode(codes)
+    np.testing.assert_array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    np.testing.assert_array_equal(got[ok], ref[ok])
+
+
+def test_e4m3_encode_roundtrip_all_finite_codes():
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    vals = oracle.e4m3_decode(codes)
+    np.testing.assert_array_equal(oracle.e4m3_encode(vals), codes)
+
+
+def test_e4m3_encode_matches_torch_on_midpoints_and_random():
+    pos = oracle.e4m3_decode(np.arange(0, 0x7F, dtype=np.uint8))   # 0 .. 448 ascending
+    mids = ((pos[:-1] + pos[1:]) / 2.0).astype(np.float32)           # ties, exact in fp32
+    rng = np.random.default_rng(1)
+    rnd = (rng.standard_normal(100_000) * np.exp(rng.uniform(-12, 6, 100_000))).astype(np.float32)
+    for x in (mids, -mids, np.clip(rnd, -448, 448).astype(np.float32)):
+        ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        np.testing.assert_array_equal(oracle.e4m3_encode(x), ref)
+
+
+def test_e4m3_saturates():
+    # reading: values beyond the largest finite e4m3fn saturate to +-448
+    got = oracle.e4m3_encode(np.array([448.0, 460.0, 464.0, 1e6, -1e6, -470.0]))
+    np.testing.assert_array_equal(got, [0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0xFE])
+
+
+# --------------------------------------------------------------------------
+# SiLU / SwiGLU
+# --------------------------------------------------------------------------
+
+def test_silu_matches_logistic():
+    z = np.linspace(-30, 30, 10001)
+    np.testing.assert_allclose(oracle.silu(z), z * expit(z), rtol=1e-14, atol=1e-300)
+    assert oracle.silu(np.array([0.0]))[0] == 0.0
+
+
+def test_swiglu_split_order_golden():
+    g = _golden("swiglu_split.json")
+    np.testing.assert_allclose(oracle.swiglu(np.array(g["h"])), np.array(g["a"]), rtol=1e-15)
+
+
+def test_swiglu_matches_torch_silu():
+    rng = np.random.default_rng(2)
+    h = rng.standard_normal((7, 24))
+    t = torch.from_numpy(h)
+    ref = (torch.nn.functional.silu(t[:, :12]) * t[:, 12:]).numpy()
+    np.testing.assert_allclose(oracle.swiglu(h), ref, rtol=1e-13, atol=1e-15)
+
+
+# --------------------------------------------------------------------------
+# quantisers
+# --------------------------------------------------------------------------
+
+def test_quantize_tokens_int8_golden():
+    g = _golden("quant_int8_rows.json")
+    q, s, v = oracle.quantize_tokens(np.array(g["x"], dtype=np.float32), "int8")
+    np.testing.assert_array_equal(q, np.array(g["q"], dtype=np.int8))
+    np.testing.assert_array_equal(s, np.array(g["scale"], dtype=np.float32))
+    np.testing.assert_array_equal(v, np.array(g["q"], dtype=np.float64))
+
+
+def test_quantize_tokens_fp8_golden():
+    g = _golden("quant_fp8_rows.json")
+    c, s, v = oracle.quantize_tokens(np.array(g["x"], dtype=np.float32), "fp8")
+    np.testing.assert_array_equal(c, np.array(g["codes"], dtype=np.uint8))
+    np.testing.assert_array_equal(s, np.array(g["scale"], dtype=np.float32))
+    np.testing.assert_array_equal(v, np.array(g["values"]))
+
+
+@pytest.mark.parametrize("usecase,qmax", [("int8", 127), ("fp8", 448)])
+def test_quantize_tokens_invariants(usecase, qmax):
+    rng = np.random.default_rng(3)
+    x = torch.from_numpy(rng.standard_normal((64, 300)).astype(np.float32)).to(torch.bfloat16).float().numpy()
+    x[5] = 0.0
+    _, s, v = oracle.quantize_tokens(x, usecase)
+    # the amax element of every non-zero row lands on +-Qmax
+    amax_idx = np.argmax(np.abs(x), axis=1)
+    for i in range(64):
+        if i == 5:
+            assert np.all(v[i] == 0) and s[i] == np.float32(1e-8)
+            continue
+        assert abs(v[i, amax_idx[i]]) == qmax
+    assert np.all(np.abs(v) <= qmax)
+    # dequantised values stay within half a quantisation step of x
+    deq = v * s[:, None]
+    if usecase == "int8":
+        assert np.all(np.abs(deq - x) <= 0.5 * s[:, None] * (1 + 1e-5))
+    else:
+        # e4m3: relative error <= 2^-4 for normals, absolute <= 2^-10 * s below
+        err = np.abs(deq - x)
+        bound = np.maximum(np.abs(x) * 2.0 ** -4, 2.0 ** -10 * s[:, None]) * (1 + 1e-5)
+        assert np.all(err <= bound)
+
+
+@pytest.mark.parametrize("usecase,qmax", [("int8", 127), ("fp8", 448)])
+def test_requantize_rows_invariants(usecase, qmax):
+    rng = np.random.default_rng(4)
+    a = rng.standard_normal((40, 96)) * np.exp(rng.uniform(-3, 3, (40, 1)))
+    a[7] = 0.0
+    q, s = oracle.requantize_rows(a, usecase)
+    for i in range(40):
+        if i == 7:
+            assert np.all(q[i] == 0)
+            continue
+        assert abs(q[i, np.argmax(np.abs(a[i]))]) == qmax
+    assert np.all(np.abs(q) <= qmax)
+    q32, s32 = oracle.requantize_rows(a, usecase, emulate_fp32=True)
+    # float32 emulation decides the same codes up to a handful of boundary cases
+    assert np.mean(q32 != q) < 1e-3
+    np.testing.assert_allclose(s32, s, rtol=1e-6)
+
+
+# --------------------------------------------------------------------------
+# dispatch layout
+# --------------------------------------------------------------------------
+
+def test_dispatch_blog_example_golden():
+    g = _golden("dispatch_blog_example.json")
+    ids = np.array(g["topk_ids"])
+    d1 = oracle.dispatch_layout(ids, g["num_experts"], 1)
+    np.testing.assert_array_equal(d1["counts"], g["counts"])
+    np.testing.assert_array_equal(d1["offsets"], g["offsets_bm1"])
+    d4 = oracle.dispatch_layout(ids, g["num_experts"], 4)
+    np.testing.assert_array_equal(d4["offsets"], g["offsets_bm4"])
+    for e in range(g["num_experts"]):
+        assert list(d4["routes"][e]) == g["routes"][e]
+
+
+@pytest.mark.parametrize("bm", [1, 16, 64, 256])
+def test_dispatch_bruteforce_and_invariants(bm):
+    rng = np.random.default_rng(5)
+    T, E, K = 97, 13, 5
+    ids = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int32)
+    ids[rng.random((T, K)) < 0.1] = -1                 # masked routes
+    d = oracle.dispatch_layout(ids, E, bm)
+    # brute-force count
+    cnt = [0] * E
+    for i in range(T):
+        for k in range(K):
+            if ids[i, k] >= 0:
+                cnt[ids[i, k]] += 1
+    np.testing.assert_array_equal(d["counts"], cnt)
+    assert d["counts"].sum() == int((ids >= 0).sum())
+    off = d["offsets"]
+    assert off[0] == 0 and np.all(off % bm == 0)
+    assert np.all(np.diff(off) >= d["counts"]) and np.all(np.diff(off) - d["counts"] < bm)
+    allr = np.sort(np.concatenate(d["routes"]))
+    np.testing.assert_array_equal(allr, np.nonzero(ids.reshape(-1) >= 0)[0])
+    for e in range(E):
+        for r in d["routes"][e]:
+            assert ids.reshape(-1)[r] == e
+
+
+def test_dispatch_rejects_out_of_range():
+    with pytest.raises(ValueError):
+        oracle.dispatch_layout(np.array([[0, 4]]), 4, 8)
+
+
+# --------------------------------------------------------------------------
+# forward: brute force, reductions, invariants
+# --------------------------------------------------------------------------
+
+def _tiny_problem(usecase, T=5, H=12, I=4, E=4, K=2, seed=6, masked=False):
+    from mixture_experts_expert_mm_amd import workloads as wl
+    cfg = wl.Config("tiny", usecase, T, H, I, E, K, 0.0, seed, 0.3 if masked else 0.0)
+    ids, wts = wl.routing(cfg)
+    x = wl.tokens(cfg).float().numpy()
+    cache = {e: wl.expert_weights(cfg, e) for e in range(E)}
+
+    def expert(e):
+        w1, w2, s1, s2 = cache[e]
+        if usecase == "fp8":
+            w1, w2 = w1.view(torch.uint8), w2.view(torch.uint8)
+        elif usecase == "bf16":
+            w1, w2 = w1.float(), w2.float()
+        return (w1.numpy(), w2.numpy(), None if s1 is None else s1.numpy(), None if s2 is None else s2.numpy())
+
+    return cfg, x, ids.numpy(), wts.numpy(), expert
+
+
+@pytest.mark.parametrize("usecase", ["bf16", "int8", "fp8"])
+@pytest.mark.parametrize("masked", [False, True])
+def test_forward_matches_bruteforce(usecase, masked):
+    cfg, x, ids, wts, expert = _tiny_problem(usecase, masked=masked)
+    y, counts = oracle.moe_forward(x, ids, wts, expert, usecase)
+    yb = oracle.moe_forward_bruteforce(x, ids, wts, expert, usecase)
+    scale = np.sqrt(np.mean(yb ** 2))
+    assert scale > 0
+    np.testing.assert_allclose(y, yb, rtol=0, atol=1e-12 * scale)
+    # subset evaluation equals the full one row for row
+    ys, _ = oracle.moe_forward(x, ids, wts, expert, usecase, tokens=[3, 0])
+    np.testing.assert_array_equal(ys, y[[3, 0]])
+
+
+def test_topk1_unit_gate_is_dense_swiglu_ffn():
+    """K = 1, g = 1: every token passes through one dense SwiGLU FFN (torch reference)."""
+    rng = np.random.default_rng(7)
+    T, H, I, E = 9, 16, 8, 3
+    x = torch.from_numpy(rng.standard_normal((T, H)).astype(np.float32)).to(torch.bfloat16).float()
+    W1 = torch.from_numpy(rng.standard_normal((E, H, 2 * I)).astype(np.float32) / 4).to(torch.bfloat16).double()
+    W2 = torch.from_numpy(rng.standard_normal((E, I, H)).astype(np.float32) / 3).to(torch.bfloat16).double()
+    ids = rng.integers(0, E, (T, 1)).astype(np.int32)
+    g = np.ones((T, 1), dtype=np.float32)
+    y, _ = oracle.moe_forward(x.numpy(), ids, g, lambda e: (W1[e].numpy(), W2[e].numpy(), None, None), "bf16")
+    ref = torch.empty((T, H), dtype=torch.float64)
+    for i in range(T):
+        e = int(ids[i, 0])
+        h = x[i].double() @ W1[e]
+        a = torch.nn.functional.silu(h[:I]) * h[I:]
+        a = a.float().to(torch.bfloat16).double()          # Linear2 operand in bf16
+        ref[i] = a @ W2[e]
+    np.testing.assert_allclose(y, ref.numpy(), rtol=1e-6, atol=1e-9)
+
+
+def test_single_expert_single_slot():
+    """E = 1, K = 1, g = 1: Y = SwiGLU(X W1) W2 for the whole batch."""
+    rng = np.random.default_rng(8)
+    T, H, I = 6, 10, 4
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    x = torch.from_numpy(x).to(torch.bfloat16).float().numpy()
+    W1 = rng.standard_normal((H, 2 * I))
+    W2 = rng.standard_normal((I, H))
+    y, c = oracle.moe_forward(x, np.zeros((T, 1), np.int32), np.ones((T, 1), np.float32),
+                              lambda e: (W1, W2, None, None), "bf16")
+    h = torch.from_numpy(x.astype(np.float64)) @ torch.from_numpy(W1)
+    a = torch.nn.functional.silu(h[:, :I]) * h[:, I:]
+    a = a.float().to(torch.bfloat16).double()
+    np.testing.assert_allclose(y, (a @ torch.from_numpy(W2)).numpy(), rtol=1e-6, atol=1e-9)
+    assert list(c) == [T]
+
+
+@pytest.mark.parametrize("usecase", ["bf16", "int8", "fp8"])
+def test_invariances(usecase):
+    cfg, x, ids, wts, expert = _tiny_problem(usecase, T=7, H=16, I=8, E=5, K=3, seed=9)
+    y, _ = oracle.moe_forward(x, ids, wts, expert, usecase)
+    # relabelling experts (weights and ids permuted together)
+    perm = np.array([3, 0, 4, 1, 2])          # new id of old expert e
+    inv = np.argsort(perm)
+    y2, _ = oracle.moe_forward(x, perm[ids].astype(np.int32), wts, lambda e: expert(int(inv[e])), usecase)
+    np.testing.assert_allclose(y2, y, rtol=0, atol=1e-13 * np.abs(y).max())
+    # permuting the top-k slots (ids and weights together)
+    sp = np.array([2, 0, 1])
+    y3, _ = oracle.moe_forward(x, ids[:, sp], wts[:, sp], expert, usecase)
+    np.testing.assert_allclose(y3, y, rtol=0, atol=1e-13 * np.abs(y).max())
+    # linear in the gate weights
+    y4, _ = oracle.moe_forward(x, ids, wts * np.float32(0.5), expert, usecase)
+    np.testing.assert_allclose(y4, 0.5 * y, rtol=0, atol=1e-13 * np.abs(y).max())
+    # zero tokens give zero output
+    y5, _ = oracle.moe_forward(np.zeros_like(x), ids, wts, expert, usecase)
+    assert np.all(y5 == 0)
+
+
+def test_zero_up_half_gives_zero():
+    rng = np.random.default_rng(10)
+    T, H, I = 4, 8, 4
+    x = torch.from_numpy(rng.standard_normal((T, H)).astype(np.float32)).to(torch.bfloat16).float().numpy()
+    W1 = rng.standard_normal((H, 2 * I))
+    W1[:, I:] = 0.0
+    y, _ = oracle.moe_forward(x, np.zeros((T, 1), np.int32), np.ones((T, 1), np.float32),
+                              lambda e: (W1, rng.standard_normal((I, H)), None, None), "bf16")
+    assert np.all(y == 0)
+
+
+@pytest.mark.parametrize("usecase,bound", [("int8", 0.04), ("fp8", 0.13)])
+def test_quantised_path_within_quantisation_error_of_bf16(usecase, bound):
+    """The A8W8 result stays within the quantisation error of the unquantised one.
+
+    Rounding to a uniform step q leaves an error of RMS q/sqrt(12).  int8:
+    q = amax/127 per row or channel, i.e. about 0.7 % of the RMS for the
+    Gaussian X, W1, W2 and ~2-3 % for the heavier-tailed SwiGLU output A, so
+    the RMS of dY/RMS(Y) is ~2 %.  e4m3: the relative step is 2^-3..2^-4,
+    ~2.6 % RMS per operand and ~5-6 % for four operands.  The bound on
+    RMS(dY)/RMS(Y) leaves about 2x margin.  A dropped or doubled scale, a
+    wrong sign or a transposed operand gives O(1) errors and fails.
+    """
+    from mixture_experts_expert_mm_amd import workloads as wl
+    base = wl.Config("q", "bf16", 48, 128, 64, 6, 2, 0.0, 11)
+    ids, wts = wl.routing(base)
+    x = wl.tokens(base).float().numpy()
+
+    def mk(cfg):
+        def expert(e):
+            w1, w2, s1, s2 = wl.expert_weights(cfg, e)
+            if cfg.usecase == "fp8":
+                w1, w2 = w1.view(torch.uint8), w2.view(torch.uint8)
+            elif cfg.usecase == "bf16":
+                w1, w2 = w1.float(), w2.float()
+            return (w1.numpy(), w2.numpy(), None if s1 is None else s1.numpy(), None if s2 is None else s2.numpy())
+        return expert
+
+    yb, _ = oracle.moe_forward(x, ids.numpy(), wts.numpy(), mk(base), "bf16")
+    yq, _ = oracle.moe_forward(x, ids.numpy(), wts.numpy(), mk(base.with_(usecase=usecase)), usecase)
+    rel = np.sqrt(np.mean((yq - yb) ** 2)) / np.sqrt(np.mean(yb ** 2))
+    assert 1e-3 < rel < bound, rel
+
+
+def test_int8_linear1_accumulator_is_exact_integer():
+    """127^2 * 7168 < 2^31, so the int8 GEMM is exact; float64 BLAS reproduces it exactly."""
+    rng = np.random.default_rng(12)
+    a = rng.integers(-127, 128, (16, 7168))
+    b = rng.integers(-127, 128, (7168, 32))
+    exact = a.astype(np.int64) @ b.astype(np.int64)
+    assert np.abs(exact).max() < 2 ** 31
+    np.testing.assert_array_equal((a.astype(np.float64) @ b.astype(np.float64)).astype(np.int64), exact)

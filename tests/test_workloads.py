@@ -1,0 +1,65 @@
+"""Seeded input generators: determinism, shapes and the stated recipe."""
+
+import numpy as np
+import torch
+
+from mixture_experts_expert_mm_amd import workloads as wl
+
+
+def test_configs_match_stated_shapes():
+    c = wl.CONFIGS
+    assert (c["tiny_bf16"].T, c["tiny_bf16"].H, c["tiny_bf16"].I, c["tiny_bf16"].E, c["tiny_bf16"].K) == (64, 256, 128, 8, 2)
+    assert (c["mid_bf16"].T, c["mid_bf16"].H, c["mid_bf16"].I, c["mid_bf16"].E, c["mid_bf16"].K) == (2048, 4096, 1408, 16, 4)
+    for n in ("dsv3_bf16", "dsv3_fp8_t128", "dsv3_fp8_t16384", "dsv3_int8"):
+        assert (c[n].H, c[n].I, c[n].E, c[n].K) == (7168, 2048, 32, 8)
+    assert c["dsv3_fp8_t128"].seed == c["dsv3_fp8_t16384"].seed      # one weight set for the sweep
+
+
+def test_routing_is_deterministic_distinct_and_normalised():
+    cfg = wl.CONFIGS["dsv3_bf16"].with_(T=512)
+    a = wl.routing(cfg)
+    b = wl.routing(cfg)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    ids, w = a[0].numpy(), a[1].numpy()
+    assert ids.dtype == np.int32 and w.dtype == np.float32
+    for row in ids:
+        assert len(set(row.tolist())) == cfg.K
+    assert np.all((ids >= 0) & (ids < cfg.E))
+    np.testing.assert_allclose(w.sum(1), 1.0, rtol=1e-6)
+    assert np.all(np.diff(w, axis=1) <= 0)                      # descending score order
+
+
+def test_bias_skews_routing():
+    skew = np.bincount(wl.routing(wl.CONFIGS["dsv3_bf16"])[0].numpy().ravel(), minlength=32)
+    flat = np.bincount(wl.routing(wl.CONFIGS["dsv3_int8"].with_(T=4096))[0].numpy().ravel(), minlength=32)
+    assert skew.max() / skew.min() > 3 * flat.max() / flat.min()
+
+
+def test_masked_routes():
+    cfg = wl.CONFIGS["tiny_bf16"].with_(masked_ratio=0.25)
+    ids, w = (t.numpy() for t in wl.routing(cfg))
+    m = ids < 0
+    assert 0.1 < m.mean() < 0.4
+    assert np.all(w[m] == 0)
+
+
+def test_tokens_and_weights():
+    cfg = wl.CONFIGS["tiny_bf16"]
+    x = wl.tokens(cfg)
+    assert x.dtype == torch.bfloat16 and x.shape == (cfg.T, cfg.H)
+    assert torch.equal(x, wl.tokens(cfg))
+    assert abs(x.float().std().item() - 1.0) < 0.05
+    w1, w2, s1, s2 = wl.expert_weights(cfg, 3)
+    assert w1.shape == (cfg.H, 2 * cfg.I) and w2.shape == (cfg.I, cfg.H) and s1 is None
+    assert abs(w1.float().std().item() * np.sqrt(cfg.H) - 1.0) < 0.05
+    assert abs(w2.float().std().item() * np.sqrt(cfg.I) - 1.0) < 0.05
+
+
+def test_quantised_weights_per_channel():
+    for uc, qmax in (("int8", 127), ("fp8", 448)):
+        cfg = wl.CONFIGS["tiny_bf16"].with_(usecase=uc)
+        q, _, s, _ = wl.expert_weights(cfg, 1)
+        qv = q.float()
+        assert torch.all(qv.abs().amax(0) == qmax)            # one element per channel hits Qmax
+        w1, _ = wl.expert_weights_f32(cfg, 1)
+        assert torch.allclose(qv * s[None, :], w1, rtol=0.07, atol=float(s.max()) * 0.51)
