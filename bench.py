@@ -1,0 +1,202 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed-expert path on one MI355X.
+
+One step = one ``mega_moe`` call (dispatch -> Linear1 + SwiGLU -> Linear2 ->
+combine) over one batch of seeded synthetic inputs already resident in HBM.
+The default workload is the mid-size bf16 layer (T=2048, hidden=4096,
+intermediate=1408, 16 experts, top-4).
+
+Prints one JSON line: throughput in TFLOP/s (FLOP = 6 * routes * hidden *
+intermediate), the roofline of the dominant kernel (Linear1, timed with HIP
+events on its stream inside the timed region) and the CPU oracle timed on
+a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "routed expert-FFN TFLOP/s and tokens/s per MoE layer; % MFMA / HBM roofline"
+PEAK = {  # MI355X published dense peaks
+    "bf16": 2500e12, "fp8": 5000e12, "int8": 5000e12, "hbm": 8.0e12,
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mid_bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU oracle time")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run one plain 1 GiB device copy (counter calibration) and exit")
+    return ap.parse_args()
+
+
+def algorithmic(cfg, counts):
+    """FLOP and minimal HBM bytes of one step and of Linear1 (see the design notes)."""
+    import numpy as np
+    R = int(np.sum(counts))
+    active = int(np.sum(np.asarray(counts) > 0))
+    b = 2 if cfg.usecase == "bf16" else 1
+    H, I = cfg.H, cfg.I
+    flop = 6.0 * R * H * I
+    l1_flop = 4.0 * R * H * I
+    w1 = active * H * 2 * I * b
+    w2 = active * I * H * b
+    scales = (active * (2 * I + H) * 4) if cfg.usecase != "bf16" else 0
+    step_bytes = w1 + w2 + scales + cfg.T * H * 2 + cfg.T * H * 2 + 8 * cfg.T * cfg.K
+    # Linear1 moves its weights, reads the pool rows and writes A once
+    l1_bytes = w1 + R * H * b + R * I * b + (active * 2 * I * 4 if cfg.usecase != "bf16" else 0)
+    return dict(R=R, flop=flop, l1_flop=l1_flop, step_bytes=step_bytes, l1_bytes=l1_bytes)
+
+
+def cpu_baseline(inp, target_s):
+    """The oracle, as it stands, on a bounded token sample of the workload."""
+    import numpy as np
+    import oracle
+    from threadpoolctl import threadpool_info
+    cfg = inp.cfg
+    w = inp.weights
+
+    def expert(e):
+        w1, w2 = w.w1[e], w.w2[e]
+        if cfg.usecase == "fp8":
+            w1, w2 = w1.view(__import__("torch").uint8), w2.view(__import__("torch").uint8)
+        elif cfg.usecase == "bf16":
+            w1, w2 = w1.float(), w2.float()
+        return (w1.numpy(), w2.numpy(), None if w.s1 is None else w.s1[e].numpy(),
+                None if w.s2 is None else w.s2[e].numpy())
+
+    x = inp.x.float().numpy()
+    ids = inp.topk_ids.numpy()
+    g = inp.topk_weights.numpy()
+    rng = np.random.default_rng(0)
+    n = min(cfg.T, 16)
+    elapsed = 0.0
+    while True:
+        toks = np.sort(rng.choice(cfg.T, n, replace=False))
+        t0 = time.perf_counter()
+        oracle.moe_forward(x, ids, g, expert, cfg.usecase, tokens=toks)
+        elapsed = time.perf_counter() - t0
+        if elapsed >= target_s / 4 or n >= cfg.T:
+            break
+        n = min(cfg.T, max(n * 2, int(n * target_s / max(elapsed, 1e-3) / 2)))
+    R = int(np.sum(ids[toks] >= 0))
+    flop = 6.0 * R * cfg.H * cfg.I
+    threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+    return {"value": flop / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} of {cfg.T} tokens ({R} routes), float64 numpy/BLAS, {elapsed:.1f} s",
+            "tokens_per_s": n / elapsed}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (the expert path here "
+              f"runs with all experts local on a single MI355X).", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from mixture_experts_expert_mm_amd import binding as B
+    from mixture_experts_expert_mm_amd import moe
+    from mixture_experts_expert_mm_amd import workloads as wl
+
+    B.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        a.fill_(1)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": 1 << 30}))
+        return
+
+    cfg = wl.CONFIGS[args.workload]
+    inp = wl.make_inputs(cfg)
+    layer = moe.ExpertLayer(cfg.T, cfg.H, cfg.I, cfg.E, cfg.K, cfg.usecase, "bf16", dev)
+    layer.load_weights(inp.weights.w1, inp.weights.w2, inp.weights.s1, inp.weights.s2)
+    x, ids, wts = inp.x.to(dev), inp.topk_ids.to(dev), inp.topk_weights.to(dev)
+    y = layer.new_y()
+    counts = torch.empty(cfg.E, dtype=torch.int32, device=dev)
+    layer.workspace(True)
+    stream = torch.cuda.current_stream(dev)
+
+    for _ in range(args.warmup):
+        layer.forward(x, ids, wts, y, counts)
+    torch.cuda.synchronize()
+
+    B.mm_trace_enable(True)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        layer.forward(x, ids, wts, y, counts)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    B.mm_trace_enable(False)
+    trace = B.mm_trace_collect()
+    gpu_ms = ev0.elapsed_time(ev1)
+    ms_per_step = gpu_ms / args.steps
+
+    al = algorithmic(cfg, counts.cpu().numpy())
+    tflops = al["flop"] / (ms_per_step * 1e-3) / 1e12
+    n_l1, t_l1 = trace["l1_swiglu"]
+    l1_ms = t_l1 / max(n_l1, 1)
+    peak_mfma = PEAK[cfg.usecase]
+    mfma_bound = al["l1_flop"] / al["l1_bytes"] > peak_mfma / PEAK["hbm"]
+    if mfma_bound:
+        ach = al["l1_flop"] / (l1_ms * 1e-3)
+        roof = {"bound": "mfma", "achieved": ach / 1e12, "peak": peak_mfma / 1e12, "unit": "TFLOP/s",
+                "frac": ach / peak_mfma, "traffic": None}
+    else:
+        ach = al["l1_bytes"] / (l1_ms * 1e-3)
+        roof = {"bound": "hbm", "achieved": ach / 1e9, "peak": PEAK["hbm"] / 1e9, "unit": "GB/s",
+                "frac": ach / PEAK["hbm"], "traffic": None}
+    roof["kernel"] = "l1_swiglu (Linear1 grouped GEMM + SwiGLU)"
+    roof["kernel_ms"] = l1_ms
+
+    out = {
+        "metric": METRIC,
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"bf16": "bf16", "fp8": "fp8_e4m3", "int8": "int8"}[cfg.usecase],
+        "data": "synthetic (seeded randn tokens and weights, top-k of randn router scores)",
+        "config": {"workload": cfg.name, "tokens": cfg.T, "hidden": cfg.H, "intermediate_hidden": cfg.I,
+                   "num_experts": cfg.E, "topk": cfg.K, "usecase": cfg.usecase, "parallelism": "none (1 GPU, all experts local)"},
+        "tokens_per_s": cfg.T / (ms_per_step * 1e-3),
+        "hbm_frac_step": al["step_bytes"] / (ms_per_step * 1e-3) / PEAK["hbm"],
+        "mfma_frac_step": al["flop"] / (ms_per_step * 1e-3) / peak_mfma,
+        "wall_s_timed": wall,
+        "kernels_ms_per_step": {k: v[1] / args.steps for k, v in trace.items() if v[0]},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

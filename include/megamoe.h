@@ -1,0 +1,256 @@
+/*
+ * megamoe.h -- C ABI of the MI355X (gfx950) routed-expert path.
+ *
+ * The library computes, on one GPU with every expert local, the fused
+ * Mega-MoE expert path defined on the Ascend CANN "mega_moe" operator page
+ * (Formula; Computation Process): EP Dispatch -> Linear1 -> SwiGLU ->
+ * Linear2 -> Token Combine,
+ *
+ *     y_i = sum_k G[i,k] * ( SwiGLU( x_i . W1[E[i,k]] ) . W2[E[i,k]] ),
+ *     SwiGLU(h) = SiLU(h[:, :I]) * h[:, I:],  SiLU(z) = z / (1 + e^-z),
+ *
+ * with the dispatch metadata of the DeepEP "Metadata System" notes (Count ->
+ * Prefix Sum -> Scatter into a BLOCK_M-padded pool that keeps the
+ * (token, top-k slot) identity of every row, sections 1, 3 and 4).
+ *
+ * Symbols: T = num_tokens, H = hidden, I = intermediate_hidden,
+ * E = num_experts, K = num_topk, P = plan.pool_rows.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers marked "device" point to device memory on the current HIP
+ *   device; the caller allocates and owns every buffer, including the
+ *   workspace.  The library never allocates, frees or synchronises device
+ *   memory and never reads device data on the host.
+ * - Every compute entry point is asynchronous on `stream` (a hipStream_t
+ *   passed as void*; NULL = the null stream).  A return of MM_OK means the
+ *   kernels were enqueued; their errors surface on the stream.
+ * - All tensors are dense, contiguous and row-major.
+ * - Argument checks happen on the host before any HIP call: a NULL
+ *   pointer, a misaligned pointer (every pointer must be 16-byte aligned)
+ *   or a plan whose checksum does not match returns MM_ERR_INVALID_ARG and
+ *   enqueues nothing.
+ * - Route ids (topk_ids) must be in [0, E) and distinct within a token, as
+ *   the Parameters table of the operator page requires; an id < 0 marks a
+ *   masked route (DeepEP notes, section 5.2): it is skipped, counted for no
+ *   expert and contributes 0.  Ids >= E or duplicated ids are not detected
+ *   on the device and give undefined results.
+ * - Workspace counters are reset by the library at the start of every
+ *   call; the caller never clears them.
+ * - Calls that share a workspace or intermediate buffers must be ordered
+ *   on one stream; overlapping calls on the same buffers race.
+ * - Results are deterministic: the top-k sum runs in slot order k = 0..K-1
+ *   in float32 (operator page, "Deterministic Computation").
+ */
+#ifndef MEGAMOE_H
+#define MEGAMOE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mm_status {
+  MM_OK = 0,
+  MM_ERR_INVALID_ARG = 1, /* NULL / misaligned pointer, bad dimension, bad plan */
+  MM_ERR_UNSUPPORTED = 2, /* use case or output dtype not supported */
+  MM_ERR_WORKSPACE = 3,   /* workspace smaller than the plan requires */
+  MM_ERR_HIP = 4          /* a HIP launch or event call failed */
+} mm_status;
+
+/* Use cases of the operator page's use-case table (Computation Process).
+ * A16W16: bf16 activations and weights.
+ * A8W8_FP8: OCP float8 e4m3fn activations and weights with float32 scales
+ *   (per-token for X, per output channel for W, per row for the SwiGLU
+ *   output), by the A8W8 formulas with Qmax = 448.
+ * A8W8_INT8: symmetric int8 in [-127, 127] with the same scales, Qmax = 127,
+ *   exact int32 accumulation. */
+typedef enum mm_usecase { MM_A16W16 = 0, MM_A8W8_FP8 = 1, MM_A8W8_INT8 = 2 } mm_usecase;
+
+/* dtype of y: bf16 (the operator's output dtype) or float32 (the same
+ * float32 value before its final round-to-nearest-even to bf16). */
+typedef enum mm_out_dtype { MM_OUT_BF16 = 0, MM_OUT_F32 = 1 } mm_out_dtype;
+
+typedef struct mm_problem {
+  int64_t num_tokens;          /* T >= 1 */
+  int64_t hidden;              /* H, multiple of 256 */
+  int64_t intermediate_hidden; /* I, multiple of 128 */
+  int64_t num_experts;         /* E in [1, 1024] */
+  int64_t num_topk;            /* K in [1, min(E, 64)] */
+  int32_t usecase;             /* mm_usecase */
+  int32_t y_dtype;             /* mm_out_dtype */
+} mm_problem;
+
+/* A plan is plain host data filled by mm_plan_create.  Callers read the
+ * sizes from it and pass it back unchanged to every entry point. */
+typedef struct mm_plan {
+  mm_problem prob;
+  int32_t block_m;            /* BLOCK_M: pool rows per expert are padded to a multiple */
+  int32_t tile_l1;            /* internal tile configuration of Linear1 */
+  int32_t tile_l2;            /* internal tile configuration of Linear2 */
+  int32_t gate_up_group;      /* gate/up interleave group of the prepared W1 */
+  int64_t pool_rows;          /* P = capacity of the padded pool, a multiple of block_m */
+  int64_t x_pool_bytes;       /* P * H * elem(usecase) */
+  int64_t a_pool_bytes;       /* P * I * elem(usecase) */
+  int64_t w1_bytes;           /* E * H * 2I * elem(usecase) (formula and prepared) */
+  int64_t w2_bytes;           /* E * I * H * elem(usecase) */
+  int64_t workspace_bytes;    /* scratch of the three-call path */
+  int64_t fused_workspace_bytes; /* scratch of mega_moe (holds the pool too) */
+  uint64_t checksum;          /* guards against a modified plan */
+  int64_t reserved[8];
+} mm_plan;
+
+/* Elements: bf16 = 2 bytes, e4m3fn / int8 = 1 byte. */
+
+/*
+ * mm_plan_create -- validate a problem and choose BLOCK_M and tiles.
+ * Host only, no HIP call.  BLOCK_M follows the expected rows per expert,
+ * T*K/E (DeepGEMM MegaMoE page, section 3.3 shape heuristic): small loads
+ * take a small BLOCK_M.  P = T*K + E*(BLOCK_M-1) rounded up to BLOCK_M,
+ * enough for any routing.
+ * Errors: MM_ERR_INVALID_ARG for NULL pointers or dimensions outside the
+ * ranges stated in mm_problem; MM_ERR_UNSUPPORTED for an unknown use case
+ * or output dtype.
+ */
+mm_status mm_plan_create(const mm_problem* problem, mm_plan* plan);
+
+/*
+ * mm_prepare_weights -- one-time relayout of the expert weights into the
+ * layout the GEMM kernels stream (DeepGEMM MegaMoE page, section 3.2: done
+ * once by the caller before repeated launches; not part of the timed path).
+ *   w1     device [E][H][2I]  formula layout of the operator page (Formula)
+ *   w2     device [E][I][H]   formula layout
+ *   w1_out device [E][2I][H]  K-contiguous rows; row n of expert e holds the
+ *                             W1 column c(n) with gate and up columns
+ *                             interleaved in groups of g = gate_up_group:
+ *                             c(n) = (n/2g)*g + n%g            if n%2g <  g
+ *                                    I + (n/2g)*g + n%g - g    otherwise
+ *   w2_out device [E][H][I]   K-contiguous (transposed)
+ * Scales stay in formula layout ([E][2I] and [E][H]).  Buffers must not
+ * overlap.
+ */
+mm_status mm_prepare_weights(const mm_plan* plan, const void* w1, const void* w2,
+                             void* w1_out, void* w2_out, void* stream);
+
+/*
+ * mm_dispatch_layout -- EP Dispatch: steps route read, count, claim +
+ * prefix, scatter + gather, and (A8W8) per-token activation quantisation.
+ * Operator page, Computation Process, EP Dispatch (and for A8W8 the
+ * quantisation "before Dispatch": s_i = max|X[i,:]|/Qmax, q_i = round(X[i,:]/s_i));
+ * DeepEP notes sections 3.2-3.5 (count in LDS, one claim atomic, scatter,
+ * pool block offsets).
+ *   topk_ids       device int32 [T][K]
+ *   x              device bf16  [T][H]
+ *   expert_counts  device int32 [E]    out: N_e (the operator's expert_token_nums)
+ *   expert_offsets device int32 [E+1]  out: padded exclusive prefix,
+ *                                      off[e+1] = off[e] + BLOCK_M*ceil(N_e/BLOCK_M)
+ *   pool_src       device int32 [P]    out: i*K+k of pool row p, -1 on padding
+ *   route_to_pool  device int32 [T*K]  out: pool row of route i*K+k, -1 if masked
+ *   x_pool         device [P][H]       out: row p = x_i (bf16) or q_i (A8W8);
+ *                                      padding rows are unspecified
+ *   x_pool_scale   device f32 [P]      out: s_i of row p (A8W8); may be NULL for A16W16
+ *   workspace      device, plan.workspace_bytes
+ * The order of the rows of one expert inside its pool range is unspecified
+ * (the operator page stacks them "in any fixed order").
+ */
+mm_status mm_dispatch_layout(const mm_plan* plan, const int32_t* topk_ids, const void* x,
+                             int32_t* expert_counts, int32_t* expert_offsets,
+                             int32_t* pool_src, int32_t* route_to_pool,
+                             void* x_pool, float* x_pool_scale,
+                             void* workspace, uint64_t workspace_bytes, void* stream);
+
+/*
+ * mm_grouped_l1_swiglu -- Linear1 per expert + SwiGLU (+ A8W8 row requant).
+ * Operator page, Expert Compute steps 1-2: H_e = X_e . W1[e] (A8W8:
+ * C = Q_e . W1q[e] in int32 / fp32, H_e = (C * s^W1_e) * s^X_e), then
+ * A_e = SiLU(H_e[:, :I]) * H_e[:, I:]; for A8W8 step 3's requantisation
+ * s^A_i = max|A_e[i,:]|/Qmax, A^q = round(A_e / s^A_i).
+ *   expert_offsets, expert_counts  as written by mm_dispatch_layout
+ *   x_pool, x_pool_scale           as written by mm_dispatch_layout
+ *   w1        device, prepared by mm_prepare_weights
+ *   w1_scale  device f32 [E][2I] formula order (A8W8), NULL for A16W16
+ *   a_pool    device [P][I] out: bf16 A (A16W16) or its int8 / e4m3 codes
+ *   a_pool_scale device f32 [P] out: s^A (A8W8), may be NULL for A16W16
+ */
+mm_status mm_grouped_l1_swiglu(const mm_plan* plan, const int32_t* expert_offsets,
+                               const int32_t* expert_counts, const void* x_pool,
+                               const float* x_pool_scale, const void* w1, const float* w1_scale,
+                               void* a_pool, float* a_pool_scale,
+                               void* workspace, uint64_t workspace_bytes, void* stream);
+
+/*
+ * mm_grouped_l2_combine -- Linear2 per expert, gate weighting, Token Combine.
+ * Operator page, Expert Compute step 3 (Y_e = A_e . W2[e]; A8W8:
+ * Y_e = (D * s^W2_e) * s^A_e) and Token Combine
+ * (y_i = sum_k G[i,k] * Y_{e_ik}[row(i,k)], stacked in token order).  Each
+ * weighted contribution is kept in float32 and the K of a token are summed
+ * in slot order.
+ *   pool_src, route_to_pool        as written by mm_dispatch_layout
+ *   a_pool, a_pool_scale           as written by mm_grouped_l1_swiglu
+ *   w2        device, prepared by mm_prepare_weights
+ *   w2_scale  device f32 [E][H] (A8W8), NULL for A16W16
+ *   topk_weights device f32 [T][K]
+ *   y         device [T][H] out, bf16 or f32 per plan.prob.y_dtype
+ */
+mm_status mm_grouped_l2_combine(const mm_plan* plan, const int32_t* expert_offsets,
+                                const int32_t* expert_counts, const int32_t* pool_src,
+                                const int32_t* route_to_pool, const void* a_pool,
+                                const float* a_pool_scale, const void* w2, const float* w2_scale,
+                                const float* topk_weights, void* y,
+                                void* workspace, uint64_t workspace_bytes, void* stream);
+
+/*
+ * mega_moe -- the whole path in one call: Dispatch, Linear1, SwiGLU,
+ * Linear2, Combine (operator page, Function and Prototype: returns y and
+ * expert_token_nums).  Every intermediate lives in the workspace.
+ *   x              device bf16 [T][H]
+ *   topk_ids       device int32 [T][K]
+ *   topk_weights   device f32 [T][K]
+ *   w1, w2         device, prepared by mm_prepare_weights
+ *   w1_scale, w2_scale  device f32 (A8W8) or NULL (A16W16)
+ *   y              device [T][H] out (bf16 or f32 per plan)
+ *   expert_token_nums device int32 [E] out: N_e
+ *   workspace      device, plan.fused_workspace_bytes
+ */
+mm_status mega_moe(const mm_plan* plan, const void* x, const int32_t* topk_ids,
+                   const float* topk_weights, const void* w1, const float* w1_scale,
+                   const void* w2, const float* w2_scale, void* y, int32_t* expert_token_nums,
+                   void* workspace, uint64_t workspace_bytes, void* stream);
+
+/*
+ * mm_debug_raw_accumulators -- the integer GEMM accumulators before any
+ * scaling, for checking that the A8W8-INT products are exact (operator
+ * page, A8W8-INT: C = Q_e . W1[e] and D = A^int8 . W2[e] in Z_32).
+ * Runs the same mainloop as the entry points with an epilogue that stores
+ * the raw int32 accumulators (A8W8_INT8 plans only).
+ *   which = 1: c_out int32 [P][2I], column order of the formula (gate then up),
+ *              from x_pool and the prepared w1;
+ *   which = 2: c_out int32 [P][H] from a_pool and the prepared w2.
+ * Padding rows of c_out are unspecified.
+ */
+mm_status mm_debug_raw_accumulators(const mm_plan* plan, int which, const int32_t* expert_offsets,
+                                    const int32_t* expert_counts, const void* act_pool,
+                                    const void* w_prepared, int32_t* c_out, void* stream);
+
+/* Kernel timing (diagnostics).  While enabled, every kernel the library
+ * launches is bracketed by two HIP events on its stream; mm_trace_collect
+ * waits for them and returns, per kernel id, the number of launches and
+ * the summed duration in milliseconds, then clears the record. */
+typedef enum mm_kernel_id {
+  MM_K_ZERO = 0, MM_K_COUNT = 1, MM_K_SCATTER = 2, MM_K_GATHER = 3,
+  MM_K_L1 = 4, MM_K_REQUANT = 5, MM_K_L2 = 6, MM_K_COMBINE = 7, MM_K_PREPARE = 8,
+  MM_K_COUNT_IDS = 9
+} mm_kernel_id;
+
+mm_status mm_trace_enable(int on);
+mm_status mm_trace_collect(int32_t* launches /* [MM_K_COUNT_IDS] */,
+                           double* total_ms /* [MM_K_COUNT_IDS] */);
+const char* mm_kernel_name(int kernel_id);
+
+const char* mm_status_string(mm_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MEGAMOE_H */

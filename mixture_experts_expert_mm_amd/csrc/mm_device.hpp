@@ -1,0 +1,118 @@
+// Device helpers for gfx950 (CDNA4): vector types, MFMA wrappers, number
+// format conversions and wavefront primitives.  Wave size is 64.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mm {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+enum Usecase : int { UC_BF16 = 0, UC_FP8 = 1, UC_I8 = 2 };
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// number formats
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// round-to-nearest-even float -> bf16 (v_cvt_pk_bf16_f32 on gfx950)
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+}
+
+// OCP e4m3fn, saturating to +-448, round-to-nearest-even.  The hardware
+// conversion rounds to nearest even; the clamp makes the saturation explicit.
+__device__ __forceinline__ uint32_t f32x2_to_e4m3x2(float a, float b) {
+  a = fminf(fmaxf(a, -448.0f), 448.0f);
+  b = fminf(fmaxf(b, -448.0f), 448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xffffu;
+}
+
+// symmetric int8: round half to even, clamp to [-127, 127]
+__device__ __forceinline__ int32_t f32_to_i8sym(float v) {
+  float r = __builtin_rintf(v);
+  r = fminf(fmaxf(r, -127.0f), 127.0f);
+  return (int32_t)r;
+}
+
+__device__ __forceinline__ float silu(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
+
+// ---------------------------------------------------------------------------
+// wavefront primitives
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  const int l = lane_id();
+  return l == 0 ? 0ull : (~0ull >> (64 - l));
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_max(T v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    T w = __shfl_xor(v, o, 64);
+    v = v > w ? v : w;
+  }
+  return v;
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// MFMA: one 32x32 output block, one K-step.  Each lane supplies 16 bytes
+// (bf16 x8, int8 x16) or 32 bytes (e4m3 x32) of its A row and B column.
+// A row  = lane % 32, B column = lane % 32; the two lane halves supply two
+// disjoint K ranges, the same ones for A and B.
+// Accumulator element i of lane l is C[8*(i/4) + 4*(l/32) + i%4][l%32].
+// ---------------------------------------------------------------------------
+
+template <int UC> struct Acc;
+template <> struct Acc<UC_BF16> { typedef f32x16 type; };
+template <> struct Acc<UC_FP8> { typedef f32x16 type; };
+template <> struct Acc<UC_I8> { typedef i32x16 type; };
+
+__device__ __forceinline__ void mfma_bf16(f32x16& c, const uint4& a, const uint4& b) {
+  c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ void mfma_i8(i32x16& c, const uint4& a, const uint4& b) {
+  c = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, a), __builtin_bit_cast(i32x4, b), c, 0, 0, 0);
+}
+
+// e4m3 x e4m3 with unit block scales (E8M0 127 = 2^0)
+__device__ __forceinline__ void mfma_fp8(f32x16& c, const uint4& a0, const uint4& a1, const uint4& b0, const uint4& b1) {
+  i32x8 a, b;
+  a[0] = a0.x; a[1] = a0.y; a[2] = a0.z; a[3] = a0.w; a[4] = a1.x; a[5] = a1.y; a[6] = a1.z; a[7] = a1.w;
+  b[0] = b0.x; b[1] = b0.y; b[2] = b0.z; b[3] = b0.w; b[4] = b1.x; b[5] = b1.y; b[6] = b1.z; b[7] = b1.w;
+  c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+__device__ __forceinline__ float acc_to_f32(float v) { return v; }
+__device__ __forceinline__ float acc_to_f32(int v) { return (float)v; }
+
+}  // namespace mm

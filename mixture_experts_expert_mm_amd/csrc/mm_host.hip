@@ -1,0 +1,464 @@
+// C-ABI host side: plan, argument validation, workspace carve-up, launches,
+// kernel timing.  No entry point allocates, frees or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "mm_internal.hpp"
+
+using namespace mm;
+
+namespace {
+
+constexpr int64_t kAlign = 256;
+
+inline int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+
+int elem_size(int usecase) { return usecase == MM_A16W16 ? 2 : 1; }
+
+uint64_t plan_checksum(const mm_plan* p) {
+  // FNV-1a over every field except the checksum itself
+  const uint8_t* b = reinterpret_cast<const uint8_t*>(p);
+  const size_t n = offsetof(mm_plan, checksum);
+  uint64_t h = 1469598103934665603ull;
+  for (size_t i = 0; i < n; ++i) {
+    h ^= b[i];
+    h *= 1099511628211ull;
+  }
+  return h ^ 0x6d65676d6f65ull;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// ---------------------------------------------------------------- workspace
+struct WsLayout {
+  int64_t wave_base, a_amax, a_stage, contrib, end;                          // 3-call scratch
+  int64_t offsets, pool_src, route_to_pool, x_pool, x_pool_scale, a_pool, a_pool_scale, fused_end;
+};
+
+WsLayout ws_layout(const mm_plan& pl) {
+  const mm_problem& p = pl.prob;
+  const bool q = p.usecase != MM_A16W16;
+  const int64_t P = pl.pool_rows, R = p.num_tokens * p.num_topk;
+  WsLayout L{};
+  int64_t o = 0;
+  auto take = [&](int64_t bytes) { const int64_t at = o; o = align_up(o + bytes, kAlign); return at; };
+  L.wave_base = take(dispatch_waves(p.num_tokens, (int)p.num_topk) * p.num_experts * 4);
+  L.a_amax = q ? take(P * 4) : -1;
+  L.a_stage = q ? take(P * p.intermediate_hidden * 4) : -1;
+  L.contrib = take(R * p.hidden * 4);
+  L.end = o;
+  L.offsets = take((p.num_experts + 1) * 4);
+  L.pool_src = take(P * 4);
+  L.route_to_pool = take(R * 4);
+  L.x_pool = take(pl.x_pool_bytes);
+  L.x_pool_scale = take(P * 4);
+  L.a_pool = take(pl.a_pool_bytes);
+  L.a_pool_scale = take(P * 4);
+  L.fused_end = o;
+  return L;
+}
+
+template <typename T>
+T* at(void* ws, int64_t off) {
+  return off < 0 ? nullptr : reinterpret_cast<T*>(static_cast<uint8_t*>(ws) + off);
+}
+
+int num_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// ---------------------------------------------------------------- tracing
+struct TraceRec {
+  int id;
+  hipEvent_t a, b;
+};
+std::mutex g_trace_mu;
+bool g_trace_on = false;
+std::vector<TraceRec> g_trace;
+std::vector<hipEvent_t> g_event_pool;
+
+hipEvent_t get_event() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Launch wrapper: brackets the launch with events when tracing is on.
+template <typename F>
+mm_status run(int id, hipStream_t s, F&& f) {
+  TraceRec rec{id, nullptr, nullptr};
+  bool tr = false;
+  {
+    std::lock_guard<std::mutex> g(g_trace_mu);
+    if (g_trace_on) {
+      rec.a = get_event();
+      rec.b = get_event();
+      tr = rec.a && rec.b;
+    }
+  }
+  if (tr && hipEventRecord(rec.a, s) != hipSuccess) return MM_ERR_HIP;
+  if (f() != hipSuccess) return MM_ERR_HIP;
+  if (tr) {
+    if (hipEventRecord(rec.b, s) != hipSuccess) return MM_ERR_HIP;
+    std::lock_guard<std::mutex> g(g_trace_mu);
+    g_trace.push_back(rec);
+  }
+  return MM_OK;
+}
+
+#define MM_TRY(x)                   \
+  do {                              \
+    const mm_status st__ = (x);     \
+    if (st__ != MM_OK) return st__; \
+  } while (0)
+
+mm_status check_plan(const mm_plan* pl) {
+  if (!pl) return MM_ERR_INVALID_ARG;
+  if (pl->checksum != plan_checksum(pl)) return MM_ERR_INVALID_ARG;
+  return MM_OK;
+}
+
+// ---------------------------------------------------------------- stages
+mm_status do_dispatch(const mm_plan& pl, const int32_t* ids, const void* x, int32_t* counts, int32_t* offsets,
+                      int32_t* pool_src, int32_t* r2p, void* x_pool, float* x_pool_scale, void* ws, hipStream_t s) {
+  const mm_problem& p = pl.prob;
+  const WsLayout L = ws_layout(pl);
+  DispatchArgs d{};
+  d.topk_ids = ids;
+  d.x = x;
+  d.counts = counts;
+  d.offsets = offsets;
+  d.pool_src = pool_src;
+  d.route_to_pool = r2p;
+  d.x_pool = x_pool;
+  d.x_pool_scale = x_pool_scale;
+  d.wave_base = at<int32_t>(ws, L.wave_base);
+  d.T = p.num_tokens;
+  d.H = p.hidden;
+  d.P = pl.pool_rows;
+  d.E = (int)p.num_experts;
+  d.K = (int)p.num_topk;
+  d.block_m = pl.block_m;
+  d.usecase = p.usecase;
+  MM_TRY(run(MM_K_ZERO, s, [&] { return launch_zero(counts, d.E, nullptr, 0, s); }));
+  MM_TRY(run(MM_K_COUNT, s, [&] { return launch_count(d, s); }));
+  MM_TRY(run(MM_K_SCATTER, s, [&] { return launch_scatter(d, s); }));
+  MM_TRY(run(MM_K_GATHER, s, [&] { return launch_gather(d, s); }));
+  return MM_OK;
+}
+
+mm_status do_l1(const mm_plan& pl, const int32_t* offsets, const int32_t* counts, const void* x_pool,
+                const float* x_pool_scale, const void* w1, const float* w1_scale, void* a_pool, float* a_pool_scale,
+                void* ws, hipStream_t s) {
+  const mm_problem& p = pl.prob;
+  const WsLayout L = ws_layout(pl);
+  GemmArgs g{};
+  g.A = static_cast<const uint8_t*>(x_pool);
+  g.B = static_cast<const uint8_t*>(w1);
+  g.offsets = offsets;
+  g.counts = counts;
+  g.P = pl.pool_rows;
+  g.E = (int)p.num_experts;
+  g.N = (int)(2 * p.intermediate_hidden);
+  g.Kdim = (int)p.hidden;
+  g.I = (int)p.intermediate_hidden;
+  g.H = (int)p.hidden;
+  g.K = (int)p.num_topk;
+  g.gate_up_group = pl.gate_up_group;
+  g.x_scale = x_pool_scale;
+  g.w_scale = w1_scale;
+  g.a_out = a_pool;
+  g.a_stage = at<float>(ws, L.a_stage);
+  g.a_amax = at<uint32_t>(ws, L.a_amax);
+  const int grid = gemm_grid(pl.tile_l1, pl.pool_rows, g.N, num_cus());
+  if (p.usecase != MM_A16W16)
+    MM_TRY(run(MM_K_ZERO, s, [&] { return launch_zero(nullptr, 0, g.a_amax, pl.pool_rows, s); }));
+  MM_TRY(run(MM_K_L1, s, [&] { return launch_gemm(0, p.usecase, pl.tile_l1, g, grid, s); }));
+  if (p.usecase != MM_A16W16) {
+    RequantArgs r{};
+    r.a_stage = g.a_stage;
+    r.a_amax = g.a_amax;
+    r.offsets = offsets;
+    r.counts = counts;
+    r.E = g.E;
+    r.a_pool = a_pool;
+    r.a_scale = a_pool_scale;
+    r.P = pl.pool_rows;
+    r.I = g.I;
+    r.usecase = p.usecase;
+    MM_TRY(run(MM_K_REQUANT, s, [&] { return launch_requant(r, s); }));
+  }
+  return MM_OK;
+}
+
+mm_status do_l2(const mm_plan& pl, const int32_t* offsets, const int32_t* counts, const int32_t* pool_src,
+                const int32_t* r2p, const void* a_pool, const float* a_pool_scale, const void* w2,
+                const float* w2_scale, const float* topk_w, void* y, void* ws, hipStream_t s) {
+  const mm_problem& p = pl.prob;
+  const WsLayout L = ws_layout(pl);
+  GemmArgs g{};
+  g.A = static_cast<const uint8_t*>(a_pool);
+  g.B = static_cast<const uint8_t*>(w2);
+  g.offsets = offsets;
+  g.counts = counts;
+  g.pool_src = pool_src;
+  g.P = pl.pool_rows;
+  g.E = (int)p.num_experts;
+  g.N = (int)p.hidden;
+  g.Kdim = (int)p.intermediate_hidden;
+  g.I = (int)p.intermediate_hidden;
+  g.H = (int)p.hidden;
+  g.K = (int)p.num_topk;
+  g.a_scale = a_pool_scale;
+  g.w_scale = w2_scale;
+  g.topk_w = topk_w;
+  g.contrib = at<float>(ws, L.contrib);
+  const int grid = gemm_grid(pl.tile_l2, pl.pool_rows, g.N, num_cus());
+  MM_TRY(run(MM_K_L2, s, [&] { return launch_gemm(1, p.usecase, pl.tile_l2, g, grid, s); }));
+  CombineArgs c{};
+  c.contrib = g.contrib;
+  c.route_to_pool = r2p;
+  c.y = y;
+  c.T = p.num_tokens;
+  c.H = (int)p.hidden;
+  c.K = (int)p.num_topk;
+  c.y_f32 = p.y_dtype == MM_OUT_F32;
+  MM_TRY(run(MM_K_COMBINE, s, [&] { return launch_combine(c, s); }));
+  return MM_OK;
+}
+
+bool ok16(const void* p) { return p && aligned(p, 16); }
+bool ok4(const void* p) { return p && aligned(p, 4); }
+
+}  // namespace
+
+extern "C" {
+
+mm_status mm_plan_create(const mm_problem* problem, mm_plan* plan) {
+  if (!problem || !plan) return MM_ERR_INVALID_ARG;
+  const mm_problem p = *problem;
+  if (p.usecase < MM_A16W16 || p.usecase > MM_A8W8_INT8) return MM_ERR_UNSUPPORTED;
+  if (p.y_dtype != MM_OUT_BF16 && p.y_dtype != MM_OUT_F32) return MM_ERR_UNSUPPORTED;
+  if (p.num_tokens < 1 || p.num_tokens > (1 << 24)) return MM_ERR_INVALID_ARG;
+  if (p.hidden < 256 || p.hidden > 16384 || p.hidden % 256) return MM_ERR_INVALID_ARG;
+  if (p.intermediate_hidden < 128 || p.intermediate_hidden > 16384 || p.intermediate_hidden % 128)
+    return MM_ERR_INVALID_ARG;
+  if (p.num_experts < 1 || p.num_experts > 1024) return MM_ERR_INVALID_ARG;
+  if (p.num_topk < 1 || p.num_topk > 64 || p.num_topk > p.num_experts) return MM_ERR_INVALID_ARG;
+  const int64_t R = p.num_tokens * p.num_topk;
+  if (R > (int64_t)1 << 30) return MM_ERR_INVALID_ARG;
+
+  mm_plan pl;
+  std::memset(&pl, 0, sizeof(pl));
+  pl.prob = p;
+  // BLOCK_M from the expected rows per expert (small loads -> small blocks)
+  const double expected = (double)R / (double)p.num_experts;
+  int tile = expected < 16 ? TILE_M32_N256 : expected < 96 ? TILE_M64_N256 : TILE_M128_N256;
+  pl.tile_l1 = tile;
+  pl.tile_l2 = tile;
+  pl.block_m = tile_bm(tile);
+  pl.gate_up_group = 32;
+  const int64_t P = align_up(R + p.num_experts * (pl.block_m - 1), pl.block_m);
+  if (P > ((int64_t)1 << 31) - 1) return MM_ERR_INVALID_ARG;
+  pl.pool_rows = P;
+  const int es = elem_size(p.usecase);
+  pl.x_pool_bytes = P * p.hidden * es;
+  pl.a_pool_bytes = P * p.intermediate_hidden * es;
+  pl.w1_bytes = p.num_experts * p.hidden * 2 * p.intermediate_hidden * es;
+  pl.w2_bytes = p.num_experts * p.intermediate_hidden * p.hidden * es;
+  const WsLayout L = ws_layout(pl);
+  pl.workspace_bytes = L.end;
+  pl.fused_workspace_bytes = L.fused_end;
+  pl.checksum = plan_checksum(&pl);
+  *plan = pl;
+  return MM_OK;
+}
+
+mm_status mm_prepare_weights(const mm_plan* plan, const void* w1, const void* w2, void* w1_out, void* w2_out,
+                             void* stream) {
+  MM_TRY(check_plan(plan));
+  if (!ok16(w1) || !ok16(w2) || !ok16(w1_out) || !ok16(w2_out)) return MM_ERR_INVALID_ARG;
+  const mm_problem& p = plan->prob;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return run(MM_K_PREPARE, s, [&] {
+    return launch_prepare(w1, w2, w1_out, w2_out, (int)p.num_experts, (int)p.hidden, (int)p.intermediate_hidden,
+                          elem_size(p.usecase), plan->gate_up_group, s);
+  });
+}
+
+mm_status mm_dispatch_layout(const mm_plan* plan, const int32_t* topk_ids, const void* x, int32_t* expert_counts,
+                             int32_t* expert_offsets, int32_t* pool_src, int32_t* route_to_pool, void* x_pool,
+                             float* x_pool_scale, void* workspace, uint64_t workspace_bytes, void* stream) {
+  MM_TRY(check_plan(plan));
+  const bool q = plan->prob.usecase != MM_A16W16;
+  if (!ok4(topk_ids) || !ok16(x) || !ok4(expert_counts) || !ok4(expert_offsets) || !ok4(pool_src) ||
+      !ok4(route_to_pool) || !ok16(x_pool) || !ok16(workspace))
+    return MM_ERR_INVALID_ARG;
+  if (q && !ok4(x_pool_scale)) return MM_ERR_INVALID_ARG;
+  if ((int64_t)workspace_bytes < plan->workspace_bytes) return MM_ERR_WORKSPACE;
+  return do_dispatch(*plan, topk_ids, x, expert_counts, expert_offsets, pool_src, route_to_pool, x_pool,
+                     q ? x_pool_scale : nullptr, workspace, static_cast<hipStream_t>(stream));
+}
+
+mm_status mm_grouped_l1_swiglu(const mm_plan* plan, const int32_t* expert_offsets, const int32_t* expert_counts,
+                               const void* x_pool, const float* x_pool_scale, const void* w1, const float* w1_scale,
+                               void* a_pool, float* a_pool_scale, void* workspace, uint64_t workspace_bytes,
+                               void* stream) {
+  MM_TRY(check_plan(plan));
+  const bool q = plan->prob.usecase != MM_A16W16;
+  if (!ok4(expert_offsets) || !ok4(expert_counts) || !ok16(x_pool) || !ok16(w1) || !ok16(a_pool) ||
+      !ok16(workspace))
+    return MM_ERR_INVALID_ARG;
+  if (q && (!ok4(x_pool_scale) || !ok4(w1_scale) || !ok4(a_pool_scale))) return MM_ERR_INVALID_ARG;
+  if ((int64_t)workspace_bytes < plan->workspace_bytes) return MM_ERR_WORKSPACE;
+  return do_l1(*plan, expert_offsets, expert_counts, x_pool, x_pool_scale, w1, w1_scale, a_pool, a_pool_scale,
+               workspace, static_cast<hipStream_t>(stream));
+}
+
+mm_status mm_grouped_l2_combine(const mm_plan* plan, const int32_t* expert_offsets, const int32_t* expert_counts,
+                                const int32_t* pool_src, const int32_t* route_to_pool, const void* a_pool,
+                                const float* a_pool_scale, const void* w2, const float* w2_scale,
+                                const float* topk_weights, void* y, void* workspace, uint64_t workspace_bytes,
+                                void* stream) {
+  MM_TRY(check_plan(plan));
+  const bool q = plan->prob.usecase != MM_A16W16;
+  if (!ok4(expert_offsets) || !ok4(expert_counts) || !ok4(pool_src) || !ok4(route_to_pool) || !ok16(a_pool) ||
+      !ok16(w2) || !ok4(topk_weights) || !ok16(y) || !ok16(workspace))
+    return MM_ERR_INVALID_ARG;
+  if (q && (!ok4(a_pool_scale) || !ok4(w2_scale))) return MM_ERR_INVALID_ARG;
+  if ((int64_t)workspace_bytes < plan->workspace_bytes) return MM_ERR_WORKSPACE;
+  return do_l2(*plan, expert_offsets, expert_counts, pool_src, route_to_pool, a_pool, a_pool_scale, w2, w2_scale,
+               topk_weights, y, workspace, static_cast<hipStream_t>(stream));
+}
+
+mm_status mega_moe(const mm_plan* plan, const void* x, const int32_t* topk_ids, const float* topk_weights,
+                   const void* w1, const float* w1_scale, const void* w2, const float* w2_scale, void* y,
+                   int32_t* expert_token_nums, void* workspace, uint64_t workspace_bytes, void* stream) {
+  MM_TRY(check_plan(plan));
+  const bool q = plan->prob.usecase != MM_A16W16;
+  if (!ok16(x) || !ok4(topk_ids) || !ok4(topk_weights) || !ok16(w1) || !ok16(w2) || !ok16(y) ||
+      !ok4(expert_token_nums) || !ok16(workspace))
+    return MM_ERR_INVALID_ARG;
+  if (q && (!ok4(w1_scale) || !ok4(w2_scale))) return MM_ERR_INVALID_ARG;
+  if ((int64_t)workspace_bytes < plan->fused_workspace_bytes) return MM_ERR_WORKSPACE;
+  const WsLayout L = ws_layout(*plan);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t* offsets = at<int32_t>(workspace, L.offsets);
+  int32_t* pool_src = at<int32_t>(workspace, L.pool_src);
+  int32_t* r2p = at<int32_t>(workspace, L.route_to_pool);
+  void* x_pool = at<uint8_t>(workspace, L.x_pool);
+  float* xs = q ? at<float>(workspace, L.x_pool_scale) : nullptr;
+  void* a_pool = at<uint8_t>(workspace, L.a_pool);
+  float* as = q ? at<float>(workspace, L.a_pool_scale) : nullptr;
+  MM_TRY(do_dispatch(*plan, topk_ids, x, expert_token_nums, offsets, pool_src, r2p, x_pool, xs, workspace, s));
+  MM_TRY(do_l1(*plan, offsets, expert_token_nums, x_pool, xs, w1, w1_scale, a_pool, as, workspace, s));
+  MM_TRY(do_l2(*plan, offsets, expert_token_nums, pool_src, r2p, a_pool, as, w2, w2_scale, topk_weights, y,
+               workspace, s));
+  return MM_OK;
+}
+
+mm_status mm_debug_raw_accumulators(const mm_plan* plan, int which, const int32_t* expert_offsets,
+                                    const int32_t* expert_counts, const void* act_pool, const void* w_prepared,
+                                    int32_t* c_out, void* stream) {
+  MM_TRY(check_plan(plan));
+  const mm_problem& p = plan->prob;
+  if (p.usecase != MM_A8W8_INT8) return MM_ERR_UNSUPPORTED;
+  if ((which != 1 && which != 2) || !ok4(expert_offsets) || !ok4(expert_counts) || !ok16(act_pool) ||
+      !ok16(w_prepared) || !ok4(c_out))
+    return MM_ERR_INVALID_ARG;
+  GemmArgs g{};
+  g.A = static_cast<const uint8_t*>(act_pool);
+  g.B = static_cast<const uint8_t*>(w_prepared);
+  g.offsets = expert_offsets;
+  g.counts = expert_counts;
+  g.P = plan->pool_rows;
+  g.E = (int)p.num_experts;
+  g.I = (int)p.intermediate_hidden;
+  g.H = (int)p.hidden;
+  g.K = (int)p.num_topk;
+  g.raw_out = c_out;
+  if (which == 1) {
+    g.N = (int)(2 * p.intermediate_hidden);
+    g.Kdim = (int)p.hidden;
+    g.gate_up_group = plan->gate_up_group;
+  } else {
+    g.N = (int)p.hidden;
+    g.Kdim = (int)p.intermediate_hidden;
+    g.gate_up_group = 0;
+  }
+  const int tile = which == 1 ? plan->tile_l1 : plan->tile_l2;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int grid = gemm_grid(tile, plan->pool_rows, g.N, num_cus());
+  return run(which == 1 ? MM_K_L1 : MM_K_L2, s, [&] { return launch_gemm(2, p.usecase, tile, g, grid, s); });
+}
+
+mm_status mm_trace_enable(int on) {
+  std::lock_guard<std::mutex> g(g_trace_mu);
+  g_trace_on = on != 0;
+  return MM_OK;
+}
+
+mm_status mm_trace_collect(int32_t* launches, double* total_ms) {
+  if (!launches || !total_ms) return MM_ERR_INVALID_ARG;
+  std::vector<TraceRec> recs;
+  {
+    std::lock_guard<std::mutex> g(g_trace_mu);
+    recs.swap(g_trace);
+  }
+  for (int i = 0; i < MM_K_COUNT_IDS; ++i) {
+    launches[i] = 0;
+    total_ms[i] = 0.0;
+  }
+  mm_status st = MM_OK;
+  for (const TraceRec& r : recs) {
+    float ms = 0.0f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) {
+      st = MM_ERR_HIP;
+    } else if (r.id >= 0 && r.id < MM_K_COUNT_IDS) {
+      launches[r.id] += 1;
+      total_ms[r.id] += ms;
+    }
+  }
+  std::lock_guard<std::mutex> g(g_trace_mu);
+  for (const TraceRec& r : recs) {
+    g_event_pool.push_back(r.a);
+    g_event_pool.push_back(r.b);
+  }
+  return st;
+}
+
+const char* mm_kernel_name(int id) {
+  static const char* names[] = {"zero", "count", "scatter", "gather", "l1_swiglu", "requant", "l2_gate", "combine", "prepare"};
+  if (id < 0 || id >= MM_K_COUNT_IDS) return "unknown";
+  return names[id];
+}
+
+const char* mm_status_string(mm_status s) {
+  switch (s) {
+    case MM_OK: return "ok";
+    case MM_ERR_INVALID_ARG: return "invalid argument";
+    case MM_ERR_UNSUPPORTED: return "unsupported";
+    case MM_ERR_WORKSPACE: return "workspace too small";
+    case MM_ERR_HIP: return "HIP launch failure";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

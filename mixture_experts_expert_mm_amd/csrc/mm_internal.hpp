@@ -1,0 +1,95 @@
+// Internal interfaces between the C-ABI host code and the kernel launchers.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/megamoe.h"
+
+namespace mm {
+
+// Wavefront-to-route mapping shared by the count and scatter kernels: one
+// wave owns floor(64/K) consecutive tokens (its lanes hold (token, slot)
+// pairs, lane = t*K + k; the remaining lanes idle).
+inline int tokens_per_wave(int K) { return 64 / K; }
+inline int64_t dispatch_waves(int64_t T, int K) { return (T + tokens_per_wave(K) - 1) / tokens_per_wave(K); }
+constexpr int kDispatchWavesPerBlock = 4;
+
+struct DispatchArgs {
+  const int32_t* topk_ids;   // [T][K]
+  const void* x;             // bf16 [T][H]
+  int32_t* counts;           // [E]
+  int32_t* offsets;          // [E+1]
+  int32_t* pool_src;         // [P]
+  int32_t* route_to_pool;    // [T*K]
+  void* x_pool;              // [P][H]
+  float* x_pool_scale;       // [P] (A8W8)
+  int32_t* wave_base;        // ws: [waves][E]
+  int64_t T, H, P;
+  int E, K, block_m, usecase;
+};
+
+// Tile configurations of the grouped GEMMs (compile-time instances).
+enum TileCfg : int {
+  TILE_M32_N256 = 0,   // weight-streaming regime: few rows per expert
+  TILE_M64_N256 = 1,
+  TILE_M128_N256 = 2,  // compute regime
+  TILE_COUNT = 3
+};
+inline int tile_bm(int t) { return t == TILE_M32_N256 ? 32 : t == TILE_M64_N256 ? 64 : 128; }
+constexpr int kTileBN = 256;
+
+struct GemmArgs {
+  const uint8_t* A;          // pool rows [P][Kdim]
+  const uint8_t* B;          // prepared weights [E][N][Kdim]
+  const int32_t* offsets;    // [E+1]
+  const int32_t* counts;     // [E]
+  const int32_t* pool_src;   // [P]
+  int64_t P;                 // pool capacity (rows)
+  int E, N, Kdim, I, H, K;
+  int gate_up_group;
+  // Linear1 (mode 0)
+  const float* x_scale;      // [P] (A8W8)
+  const float* w_scale;      // [E][N] formula order (A8W8)
+  void* a_out;               // [P][I] bf16 (A16W16)
+  float* a_stage;            // [P][I] f32 (A8W8)
+  uint32_t* a_amax;          // [P] (A8W8)
+  // Linear2 (mode 1)
+  const float* a_scale;      // [P] (A8W8)
+  const float* topk_w;       // [T*K]
+  float* contrib;            // [T*K][H]
+  // debug (mode 2: raw int32 accumulators)
+  int32_t* raw_out;
+};
+
+struct RequantArgs {
+  const float* a_stage;      // [P][I]
+  const uint32_t* a_amax;    // [P]
+  const int32_t* offsets;    // [E+1]
+  const int32_t* counts;     // [E]
+  void* a_pool;              // [P][I] codes
+  float* a_scale;            // [P]
+  int64_t P;
+  int E, I, usecase;
+};
+
+struct CombineArgs {
+  const float* contrib;        // [T*K][H]
+  const int32_t* route_to_pool;// [T*K]
+  void* y;                     // [T][H]
+  int64_t T;
+  int H, K, y_f32;
+};
+
+// launchers (return hipError_t of the launch)
+hipError_t launch_zero(int32_t* counts, int E, uint32_t* a_amax, int64_t P, hipStream_t s);
+hipError_t launch_count(const DispatchArgs& a, hipStream_t s);
+hipError_t launch_scatter(const DispatchArgs& a, hipStream_t s);
+hipError_t launch_gather(const DispatchArgs& a, hipStream_t s);
+hipError_t launch_prepare(const void* w1, const void* w2, void* w1o, void* w2o, int E, int H, int I,
+                          int esz, int group, hipStream_t s);
+hipError_t launch_gemm(int mode, int usecase, int tile, const GemmArgs& a, int grid, hipStream_t s);
+int gemm_grid(int tile, int64_t P, int N, int num_cus);
+hipError_t launch_requant(const RequantArgs& a, hipStream_t s);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+
+}  // namespace mm

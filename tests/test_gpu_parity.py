@@ -1,0 +1,310 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bars: dispatch metadata bit-exact (counts, padded offsets, per-expert
+(token, slot) multisets, inverse map); quantised activation codes and
+scales bit-exact (both sides decide them in IEEE float32); int8 GEMM
+accumulators exact; Y within max|dY|/rms(Y_oracle) <= 1e-2 (bf16) or
+5e-2 (fp8 / int8), evaluated on the float32 output of the kernel, with the
+bf16 output equal bit for bit to the round-to-nearest-even of that float32
+output; fused == three-call bit for bit; run-to-run bit-identical.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mixture_experts_expert_mm_amd import binding as B
+from mixture_experts_expert_mm_amd import moe
+from mixture_experts_expert_mm_amd import workloads as wl
+
+from gpu_helpers import (TOL, bf16_bits_of_f32, cpu_inputs, device_inputs, expert_fn, log, make_layer, oracle_y,
+                         rel_err)
+
+pytestmark = pytest.mark.gpu
+
+# shapes that span several tiles and a ragged tail in every GEMM dimension
+SMALL = {
+    "bm32": dict(T=20, H=256, I=128, E=16, K=2),
+    "bm64": dict(T=200, H=512, I=256, E=8, K=2),
+    "bm128": dict(T=333, H=768, I=384, E=6, K=3),
+}
+
+
+def small_cfg(shape: str, usecase: str, **kw) -> wl.Config:
+    s = SMALL[shape]
+    return wl.Config(f"{shape}_{usecase}", usecase, s["T"], s["H"], s["I"], s["E"], s["K"], 0.5, 2024, **kw)
+
+
+def check_dispatch(layer: moe.ExpertLayer, inp: wl.Inputs, im, sample_rows=None):
+    """Bit-exact dispatch metadata and pool rows against the oracle."""
+    c = inp.cfg
+    ids = inp.topk_ids.numpy()
+    d = oracle.dispatch_layout(ids, c.E, layer.plan.block_m)
+    counts = im.expert_counts.cpu().numpy()
+    offs = im.expert_offsets.cpu().numpy()
+    psrc = im.pool_src.cpu().numpy()
+    r2p = im.route_to_pool.cpu().numpy()
+    np.testing.assert_array_equal(counts, d["counts"])
+    np.testing.assert_array_equal(offs, d["offsets"])
+    assert counts.sum() == int(((ids >= 0) & (ids < c.E)).sum())
+    for e in range(c.E):
+        o, n, o1 = offs[e], counts[e], offs[e + 1]
+        np.testing.assert_array_equal(np.sort(psrc[o:o + n]), d["routes"][e])
+        assert np.all(psrc[o + n:o1] == -1)
+    flat = ids.reshape(-1)
+    valid = (flat >= 0) & (flat < c.E)
+    assert np.all(r2p[~valid] == -1)
+    rv = np.nonzero(valid)[0]
+    np.testing.assert_array_equal(psrc[r2p[rv]], rv)
+    # pool rows: x_i itself (bf16) or its quantised codes and scale
+    rows = np.concatenate([np.arange(offs[e], offs[e] + counts[e]) for e in range(c.E)])
+    if sample_rows is not None and rows.size > sample_rows:
+        rows = np.random.default_rng(0).choice(rows, sample_rows, replace=False)
+    tok = psrc[rows] // c.K
+    rows_t = torch.from_numpy(rows).cuda()
+    if c.usecase == "bf16":
+        xp = im.x_pool.view(torch.int16).view(-1, c.H)[rows_t].cpu()
+        np.testing.assert_array_equal(xp.numpy(), inp.x.view(torch.int16)[torch.from_numpy(tok)].numpy())
+    else:
+        codes, s, _ = oracle.quantize_tokens(inp.x.float().numpy()[tok], c.usecase)
+        xp = im.x_pool.view(-1, c.H)[rows_t].cpu().numpy()
+        np.testing.assert_array_equal(xp.view(np.uint8), codes.view(np.uint8))
+        np.testing.assert_array_equal(im.x_pool_scale[rows_t].cpu().numpy(), s)
+
+
+# ---------------------------------------------------------------------------
+# dispatch
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", list(wl.CONFIGS))
+def test_dispatch_metadata_full_configs(name):
+    cfg = wl.CONFIGS[name]
+    log(f"[dispatch] {name}")
+    inp = cpu_inputs(cfg)
+    layer = moe.ExpertLayer(cfg.T, cfg.H, cfg.I, cfg.E, cfg.K, cfg.usecase, "f32", "cuda")
+    im = layer.new_intermediates()
+    x, ids, _ = device_inputs(inp)
+    layer.dispatch(x, ids, im)
+    torch.cuda.synchronize()
+    check_dispatch(layer, inp, im, sample_rows=4096)
+
+
+@pytest.mark.parametrize("shape", list(SMALL))
+@pytest.mark.parametrize("usecase", ["bf16", "fp8", "int8"])
+def test_dispatch_small_masked(shape, usecase):
+    cfg = small_cfg(shape, usecase, masked_ratio=0.2)
+    log(f"[dispatch masked] {cfg.name}")
+    inp = wl.make_inputs(cfg)
+    layer = moe.ExpertLayer(cfg.T, cfg.H, cfg.I, cfg.E, cfg.K, cfg.usecase, "f32", "cuda")
+    im = layer.new_intermediates()
+    x, ids, _ = device_inputs(inp)
+    layer.dispatch(x, ids, im)
+    torch.cuda.synchronize()
+    check_dispatch(layer, inp, im)
+
+
+@pytest.mark.parametrize("usecase", ["fp8", "int8"])
+def test_activation_quantiser_all_bf16_patterns(usecase):
+    """Every finite bf16 bit pattern goes through the dispatch quantiser once."""
+    bits = np.arange(65536, dtype=np.uint32)
+    f = (bits << 16).view(np.float32)
+    finite = bits[np.isfinite(f)]
+    rng = np.random.default_rng(5)
+    H = 256
+    n = (finite.size + H - 1) // H * H
+    pat = np.concatenate([finite, rng.choice(finite, n - finite.size)])
+    rng.shuffle(pat)
+    x = torch.from_numpy(pat.astype(np.uint16).view(np.int16).reshape(-1, H)).view(torch.bfloat16)
+    T = x.shape[0]
+    log(f"[quantiser] {usecase} T={T}")
+    layer = moe.ExpertLayer(T, H, 128, 1, 1, usecase, "f32", "cuda")
+    im = layer.new_intermediates()
+    ids = torch.zeros((T, 1), dtype=torch.int32)
+    layer.dispatch(x.cuda(), ids.cuda(), im)
+    torch.cuda.synchronize()
+    codes, s, _ = oracle.quantize_tokens(x.float().numpy(), usecase)
+    psrc = im.pool_src.cpu().numpy()[:T]
+    xp = im.x_pool.view(-1, H)[:T].cpu().numpy().view(np.uint8)
+    np.testing.assert_array_equal(xp, codes.view(np.uint8)[psrc])
+    np.testing.assert_array_equal(im.x_pool_scale[:T].cpu().numpy(), s[psrc])
+
+
+# ---------------------------------------------------------------------------
+# Y parity, small shapes (every element compared)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("shape", list(SMALL))
+@pytest.mark.parametrize("usecase", ["bf16", "fp8", "int8"])
+@pytest.mark.parametrize("masked", [0.0, 0.25])
+def test_y_parity_small(shape, usecase, masked):
+    cfg = small_cfg(shape, usecase, masked_ratio=masked)
+    log(f"[y small] {cfg.name} masked={masked}")
+    inp = wl.make_inputs(cfg)
+    x, ids, wts = device_inputs(inp)
+    layer32 = make_layer(inp, "f32")
+    y32, counts = layer32.forward(x, ids, wts)
+    layer16 = make_layer(inp, "bf16")
+    y16, _ = layer16.forward(x, ids, wts)
+    torch.cuda.synchronize()
+    y_or = oracle_y(inp)
+    err = rel_err(y32.cpu().double().numpy(), y_or)
+    log(f"    max|dY|/rms = {err:.3e}")
+    assert err <= TOL[usecase], err
+    assert torch.equal(y16.view(torch.int16).cpu(), bf16_bits_of_f32(y32).cpu())
+    ids_np = inp.topk_ids.numpy()
+    np.testing.assert_array_equal(counts.cpu().numpy(), np.bincount(ids_np[ids_np >= 0], minlength=cfg.E))
+
+
+def test_tiny_config_all_elements():
+    cfg = wl.CONFIGS["tiny_bf16"]
+    inp = cpu_inputs(cfg)
+    x, ids, wts = device_inputs(inp)
+    y32, _ = make_layer(inp, "f32").forward(x, ids, wts)
+    torch.cuda.synchronize()
+    err = rel_err(y32.cpu().double().numpy(), oracle_y(inp))
+    log(f"[tiny] max|dY|/rms = {err:.3e}")
+    assert err <= TOL["bf16"]
+
+
+# ---------------------------------------------------------------------------
+# exact integer accumulators (A8W8-INT)
+# ---------------------------------------------------------------------------
+
+def test_int8_accumulators_exact():
+    cfg = small_cfg("bm64", "int8")
+    inp = wl.make_inputs(cfg)
+    layer = make_layer(inp, "f32")
+    x, ids, wts = device_inputs(inp)
+    im = layer.new_intermediates()
+    layer.dispatch(x, ids, im)
+    layer.linear1(im)
+    P = layer.plan.pool_rows
+    c1 = torch.empty((P, 2 * cfg.I), dtype=torch.int32, device="cuda")
+    c2 = torch.empty((P, cfg.H), dtype=torch.int32, device="cuda")
+    B.mm_debug_raw_accumulators(layer.plan, 1, im.expert_offsets, im.expert_counts, im.x_pool, layer.w1, c1)
+    B.mm_debug_raw_accumulators(layer.plan, 2, im.expert_offsets, im.expert_counts, im.a_pool, layer.w2, c2)
+    torch.cuda.synchronize()
+    offs = im.expert_offsets.cpu().numpy()
+    counts = im.expert_counts.cpu().numpy()
+    psrc = im.pool_src.cpu().numpy()
+    q, _, _ = oracle.quantize_tokens(inp.x.float().numpy(), "int8")
+    a_codes = im.a_pool.view(torch.int8).view(P, cfg.I).cpu().numpy().astype(np.int64)
+    c1 = c1.cpu().numpy()
+    c2 = c2.cpu().numpy()
+    for e in range(cfg.E):
+        rows = np.arange(offs[e], offs[e] + counts[e])
+        if rows.size == 0:
+            continue
+        w1 = inp.weights.w1[e].numpy().astype(np.int64)
+        w2 = inp.weights.w2[e].numpy().astype(np.int64)
+        np.testing.assert_array_equal(c1[rows], q[psrc[rows] // cfg.K].astype(np.int64) @ w1)
+        np.testing.assert_array_equal(c2[rows], a_codes[rows] @ w2)
+        assert np.all(np.abs(a_codes[rows]) <= 127)
+
+
+# ---------------------------------------------------------------------------
+# fused vs three-call, determinism, edge cases
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("usecase", ["bf16", "fp8", "int8"])
+def test_fused_equals_three_call_and_is_deterministic(usecase):
+    cfg = small_cfg("bm128", usecase)
+    inp = wl.make_inputs(cfg)
+    layer = make_layer(inp, "f32")
+    x, ids, wts = device_inputs(inp)
+    y_f, c_f = layer.forward(x, ids, wts)
+    y_f2, _ = layer.forward(x, ids, wts)
+    y_3, im = layer.forward_3call(x, ids, wts)
+    torch.cuda.synchronize()
+    assert torch.equal(y_f.view(torch.int32), y_f2.view(torch.int32))
+    assert torch.equal(y_f.view(torch.int32), y_3.view(torch.int32))
+    assert torch.equal(c_f, im.expert_counts)
+
+
+def _edge_inputs(T, H, I, E, K, ids_np, usecase="bf16", seed=77):
+    cfg = wl.Config("edge", usecase, T, H, I, E, K, 0.0, seed)
+    ids = torch.from_numpy(ids_np.astype(np.int32))
+    wts = torch.from_numpy(np.random.default_rng(seed).random((T, K)).astype(np.float32))
+    wts[ids < 0] = 0.0
+    return wl.Inputs(cfg, wl.tokens(cfg), ids, wts, wl.all_weights(cfg))
+
+
+@pytest.mark.parametrize("case", ["one_expert", "empty_expert", "single_token", "topk1", "odd_tokens", "ids_out_of_range"])
+def test_edge_cases(case):
+    H, I = 256, 128
+    rng = np.random.default_rng(3)
+    if case == "one_expert":
+        T, E, K = 150, 4, 1
+        ids = np.full((T, 1), 2)
+    elif case == "empty_expert":
+        T, E, K = 90, 6, 2
+        ids = np.stack([rng.choice([0, 1, 2, 4, 5], 2, replace=False) for _ in range(T)])
+    elif case == "single_token":
+        T, E, K = 1, 8, 4
+        ids = np.array([[7, 0, 3, 5]])
+    elif case == "topk1":
+        T, E, K = 77, 5, 1
+        ids = rng.integers(0, E, (T, 1))
+    elif case == "odd_tokens":
+        T, E, K = 67, 9, 3
+        ids = np.stack([rng.permutation(E)[:K] for _ in range(T)])
+    else:   # ids >= E are skipped like masked routes
+        T, E, K = 40, 4, 2
+        ids = np.stack([rng.permutation(E)[:K] for _ in range(T)])
+        ids[::5, 1] = E + 3
+    inp = _edge_inputs(T, H, I, E, K, ids)
+    log(f"[edge] {case}")
+    layer = make_layer(inp, "f32")
+    x, idt, wts = device_inputs(inp)
+    y, counts = layer.forward(x, idt, wts)
+    torch.cuda.synchronize()
+    ids_or = ids.copy()
+    ids_or[ids_or >= E] = -1
+    y_or, _ = oracle.moe_forward(inp.x.float().numpy(), ids_or, inp.topk_weights.numpy(), expert_fn(inp), "bf16")
+    assert rel_err(y.cpu().double().numpy(), y_or) <= TOL["bf16"]
+    np.testing.assert_array_equal(counts.cpu().numpy(), np.bincount(ids_or[ids_or >= 0], minlength=E))
+
+
+def test_prepare_weights_layout():
+    cfg = small_cfg("bm64", "bf16")
+    inp = wl.make_inputs(cfg)
+    layer = make_layer(inp, "f32")
+    torch.cuda.synchronize()
+    g = layer.plan.gate_up_group
+    n = np.arange(2 * cfg.I)
+    q, m = n // (2 * g), n % (2 * g)
+    col = np.where(m < g, q * g + m, cfg.I + q * g + (m - g))
+    w1 = inp.weights.w1.view(torch.int16)
+    exp1 = w1[:, :, torch.from_numpy(col)].transpose(1, 2).contiguous()
+    assert torch.equal(layer.w1.view(torch.int16).cpu(), exp1)
+    assert torch.equal(layer.w2.view(torch.int16).cpu(), inp.weights.w2.view(torch.int16).transpose(1, 2).contiguous())
+
+
+# ---------------------------------------------------------------------------
+# full-size configurations, the launch configuration the benchmark times,
+# sampled tokens against the per-token oracle
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["mid_bf16", "dsv3_bf16", "dsv3_fp8_t128", "dsv3_fp8_t16384", "dsv3_int8"])
+def test_full_config_sampled_tokens(name):
+    cfg = wl.CONFIGS[name]
+    log(f"[full] {name}: generating inputs")
+    inp = cpu_inputs(cfg)
+    x, ids, wts = device_inputs(inp)
+    layer = make_layer(inp, "f32")
+    y32, counts = layer.forward(x, ids, wts)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(11)
+    tokens = np.sort(rng.choice(cfg.T, min(cfg.T, 12), replace=False))
+    log(f"[full] {name}: oracle on {tokens.size} tokens")
+    y_or = oracle_y(inp, tokens=tokens)
+    err = rel_err(y32[torch.from_numpy(tokens).cuda()].cpu().double().numpy(), y_or)
+    log(f"[full] {name}: max|dY|/rms = {err:.3e}")
+    assert err <= TOL[cfg.usecase], err
+    ids_np = inp.topk_ids.numpy()
+    np.testing.assert_array_equal(counts.cpu().numpy(), np.bincount(ids_np.ravel(), minlength=cfg.E))
+    del layer
+    torch.cuda.empty_cache()
