@@ -12,6 +12,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 enum Usecase : int { UC_BF16 = 0, UC_FP8 = 1, UC_I8 = 2 };
 
@@ -96,19 +97,18 @@ template <> struct Acc<UC_BF16> { typedef f32x16 type; };
 template <> struct Acc<UC_FP8> { typedef f32x16 type; };
 template <> struct Acc<UC_I8> { typedef i32x16 type; };
 
-__device__ __forceinline__ void mfma_bf16(f32x16& c, const uint4& a, const uint4& b) {
+__device__ __forceinline__ void mfma_bf16(f32x16& c, const u32x4& a, const u32x4& b) {
   c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-__device__ __forceinline__ void mfma_i8(i32x16& c, const uint4& a, const uint4& b) {
+__device__ __forceinline__ void mfma_i8(i32x16& c, const u32x4& a, const u32x4& b) {
   c = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, a), __builtin_bit_cast(i32x4, b), c, 0, 0, 0);
 }
 
 // e4m3 x e4m3 with unit block scales (E8M0 127 = 2^0)
-__device__ __forceinline__ void mfma_fp8(f32x16& c, const uint4& a0, const uint4& a1, const uint4& b0, const uint4& b1) {
-  i32x8 a, b;
-  a[0] = a0.x; a[1] = a0.y; a[2] = a0.z; a[3] = a0.w; a[4] = a1.x; a[5] = a1.y; a[6] = a1.z; a[7] = a1.w;
-  b[0] = b0.x; b[1] = b0.y; b[2] = b0.z; b[3] = b0.w; b[4] = b1.x; b[5] = b1.y; b[6] = b1.z; b[7] = b1.w;
+__device__ __forceinline__ void mfma_fp8(f32x16& c, const u32x4& a0, const u32x4& a1, const u32x4& b0, const u32x4& b1) {
+  const i32x8 a = __builtin_bit_cast(i32x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+  const i32x8 b = __builtin_bit_cast(i32x8, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
   c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 

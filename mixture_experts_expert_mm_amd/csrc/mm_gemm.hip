@@ -30,21 +30,27 @@ constexpr int kRowBytes = 128;          // K bytes per stage row
 constexpr int kLdsRow = 144;            // padded LDS row pitch
 constexpr int kMaxExperts = 1024;
 
+// waves of a workgroup: WM along M x WN along N (a wave's N range must hold
+// whole 64-row gate/up groups, so WTN >= 64)
 template <int BM> struct WaveGrid;
 template <> struct WaveGrid<32> { static constexpr int WM = 1, WN = 4; };
-template <> struct WaveGrid<64> { static constexpr int WM = 1, WN = 4; };
-template <> struct WaveGrid<128> { static constexpr int WM = 2, WN = 2; };
+template <> struct WaveGrid<64> { static constexpr int WM = 2, WN = 4; };
+template <> struct WaveGrid<128> { static constexpr int WM = 2, WN = 4; };
+template <> struct WaveGrid<256> { static constexpr int WM = 2, WN = 4; };
+template <int BM> constexpr int threads_of() { return 64 * WaveGrid<BM>::WM * WaveGrid<BM>::WN; }
 
 template <int UC, int BM, int MODE, bool WIDEN>
-__global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs a) {
+__global__ __launch_bounds__(threads_of<BM>()) __attribute__((amdgpu_waves_per_eu(threads_of<BM>() / 256, threads_of<BM>() / 256)))
+void k_gemm(GemmArgs a) {
   constexpr int WM = WaveGrid<BM>::WM, WN = WaveGrid<BM>::WN;
+  constexpr int NT = threads_of<BM>();
   constexpr int WTM = BM / WM, WTN = kBN / WN;
   constexpr int MB = WTM / 32, NB = WTN / 32;
   constexpr int ROWS = BM + kBN;
   // global bytes per row per stage: 128, or 64 e4m3 widened to 128 bytes of bf16
   constexpr int GB = WIDEN ? 64 : kRowBytes;
   constexpr int GCH = GB / 16;                             // 16-byte global chunks per row
-  constexpr int CH = (ROWS * GCH + 255) / 256;             // chunks per thread per stage
+  constexpr int CH = (ROWS * GCH + NT - 1) / NT;           // chunks per thread per stage
   constexpr int STAGE = ROWS * kLdsRow;
   constexpr int ESZ = (UC == UC_BF16) ? 2 : 1;
   constexpr bool MF_BF16 = (UC == UC_BF16) || WIDEN;       // MFMA operand type
@@ -58,8 +64,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs a) {
   const int h = l / 32, lr = l % 32;
   const int wm = w / WN, wn = w % WN;
 
-  for (int e = t; e <= a.E; e += 256) off_s[e] = a.offsets[e];
-  for (int e = t; e < a.E; e += 256) cnt_s[e] = a.counts[e];
+  for (int e = t; e <= a.E; e += NT) off_s[e] = a.offsets[e];
+  for (int e = t; e < a.E; e += NT) cnt_s[e] = a.counts[e];
   __syncthreads();
 
   const int64_t kbytes = (int64_t)a.Kdim * ESZ;
@@ -79,31 +85,41 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs a) {
     const int e = lo;
     const int valid = min(BM, off_s[e] + cnt_s[e] - row0);
 
-    // global chunk addresses of this thread (stage kb adds kb * GB bytes)
-    const uint8_t* gptr[CH];
+    // Global chunk addresses: the A and B tile origins are wave-uniform (scalar
+    // bases); each thread keeps 32-bit offsets.  Chunk j of thread t is chunk
+    // c = t + NT*j of the stage; rows [0, BM) are A rows, the rest B rows.
+    const uint8_t* abase = a.A + (int64_t)row0 * kbytes;
+    const uint8_t* bbase = a.B + ((int64_t)e * a.N + n0) * kbytes;
+    uint32_t goff[CH];
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
-      const int c = min(t + 256 * j, ROWS * GCH - 1);
+      const int c = min(t + NT * j, ROWS * GCH - 1);
       const int row = c / GCH, col = c % GCH;
-      if (row < BM) gptr[j] = a.A + (int64_t)(row0 + row) * kbytes + col * 16;
-      else gptr[j] = a.B + ((int64_t)e * a.N + n0 + (row - BM)) * kbytes + col * 16;
+      goff[j] = (uint32_t)((row < BM ? row : row - BM) * kbytes + col * 16);
     }
-    uint4 stg[CH];
+    u32x4 stg[CH];
     auto load_stage = [&](int kb) {
+      const uint8_t* ab = abase + (int64_t)kb * GB;
+      const uint8_t* bb = bbase + (int64_t)kb * GB;
 #pragma unroll
-      for (int j = 0; j < CH; ++j)
-        if (CH * 256 == ROWS * GCH || t + 256 * j < ROWS * GCH)
-          stg[j] = *reinterpret_cast<const uint4*>(gptr[j] + (int64_t)kb * GB);
+      for (int j = 0; j < CH; ++j) {
+        const int c = t + NT * j;
+        if (CH * NT == ROWS * GCH || c < ROWS * GCH) {
+          // rows of chunk j are all A rows or all B rows when NT divides BM*GCH
+          const bool is_a = (BM * GCH) % NT == 0 ? (j < BM * GCH / NT) : (c / GCH < BM);
+          stg[j] = *reinterpret_cast<const u32x4*>((is_a ? ab : bb) + goff[j]);
+        }
+      }
     };
     auto store_stage = [&](int buf) {
       uint8_t* base = lds + buf * STAGE;
 #pragma unroll
       for (int j = 0; j < CH; ++j) {
-        const int c = t + 256 * j;
-        if (CH * 256 != ROWS * GCH && c >= ROWS * GCH) continue;
+        const int c = t + NT * j;
+        if (CH * NT != ROWS * GCH && c >= ROWS * GCH) continue;
         if constexpr (WIDEN) {
           // 16 e4m3 -> 16 bf16 (exact: every e4m3 value is a bf16 value)
-          const uint32_t wv[4] = {stg[j].x, stg[j].y, stg[j].z, stg[j].w};
+          const u32x4 wv = stg[j];
           uint32_t o[8];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
@@ -111,10 +127,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs a) {
             o[2 * q + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wv[q], 1.0f, true));
           }
           uint8_t* d = base + (c / GCH) * kLdsRow + (c % GCH) * 32;
-          *reinterpret_cast<uint4*>(d) = make_uint4(o[0], o[1], o[2], o[3]);
-          *reinterpret_cast<uint4*>(d + 16) = make_uint4(o[4], o[5], o[6], o[7]);
+          *reinterpret_cast<u32x4*>(d) = u32x4{o[0], o[1], o[2], o[3]};
+          *reinterpret_cast<u32x4*>(d + 16) = u32x4{o[4], o[5], o[6], o[7]};
         } else {
-          *reinterpret_cast<uint4*>(base + (c / GCH) * kLdsRow + (c % GCH) * 16) = stg[j];
+          *reinterpret_cast<u32x4*>(base + (c / GCH) * kLdsRow + (c % GCH) * 16) = stg[j];
         }
       }
     };
@@ -138,16 +154,16 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs a) {
       if constexpr (UC == UC_FP8 && !WIDEN) {
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-          uint4 af[MB][2], bfr[NB][2];
+          u32x4 af[MB][2], bfr[NB][2];
 #pragma unroll
           for (int i = 0; i < MB; ++i) {
-            af[i][0] = *reinterpret_cast<const uint4*>(As + i * 32 * kLdsRow + s * 32);
-            af[i][1] = *reinterpret_cast<const uint4*>(As + i * 32 * kLdsRow + s * 32 + 16);
+            af[i][0] = *reinterpret_cast<const u32x4*>(As + i * 32 * kLdsRow + s * 32);
+            af[i][1] = *reinterpret_cast<const u32x4*>(As + i * 32 * kLdsRow + s * 32 + 16);
           }
 #pragma unroll
           for (int j = 0; j < NB; ++j) {
-            bfr[j][0] = *reinterpret_cast<const uint4*>(Bs + j * 32 * kLdsRow + s * 32);
-            bfr[j][1] = *reinterpret_cast<const uint4*>(Bs + j * 32 * kLdsRow + s * 32 + 16);
+            bfr[j][0] = *reinterpret_cast<const u32x4*>(Bs + j * 32 * kLdsRow + s * 32);
+            bfr[j][1] = *reinterpret_cast<const u32x4*>(Bs + j * 32 * kLdsRow + s * 32 + 16);
           }
 #pragma unroll
           for (int i = 0; i < MB; ++i)
@@ -157,11 +173,11 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs a) {
       } else {
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          uint4 af[MB], bfr[NB];
+          u32x4 af[MB], bfr[NB];
 #pragma unroll
-          for (int i = 0; i < MB; ++i) af[i] = *reinterpret_cast<const uint4*>(As + i * 32 * kLdsRow + s * 16);
+          for (int i = 0; i < MB; ++i) af[i] = *reinterpret_cast<const u32x4*>(As + i * 32 * kLdsRow + s * 16);
 #pragma unroll
-          for (int j = 0; j < NB; ++j) bfr[j] = *reinterpret_cast<const uint4*>(Bs + j * 32 * kLdsRow + s * 16);
+          for (int j = 0; j < NB; ++j) bfr[j] = *reinterpret_cast<const u32x4*>(Bs + j * 32 * kLdsRow + s * 16);
 #pragma unroll
           for (int i = 0; i < MB; ++i)
 #pragma unroll
@@ -277,7 +293,7 @@ static hipError_t launch_one(const GemmArgs& a, int grid, hipStream_t s) {
     if (err != hipSuccess) return err;
     attr_set = true;
   }
-  hipLaunchKernelGGL((k_gemm<UC, BM, MODE, WIDEN>), dim3(grid), dim3(256), lds, s, a);
+  hipLaunchKernelGGL((k_gemm<UC, BM, MODE, WIDEN>), dim3(grid), dim3(threads_of<BM>()), lds, s, a);
   return hipGetLastError();
 }
 
@@ -286,7 +302,8 @@ static hipError_t launch_bm(int tile, const GemmArgs& a, int grid, hipStream_t s
   switch (tile) {
     case TILE_M32_N256: return launch_one<UC, 32, MODE>(a, grid, s);
     case TILE_M64_N256: return launch_one<UC, 64, MODE>(a, grid, s);
-    default: return launch_one<UC, 128, MODE>(a, grid, s);
+    case TILE_M128_N256: return launch_one<UC, 128, MODE>(a, grid, s);
+    default: return launch_one<UC, 256, MODE>(a, grid, s);
   }
 }
 

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <vector>
@@ -271,6 +272,11 @@ mm_status mm_plan_create(const mm_problem* problem, mm_plan* plan) {
   // BLOCK_M from the expected rows per expert (small loads -> small blocks)
   const double expected = (double)R / (double)p.num_experts;
   int tile = expected < 16 ? TILE_M32_N256 : expected < 96 ? TILE_M64_N256 : TILE_M128_N256;
+  // tuning override: MM_FORCE_TILE=<0..3> selects BLOCK_M 32/64/128/256
+  if (const char* f = std::getenv("MM_FORCE_TILE")) {
+    const int v = std::atoi(f);
+    if (v >= 0 && v < TILE_COUNT) tile = v;
+  }
   pl.tile_l1 = tile;
   pl.tile_l2 = tile;
   pl.block_m = tile_bm(tile);
