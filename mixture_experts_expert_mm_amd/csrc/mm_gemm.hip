@@ -27,114 +27,170 @@ namespace mm {
 
 constexpr int kBN = 256;
 constexpr int kRowBytes = 128;          // K bytes per stage row
-constexpr int kLdsRow = 144;            // padded LDS row pitch
 constexpr int kMaxExperts = 1024;
 
-// waves of a workgroup: WM along M x WN along N (a wave's N range must hold
-// whole 64-row gate/up groups, so WTN >= 64)
-template <int BM> struct WaveGrid;
-template <> struct WaveGrid<32> { static constexpr int WM = 1, WN = 4; };
-template <> struct WaveGrid<64> { static constexpr int WM = 2, WN = 4; };
-template <> struct WaveGrid<128> { static constexpr int WM = 2, WN = 4; };
-template <> struct WaveGrid<256> { static constexpr int WM = 2, WN = 4; };
-template <int BM> constexpr int threads_of() { return 64 * WaveGrid<BM>::WM * WaveGrid<BM>::WN; }
+// Workgroup shapes: 4 waves (one per SIMD), WM along M x WN along N; a wave's
+// N range must hold whole 64-row gate/up groups (WTN >= 64).
+template <int BM> struct TileShape;
+template <> struct TileShape<64> { static constexpr int WM = 1, WN = 4; };
+template <> struct TileShape<128> { static constexpr int WM = 2, WN = 4; };
+template <int BM> constexpr int threads_of() { return 64 * TileShape<BM>::WM * TileShape<BM>::WN; }
+constexpr int kStages = 3;   // LDS ring slots
 
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// LDS fragment read outside the compiler's view: the compiler would otherwise
+// wait for every in-flight LDS-DMA before any LDS read it cannot disambiguate.
+template <int OFF>
+__device__ __forceinline__ u32x4 ds_read16(uint32_t addr) {
+  u32x4 v;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+  return v;
+}
+template <int N>
+__device__ __forceinline__ void lgkm_wait() { asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N)); }
+__device__ __forceinline__ void tie(u32x4& v) { asm volatile("" : "+v"(v)); }
+// wait until at most VM of this wave's LDS-DMA loads are in flight and all its
+// LDS reads returned, then the workgroup barrier
+template <int VM>
+__device__ __forceinline__ void vm_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(VM) : "memory");
+}
+
+// Loads of one K-stage straight into LDS slot kb % S: instruction i of wave wv
+// moves DMA group g = wv + NW*i (8 rows); groups below BM/8 are A rows.
+// The tile bases become buffer descriptors here (reads past a tile return
+// zero); the descriptor type cannot appear in a signature the host pass sees.
+template <int D, int NW, int BM, int STAGE, int S>
+__device__ __forceinline__ void issue_stage(uint8_t* lds, const uint8_t* abase, int abytes, const uint8_t* bbase,
+                                            int bbytes, const uint32_t* doff, int wv, int kb) {
+  const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc((void*)abase, (short)0, abytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc((void*)bbase, (short)0, bbytes, 0x00020000);
+  const int slot = kb % S;
+  const int koff = __builtin_amdgcn_readfirstlane(kb * kRowBytes);   // scalar offset of stage kb
+#pragma unroll
+  for (int i = 0; i < D; ++i) {
+    const int g = wv + NW * i;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(g < BM / 8 ? ar : br, (lds_ptr_t)(lds + slot * STAGE + g * 1024), 16,
+                                             doff[i], koff, 0, 0);
+  }
+}
+
+// 16 e4m3 -> 16 bf16 (exact: every e4m3 value is a bf16 value)
+__device__ __forceinline__ void widen_e4m3(const u32x4& w, u32x4& lo, u32x4& hi) {
+#define CVT(x, hi_) __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((x), 1.0f, (hi_)))
+  lo = u32x4{CVT(w[0], false), CVT(w[0], true), CVT(w[1], false), CVT(w[1], true)};
+  hi = u32x4{CVT(w[2], false), CVT(w[2], true), CVT(w[3], false), CVT(w[3], true)};
+#undef CVT
+}
+
+// Mainloop data layout.  A stage holds BLOCK_M A rows then 256 B rows of 128
+// K-bytes (eight 16-byte chunks) each, filled by buffer loads straight into
+// LDS: one wave instruction moves 8 rows (64 lanes x 16 bytes, lane i -> byte
+// 16*i of the group).  Chunk c of row r sits at position c ^ ((r / 2) % 8):
+// LDS serves a 16-byte read of 16 lanes per pass over 64 banks, and 16
+// consecutive rows at one chunk then hit 16 distinct bank groups.  A lane's
+// MFMA operand covers chunks 4h..4h+3 of its row (h = lane / 32), the same
+// chunks for A and B, so every product pairs equal k.
+//
+// Pipeline per stage k (three LDS slots): wait for stage k's loads and a
+// barrier; issue the loads of stage k+2 into the slot stage k-1 used; read
+// stage k's fragments and run its MFMAs chunk by chunk as the reads land.
+// Two waves per SIMD overlap one wave's reads with the other's MFMAs.
+//
+// Epilogue: the accumulators go through the (then idle) LDS ring as a
+// float32 tile, so each output row leaves as one contiguous store.
 template <int UC, int BM, int MODE, bool WIDEN>
 __global__ __launch_bounds__(threads_of<BM>()) __attribute__((amdgpu_waves_per_eu(threads_of<BM>() / 256, threads_of<BM>() / 256)))
 void k_gemm(GemmArgs a) {
-  constexpr int WM = WaveGrid<BM>::WM, WN = WaveGrid<BM>::WN;
-  constexpr int NT = threads_of<BM>();
+  constexpr int WM = TileShape<BM>::WM, WN = TileShape<BM>::WN, S = kStages;
+  constexpr int NT = threads_of<BM>(), NW = NT / 64;
   constexpr int WTM = BM / WM, WTN = kBN / WN;
   constexpr int MB = WTM / 32, NB = WTN / 32;
   constexpr int ROWS = BM + kBN;
-  // global bytes per row per stage: 128, or 64 e4m3 widened to 128 bytes of bf16
-  constexpr int GB = WIDEN ? 64 : kRowBytes;
-  constexpr int GCH = GB / 16;                             // 16-byte global chunks per row
-  constexpr int CH = (ROWS * GCH + NT - 1) / NT;           // chunks per thread per stage
-  constexpr int STAGE = ROWS * kLdsRow;
+  constexpr int STAGE = ROWS * kRowBytes;
+  constexpr int GROUPS = ROWS / 8;
+  static_assert(GROUPS % NW == 0, "DMA groups must split evenly over the waves");
+  constexpr int D = GROUPS / NW;                           // DMA instructions per wave per stage
+  static_assert(2 * D <= 63, "vmcnt range");
   constexpr int ESZ = (UC == UC_BF16) ? 2 : 1;
-  constexpr bool MF_BF16 = (UC == UC_BF16) || WIDEN;       // MFMA operand type
+  constexpr int NFR = MB + NB;                             // fragment reads per chunk index
+  // epilogue tile in LDS (float32): Linear1 keeps the 128 SwiGLU columns,
+  // Linear2 / raw keep all 256; pitch = 8 (mod 16) floats keeps the two lane
+  // halves of an accumulator write in different bank halves
+  constexpr int OCOLS = (MODE == 0) ? kBN / 2 : kBN;
+  constexpr int OPITCH = OCOLS + 8;
+  static_assert(BM * OPITCH * 4 + 3 * BM * 4 <= S * STAGE, "epilogue tile fits the ring");
   typedef typename Acc<UC>::type AccT;
 
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   __shared__ int32_t off_s[kMaxExperts + 1];
   __shared__ int32_t cnt_s[kMaxExperts];
 
-  const int t = threadIdx.x, w = t / 64, l = lane_id();
+  const int t = threadIdx.x, l = lane_id();
+  const int wv = __builtin_amdgcn_readfirstlane(t / 64);
   const int h = l / 32, lr = l % 32;
-  const int wm = w / WN, wn = w % WN;
+  const int wm = wv / WN, wn = wv % WN;
 
   for (int e = t; e <= a.E; e += NT) off_s[e] = a.offsets[e];
   for (int e = t; e < a.E; e += NT) cnt_s[e] = a.counts[e];
   __syncthreads();
 
-  const int64_t kbytes = (int64_t)a.Kdim * ESZ;
-  const int nk = (int)(kbytes / GB);
+  const int kbytes = a.Kdim * ESZ;
+  const int nk = kbytes / kRowBytes;
   const int n_tiles = a.N / kBN;
   const int total = (off_s[a.E] / BM) * n_tiles;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_ptr_t)lds;
 
-  for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
-    const int mblk = tile / n_tiles, nblk = tile % n_tiles;
-    const int row0 = mblk * BM, n0 = nblk * kBN;
-    // expert of this M-block: the largest e with off[e] <= row0
+  // per-lane LDS addresses of the four fragment chunks (stage slot added per stage)
+  uint32_t aoff[4], boff[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t cpos = (uint32_t)(((4 * h + q) ^ ((lr >> 1) & 7)) << 4);
+    aoff[q] = lds_base + (uint32_t)(wm * WTM + lr) * kRowBytes + cpos;
+    boff[q] = lds_base + (uint32_t)(BM + wn * WTN + lr) * kRowBytes + cpos;
+  }
+  // per-lane byte offsets of the DMA rows inside their tile: row r = 8g + l/8
+  // lands its logical chunk (l%8) ^ ((r/2)%8) at position l%8
+  uint32_t doff[D];
+#pragma unroll
+  for (int i = 0; i < D; ++i) {
+    const int g = wv + NW * i;
+    const int r = 8 * g + l / 8;
+    doff[i] = (uint32_t)((r < BM ? r : r - BM) * kbytes + (((l & 7) ^ ((r >> 1) & 7)) << 4));
+  }
+  float* otile = reinterpret_cast<float*>(lds);               // epilogue tile [BM][OPITCH]
+  float* orow = reinterpret_cast<float*>(lds) + BM * OPITCH;  // per-row s^X (Linear1) / s^A (Linear2) [BM]
+  float* ogw = orow + BM;                                      // per-row gate weight [BM]
+  int32_t* oroute = reinterpret_cast<int32_t*>(ogw + BM);     // per-row route i*K+k [BM]
+
+  // Tile order: expert-major, then N-block, then M-block, so tiles that run
+  // together share weight tiles (same expert and N-block) and activation
+  // tiles (same M-block).  Workgroup w runs on XCD w % 8 (round-robin
+  // dispatch); each XCD walks its own contiguous slice of the list so the
+  // sharing happens inside one L2.
+  const int nxcd = gridDim.x >= 8 ? 8 : 1;
+  const int xcd = blockIdx.x % nxcd, wgx = blockIdx.x / nxcd, per_x = gridDim.x / nxcd;
+  const int slice = (total + nxcd - 1) / nxcd;
+  const int t_beg = xcd * slice, t_end = min(total, t_beg + slice);
+  const bool in_grid = (int)blockIdx.x < per_x * nxcd;   // a tail beyond a multiple of 8 stays idle
+  for (int tile = t_beg + wgx; in_grid && tile < t_end; tile += per_x) {
+    // expert of this tile: the largest e with (off[e] / BM) * n_tiles <= tile
     int lo = 0, hi = a.E;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if (off_s[mid] <= row0) lo = mid; else hi = mid;
+      if ((off_s[mid] / BM) * n_tiles <= tile) lo = mid; else hi = mid;
     }
     const int e = lo;
+    const int mb0 = off_s[e] / BM, nmb = (off_s[e + 1] - off_s[e]) / BM;
+    const int local = tile - mb0 * n_tiles;
+    const int nblk = local / nmb, mblk = mb0 + local % nmb;
+    const int row0 = mblk * BM, n0 = nblk * kBN;
     const int valid = min(BM, off_s[e] + cnt_s[e] - row0);
-
-    // Global chunk addresses: the A and B tile origins are wave-uniform (scalar
-    // bases); each thread keeps 32-bit offsets.  Chunk j of thread t is chunk
-    // c = t + NT*j of the stage; rows [0, BM) are A rows, the rest B rows.
     const uint8_t* abase = a.A + (int64_t)row0 * kbytes;
     const uint8_t* bbase = a.B + ((int64_t)e * a.N + n0) * kbytes;
-    uint32_t goff[CH];
-#pragma unroll
-    for (int j = 0; j < CH; ++j) {
-      const int c = min(t + NT * j, ROWS * GCH - 1);
-      const int row = c / GCH, col = c % GCH;
-      goff[j] = (uint32_t)((row < BM ? row : row - BM) * kbytes + col * 16);
-    }
-    u32x4 stg[CH];
-    auto load_stage = [&](int kb) {
-      const uint8_t* ab = abase + (int64_t)kb * GB;
-      const uint8_t* bb = bbase + (int64_t)kb * GB;
-#pragma unroll
-      for (int j = 0; j < CH; ++j) {
-        const int c = t + NT * j;
-        if (CH * NT == ROWS * GCH || c < ROWS * GCH) {
-          // rows of chunk j are all A rows or all B rows when NT divides BM*GCH
-          const bool is_a = (BM * GCH) % NT == 0 ? (j < BM * GCH / NT) : (c / GCH < BM);
-          stg[j] = *reinterpret_cast<const u32x4*>((is_a ? ab : bb) + goff[j]);
-        }
-      }
-    };
-    auto store_stage = [&](int buf) {
-      uint8_t* base = lds + buf * STAGE;
-#pragma unroll
-      for (int j = 0; j < CH; ++j) {
-        const int c = t + NT * j;
-        if (CH * NT != ROWS * GCH && c >= ROWS * GCH) continue;
-        if constexpr (WIDEN) {
-          // 16 e4m3 -> 16 bf16 (exact: every e4m3 value is a bf16 value)
-          const u32x4 wv = stg[j];
-          uint32_t o[8];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            o[2 * q] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wv[q], 1.0f, false));
-            o[2 * q + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wv[q], 1.0f, true));
-          }
-          uint8_t* d = base + (c / GCH) * kLdsRow + (c % GCH) * 32;
-          *reinterpret_cast<u32x4*>(d) = u32x4{o[0], o[1], o[2], o[3]};
-          *reinterpret_cast<u32x4*>(d + 16) = u32x4{o[4], o[5], o[6], o[7]};
-        } else {
-          *reinterpret_cast<u32x4*>(base + (c / GCH) * kLdsRow + (c % GCH) * 16) = stg[j];
-        }
-      }
-    };
 
+#define MM_ISSUE(kb_) issue_stage<D, NW, BM, STAGE, S>(lds, abase, BM * kbytes, bbase, kBN * kbytes, doff, wv, (kb_))
     AccT acc[MB][NB];
 #pragma unroll
     for (int i = 0; i < MB; ++i)
@@ -143,136 +199,172 @@ void k_gemm(GemmArgs a) {
 #pragma unroll
         for (int q = 0; q < 16; ++q) acc[i][j][q] = 0;
 
-    load_stage(0);
-    store_stage(0);
-    __syncthreads();
+    // every wave is done with the previous tile's LDS use and stores
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+    for (int st = 0; st < S - 1; ++st)
+      if (st < nk) MM_ISSUE(st);
     for (int kb = 0; kb < nk; ++kb) {
-      const int cur = kb & 1;
-      if (kb + 1 < nk) load_stage(kb + 1);
-      const uint8_t* As = lds + cur * STAGE + (wm * WTM + lr) * kLdsRow + h * 64;
-      const uint8_t* Bs = lds + cur * STAGE + (BM + wn * WTN + lr) * kLdsRow + h * 64;
-      if constexpr (UC == UC_FP8 && !WIDEN) {
+      // stage kb landed for every wave; everyone is done with stage kb-1's slot
+      if (kb + 1 < nk) vm_barrier<D>(); else vm_barrier<0>();
+      if (kb + S - 1 < nk) MM_ISSUE(kb + S - 1);
+      const uint32_t so = (uint32_t)((kb % S) * STAGE);
+      u32x4 fa[MB][4], fb[NB][4];
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          u32x4 af[MB][2], bfr[NB][2];
+      for (int q = 0; q < 4; ++q) {
+        if constexpr (MB > 0) fa[0][q] = ds_read16<0>(aoff[q] + so);
+        if constexpr (MB > 1) fa[1][q] = ds_read16<4096>(aoff[q] + so);
+        if constexpr (NB > 0) fb[0][q] = ds_read16<0>(boff[q] + so);
+        if constexpr (NB > 1) fb[1][q] = ds_read16<4096>(boff[q] + so);
+        if constexpr (NB > 2) fb[2][q] = ds_read16<8192>(boff[q] + so);
+        if constexpr (NB > 3) fb[3][q] = ds_read16<12288>(boff[q] + so);
+      }
 #pragma unroll
-          for (int i = 0; i < MB; ++i) {
-            af[i][0] = *reinterpret_cast<const u32x4*>(As + i * 32 * kLdsRow + s * 32);
-            af[i][1] = *reinterpret_cast<const u32x4*>(As + i * 32 * kLdsRow + s * 32 + 16);
+      for (int q = 0; q < 4; ++q) {
+        // chunk q has landed once at most NFR*(3-q) reads are outstanding
+        if (q == 0) lgkm_wait<(NFR * 3 > 15 ? 15 : NFR * 3)>();
+        else if (q == 1) lgkm_wait<(NFR * 2 > 15 ? 15 : NFR * 2)>();
+        else if (q == 2) lgkm_wait<NFR>();
+        else lgkm_wait<0>();
+#pragma unroll
+        for (int i = 0; i < MB; ++i) tie(fa[i][q]);
+#pragma unroll
+        for (int j = 0; j < NB; ++j) tie(fb[j][q]);
+        if constexpr (UC == UC_FP8 && !WIDEN) {
+          if (q & 1) {
+#pragma unroll
+            for (int i = 0; i < MB; ++i)
+#pragma unroll
+              for (int j = 0; j < NB; ++j) mfma_fp8(acc[i][j], fa[i][q - 1], fa[i][q], fb[j][q - 1], fb[j][q]);
           }
+        } else if constexpr (WIDEN) {
+          u32x4 alo[MB], ahi[MB], blo[NB], bhi[NB];
 #pragma unroll
-          for (int j = 0; j < NB; ++j) {
-            bfr[j][0] = *reinterpret_cast<const u32x4*>(Bs + j * 32 * kLdsRow + s * 32);
-            bfr[j][1] = *reinterpret_cast<const u32x4*>(Bs + j * 32 * kLdsRow + s * 32 + 16);
-          }
+          for (int i = 0; i < MB; ++i) widen_e4m3(fa[i][q], alo[i], ahi[i]);
 #pragma unroll
-          for (int i = 0; i < MB; ++i)
-#pragma unroll
-            for (int j = 0; j < NB; ++j) mfma_fp8(acc[i][j], af[i][0], af[i][1], bfr[j][0], bfr[j][1]);
-        }
-      } else {
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          u32x4 af[MB], bfr[NB];
-#pragma unroll
-          for (int i = 0; i < MB; ++i) af[i] = *reinterpret_cast<const u32x4*>(As + i * 32 * kLdsRow + s * 16);
-#pragma unroll
-          for (int j = 0; j < NB; ++j) bfr[j] = *reinterpret_cast<const u32x4*>(Bs + j * 32 * kLdsRow + s * 16);
+          for (int j = 0; j < NB; ++j) widen_e4m3(fb[j][q], blo[j], bhi[j]);
 #pragma unroll
           for (int i = 0; i < MB; ++i)
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
-              if constexpr (MF_BF16) mfma_bf16(acc[i][j], af[i], bfr[j]);
-              else mfma_i8(acc[i][j], af[i], bfr[j]);
+              mfma_bf16(acc[i][j], alo[i], blo[j]);
+              mfma_bf16(acc[i][j], ahi[i], bhi[j]);
+            }
+        } else {
+#pragma unroll
+          for (int i = 0; i < MB; ++i)
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+              if constexpr (UC == UC_BF16) mfma_bf16(acc[i][j], fa[i][q], fb[j][q]);
+              else mfma_i8(acc[i][j], fa[i][q], fb[j][q]);
             }
         }
       }
-      if (kb + 1 < nk) store_stage(cur ^ 1);
+    }
+#undef MM_ISSUE
+    // ------------------------------------------------------------ epilogue
+    // all waves are done reading the ring: it becomes the output tile
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if constexpr (MODE == 0 && UC != UC_BF16) {
+      for (int r = t; r < BM; r += NT) orow[r] = r < valid ? a.x_scale[row0 + r] : 0.0f;
       __syncthreads();
     }
-
-    // ------------------------------------------------------------ epilogue
-    if constexpr (MODE == 0) {
-      // blocks alternate gate (even) / up (odd); pair j covers 32 output columns
-      const int colbase = (n0 + wn * WTN) / 2;
 #pragma unroll
-      for (int i = 0; i < MB; ++i) {
+    for (int i = 0; i < MB; ++i) {
+      const int rb = wm * WTM + i * 32 + 4 * h;
+      if constexpr (MODE == 0) {
+        // gate/up pair j -> 32 output columns
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int rl = wm * WTM + i * 32 + 8 * (q / 4) + 4 * h + (q % 4);
-          const bool ok = rl < valid;
-          const int64_t p = (int64_t)row0 + rl;
-          float rmax = 0.0f;
-          float sx = 1.0f;
-          if constexpr (UC != UC_BF16) sx = ok ? a.x_scale[p] : 0.0f;
+        for (int j = 0; j < NB / 2; ++j) {
+          const int oc = wn * (WTN / 2) + j * 32 + lr;
+          float gs = 1.0f, us = 1.0f;
+          if constexpr (UC != UC_BF16) {
+            const int col = n0 / 2 + oc;
+            gs = a.w_scale[(int64_t)e * 2 * a.I + col];
+            us = a.w_scale[(int64_t)e * 2 * a.I + a.I + col];
+          }
 #pragma unroll
-          for (int j = 0; j < NB / 2; ++j) {
-            const int col = colbase + j * 32 + lr;
+          for (int q = 0; q < 16; ++q) {
+            const int r = rb + 8 * (q / 4) + (q % 4);
             float g = acc_to_f32(acc[i][2 * j][q]);
             float u = acc_to_f32(acc[i][2 * j + 1][q]);
             if constexpr (UC != UC_BF16) {
-              const float* ws = a.w_scale + (int64_t)e * 2 * a.I;
-              g = (g * ws[col]) * sx;
-              u = (u * ws[a.I + col]) * sx;
+              const float sx = orow[r];
+              g = (g * gs) * sx;
+              u = (u * us) * sx;
             }
-            const float av = silu(g) * u;
-            if constexpr (UC == UC_BF16) {
-              if (ok) static_cast<uint16_t*>(a.a_out)[p * a.I + col] = f32_to_bf16_bits(av);
-            } else {
-              if (ok) a.a_stage[p * a.I + col] = av;
-              rmax = fmaxf(rmax, fabsf(av));
-            }
+            otile[r * OPITCH + oc] = silu(g) * u;
           }
-          if constexpr (UC != UC_BF16) {
+        }
+      } else {
 #pragma unroll
-            for (int o = 16; o > 0; o >>= 1) rmax = fmaxf(rmax, __shfl_xor(rmax, o, 64));
-            if (ok && lr == 0) atomicMax(&a.a_amax[p], __float_as_uint(rmax));
+        for (int j = 0; j < NB; ++j) {
+          const int oc = wn * WTN + j * 32 + lr;
+          float ws = 1.0f;
+          if constexpr (MODE == 1 && UC != UC_BF16) ws = a.w_scale[(int64_t)e * a.H + n0 + oc];
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            const int r = rb + 8 * (q / 4) + (q % 4);
+            if constexpr (MODE == 2) reinterpret_cast<int32_t*>(otile)[r * OPITCH + oc] = acc[i][j][q];
+            else otile[r * OPITCH + oc] = acc_to_f32(acc[i][j][q]) * ws;
           }
         }
       }
-    } else if constexpr (MODE == 1) {
-#pragma unroll
-      for (int i = 0; i < MB; ++i) {
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int rl = wm * WTM + i * 32 + 8 * (q / 4) + 4 * h + (q % 4);
-          if (rl >= valid) continue;
-          const int64_t p = (int64_t)row0 + rl;
-          const int32_t r = a.pool_src[p];
-          float rs = 1.0f;
-          if constexpr (UC != UC_BF16) rs = a.a_scale[p];
-          const float gw = a.topk_w[r];
-          float* dst = a.contrib + (int64_t)r * a.H;
-#pragma unroll
-          for (int j = 0; j < NB; ++j) {
-            const int col = n0 + wn * WTN + j * 32 + lr;
-            float v = acc_to_f32(acc[i][j][q]);
-            if constexpr (UC != UC_BF16) v = (v * a.w_scale[(int64_t)e * a.H + col]) * rs;
-            dst[col] = v * gw;
-          }
+    }
+    if constexpr (MODE == 1) {
+      // per-row route, A8W8 row scale s^A and the route's gate weight G[i,k]
+      for (int r = t; r < BM; r += NT) {
+        if (r < valid) {
+          const int64_t p = (int64_t)row0 + r;
+          const int32_t route = a.pool_src[p];
+          oroute[r] = route;
+          ogw[r] = a.topk_w[route];
+          orow[r] = (UC != UC_BF16) ? a.a_scale[p] : 1.0f;
         }
       }
-    } else {
-      // raw accumulators, formula column order
+    }
+    __syncthreads();
+    // cooperative row-major pass: 16-byte column chunks, one row per group of
+    // CPR consecutive threads (BM * CPR is a multiple of the thread count, so
+    // every thread runs the same number of trips)
+    constexpr int CPR = OCOLS / 4;                       // float4 chunks per row
+    static_assert((BM * CPR) % NT == 0 && CPR <= 64 && 64 % CPR == 0, "row groups stay inside a wave");
+    for (int idx = t; idx < BM * CPR; idx += NT) {
+      const int r = idx / CPR, c4 = idx % CPR;
+      const bool ok = r < valid;
+      const int64_t p = (int64_t)row0 + r;
+      const f32x4 v = *reinterpret_cast<const f32x4*>(otile + r * OPITCH + c4 * 4);
+      if constexpr (MODE == 0) {
+        const int col = n0 / 2 + c4 * 4;
+        if constexpr (UC == UC_BF16) {
+          uint2 o;
+          o.x = pack_bf16x2(v[0], v[1]);
+          o.y = pack_bf16x2(v[2], v[3]);
+          if (ok) *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.a_out) + p * a.I + col) = o;
+        } else {
+          if (ok) *reinterpret_cast<f32x4*>(a.a_stage + p * a.I + col) = v;
+          // row amax of this tile's columns; the row's tiles combine by atomicMax
+          float m = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
 #pragma unroll
-      for (int i = 0; i < MB; ++i) {
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int rl = wm * WTM + i * 32 + 8 * (q / 4) + 4 * h + (q % 4);
-          if (rl >= valid) continue;
-          const int64_t p = (int64_t)row0 + rl;
-#pragma unroll
-          for (int j = 0; j < NB; ++j) {
-            const int n = n0 + wn * WTN + j * 32 + lr;
-            int col = n;
-            if (a.gate_up_group > 0) {
-              const int g2 = 2 * a.gate_up_group;
-              const int qq = n / g2, m = n % g2;
-              col = (m < a.gate_up_group) ? qq * a.gate_up_group + m : a.I + qq * a.gate_up_group + (m - a.gate_up_group);
-            }
-            if constexpr (UC == UC_I8) a.raw_out[p * a.N + col] = acc[i][j][q];
-          }
+          for (int o = CPR / 2; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+          if (ok && c4 == 0) atomicMax(&a.a_amax[p], __float_as_uint(m));
         }
+      } else if constexpr (MODE == 1) {
+        // contribution of route i*K+k: ((D * s^W2) * s^A) * G[i,k]
+        const float rs = orow[r], gw = ogw[r];
+        f32x4 o;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) o[c] = (UC != UC_BF16) ? (v[c] * rs) * gw : v[c] * gw;
+        if (ok) *reinterpret_cast<f32x4*>(a.contrib + (int64_t)oroute[r] * a.H + n0 + c4 * 4) = o;
+      } else {
+        const int n = n0 + c4 * 4;
+        int col = n;
+        if (a.gate_up_group > 0) {
+          const int g2 = 2 * a.gate_up_group;
+          const int qq = n / g2, m = n % g2;
+          col = (m < a.gate_up_group) ? qq * a.gate_up_group + m : a.I + qq * a.gate_up_group + (m - a.gate_up_group);
+        }
+        if (ok) *reinterpret_cast<i32x4*>(a.raw_out + p * a.N + col) = __builtin_bit_cast(i32x4, v);
       }
     }
   }
@@ -285,7 +377,7 @@ static hipError_t launch_one(const GemmArgs& a, int grid, hipStream_t s) {
   // requantisation that follows Linear1 would turn that rounding into code
   // changes.  Linear2 keeps the e4m3 MFMA (nothing is quantised after it).
   constexpr bool WIDEN = (UC == UC_FP8) && (MODE == 0);
-  constexpr size_t lds = 2 * (size_t)(BM + kBN) * kLdsRow;
+  constexpr size_t lds = (size_t)kStages * (BM + kBN) * kRowBytes;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t err = hipFuncSetAttribute((const void*)k_gemm<UC, BM, MODE, WIDEN>,
@@ -300,10 +392,8 @@ static hipError_t launch_one(const GemmArgs& a, int grid, hipStream_t s) {
 template <int UC, int MODE>
 static hipError_t launch_bm(int tile, const GemmArgs& a, int grid, hipStream_t s) {
   switch (tile) {
-    case TILE_M32_N256: return launch_one<UC, 32, MODE>(a, grid, s);
     case TILE_M64_N256: return launch_one<UC, 64, MODE>(a, grid, s);
-    case TILE_M128_N256: return launch_one<UC, 128, MODE>(a, grid, s);
-    default: return launch_one<UC, 256, MODE>(a, grid, s);
+    default: return launch_one<UC, 128, MODE>(a, grid, s);
   }
 }
 

@@ -30,13 +30,12 @@ struct DispatchArgs {
 
 // Tile configurations of the grouped GEMMs (compile-time instances).
 enum TileCfg : int {
-  TILE_M32_N256 = 0,   // weight-streaming regime: few rows per expert
-  TILE_M64_N256 = 1,
-  TILE_M128_N256 = 2,
-  TILE_M256_N256 = 3,  // compute regime
-  TILE_COUNT = 4
+  TILE_M64_N256 = 0,   // weight-streaming regime: few rows per expert
+  TILE_M128_N256 = 1,
+  TILE_M256_N256 = 2,  // compute regime
+  TILE_COUNT = 3
 };
-inline int tile_bm(int t) { return t == TILE_M32_N256 ? 32 : t == TILE_M64_N256 ? 64 : t == TILE_M128_N256 ? 128 : 256; }
+inline int tile_bm(int t) { return t == TILE_M64_N256 ? 64 : t == TILE_M128_N256 ? 128 : 256; }
 constexpr int kTileBN = 256;
 
 struct GemmArgs {

@@ -60,7 +60,7 @@ def test_plan_sizes_and_block_m():
     small = B.mm_plan_create(128, 7168, 2048, 32, 8, "fp8")
     assert small.block_m == 64 and small.x_pool_bytes == small.pool_rows * 7168
     tiny = B.mm_plan_create(20, 256, 128, 16, 2, "int8")
-    assert tiny.block_m == 32
+    assert tiny.block_m == 64
 
 
 @pytest.mark.parametrize("dims", [
