@@ -60,6 +60,29 @@ def algorithmic(cfg, counts):
     return dict(R=R, flop=flop, l1_flop=l1_flop, step_bytes=step_bytes, l1_bytes=l1_bytes)
 
 
+def measured_traffic(workload):
+    """HBM bytes per Linear1 launch from the committed counter summary.
+
+    profiles/gemm_hbm_traffic.json holds FETCH_SIZE / WRITE_SIZE of the GEMM
+    kernels (rocprofv3 --pmc), scaled by a plain-copy calibration.  They are
+    only valid for the kernel source they were taken on: if the GEMM source
+    changed since, the traffic is unknown (None).
+    """
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "gemm_hbm_traffic.json")
+    try:
+        prof = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    h = hashlib.sha256()
+    for f in ("mm_gemm.hip", "mm_device.hpp"):
+        h.update(open(os.path.join(ROOT, "mixture_experts_expert_mm_amd", "csrc", f), "rb").read())
+    if h.hexdigest() != prof.get("source_sha256"):
+        return None
+    ent = prof.get("workloads", {}).get(workload, {}).get("l1_swiglu")
+    return None if ent is None else ent["traffic_bytes"]
+
+
 def cpu_baseline(inp, target_s):
     """The oracle, as it stands, on a bounded token sample of the workload."""
     import numpy as np
@@ -168,6 +191,8 @@ def main():
         ach = al["l1_bytes"] / (l1_ms * 1e-3)
         roof = {"bound": "hbm", "achieved": ach / 1e9, "peak": PEAK["hbm"] / 1e9, "unit": "GB/s",
                 "frac": ach / PEAK["hbm"], "traffic": None}
+    roof["traffic"] = measured_traffic(cfg.name)
+    roof["algorithmic_bytes"] = al["l1_bytes"]
     roof["kernel"] = "l1_swiglu (Linear1 grouped GEMM + SwiGLU)"
     roof["kernel_ms"] = l1_ms
 
