@@ -31,11 +31,10 @@ struct DispatchArgs {
 // Tile configurations of the grouped GEMMs (compile-time instances).
 enum TileCfg : int {
   TILE_M64_N256 = 0,   // weight-streaming regime: few rows per expert
-  TILE_M128_N256 = 1,
-  TILE_M256_N256 = 2,  // compute regime
-  TILE_COUNT = 3
+  TILE_M128_N256 = 1,  // compute regime
+  TILE_COUNT = 2
 };
-inline int tile_bm(int t) { return t == TILE_M64_N256 ? 64 : t == TILE_M128_N256 ? 128 : 256; }
+inline int tile_bm(int t) { return t == TILE_M64_N256 ? 64 : 128; }
 constexpr int kTileBN = 256;
 
 struct GemmArgs {

@@ -268,8 +268,9 @@ def test_edge_cases(case):
     np.testing.assert_array_equal(counts.cpu().numpy(), np.bincount(ids_or[ids_or >= 0], minlength=E))
 
 
-def test_prepare_weights_layout():
-    cfg = small_cfg("bm64", "bf16")
+@pytest.mark.parametrize("usecase", ["bf16", "fp8"])
+def test_prepare_weights_layout(usecase):
+    cfg = small_cfg("bm64", usecase)
     inp = wl.make_inputs(cfg)
     layer = make_layer(inp, "f32")
     torch.cuda.synchronize()
@@ -277,10 +278,11 @@ def test_prepare_weights_layout():
     n = np.arange(2 * cfg.I)
     q, m = n // (2 * g), n % (2 * g)
     col = np.where(m < g, q * g + m, cfg.I + q * g + (m - g))
-    w1 = inp.weights.w1.view(torch.int16)
+    view = torch.int16 if usecase == "bf16" else torch.uint8
+    w1 = inp.weights.w1.view(view)
     exp1 = w1[:, :, torch.from_numpy(col)].transpose(1, 2).contiguous()
-    assert torch.equal(layer.w1.view(torch.int16).cpu(), exp1)
-    assert torch.equal(layer.w2.view(torch.int16).cpu(), inp.weights.w2.view(torch.int16).transpose(1, 2).contiguous())
+    assert torch.equal(layer.w1.view(view).cpu(), exp1)
+    assert torch.equal(layer.w2.view(view).cpu(), inp.weights.w2.view(view).transpose(1, 2).contiguous())
 
 
 # ---------------------------------------------------------------------------
