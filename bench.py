@@ -2,14 +2,16 @@
 """Benchmark of the routed-expert path on one MI355X.
 
 One step = one ``mega_moe`` call (dispatch -> Linear1 + SwiGLU -> Linear2 ->
-combine) over one batch of seeded synthetic inputs already resident in HBM.
-The default workload is the mid-size bf16 layer (T=2048, hidden=4096,
-intermediate=1408, 16 experts, top-4).
+combine, one persistent kernel after a zeroing pre-pass) over one batch of
+seeded synthetic inputs already resident in HBM.  The default workload is
+the mid-size bf16 layer (T=2048, hidden=4096, intermediate=1408, 16 experts,
+top-4).
 
 Prints one JSON line: throughput in TFLOP/s (FLOP = 6 * routes * hidden *
-intermediate), the roofline of the dominant kernel (Linear1, timed with HIP
-events on its stream inside the timed region) and the CPU oracle timed on
-a bounded sample of the same workload.
+intermediate), the roofline of the dominant kernel (the fused kernel, timed
+with HIP events on its stream inside the timed region), a per-phase
+breakdown from the three-call path, and the CPU oracle timed on a bounded
+sample of the same workload.
 """
 
 from __future__ import annotations
@@ -60,27 +62,58 @@ def algorithmic(cfg, counts):
     return dict(R=R, flop=flop, l1_flop=l1_flop, step_bytes=step_bytes, l1_bytes=l1_bytes)
 
 
-def measured_traffic(workload):
-    """HBM bytes per Linear1 launch from the committed counter summary.
-
-    profiles/gemm_hbm_traffic.json holds FETCH_SIZE / WRITE_SIZE of the GEMM
-    kernels (rocprofv3 --pmc), scaled by a plain-copy calibration.  They are
-    only valid for the kernel source they were taken on: if the GEMM source
-    changed since, the traffic is unknown (None).
-    """
+def source_digest():
+    """sha256 over the HIP sources the kernels are built from."""
+    import glob
     import hashlib
-    path = os.path.join(ROOT, "profiles", "gemm_hbm_traffic.json")
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "mixture_experts_expert_mm_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, kernel="mega"):
+    """HBM bytes per launch of `kernel` from the committed counter summary.
+
+    profiles/hbm_traffic.json holds FETCH_SIZE / WRITE_SIZE of the kernels
+    (rocprofv3 --pmc), scaled by a plain-copy calibration.  They are only
+    valid for the kernel sources they were taken on: if a source changed
+    since, the traffic is unknown (None).
+    """
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     try:
         prof = json.load(open(path))
     except (OSError, ValueError):
         return None
-    h = hashlib.sha256()
-    for f in ("mm_gemm.hip", "mm_device.hpp"):
-        h.update(open(os.path.join(ROOT, "mixture_experts_expert_mm_amd", "csrc", f), "rb").read())
-    if h.hexdigest() != prof.get("source_sha256"):
+    if source_digest() != prof.get("source_sha256"):
         return None
-    ent = prof.get("workloads", {}).get(workload, {}).get("l1_swiglu")
+    ent = prof.get("workloads", {}).get(workload, {}).get(kernel)
     return None if ent is None else ent["traffic_bytes"]
+
+
+def phase_breakdown(layer, x, ids, wts, steps):
+    """Per-kernel milliseconds of the three-call path (same device code as
+    the phases of the fused kernel), averaged over `steps` calls."""
+    from mixture_experts_expert_mm_amd import binding as B
+    import torch
+    im = layer.new_intermediates()
+    y = layer.new_y()
+
+    def once():
+        layer.dispatch(x, ids, im)
+        layer.linear1(im)
+        layer.linear2_combine(im, wts, y)
+    once()
+    torch.cuda.synchronize()
+    B.mm_trace_collect()
+    B.mm_trace_enable(True)
+    for _ in range(steps):
+        once()
+    torch.cuda.synchronize()
+    B.mm_trace_enable(False)
+    tr = B.mm_trace_collect()
+    return {k: v[1] / steps for k, v in tr.items() if v[0]}
 
 
 def cpu_baseline(inp, target_s):
@@ -187,22 +220,25 @@ def main():
 
     al = algorithmic(cfg, counts.cpu().numpy())
     tflops = al["flop"] / (ms_per_step * 1e-3) / 1e12
-    n_l1, t_l1 = trace["l1_swiglu"]
-    l1_ms = t_l1 / max(n_l1, 1)
+    n_k, t_k = trace["mega"]
+    k_ms = t_k / max(n_k, 1)
     peak_mfma = PEAK[cfg.usecase]
-    mfma_bound = al["l1_flop"] / al["l1_bytes"] > peak_mfma / PEAK["hbm"]
+    # the fused kernel does the whole step: its algorithmic work is the step's
+    mfma_bound = al["flop"] / al["step_bytes"] > peak_mfma / PEAK["hbm"]
     if mfma_bound:
-        ach = al["l1_flop"] / (l1_ms * 1e-3)
+        ach = al["flop"] / (k_ms * 1e-3)
         roof = {"bound": "mfma", "achieved": ach / 1e12, "peak": peak_mfma / 1e12, "unit": "TFLOP/s",
                 "frac": ach / peak_mfma, "traffic": None}
     else:
-        ach = al["l1_bytes"] / (l1_ms * 1e-3)
+        ach = al["step_bytes"] / (k_ms * 1e-3)
         roof = {"bound": "hbm", "achieved": ach / 1e9, "peak": PEAK["hbm"] / 1e9, "unit": "GB/s",
                 "frac": ach / PEAK["hbm"], "traffic": None}
     roof["traffic"] = measured_traffic(cfg.name)
-    roof["algorithmic_bytes"] = al["l1_bytes"]
-    roof["kernel"] = "l1_swiglu (Linear1 grouped GEMM + SwiGLU)"
-    roof["kernel_ms"] = l1_ms
+    roof["algorithmic_bytes"] = al["step_bytes"]
+    roof["algorithmic_flop"] = al["flop"]
+    roof["kernel"] = "mega (fused persistent kernel: dispatch, Linear1 + SwiGLU, Linear2, combine)"
+    roof["kernel_ms"] = k_ms
+    phases = phase_breakdown(layer, x, ids, wts, max(2, min(args.steps, 10)))
 
     out = {
         "metric": METRIC,
@@ -224,6 +260,7 @@ def main():
         "mfma_frac_step": al["flop"] / (ms_per_step * 1e-3) / peak_mfma,
         "wall_s_timed": wall,
         "kernels_ms_per_step": {k: v[1] / args.steps for k, v in trace.items() if v[0]},
+        "three_call_phases_ms": phases,
         "roofline": roof,
     }
     if not args.no_cpu_baseline:

@@ -204,6 +204,17 @@ mm_status mm_grouped_l2_combine(const mm_plan* plan, const int32_t* expert_offse
  * mega_moe -- the whole path in one call: Dispatch, Linear1, SwiGLU,
  * Linear2, Combine (operator page, Function and Prototype: returns y and
  * expert_token_nums).  Every intermediate lives in the workspace.
+ * It runs as one persistent kernel (one workgroup per compute unit, the
+ * whole grid resident at once) after a small pre-pass that clears the
+ * counters and stores the kernel's arguments in the workspace: the
+ * phases count, scatter, gather, Linear1, (A8W8) requantisation, Linear2
+ * and combine follow each other inside the kernel, separated by grid-wide
+ * barriers.  The results are bitwise those of the three-call path.
+ * Device-side conditions (an expert id >= E, a barrier that timed out) are
+ * recorded in the workspace error word, see mm_read_device_error.  A device
+ * that cannot hold one workgroup per compute unit makes the call fail with
+ * MM_ERR_HIP before anything runs; work on other streams that occupies
+ * compute units only delays the kernel.
  *   x              device bf16 [T][H]
  *   topk_ids       device int32 [T][K]
  *   topk_weights   device f32 [T][K]
@@ -217,6 +228,25 @@ mm_status mega_moe(const mm_plan* plan, const void* x, const int32_t* topk_ids,
                    const float* topk_weights, const void* w1, const float* w1_scale,
                    const void* w2, const float* w2_scale, void* y, int32_t* expert_token_nums,
                    void* workspace, uint64_t workspace_bytes, void* stream);
+
+/* Bits of the device error word. */
+typedef enum mm_device_error {
+  MM_DEVERR_NONE = 0,
+  MM_DEVERR_BAD_EXPERT = 1,      /* a route named an expert id >= E (skipped like a masked route) */
+  MM_DEVERR_BARRIER_TIMEOUT = 2, /* a grid barrier of mega_moe gave up waiting; y is unspecified */
+  MM_DEVERR_BAD_OFFSETS = 4      /* a GEMM got offsets/counts that do not describe a padded pool
+                                    of at most P rows: it ran no tile (its outputs are unspecified) */
+} mm_device_error;
+
+/*
+ * mm_read_device_error -- copies the error word of this workspace into
+ * *host_out, asynchronously on `stream`: read it after the stream has
+ * synchronised.  mega_moe and mm_dispatch_layout clear the word when they
+ * start; the two GEMM entry points only add bits to it.  Diagnostics only.
+ *   workspace  the workspace passed to that call
+ *   host_out   host int32, receives an OR of mm_device_error bits
+ */
+mm_status mm_read_device_error(const mm_plan* plan, const void* workspace, int32_t* host_out, void* stream);
 
 /*
  * mm_debug_raw_accumulators -- the integer GEMM accumulators before any
@@ -240,7 +270,8 @@ mm_status mm_debug_raw_accumulators(const mm_plan* plan, int which, const int32_
 typedef enum mm_kernel_id {
   MM_K_ZERO = 0, MM_K_COUNT = 1, MM_K_SCATTER = 2, MM_K_GATHER = 3,
   MM_K_L1 = 4, MM_K_REQUANT = 5, MM_K_L2 = 6, MM_K_COMBINE = 7, MM_K_PREPARE = 8,
-  MM_K_COUNT_IDS = 9
+  MM_K_MEGA = 9,                 /* the fused persistent kernel of mega_moe */
+  MM_K_COUNT_IDS = 10
 } mm_kernel_id;
 
 mm_status mm_trace_enable(int on);

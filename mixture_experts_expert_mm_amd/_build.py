@@ -11,7 +11,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libmegamoe.so")
-SOURCES = ["mm_dispatch.hip", "mm_gemm.hip", "mm_host.hip"]
+SOURCES = ["mm_dispatch.hip", "mm_gemm.hip", "mm_mega.hip", "mm_host.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -18,7 +18,8 @@ from . import _build
 MM_A16W16, MM_A8W8_FP8, MM_A8W8_INT8 = 0, 1, 2
 MM_OUT_BF16, MM_OUT_F32 = 0, 1
 USECASE = {"bf16": MM_A16W16, "fp8": MM_A8W8_FP8, "int8": MM_A8W8_INT8}
-KERNEL_IDS = 9
+KERNEL_IDS = 10
+MM_DEVERR_BAD_EXPERT, MM_DEVERR_BARRIER_TIMEOUT, MM_DEVERR_BAD_OFFSETS = 1, 2, 4
 
 
 class MMProblem(ctypes.Structure):
@@ -54,8 +55,8 @@ class MMPlan(ctypes.Structure):
 
 EXPORTS = [
     "mm_plan_create", "mm_prepare_weights", "mm_dispatch_layout", "mm_grouped_l1_swiglu",
-    "mm_grouped_l2_combine", "mega_moe", "mm_debug_raw_accumulators", "mm_trace_enable",
-    "mm_trace_collect", "mm_kernel_name", "mm_status_string",
+    "mm_grouped_l2_combine", "mega_moe", "mm_read_device_error", "mm_debug_raw_accumulators",
+    "mm_trace_enable", "mm_trace_collect", "mm_kernel_name", "mm_status_string",
 ]
 
 _lib = None
@@ -87,6 +88,7 @@ def load() -> ctypes.CDLL:
     lib.mm_grouped_l1_swiglu.argtypes = [P, i32p, i32p, vp, f32p, vp, f32p, vp, f32p, vp, u64, vp]
     lib.mm_grouped_l2_combine.argtypes = [P, i32p, i32p, i32p, i32p, vp, f32p, vp, f32p, f32p, vp, vp, u64, vp]
     lib.mega_moe.argtypes = [P, vp, i32p, f32p, vp, f32p, vp, f32p, vp, i32p, vp, u64, vp]
+    lib.mm_read_device_error.argtypes = [P, vp, ctypes.POINTER(ctypes.c_int32), vp]
     lib.mm_debug_raw_accumulators.argtypes = [P, ctypes.c_int, i32p, i32p, vp, vp, i32p, vp]
     lib.mm_trace_enable.argtypes = [ctypes.c_int]
     lib.mm_trace_collect.argtypes = [ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_double)]
@@ -171,6 +173,15 @@ def mega_moe(plan, x, topk_ids, topk_weights, w1, w1_scale, w2, w2_scale, y, exp
         ctypes.byref(plan), _ptr(x), _ptr(topk_ids), _ptr(topk_weights), _ptr(w1), _ptr(w1_scale),
         _ptr(w2), _ptr(w2_scale), _ptr(y), _ptr(expert_token_nums), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def mm_read_device_error(plan, workspace, stream=None) -> int:
+    """The device error word (mm_device_error bits) of the last call on `workspace`."""
+    out = ctypes.c_int32(0)
+    _check("mm_read_device_error", load().mm_read_device_error(
+        ctypes.byref(plan), _ptr(workspace), ctypes.byref(out), _stream(stream)))
+    torch.cuda.synchronize()
+    return out.value
 
 
 def mm_debug_raw_accumulators(plan, which, expert_offsets, expert_counts, act_pool, w_prepared, c_out,

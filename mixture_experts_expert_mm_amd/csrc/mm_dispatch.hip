@@ -1,221 +1,45 @@
-// EP Dispatch on one GPU: route read, count, claim + prefix, scatter, gather
-// (+ per-token activation quantisation), and the one-time weight relayout.
-//
-// Count -> Prefix Sum -> Scatter follows the DeepEP "Metadata System" notes
-// (sections 3.2-3.5): routes are counted in LDS, each wavefront claims its
-// range inside an expert with one global atomic per expert it touches (the
-// returned old value is the wave's base inside that expert), and the final
-// slot of a route is the wave base plus its rank among the lanes of the
-// same expert (ballot + popcount).  Pool rows of expert e start at the
-// padded prefix off[e] (a multiple of BLOCK_M).
-#include "mm_device.hpp"
-#include "mm_internal.hpp"
+// EP Dispatch kernels of the three-call path (thin wrappers over the
+// device bodies shared with the fused kernel), the per-call counter reset
+// and the one-time weight relayout.
+#include "mm_dispatch_dev.hpp"
 
 namespace mm {
 
 // ---------------------------------------------------------------------------
-// reset of the per-call counters
+// reset of the per-call counters and control words
 // ---------------------------------------------------------------------------
-__global__ void k_zero(int32_t* __restrict__ counts, int E, uint32_t* __restrict__ a_amax, int64_t P) {
+__global__ void k_zero(int32_t* __restrict__ counts, int E, uint32_t* __restrict__ a_amax, int64_t P,
+                       uint32_t* __restrict__ ctl) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   if (counts)
     for (int64_t j = i; j < E; j += stride) counts[j] = 0;
   if (a_amax)
     for (int64_t j = i; j < P; j += stride) a_amax[j] = 0u;
+  if (ctl && i < kCtlWords) ctl[i] = 0u;
 }
 
-// Route of lane l of global wave gw: token gw*tpw + l/K, slot l%K.  Returns
-// the expert id, or -1 for idle lanes, masked routes (id < 0) and ids >= E.
-__device__ __forceinline__ int read_route(const DispatchArgs& a, int64_t gw, int l, int64_t* route) {
-  const int tpw = 64 / a.K;
-  const int64_t tok = gw * tpw + l / a.K;
-  const int slot = l % a.K;
-  *route = -1;
-  if (l >= tpw * a.K || tok >= a.T) return -1;
-  *route = tok * a.K + slot;
-  const int e = a.topk_ids[*route];
-  return (e >= 0 && e < a.E) ? e : -1;
-}
-
-// ---------------------------------------------------------------------------
-// count + claim: LDS histogram per wave, one global atomic per (wave, expert)
-// ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_count(DispatchArgs a, int64_t nwaves) {
   extern __shared__ int32_t smem[];
-  const int w = threadIdx.x / 64, l = lane_id();
-  int32_t* hist = smem + w * a.E;
-  const int64_t gw = (int64_t)blockIdx.x * kDispatchWavesPerBlock + w;
-  for (int e = l; e < a.E; e += 64) hist[e] = 0;
-  __syncthreads();
-  int64_t route;
-  const int e = (gw < nwaves) ? read_route(a, gw, l, &route) : -1;
-  if (e >= 0) atomicAdd(&hist[e], 1);
-  __syncthreads();
-  if (gw < nwaves) {
-    for (int ex = l; ex < a.E; ex += 64) {
-      const int c = hist[ex];
-      if (c > 0) a.wave_base[gw * a.E + ex] = atomicAdd(&a.counts[ex], c);
-    }
-  }
+  count_block<kDispatchWavesPerBlock>(a, blockIdx.x, nwaves, smem);
 }
 
-// Block-wide exclusive scan of the BLOCK_M-padded counts into off[0..E].
-__device__ void padded_prefix(const DispatchArgs& a, int32_t* off, int32_t* wsum) {
-  const int t = threadIdx.x, w = t / 64, l = lane_id();
-  const int per = (a.E + 255) / 256;
-  const int e0 = t * per;
-  int local = 0;
-  for (int j = 0; j < per; ++j) {
-    const int e = e0 + j;
-    if (e < a.E) local += (a.counts[e] + a.block_m - 1) / a.block_m * a.block_m;
-  }
-  int incl = local;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int v = __shfl_up(incl, o, 64);
-    if (l >= o) incl += v;
-  }
-  if (l == 63) wsum[w] = incl;
-  __syncthreads();
-  int excl = incl - local;
-  for (int ww = 0; ww < w; ++ww) excl += wsum[ww];
-  for (int j = 0; j < per; ++j) {
-    const int e = e0 + j;
-    if (e < a.E) {
-      off[e] = excl;
-      excl += (a.counts[e] + a.block_m - 1) / a.block_m * a.block_m;
-    }
-  }
-  if (t == 0) off[a.E] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
-  __syncthreads();
-}
-
-// ---------------------------------------------------------------------------
-// scatter: pool row of every route + identity metadata
-// ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_scatter(DispatchArgs a, int64_t nwaves) {
   extern __shared__ int32_t smem[];
   int32_t* off = smem;                     // [E+1]
   int32_t* run = smem + a.E + 1;           // [4][E]
-  __shared__ int32_t wsum[4];
-  padded_prefix(a, off, wsum);
-  const int t = threadIdx.x, w = t / 64, l = lane_id();
-
+  __shared__ int32_t wsum[kDispatchWavesPerBlock];
+  padded_prefix<256>(a, off, wsum);
   if (blockIdx.x == 0)
-    for (int e = t; e <= a.E; e += 256) a.offsets[e] = off[e];
-
-  // padding rows of expert e (e = blockIdx.x mod gridDim.x) carry no route
-  for (int e = blockIdx.x; e < a.E; e += gridDim.x) {
-    const int64_t p0 = (int64_t)off[e] + a.counts[e], p1 = off[e + 1];
-    for (int64_t p = p0 + t; p < p1; p += 256) a.pool_src[p] = -1;
-  }
-
-  const int64_t gw = (int64_t)blockIdx.x * kDispatchWavesPerBlock + w;
-  if (gw >= nwaves) return;
-  int32_t* myrun = run + w * a.E;
-  // running pool position per expert: padded prefix + the wave's claimed base
-  // (entries of experts this wave does not touch are never read)
-  for (int e = l; e < a.E; e += 64) myrun[e] = off[e] + a.wave_base[gw * a.E + e];
-  __builtin_amdgcn_wave_barrier();
-
-  int64_t route;
-  const int e = read_route(a, gw, l, &route);
-  int32_t p = -1;
-  uint64_t act = ballot(e >= 0);
-  while (act) {
-    const int leader = __ffsll((unsigned long long)act) - 1;
-    const int le = __shfl(e, leader, 64);
-    const uint64_t m = ballot(e == le);
-    const int base = myrun[le];
-    if (e == le) p = base + __popcll(m & lanemask_lt());
-    __builtin_amdgcn_wave_barrier();
-    if (l == leader) myrun[le] = base + __popcll(m);
-    __builtin_amdgcn_wave_barrier();
-    act &= ~m;
-  }
-  if (route >= 0) {
-    a.route_to_pool[route] = p;
-    if (p >= 0) a.pool_src[p] = (int32_t)route;
-  }
+    for (int e = threadIdx.x; e <= a.E; e += 256) a.offsets[e] = off[e];
+  scatter_block<kDispatchWavesPerBlock>(a, blockIdx.x, gridDim.x, nwaves, off, run);
 }
-
-// ---------------------------------------------------------------------------
-// gather: one block per token; reads x_i once, writes its K pool rows.
-// A8W8: s_i = max(max|x_i| / Qmax, 1e-8) and q = round(x_i / s_i) in IEEE
-// float32 (correctly rounded division), int8 ties-to-even clamped to
-// [-127,127] or e4m3fn ties-to-even saturated to +-448.
-// ---------------------------------------------------------------------------
-constexpr int kGatherMaxChunks = 8;   // H <= 8 * 256 * 8 = 16384
 
 template <int UC>
 __global__ __launch_bounds__(256) void k_gather(DispatchArgs a) {
-  const int64_t i = blockIdx.x;
-  const int t = threadIdx.x;
   __shared__ int32_t dst[64];
   __shared__ float red[4];
-  if (t < a.K) dst[t] = a.route_to_pool[i * a.K + t];
-  const int nchunk = (int)(a.H / 8);
-  const uint4* xr = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + i * a.H);
-  if constexpr (UC == UC_BF16) {
-    __syncthreads();
-    for (int c = t; c < nchunk; c += 256) {
-      const uint4 v = xr[c];
-      for (int k = 0; k < a.K; ++k) {
-        const int p = dst[k];
-        if (p >= 0) reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.x_pool) + (int64_t)p * a.H)[c] = v;
-      }
-    }
-  } else {
-    uint4 v[kGatherMaxChunks];
-    float m = 0.0f;
-#pragma unroll
-    for (int j = 0; j < kGatherMaxChunks; ++j) {
-      const int c = t + j * 256;
-      if (c < nchunk) {
-        v[j] = xr[c];
-        const uint32_t wv[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          m = fmaxf(m, fabsf(bf16_bits_to_f32(wv[q] & 0xffffu)));
-          m = fmaxf(m, fabsf(bf16_bits_to_f32(wv[q] >> 16)));
-        }
-      }
-    }
-    m = wave_max(m);
-    if (lane_id() == 0) red[t / 64] = m;
-    __syncthreads();
-    const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    const float qmax = (UC == UC_I8) ? 127.0f : 448.0f;
-    const float s = fmaxf(amax / qmax, 1e-8f);
-#pragma unroll
-    for (int j = 0; j < kGatherMaxChunks; ++j) {
-      const int c = t + j * 256;
-      if (c < nchunk) {
-        const uint32_t wv[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
-        uint32_t o[2];
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const float f0 = bf16_bits_to_f32(wv[2 * q] & 0xffffu) / s;
-          const float f1 = bf16_bits_to_f32(wv[2 * q] >> 16) / s;
-          const float f2 = bf16_bits_to_f32(wv[2 * q + 1] & 0xffffu) / s;
-          const float f3 = bf16_bits_to_f32(wv[2 * q + 1] >> 16) / s;
-          if constexpr (UC == UC_I8) {
-            o[q] = (uint32_t)(f32_to_i8sym(f0) & 0xff) | ((uint32_t)(f32_to_i8sym(f1) & 0xff) << 8) |
-                   ((uint32_t)(f32_to_i8sym(f2) & 0xff) << 16) | ((uint32_t)(f32_to_i8sym(f3) & 0xff) << 24);
-          } else {
-            o[q] = f32x2_to_e4m3x2(f0, f1) | (f32x2_to_e4m3x2(f2, f3) << 16);
-          }
-        }
-        const uint2 ov = make_uint2(o[0], o[1]);
-        for (int k = 0; k < a.K; ++k) {
-          const int p = dst[k];
-          if (p >= 0) reinterpret_cast<uint2*>(static_cast<uint8_t*>(a.x_pool) + (int64_t)p * a.H)[c] = ov;
-        }
-      }
-    }
-    if (t < a.K && dst[t] >= 0) a.x_pool_scale[dst[t]] = s;
-  }
+  gather_token<UC, 256>(a, blockIdx.x, dst, red);
 }
 
 // ---------------------------------------------------------------------------
@@ -253,12 +77,12 @@ __global__ __launch_bounds__(256) void k_transpose(const T* __restrict__ in, T* 
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-hipError_t launch_zero(int32_t* counts, int E, uint32_t* a_amax, int64_t P, hipStream_t s) {
+hipError_t launch_zero(int32_t* counts, int E, uint32_t* a_amax, int64_t P, uint32_t* ctl, hipStream_t s) {
   const int64_t n = a_amax ? (P > E ? P : E) : E;
   int grid = (int)((n + 255) / 256);
   if (grid > 1024) grid = 1024;
   if (grid < 1) grid = 1;
-  hipLaunchKernelGGL(k_zero, dim3(grid), dim3(256), 0, s, counts, E, a_amax, P);
+  hipLaunchKernelGGL(k_zero, dim3(grid), dim3(256), 0, s, counts, E, a_amax, P, ctl);
   return hipGetLastError();
 }
 

@@ -36,8 +36,8 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 // ---------------------------------------------------------------- workspace
 struct WsLayout {
-  int64_t wave_base, a_amax, a_stage, contrib, end;                          // 3-call scratch
-  int64_t offsets, pool_src, route_to_pool, x_pool, x_pool_scale, a_pool, a_pool_scale, fused_end;
+  int64_t ctl, wave_base, a_amax, a_stage, contrib, end;                     // 3-call scratch
+  int64_t mega_args, offsets, pool_src, route_to_pool, x_pool, x_pool_scale, a_pool, a_pool_scale, fused_end;
 };
 
 WsLayout ws_layout(const mm_plan& pl) {
@@ -47,11 +47,13 @@ WsLayout ws_layout(const mm_plan& pl) {
   WsLayout L{};
   int64_t o = 0;
   auto take = [&](int64_t bytes) { const int64_t at = o; o = align_up(o + bytes, kAlign); return at; };
+  L.ctl = take(kCtlWords * 4);
   L.wave_base = take(dispatch_waves(p.num_tokens, (int)p.num_topk) * p.num_experts * 4);
   L.a_amax = q ? take(P * 4) : -1;
   L.a_stage = q ? take(P * p.intermediate_hidden * 4) : -1;
   L.contrib = take(R * p.hidden * 4);
   L.end = o;
+  L.mega_args = take(sizeof(MegaArgs));
   L.offsets = take((p.num_experts + 1) * 4);
   L.pool_src = take(P * 4);
   L.route_to_pool = take(R * 4);
@@ -137,8 +139,10 @@ mm_status check_plan(const mm_plan* pl) {
 }
 
 // ---------------------------------------------------------------- stages
-mm_status do_dispatch(const mm_plan& pl, const int32_t* ids, const void* x, int32_t* counts, int32_t* offsets,
-                      int32_t* pool_src, int32_t* r2p, void* x_pool, float* x_pool_scale, void* ws, hipStream_t s) {
+// Argument blocks of each step; the three-call path launches them as
+// separate kernels, mega_moe hands all of them to the fused kernel.
+DispatchArgs dispatch_args(const mm_plan& pl, const int32_t* ids, const void* x, int32_t* counts, int32_t* offsets,
+                           int32_t* pool_src, int32_t* r2p, void* x_pool, float* x_pool_scale, void* ws) {
   const mm_problem& p = pl.prob;
   const WsLayout L = ws_layout(pl);
   DispatchArgs d{};
@@ -151,6 +155,7 @@ mm_status do_dispatch(const mm_plan& pl, const int32_t* ids, const void* x, int3
   d.x_pool = x_pool;
   d.x_pool_scale = x_pool_scale;
   d.wave_base = at<int32_t>(ws, L.wave_base);
+  d.err = at<uint32_t>(ws, L.ctl) + 1;
   d.T = p.num_tokens;
   d.H = p.hidden;
   d.P = pl.pool_rows;
@@ -158,16 +163,11 @@ mm_status do_dispatch(const mm_plan& pl, const int32_t* ids, const void* x, int3
   d.K = (int)p.num_topk;
   d.block_m = pl.block_m;
   d.usecase = p.usecase;
-  MM_TRY(run(MM_K_ZERO, s, [&] { return launch_zero(counts, d.E, nullptr, 0, s); }));
-  MM_TRY(run(MM_K_COUNT, s, [&] { return launch_count(d, s); }));
-  MM_TRY(run(MM_K_SCATTER, s, [&] { return launch_scatter(d, s); }));
-  MM_TRY(run(MM_K_GATHER, s, [&] { return launch_gather(d, s); }));
-  return MM_OK;
+  return d;
 }
 
-mm_status do_l1(const mm_plan& pl, const int32_t* offsets, const int32_t* counts, const void* x_pool,
-                const float* x_pool_scale, const void* w1, const float* w1_scale, void* a_pool, float* a_pool_scale,
-                void* ws, hipStream_t s) {
+GemmArgs l1_args(const mm_plan& pl, const int32_t* offsets, const int32_t* counts, const void* x_pool,
+                 const float* x_pool_scale, const void* w1, const float* w1_scale, void* a_pool, void* ws) {
   const mm_problem& p = pl.prob;
   const WsLayout L = ws_layout(pl);
   GemmArgs g{};
@@ -183,35 +183,34 @@ mm_status do_l1(const mm_plan& pl, const int32_t* offsets, const int32_t* counts
   g.H = (int)p.hidden;
   g.K = (int)p.num_topk;
   g.gate_up_group = pl.gate_up_group;
+  g.routes = p.num_tokens * p.num_topk;
+  g.err = at<uint32_t>(ws, L.ctl) + 1;
   g.x_scale = x_pool_scale;
   g.w_scale = w1_scale;
   g.a_out = a_pool;
   g.a_stage = at<float>(ws, L.a_stage);
   g.a_amax = at<uint32_t>(ws, L.a_amax);
-  const int grid = gemm_grid(pl.tile_l1, pl.pool_rows, g.N, num_cus());
-  if (p.usecase != MM_A16W16)
-    MM_TRY(run(MM_K_ZERO, s, [&] { return launch_zero(nullptr, 0, g.a_amax, pl.pool_rows, s); }));
-  MM_TRY(run(MM_K_L1, s, [&] { return launch_gemm(0, p.usecase, pl.tile_l1, g, grid, s); }));
-  if (p.usecase != MM_A16W16) {
-    RequantArgs r{};
-    r.a_stage = g.a_stage;
-    r.a_amax = g.a_amax;
-    r.offsets = offsets;
-    r.counts = counts;
-    r.E = g.E;
-    r.a_pool = a_pool;
-    r.a_scale = a_pool_scale;
-    r.P = pl.pool_rows;
-    r.I = g.I;
-    r.usecase = p.usecase;
-    MM_TRY(run(MM_K_REQUANT, s, [&] { return launch_requant(r, s); }));
-  }
-  return MM_OK;
+  return g;
 }
 
-mm_status do_l2(const mm_plan& pl, const int32_t* offsets, const int32_t* counts, const int32_t* pool_src,
-                const int32_t* r2p, const void* a_pool, const float* a_pool_scale, const void* w2,
-                const float* w2_scale, const float* topk_w, void* y, void* ws, hipStream_t s) {
+RequantArgs requant_args(const mm_plan& pl, const GemmArgs& l1, void* a_pool, float* a_pool_scale) {
+  RequantArgs r{};
+  r.a_stage = l1.a_stage;
+  r.a_amax = l1.a_amax;
+  r.offsets = l1.offsets;
+  r.counts = l1.counts;
+  r.E = l1.E;
+  r.a_pool = a_pool;
+  r.a_scale = a_pool_scale;
+  r.P = pl.pool_rows;
+  r.I = l1.I;
+  r.usecase = pl.prob.usecase;
+  return r;
+}
+
+GemmArgs l2_args(const mm_plan& pl, const int32_t* offsets, const int32_t* counts, const int32_t* pool_src,
+                 const void* a_pool, const float* a_pool_scale, const void* w2, const float* w2_scale,
+                 const float* topk_w, void* ws) {
   const mm_problem& p = pl.prob;
   const WsLayout L = ws_layout(pl);
   GemmArgs g{};
@@ -227,22 +226,75 @@ mm_status do_l2(const mm_plan& pl, const int32_t* offsets, const int32_t* counts
   g.I = (int)p.intermediate_hidden;
   g.H = (int)p.hidden;
   g.K = (int)p.num_topk;
+  g.routes = p.num_tokens * p.num_topk;
+  g.err = at<uint32_t>(ws, L.ctl) + 1;
   g.a_scale = a_pool_scale;
   g.w_scale = w2_scale;
   g.topk_w = topk_w;
   g.contrib = at<float>(ws, L.contrib);
-  const int grid = gemm_grid(pl.tile_l2, pl.pool_rows, g.N, num_cus());
-  MM_TRY(run(MM_K_L2, s, [&] { return launch_gemm(1, p.usecase, pl.tile_l2, g, grid, s); }));
+  return g;
+}
+
+CombineArgs combine_args(const mm_plan& pl, const float* contrib, const int32_t* r2p, void* y) {
+  const mm_problem& p = pl.prob;
   CombineArgs c{};
-  c.contrib = g.contrib;
+  c.contrib = contrib;
   c.route_to_pool = r2p;
   c.y = y;
   c.T = p.num_tokens;
   c.H = (int)p.hidden;
   c.K = (int)p.num_topk;
   c.y_f32 = p.y_dtype == MM_OUT_F32;
+  return c;
+}
+
+mm_status do_dispatch(const mm_plan& pl, const int32_t* ids, const void* x, int32_t* counts, int32_t* offsets,
+                      int32_t* pool_src, int32_t* r2p, void* x_pool, float* x_pool_scale, void* ws, hipStream_t s) {
+  const DispatchArgs d = dispatch_args(pl, ids, x, counts, offsets, pool_src, r2p, x_pool, x_pool_scale, ws);
+  uint32_t* ctl = at<uint32_t>(ws, ws_layout(pl).ctl);
+  MM_TRY(run(MM_K_ZERO, s, [&] { return launch_zero(counts, d.E, nullptr, 0, ctl, s); }));
+  MM_TRY(run(MM_K_COUNT, s, [&] { return launch_count(d, s); }));
+  MM_TRY(run(MM_K_SCATTER, s, [&] { return launch_scatter(d, s); }));
+  MM_TRY(run(MM_K_GATHER, s, [&] { return launch_gather(d, s); }));
+  return MM_OK;
+}
+
+mm_status do_l1(const mm_plan& pl, const int32_t* offsets, const int32_t* counts, const void* x_pool,
+                const float* x_pool_scale, const void* w1, const float* w1_scale, void* a_pool, float* a_pool_scale,
+                void* ws, hipStream_t s) {
+  const mm_problem& p = pl.prob;
+  const GemmArgs g = l1_args(pl, offsets, counts, x_pool, x_pool_scale, w1, w1_scale, a_pool, ws);
+  const int grid = gemm_grid(pl.tile_l1, pl.pool_rows, g.N, num_cus());
+  if (p.usecase != MM_A16W16)
+    MM_TRY(run(MM_K_ZERO, s, [&] { return launch_zero(nullptr, 0, g.a_amax, pl.pool_rows, nullptr, s); }));
+  MM_TRY(run(MM_K_L1, s, [&] { return launch_gemm(0, p.usecase, pl.tile_l1, g, grid, s); }));
+  if (p.usecase != MM_A16W16) {
+    const RequantArgs r = requant_args(pl, g, a_pool, a_pool_scale);
+    MM_TRY(run(MM_K_REQUANT, s, [&] { return launch_requant(r, s); }));
+  }
+  return MM_OK;
+}
+
+mm_status do_l2(const mm_plan& pl, const int32_t* offsets, const int32_t* counts, const int32_t* pool_src,
+                const int32_t* r2p, const void* a_pool, const float* a_pool_scale, const void* w2,
+                const float* w2_scale, const float* topk_w, void* y, void* ws, hipStream_t s) {
+  const mm_problem& p = pl.prob;
+  const GemmArgs g = l2_args(pl, offsets, counts, pool_src, a_pool, a_pool_scale, w2, w2_scale, topk_w, ws);
+  const int grid = gemm_grid(pl.tile_l2, pl.pool_rows, g.N, num_cus());
+  MM_TRY(run(MM_K_L2, s, [&] { return launch_gemm(1, p.usecase, pl.tile_l2, g, grid, s); }));
+  const CombineArgs c = combine_args(pl, g.contrib, r2p, y);
   MM_TRY(run(MM_K_COMBINE, s, [&] { return launch_combine(c, s); }));
   return MM_OK;
+}
+
+// Polls a fused-kernel grid barrier makes before giving up (about seconds);
+// MM_BARRIER_SPIN overrides it, which tests use to exercise the time-out.
+uint32_t barrier_spin_limit() {
+  if (const char* v = std::getenv("MM_BARRIER_SPIN")) {
+    const long n = std::atol(v);
+    if (n > 0) return (uint32_t)n;
+  }
+  return 1u << 21;
 }
 
 bool ok16(const void* p) { return p && aligned(p, 16); }
@@ -373,10 +425,30 @@ mm_status mega_moe(const mm_plan* plan, const void* x, const int32_t* topk_ids, 
   float* xs = q ? at<float>(workspace, L.x_pool_scale) : nullptr;
   void* a_pool = at<uint8_t>(workspace, L.a_pool);
   float* as = q ? at<float>(workspace, L.a_pool_scale) : nullptr;
-  MM_TRY(do_dispatch(*plan, topk_ids, x, expert_token_nums, offsets, pool_src, r2p, x_pool, xs, workspace, s));
-  MM_TRY(do_l1(*plan, offsets, expert_token_nums, x_pool, xs, w1, w1_scale, a_pool, as, workspace, s));
-  MM_TRY(do_l2(*plan, offsets, expert_token_nums, pool_src, r2p, a_pool, as, w2, w2_scale, topk_weights, y,
-               workspace, s));
+  const mm_plan& pl = *plan;
+  MegaArgs m{};
+  m.d = dispatch_args(pl, topk_ids, x, expert_token_nums, offsets, pool_src, r2p, x_pool, xs, workspace);
+  m.l1 = l1_args(pl, offsets, expert_token_nums, x_pool, xs, w1, w1_scale, a_pool, workspace);
+  m.rq = requant_args(pl, m.l1, a_pool, as);
+  m.l2 = l2_args(pl, offsets, expert_token_nums, pool_src, a_pool, as, w2, w2_scale, topk_weights, workspace);
+  m.cb = combine_args(pl, m.l2.contrib, r2p, y);
+  m.ctl = at<uint32_t>(workspace, L.ctl);
+  m.nwaves = dispatch_waves(pl.prob.num_tokens, (int)pl.prob.num_topk);
+  m.spin_limit = barrier_spin_limit();
+  MegaArgs* dev_args = at<MegaArgs>(workspace, L.mega_args);
+  MM_TRY(run(MM_K_ZERO, s, [&] { return launch_mega_prep(m, dev_args, s); }));
+  MM_TRY(run(MM_K_MEGA, s, [&] {
+    return launch_mega(pl.prob.usecase, pl.tile_l1, dev_args, mega_grid(pl.tile_l1, num_cus()), s);
+  }));
+  return MM_OK;
+}
+
+mm_status mm_read_device_error(const mm_plan* plan, const void* workspace, int32_t* host_out, void* stream) {
+  MM_TRY(check_plan(plan));
+  if (!ok16(workspace) || !host_out) return MM_ERR_INVALID_ARG;
+  const uint8_t* word = static_cast<const uint8_t*>(workspace) + ws_layout(*plan).ctl + 4;
+  if (hipMemcpyAsync(host_out, word, 4, hipMemcpyDeviceToHost, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return MM_ERR_HIP;
   return MM_OK;
 }
 
@@ -451,7 +523,8 @@ mm_status mm_trace_collect(int32_t* launches, double* total_ms) {
 }
 
 const char* mm_kernel_name(int id) {
-  static const char* names[] = {"zero", "count", "scatter", "gather", "l1_swiglu", "requant", "l2_gate", "combine", "prepare"};
+  static const char* names[] = {"zero",    "count",   "scatter", "gather", "l1_swiglu",
+                                "requant", "l2_gate", "combine", "prepare", "mega"};
   if (id < 0 || id >= MM_K_COUNT_IDS) return "unknown";
   return names[id];
 }

@@ -24,6 +24,7 @@ struct DispatchArgs {
   void* x_pool;              // [P][H]
   float* x_pool_scale;       // [P] (A8W8)
   int32_t* wave_base;        // ws: [waves][E]
+  uint32_t* err;             // ws: device error word (mm_device_error bits)
   int64_t T, H, P;
   int E, K, block_m, usecase;
 };
@@ -44,6 +45,8 @@ struct GemmArgs {
   const int32_t* counts;     // [E]
   const int32_t* pool_src;   // [P]
   int64_t P;                 // pool capacity (rows)
+  int64_t routes;            // T*K
+  uint32_t* err;             // device error word (mm_device_error bits)
   int E, N, Kdim, I, H, K;
   int gate_up_group;
   // Linear1 (mode 0)
@@ -79,8 +82,27 @@ struct CombineArgs {
   int H, K, y_f32;
 };
 
+// Control words at the start of the workspace, cleared by the pre-pass of
+// every call: [1] is the device error word (mm_device_error bits); the fused
+// kernel's grid barriers use [0], [2] and [16..47].
+constexpr int kCtlWords = 64;
+
+// Everything the fused persistent kernel needs: the arguments of each phase.
+struct MegaArgs {
+  DispatchArgs d;
+  GemmArgs l1, l2;
+  RequantArgs rq;
+  CombineArgs cb;
+  uint32_t* ctl;             // [kCtlWords]
+  int64_t nwaves;            // dispatch waves
+  uint32_t spin_limit;       // polls before a grid barrier gives up
+};
+
 // launchers (return hipError_t of the launch)
-hipError_t launch_zero(int32_t* counts, int E, uint32_t* a_amax, int64_t P, hipStream_t s);
+hipError_t launch_zero(int32_t* counts, int E, uint32_t* a_amax, int64_t P, uint32_t* ctl, hipStream_t s);
+hipError_t launch_mega_prep(const MegaArgs& a, MegaArgs* dev_args, hipStream_t s);
+hipError_t launch_mega(int usecase, int tile, const MegaArgs* dev_args, int grid, hipStream_t s);
+int mega_grid(int tile, int num_cus);
 hipError_t launch_count(const DispatchArgs& a, hipStream_t s);
 hipError_t launch_scatter(const DispatchArgs& a, hipStream_t s);
 hipError_t launch_gather(const DispatchArgs& a, hipStream_t s);

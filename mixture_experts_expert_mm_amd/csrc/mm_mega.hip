@@ -1,0 +1,234 @@
+// The fused persistent kernel of mega_moe: every step of the routed-expert
+// path in one launch.  One workgroup per compute unit, the whole grid
+// resident at once; the phases run in order
+//   count + claim | prefix + scatter | gather | Linear1 + SwiGLU |
+//   (A8W8) requantisation | Linear2 + gate | combine
+// separated by grid-wide barriers, and each phase is the same device code
+// the three-call path runs as separate kernels, so the results are bitwise
+// those of that path.  The counters it relies on (expert counts, A8W8 row
+// amax, barrier arrivals, error word) are cleared by a small pre-pass.
+#include "mm_dispatch_dev.hpp"
+#include "mm_gemm_dev.hpp"
+
+namespace mm {
+
+// Grid-wide barrier, hierarchical over the XCDs.  Control words (cleared by
+// the pre-pass): ctl[0] XCDs released, ctl[1] error word, ctl[2] workgroups
+// registered, ctl[16 + x] arrivals on XCD x, ctl[32 + x] workgroups on XCD x.
+//
+// Every workgroup registers its XCD at kernel start.  At barrier n each wave
+// has its stores in L2 (workgroup barrier); thread 0 adds one arrival for its
+// XCD, and the last workgroup of an XCD to arrive writes that XCD's L2 back
+// (one device-scope release per XCD, not one per workgroup) and releases the
+// XCD; every workgroup then waits for all active XCDs and acquires.  Polls
+// are relaxed device-scope loads with a sleep between them.  After spin_limit
+// polls a wait gives up: it sets MM_DEVERR_BARRIER_TIMEOUT and the block
+// leaves the kernel, so no phase runs on data another block may not have
+// finished; blocks waiting for it time out at their next barrier.
+struct BarState {
+  uint32_t xcd, wg_in_xcd, active_xcds;
+};
+
+__device__ __forceinline__ uint32_t xcc_id() {
+  // hardware register XCC_ID (20), bits 3:0: the XCD this wave runs on
+  return __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 15u;
+}
+
+__device__ bool poll_until(uint32_t* p, uint32_t target, uint32_t spin_limit) {
+  uint32_t polls = 0;
+  while (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+    if (++polls > spin_limit) return false;
+    __builtin_amdgcn_s_sleep(2);
+  }
+  return true;
+}
+
+__device__ void barrier_register(uint32_t* ctl, BarState& bs) {
+  bs = BarState{xcc_id(), 0u, 0u};
+  if (threadIdx.x == 0) {
+    __hip_atomic_fetch_add(&ctl[32 + bs.xcd], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_add(&ctl[2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+__device__ bool grid_barrier(uint32_t* ctl, uint32_t n, uint32_t spin_limit, BarState& bs, int32_t* ok_lds) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    bool ok = true;
+    if (bs.wg_in_xcd == 0) {   // first barrier: wait for every registration, then read them
+      ok = poll_until(&ctl[2], gridDim.x, spin_limit);
+      bs.wg_in_xcd = __hip_atomic_load(&ctl[32 + bs.xcd], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int x = 0; x < 16; ++x)
+        bs.active_xcds += __hip_atomic_load(&ctl[32 + x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) > 0 ? 1u : 0u;
+    }
+    if (ok) {
+      const uint32_t before = __hip_atomic_fetch_add(&ctl[16 + bs.xcd], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (before + 1 == n * bs.wg_in_xcd) {   // last of its XCD
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        __hip_atomic_fetch_add(&ctl[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      ok = poll_until(&ctl[0], n * bs.active_xcds, spin_limit);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if (!ok) __hip_atomic_fetch_or(&ctl[1], (uint32_t)MM_DEVERR_BARRIER_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *ok_lds = ok ? 1 : 0;
+  }
+  __syncthreads();
+  return *ok_lds != 0;
+}
+
+template <int BM>
+constexpr int mega_lds_bytes() {
+  return lds_bytes_of<BM, 0>() > lds_bytes_of<BM, 1>() ? lds_bytes_of<BM, 0>() : lds_bytes_of<BM, 1>();
+}
+
+template <int UC, int BM>
+__global__ __launch_bounds__(threads_of<BM>()) __attribute__((amdgpu_waves_per_eu(threads_of<BM>() / 256, threads_of<BM>() / 256)))
+void k_mega(const MegaArgs* mp) {
+  // The arguments sit in device memory (written by the pre-pass) rather than
+  // in the kernel-argument segment, so each phase loads the fields it uses
+  // where it uses them instead of holding all of them in scalar registers
+  // for the whole kernel.
+  const MegaArgs& m = *mp;
+  constexpr int NT = threads_of<BM>(), NW = NT / 64;
+  constexpr bool WIDEN = (UC == UC_FP8);   // e4m3 Linear1 on bf16 MFMA, as in the three-call path
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  __shared__ int32_t off_s[kMaxExperts + 1];
+  __shared__ int32_t cnt_s[kMaxExperts];
+  __shared__ int32_t wsum[NW];
+  __shared__ int32_t dst[64];
+  __shared__ float red[NW];
+  __shared__ int32_t ok;
+  static_assert((kMaxExperts + 1 + (int64_t)NW * kMaxExperts) * 4 <= mega_lds_bytes<BM>(), "dispatch scratch fits");
+  int32_t* smem = reinterpret_cast<int32_t*>(lds);
+  const int t = threadIdx.x;
+  uint32_t* const ctl = m.ctl;
+  const uint32_t spin = m.spin_limit;
+  const int64_t nwaves = m.nwaves;
+  BarState bs;
+  barrier_register(ctl, bs);
+  uint32_t nb = 0;
+  const int64_t nvb = (nwaves + NW - 1) / NW;   // virtual dispatch blocks of NW waves
+
+  // count + claim (each phase copies the arguments it needs into registers)
+  {
+    const DispatchArgs d = m.d;
+    for (int64_t vb = blockIdx.x; vb < nvb; vb += gridDim.x) count_block<NW>(d, vb, nwaves, smem);
+  }
+  if (!grid_barrier(ctl, ++nb, spin, bs, &ok)) return;
+
+  // padded prefix (every block, into LDS) + scatter
+  {
+    const DispatchArgs d = m.d;
+    padded_prefix<NT>(d, off_s, wsum);
+    if (blockIdx.x == 0)
+      for (int e = t; e <= d.E; e += NT) d.offsets[e] = off_s[e];
+    for (int64_t vb = blockIdx.x; vb < nvb; vb += gridDim.x) scatter_block<NW>(d, vb, nvb, nwaves, off_s, smem);
+  }
+  if (!grid_barrier(ctl, ++nb, spin, bs, &ok)) return;
+
+  // gather (+ A8W8 activation quantisation), one token per block at a time
+  {
+    const DispatchArgs d = m.d;
+    for (int64_t tok = blockIdx.x; tok < d.T; tok += gridDim.x) gather_token<UC, NT>(d, tok, dst, red);
+  }
+  if (!grid_barrier(ctl, ++nb, spin, bs, &ok)) return;
+
+  // Linear1 + SwiGLU (gemm_tiles leaves the offsets and counts in off_s / cnt_s)
+  {
+    const GemmArgs g = m.l1;
+    gemm_tiles<UC, BM, 0, WIDEN>(g, lds, off_s, cnt_s);
+  }
+  if (!grid_barrier(ctl, ++nb, spin, bs, &ok)) return;
+
+  if constexpr (UC != UC_BF16) {
+    // per-row requantisation of A, one wave per pool row
+    const RequantArgs r = m.rq;
+    const int64_t used = off_s[r.E], nwv = (int64_t)gridDim.x * NW;
+    for (int64_t p = (int64_t)blockIdx.x * NW + t / 64; p < used; p += nwv) requant_row<UC>(r, p, off_s, cnt_s);
+    if (!grid_barrier(ctl, ++nb, spin, bs, &ok)) return;
+  }
+
+  // Linear2 + gate weight into the combine slots
+  {
+    const GemmArgs g = m.l2;
+    gemm_tiles<UC, BM, 1, false>(g, lds, off_s, cnt_s);
+  }
+  if (!grid_barrier(ctl, ++nb, spin, bs, &ok)) return;
+
+  // combine: 8 columns of one token per item, four items per thread at a time
+  const CombineArgs c = m.cb;
+  const int64_t work = c.T * (c.H / 8), stride = (int64_t)gridDim.x * NT;
+  for (int64_t idx = (int64_t)blockIdx.x * NT + t; idx < work; idx += 4 * stride) combine_8u<4>(c, idx, stride, work);
+}
+
+// Pre-pass: clears the counters the fused kernel accumulates into (expert
+// counts, A8W8 row amax, control words) and stores the kernel's arguments
+// in the workspace.
+__global__ __launch_bounds__(256) void k_mega_prep(MegaArgs m, MegaArgs* out, int quantized) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t j = i; j < m.d.E; j += stride) m.d.counts[j] = 0;
+  if (quantized)
+    for (int64_t j = i; j < m.l1.P; j += stride) m.l1.a_amax[j] = 0u;
+  if (i < kCtlWords) m.ctl[i] = 0u;
+  constexpr int words = (int)(sizeof(MegaArgs) / 4);
+  static_assert(sizeof(MegaArgs) % 4 == 0, "argument block copies as words");
+  if (blockIdx.x == 0) {
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(&m);
+    for (int w = threadIdx.x; w < words; w += blockDim.x) reinterpret_cast<uint32_t*>(out)[w] = src[w];
+  }
+}
+
+// The grid barriers need every workgroup of the grid resident at once.  The
+// grid is one workgroup per CU and the kernel's LDS use admits one per CU,
+// which the occupancy query confirms here; the launch is an ordinary one (a
+// cooperative launch guarantees the same on an idle device but costs tens of
+// microseconds more per call).  Work of other streams that holds CUs only
+// delays the late workgroups, which the barriers wait for (bounded).
+template <int UC, int BM>
+static hipError_t launch_mega_one(const MegaArgs* dev_args, int grid, hipStream_t s) {
+  constexpr size_t lds = (size_t)mega_lds_bytes<BM>();
+  static int per_cu = -1;
+  if (per_cu < 0) {
+    hipError_t err = hipFuncSetAttribute((const void*)k_mega<UC, BM>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (err != hipSuccess) return err;
+    int n = 0;
+    err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_mega<UC, BM>, threads_of<BM>(), lds);
+    if (err != hipSuccess) return err;
+    per_cu = n;
+  }
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return hipErrorInvalidDevice;
+  if (per_cu < 1 || grid > per_cu * cus) return hipErrorCooperativeLaunchTooLarge;
+  hipLaunchKernelGGL((k_mega<UC, BM>), dim3(grid), dim3(threads_of<BM>()), lds, s, dev_args);
+  return hipGetLastError();
+}
+
+template <int UC>
+static hipError_t launch_mega_bm(int tile, const MegaArgs* a, int grid, hipStream_t s) {
+  return tile == TILE_M64_N256 ? launch_mega_one<UC, 64>(a, grid, s) : launch_mega_one<UC, 128>(a, grid, s);
+}
+
+hipError_t launch_mega_prep(const MegaArgs& a, MegaArgs* dev_args, hipStream_t s) {
+  const int quantized = a.d.usecase != UC_BF16;
+  const int64_t n = quantized ? (a.l1.P > a.d.E ? a.l1.P : a.d.E) : a.d.E;
+  int grid = (int)((n + 255) / 256);
+  if (grid > 1024) grid = 1024;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(k_mega_prep, dim3(grid), dim3(256), 0, s, a, dev_args, quantized);
+  return hipGetLastError();
+}
+
+hipError_t launch_mega(int usecase, int tile, const MegaArgs* dev_args, int grid, hipStream_t s) {
+  switch (usecase) {
+    case UC_BF16: return launch_mega_bm<UC_BF16>(tile, dev_args, grid, s);
+    case UC_FP8: return launch_mega_bm<UC_FP8>(tile, dev_args, grid, s);
+    default: return launch_mega_bm<UC_I8>(tile, dev_args, grid, s);
+  }
+}
+
+int mega_grid(int /*tile*/, int num_cus) { return num_cus; }   // one resident workgroup per CU
+
+}  // namespace mm

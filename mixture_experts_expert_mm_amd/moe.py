@@ -95,6 +95,11 @@ class ExpertLayer:
                    self.workspace(True), stream)
         return y, counts
 
+    def device_error(self, fused: bool = True) -> int:
+        """The device error word of the last call on this layer's workspace
+        (mm_device_error bits; waits for the device)."""
+        return B.mm_read_device_error(self.plan, self.workspace(fused))
+
     def dispatch(self, x, topk_ids, im: Intermediates, stream=None):
         B.mm_dispatch_layout(self.plan, topk_ids, x, im.expert_counts, im.expert_offsets, im.pool_src,
                              im.route_to_pool, im.x_pool, im.x_pool_scale, self.workspace(False), stream)

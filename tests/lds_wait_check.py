@@ -144,4 +144,5 @@ def check_function(asm_text: str, name: str):
 
 
 def gemm_functions(asm_text: str):
-    return [m.group(1) for m in re.finditer(r"^(_ZN2mm6k_gemm\w+):", asm_text, flags=re.M)]
+    """The kernels that run the GEMM mainloop: k_gemm and the fused k_mega."""
+    return [m.group(1) for m in re.finditer(r"^(_ZN2mm6k_(?:gemm|mega)\w+):", asm_text, flags=re.M)]

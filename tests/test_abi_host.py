@@ -102,6 +102,8 @@ def test_entry_points_validate_before_any_hip_call():
     q = B.mm_plan_create(64, 256, 128, 8, 2, "int8")
     assert lib.mega_moe(ctypes.byref(q), good, good, good, good, None, good, None, good, good, good,
                         1 << 40, None) == 1
+    # the error word needs a host destination
+    assert lib.mm_read_device_error(P, good, None, None) == 1
     # raw accumulators exist for int8 only
     assert lib.mm_debug_raw_accumulators(P, 1, good, good, good, good, good, None) == 2
     assert lib.mm_debug_raw_accumulators(ctypes.byref(q), 3, good, good, good, good, good, None) == 1
@@ -111,3 +113,4 @@ def test_names():
     _lib()
     assert B.status_string(3) == "workspace too small"
     assert B.mm_kernel_name(4) == "l1_swiglu"
+    assert B.mm_kernel_name(9) == "mega"

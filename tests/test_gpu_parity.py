@@ -222,6 +222,59 @@ def test_fused_equals_three_call_and_is_deterministic(usecase):
     assert torch.equal(y_f.view(torch.int32), y_f2.view(torch.int32))
     assert torch.equal(y_f.view(torch.int32), y_3.view(torch.int32))
     assert torch.equal(c_f, im.expert_counts)
+    assert layer.device_error(fused=True) == 0 and layer.device_error(fused=False) == 0
+
+
+def test_fused_barrier_timeout_is_reported_and_recovers(monkeypatch):
+    """A grid barrier that gives up (forced from the host with a one-poll
+    limit) sets its error bit and every block still leaves the kernel; the
+    next call with the normal limit is exact again."""
+    cfg = small_cfg("bm64", "bf16")
+    inp = wl.make_inputs(cfg)
+    layer = make_layer(inp, "f32")
+    x, ids, wts = device_inputs(inp)
+    y_ok, _ = layer.forward(x, ids, wts)
+    y_ok = y_ok.clone()
+    torch.cuda.synchronize()
+    assert layer.device_error() == 0
+    monkeypatch.setenv("MM_BARRIER_SPIN", "1")
+    log("[timeout] mega_moe with a one-poll barrier limit")
+    layer.forward(x, ids, wts)
+    torch.cuda.synchronize()
+    assert layer.device_error() & B.MM_DEVERR_BARRIER_TIMEOUT
+    monkeypatch.delenv("MM_BARRIER_SPIN")
+    y2, _ = layer.forward(x, ids, wts)
+    torch.cuda.synchronize()
+    assert layer.device_error() == 0
+    assert torch.equal(y_ok.view(torch.int32), y2.view(torch.int32))
+
+
+@pytest.mark.parametrize("corrupt", ["past_pool", "unaligned", "count_overflow"])
+def test_gemm_rejects_offsets_outside_the_pool(corrupt):
+    """Offsets a caller hands to the GEMM entry points that do not describe a
+    padded pool of at most P rows run no tile and raise
+    MM_DEVERR_BAD_OFFSETS (the kernel never addresses outside the pool)."""
+    cfg = small_cfg("bm64", "bf16")
+    inp = wl.make_inputs(cfg)
+    layer = make_layer(inp, "f32")
+    x, ids, wts = device_inputs(inp)
+    im = layer.new_intermediates()
+    layer.dispatch(x, ids, im)
+    torch.cuda.synchronize()
+    assert layer.device_error(fused=False) == 0
+    bm = layer.plan.block_m
+    off = im.expert_offsets.clone()
+    if corrupt == "past_pool":
+        off[-1] = layer.plan.pool_rows + bm
+    elif corrupt == "unaligned":
+        off[1:] += 1
+    else:
+        im.expert_counts[0] = int(off[1] - off[0]) + 1
+    im.expert_offsets.copy_(off)
+    log(f"[bad offsets] {corrupt}")
+    layer.linear1(im)
+    torch.cuda.synchronize()
+    assert layer.device_error(fused=False) & B.MM_DEVERR_BAD_OFFSETS
 
 
 def _edge_inputs(T, H, I, E, K, ids_np, usecase="bf16", seed=77):
@@ -266,6 +319,7 @@ def test_edge_cases(case):
     y_or, _ = oracle.moe_forward(inp.x.float().numpy(), ids_or, inp.topk_weights.numpy(), expert_fn(inp), "bf16")
     assert rel_err(y.cpu().double().numpy(), y_or) <= TOL["bf16"]
     np.testing.assert_array_equal(counts.cpu().numpy(), np.bincount(ids_or[ids_or >= 0], minlength=E))
+    assert layer.device_error() == (B.MM_DEVERR_BAD_EXPERT if case == "ids_out_of_range" else 0)
 
 
 @pytest.mark.parametrize("usecase", ["bf16", "fp8"])

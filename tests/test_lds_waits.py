@@ -13,21 +13,32 @@ from lds_wait_check import check_function, gemm_functions
 from mixture_experts_expert_mm_amd import _build
 
 
-@pytest.fixture(scope="module")
-def gemm_asm(tmp_path_factory):
-    out = tmp_path_factory.mktemp("asm") / "mm_gemm.s"
+def _asm(tmp_path_factory, src):
+    out = tmp_path_factory.mktemp("asm") / (src + ".s")
     cmd = [_build.HIPCC, *[f for f in _build.FLAGS if f != "-fPIC"], "--cuda-device-only", "-S",
-           os.path.join(_build.CSRC, "mm_gemm.hip"), "-o", str(out)]
+           os.path.join(_build.CSRC, src), "-o", str(out)]
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     assert r.returncode == 0, r.stdout
     return out.read_text()
 
 
-def test_every_gemm_kernel_waits_before_use(gemm_asm):
-    names = gemm_functions(gemm_asm)
-    assert len(names) >= 12
+@pytest.fixture(scope="module")
+def gemm_asm(tmp_path_factory):
+    return _asm(tmp_path_factory, "mm_gemm.hip")
+
+
+@pytest.fixture(scope="module")
+def mega_asm(tmp_path_factory):
+    return _asm(tmp_path_factory, "mm_mega.hip")
+
+
+@pytest.mark.parametrize("which,min_kernels", [("gemm", 12), ("mega", 6)])
+def test_every_gemm_kernel_waits_before_use(which, min_kernels, request):
+    text = request.getfixturevalue(which + "_asm")
+    names = gemm_functions(text)
+    assert len(names) >= min_kernels
     for n in names:
-        report, nreads = check_function(gemm_asm, n)
+        report, nreads = check_function(text, n)
         assert nreads > 0, n
         assert report == [], (n, report[:5])
 
