@@ -8,14 +8,11 @@ namespace mm {
 // ---------------------------------------------------------------------------
 // reset of the per-call counters and control words
 // ---------------------------------------------------------------------------
-__global__ void k_zero(int32_t* __restrict__ counts, int E, uint32_t* __restrict__ a_amax, int64_t P,
-                       uint32_t* __restrict__ ctl) {
+__global__ void k_zero(int32_t* __restrict__ counts, int E, uint32_t* __restrict__ ctl) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   if (counts)
     for (int64_t j = i; j < E; j += stride) counts[j] = 0;
-  if (a_amax)
-    for (int64_t j = i; j < P; j += stride) a_amax[j] = 0u;
   if (ctl && i < kCtlWords) ctl[i] = 0u;
 }
 
@@ -77,12 +74,10 @@ __global__ __launch_bounds__(256) void k_transpose(const T* __restrict__ in, T* 
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-hipError_t launch_zero(int32_t* counts, int E, uint32_t* a_amax, int64_t P, uint32_t* ctl, hipStream_t s) {
-  const int64_t n = a_amax ? (P > E ? P : E) : E;
-  int grid = (int)((n + 255) / 256);
-  if (grid > 1024) grid = 1024;
+hipError_t launch_zero(int32_t* counts, int E, uint32_t* ctl, hipStream_t s) {
+  int grid = (E + 255) / 256;
   if (grid < 1) grid = 1;
-  hipLaunchKernelGGL(k_zero, dim3(grid), dim3(256), 0, s, counts, E, a_amax, P, ctl);
+  hipLaunchKernelGGL(k_zero, dim3(grid), dim3(256), 0, s, counts, E, ctl);
   return hipGetLastError();
 }
 

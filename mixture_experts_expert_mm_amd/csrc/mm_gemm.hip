@@ -20,7 +20,7 @@ static hipError_t launch_one(const GemmArgs& a, int grid, hipStream_t s) {
   // requantisation that follows Linear1 would turn that rounding into code
   // changes.  Linear2 keeps the e4m3 MFMA (nothing is quantised after it).
   constexpr bool WIDEN = (UC == UC_FP8) && (MODE == 0);
-  constexpr size_t lds = (size_t)lds_bytes_of<BM, MODE>();
+  constexpr size_t lds = (size_t)lds_bytes_of<BM>();
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t err = hipFuncSetAttribute((const void*)k_gemm<UC, BM, MODE, WIDEN>,

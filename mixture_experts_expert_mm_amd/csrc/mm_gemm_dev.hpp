@@ -7,8 +7,8 @@
 //   epilogue (step 2: A = SiLU(H[:, :I]) * H[:, I:]).  The prepared W1 rows
 //   interleave 32 gate columns with the 32 matching up columns, so every lane
 //   holds a gate accumulator and its up partner.  A16W16 stores A in bf16;
-//   A8W8 dequantises (C * s^W1) * s^X, stores A in float32 and records the
-//   row amax for the per-row requantisation (step 3).
+//   A8W8 dequantises (C * s^W1) * s^X and stores A in float32 for the
+//   per-row requantisation (step 3), which finds the row amax itself.
 // Linear2 (mode 1): Y_e = A_e . W2[e] (A8W8: (D * s^W2) * s^A), times the
 //   route's gate weight G[i,k]; the weighted row is written to the route's
 //   float32 combine slot i*K+k (Token Combine sums the slots in order).
@@ -43,23 +43,16 @@ template <int BM> struct TileShape;
 template <> struct TileShape<64> { static constexpr int WM = 1, WN = 4; };
 template <> struct TileShape<128> { static constexpr int WM = 2, WN = 4; };
 template <int BM> constexpr int threads_of() { return 64 * TileShape<BM>::WM * TileShape<BM>::WN; }
-// LDS ring slots: a 256-row tile's stage is 64 KB, so only two fit
-template <int BM> constexpr int stages_of() { return BM >= 256 ? 2 : 3; }
-constexpr int kLdsMax = 152 * 1024;   // dynamic LDS left beside the expert tables
-// Epilogue: the float32 output tile goes through LDS in NPASS row bands
-// (Linear1 keeps the 128 SwiGLU columns, Linear2 / raw all 256), plus three
-// per-row arrays.  The pitch is 8 (mod 16) floats so the two lane halves of
-// an accumulator write land in different bank halves.
-template <int MODE> constexpr int ocols_of() { return MODE == 0 ? 128 : 256; }
-template <int BM, int MODE> constexpr int epi_bytes(int npass) { return (BM / npass) * (ocols_of<MODE>() + 8) * 4 + 3 * BM * 4; }
-template <int BM, int MODE> constexpr int epi_passes() {
-  return epi_bytes<BM, MODE>(1) <= kLdsMax ? 1 : epi_bytes<BM, MODE>(2) <= kLdsMax ? 2 : 4;
-}
-template <int BM, int MODE> constexpr int lds_bytes_of() {
-  const int ring = stages_of<BM>() * (BM + 256) * 128;
-  const int epi = epi_bytes<BM, MODE>(epi_passes<BM, MODE>());
-  return ring > epi ? ring : epi;
-}
+constexpr int kStages = 3;   // LDS ring slots
+// Per-row data of a tile for its epilogue, two tiles' worth (the next tile's
+// is written while the current one is still being stored): 16 bytes a row.
+struct RowInfo {
+  int32_t route;   // Linear2: route i*K+k of the row (-1: no store)
+  float gw;        // Linear2: gate weight G[i,k]
+  float rs;        // s^X (Linear1, A8W8) or s^A (Linear2, A8W8) of the row
+  float pad;
+};
+template <int BM> constexpr int lds_bytes_of() { return kStages * (BM + 256) * 128 + 2 * BM * (int)sizeof(RowInfo); }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -71,8 +64,15 @@ __device__ __forceinline__ u32x4 ds_read16(uint32_t addr) {
   asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
   return v;
 }
+template <int OFF>
+__device__ __forceinline__ uint32_t ds_read4(uint32_t addr) {
+  uint32_t v;
+  asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+  return v;
+}
 template <int N>
 __device__ __forceinline__ void lgkm_wait() { asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N)); }
+__device__ __forceinline__ void tie(uint32_t& v) { asm volatile("" : "+v"(v)); }
 __device__ __forceinline__ void tie(u32x4& v) { asm volatile("" : "+v"(v)); }
 // wait until at most VM of this wave's LDS-DMA loads are in flight and all its
 // LDS reads returned, then the workgroup barrier
@@ -147,8 +147,12 @@ __device__ __forceinline__ void widen_e4m3(const u32x4& w, u32x4& lo, u32x4& hi)
 // MFMA operand covers chunks 4h..4h+3 of its row (h = lane / 32), the same
 // chunks for A and B, so every product pairs equal k.
 //
-// Epilogue: the accumulators go through the (then idle) LDS ring as a
-// float32 tile, so each output row leaves as one contiguous store.
+// Tiles run back to back: once a tile's last MFMAs are issued the ring is
+// free, so the first stages of the workgroup's next tile are issued at once
+// and the finished tile's epilogue (stores straight from the accumulators:
+// lanes 0-31 and 32-63 each write 32 consecutive columns of one row) runs
+// while they are in flight.
+
 // The argument block with every field forced into scalar registers: the
 // fused kernel loads its arguments from memory, and a tile base the compiler
 // cannot prove uniform would turn each buffer load into a loop over lanes.
@@ -162,6 +166,14 @@ __device__ __forceinline__ T* uniform_ptr(T* p) {
 
 __device__ __forceinline__ int uniform_int(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// The same pointer typed as global memory: after the round trip through an
+// integer the compiler no longer knows the address space and would use flat
+// instructions.
+template <typename T>
+__device__ __forceinline__ __attribute__((address_space(1))) T* gp(T* p) {
+  return (__attribute__((address_space(1))) T*)p;
+}
+
 __device__ __forceinline__ GemmArgs uniform_args(const GemmArgs& in) {
   GemmArgs a = in;
   a.A = uniform_ptr(in.A);
@@ -173,7 +185,6 @@ __device__ __forceinline__ GemmArgs uniform_args(const GemmArgs& in) {
   a.w_scale = uniform_ptr(in.w_scale);
   a.a_out = uniform_ptr(in.a_out);
   a.a_stage = uniform_ptr(in.a_stage);
-  a.a_amax = uniform_ptr(in.a_amax);
   a.a_scale = uniform_ptr(in.a_scale);
   a.topk_w = uniform_ptr(in.topk_w);
   a.contrib = uniform_ptr(in.contrib);
@@ -189,10 +200,42 @@ __device__ __forceinline__ GemmArgs uniform_args(const GemmArgs& in) {
   return a;
 }
 
+// One entry of the workgroup's tile list, resolved.
+struct TileRef {
+  int e, row0, n0, valid;
+  const uint8_t* abase;   // first A row of the tile
+  const uint8_t* bbase;   // first B row (prepared weights) of the tile
+};
+
+// Tile order: expert-major, then N-block, then M-block, so tiles that run
+// together share weight tiles (same expert and N-block) and activation tiles
+// (same M-block).  The expert of a tile is the largest e with
+// (off[e] / BM) * n_tiles <= tile.
+template <int BM>
+__device__ __forceinline__ TileRef resolve_tile(const GemmArgs& a, const int32_t* off_s, const int32_t* cnt_s,
+                                               int tile, int n_tiles, int kbytes) {
+  int lo = 0, hi = a.E;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if ((off_s[mid] / BM) * n_tiles <= tile) lo = mid; else hi = mid;
+  }
+  TileRef r;
+  r.e = lo;
+  const int mb0 = off_s[lo] / BM, nmb = (off_s[lo + 1] - off_s[lo]) / BM;
+  const int local = tile - mb0 * n_tiles;
+  const int nblk = local / nmb, mblk = mb0 + local % nmb;
+  r.row0 = mblk * BM;
+  r.n0 = nblk * kBN;
+  r.valid = min(BM, off_s[lo] + cnt_s[lo] - r.row0);
+  r.abase = a.A + (int64_t)r.row0 * kbytes;
+  r.bbase = a.B + ((int64_t)lo * a.N + r.n0) * kbytes;
+  return r;
+}
+
 template <int UC, int BM, int MODE, bool WIDEN>
 __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, int32_t* off_s, int32_t* cnt_s) {
   const GemmArgs a = uniform_args(args);
-  constexpr int WM = TileShape<BM>::WM, WN = TileShape<BM>::WN, S = stages_of<BM>();
+  constexpr int WM = TileShape<BM>::WM, WN = TileShape<BM>::WN, S = kStages;
   constexpr int NT = threads_of<BM>(), NW = NT / 64;
   constexpr int WTM = BM / WM, WTN = kBN / WN;
   constexpr int MB = WTM / 32, NB = WTN / 32;
@@ -212,20 +255,16 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
   // phase 0 may start once only the reads of the later phases are in flight
   constexpr int P0WAIT = (4 * NFR - RPP) > 15 ? 15 : (4 * NFR - RPP);
   static_assert(BM % (8 * NW) == 0, "A rows fill whole DMA instructions");
-  constexpr int OCOLS = ocols_of<MODE>();
-  constexpr int OPITCH = OCOLS + 8;
-  constexpr int NPASS = epi_passes<BM, MODE>(), EPR = BM / NPASS;   // epilogue row bands
-  static_assert(epi_bytes<BM, MODE>(NPASS) <= kLdsMax && EPR % 32 == 0, "epilogue band fits LDS");
+  static_assert(MODE != 0 || NB % 2 == 0, "Linear1 waves hold whole gate/up pairs");
   typedef typename Acc<UC>::type AccT;
-
 
   const int t = threadIdx.x, l = lane_id();
   const int wv = __builtin_amdgcn_readfirstlane(t / 64);
   const int h = l / 32, lr = l % 32;
   const int wm = wv / WN, wn = wv % WN;
 
-  for (int e = t; e <= a.E; e += NT) off_s[e] = a.offsets[e];
-  for (int e = t; e < a.E; e += NT) cnt_s[e] = a.counts[e];
+  for (int e = t; e <= a.E; e += NT) off_s[e] = gp(a.offsets)[e];
+  for (int e = t; e < a.E; e += NT) cnt_s[e] = gp(a.counts)[e];
   __syncthreads();
   // The offsets must describe a padded pool inside P rows: multiples of
   // BLOCK_M, each expert's block range holding its count.  Anything else
@@ -243,6 +282,8 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
   const int n_tiles = a.N / kBN;
   const int total = offsets_ok ? (off_s[a.E] / BM) * n_tiles : 0;
   const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_ptr_t)lds;
+  RowInfo* rowinfo = reinterpret_cast<RowInfo*>(lds + S * STAGE);   // [2][BM]
+  const uint32_t rowinfo_base = lds_base + (uint32_t)(S * STAGE);
 
   // per-lane LDS addresses of the four fragment chunks (stage slot added per stage)
   uint32_t aoff[4], boff[4];
@@ -259,39 +300,57 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
   static_assert(NW % 2 == 0, "DMA swizzle assumes an even wave count");
   const uint32_t voff =
       (uint32_t)((8 * wv + l / 8) * kbytes + (((l & 7) ^ ((4 * (wv & 1) + l / 16) & 7)) << 4));
-  float* otile = reinterpret_cast<float*>(lds);                // epilogue band [EPR][OPITCH]
-  float* orow = reinterpret_cast<float*>(lds) + EPR * OPITCH;  // per-row s^X (Linear1) / s^A (Linear2) [BM]
-  float* ogw = orow + BM;                                      // per-row gate weight [BM]
-  int32_t* oroute = reinterpret_cast<int32_t*>(ogw + BM);     // per-row route i*K+k [BM]
+  const int abytes = BM * kbytes, bbytes = kBN * kbytes;
+#define MM_DMA(tr_, i_, kb_) \
+  dma_one<NW, BM, STAGE, S>(lds, (tr_).abase, abytes, (tr_).bbase, bbytes, voff, wv, kbytes, (i_), (kb_))
 
-  // Tile order: expert-major, then N-block, then M-block, so tiles that run
-  // together share weight tiles (same expert and N-block) and activation
-  // tiles (same M-block).  Workgroup w runs on XCD w % 8 (round-robin
-  // dispatch); each XCD walks its own contiguous slice of the list so the
-  // sharing happens inside one L2.
+  // Per-row epilogue data of tile `tr` into rowinfo[buf] (thread r: row r).
+  auto fill_rowinfo = [&](const TileRef& tr, int buf) {
+    for (int r = t; r < BM; r += NT) {
+      RowInfo ri{-1, 0.0f, 1.0f, 0.0f};
+      if (r < tr.valid) {
+        const int64_t p = (int64_t)tr.row0 + r;
+        if constexpr (MODE == 0 && UC != UC_BF16) ri.rs = gp(a.x_scale)[p];
+        if constexpr (MODE == 1) {
+          int32_t route = gp(a.pool_src)[p];
+          if (route < 0 || route >= a.routes) route = -1;   // not a route of this call: row left out
+          ri.route = route;
+          ri.gw = route >= 0 ? gp(a.topk_w)[route] : 0.0f;
+          if constexpr (UC != UC_BF16) ri.rs = gp(a.a_scale)[p];
+        }
+      }
+      rowinfo[buf * BM + r] = ri;
+    }
+  };
+  // The first S stages of tile `tr` (its row data goes first: no DMA is in
+  // flight yet, so the compiler's waits for those loads cost nothing).
+  auto start_tile = [&](const TileRef& tr, int buf) {
+    fill_rowinfo(tr, buf);
+#pragma unroll
+    for (int st = 0; st < S; ++st)
+      if (st < nk) {
+#pragma unroll
+        for (int x = 0; x < D; ++x) MM_DMA(tr, x, st);
+      }
+  };
+
+  // Workgroup w runs on XCD w % 8 (round-robin dispatch); each XCD walks its
+  // own contiguous slice of the tile list so the sharing happens inside one L2.
   const int nxcd = gridDim.x >= 8 ? 8 : 1;
   const int xcd = blockIdx.x % nxcd, wgx = blockIdx.x / nxcd, per_x = gridDim.x / nxcd;
   const int slice = (total + nxcd - 1) / nxcd;
   const int t_beg = xcd * slice, t_end = min(total, t_beg + slice);
   const bool in_grid = (int)blockIdx.x < per_x * nxcd;   // a tail beyond a multiple of 8 stays idle
-  for (int tile = t_beg + wgx; in_grid && tile < t_end; tile += per_x) {
-    // expert of this tile: the largest e with (off[e] / BM) * n_tiles <= tile
-    int lo = 0, hi = a.E;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if ((off_s[mid] / BM) * n_tiles <= tile) lo = mid; else hi = mid;
-    }
-    const int e = lo;
-    const int mb0 = off_s[e] / BM, nmb = (off_s[e + 1] - off_s[e]) / BM;
-    const int local = tile - mb0 * n_tiles;
-    const int nblk = local / nmb, mblk = mb0 + local % nmb;
-    const int row0 = mblk * BM, n0 = nblk * kBN;
-    const int valid = min(BM, off_s[e] + cnt_s[e] - row0);
-    const uint8_t* abase = a.A + (int64_t)row0 * kbytes;
-    const uint8_t* bbase = a.B + ((int64_t)e * a.N + n0) * kbytes;
 
-    const int abytes = BM * kbytes, bbytes = kBN * kbytes;
-#define MM_DMA(i_, kb_) dma_one<NW, BM, STAGE, S>(lds, abase, abytes, bbase, bbytes, voff, wv, kbytes, (i_), (kb_))
+  int tile = t_beg + wgx;
+  bool have = in_grid && tile < t_end;
+  TileRef cur{};
+  int buf = 0;
+  if (have) {
+    cur = resolve_tile<BM>(a, off_s, cnt_s, tile, n_tiles, kbytes);
+    start_tile(cur, buf);
+  }
+  while (have) {
     AccT acc[MB][NB];
 #pragma unroll
     for (int i = 0; i < MB; ++i)
@@ -343,7 +402,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
     // Scheduling barriers keep this order.
     auto step = [&](int kb, auto refill_tag, auto more_tag, auto vm_tag) {
       constexpr bool REFILL = decltype(refill_tag)::value, MORE = decltype(more_tag)::value;
-      constexpr int VM = decltype(vm_tag)::value;   // this wave's DMA loads still allowed in flight
+      constexpr int VM = decltype(vm_tag)::value;   // this wave's loads still allowed in flight
       lgkm_wait<P0WAIT>();
       tie_chunks(0, CPP);
       __builtin_amdgcn_sched_barrier(0);
@@ -358,11 +417,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
       tie_chunks(CPP, 4);
       __builtin_amdgcn_sched_barrier(0);
       const uint32_t so = (uint32_t)(((kb + 1) % S) * STAGE);
-#ifndef MM_DMA_SPAN
-#define MM_DMA_SPAN 0
-#endif
-      // MFMAs after the barrier over which the DMA issues are spread
-      constexpr int NMR = MM_DMA_SPAN == 0 ? (NPH - 1) * MPP : (MM_DMA_SPAN < (NPH - 1) * MPP ? MM_DMA_SPAN : (NPH - 1) * MPP);
+      constexpr int NMR = (NPH - 1) * MPP;   // MFMAs after the barrier: DMA issues spread over them
       int dm = 0;
 #pragma unroll
       for (int p = 1; p < NPH; ++p) {
@@ -372,10 +427,10 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
           mfma_at(p, mi);
           if constexpr (REFILL) {
             const int m = (p - 1) * MPP + mi;
-            const int target = m < NMR ? ((m + 1) * D + NMR - 1) / NMR : D;
+            const int target = ((m + 1) * D + NMR - 1) / NMR;
 #pragma unroll
             for (int x = 0; x < D; ++x)
-              if (x >= dm && x < target) MM_DMA(x, kb + S);
+              if (x >= dm && x < target) MM_DMA(cur, x, kb + S);
             dm = target < D ? target : D;
           }
           if constexpr (MORE) {
@@ -395,20 +450,10 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
       __builtin_amdgcn_sched_barrier(0);
     };
 
-    // every wave is done with the previous tile's LDS use and stores
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-#pragma unroll
-    for (int st = 0; st < S; ++st)
-      if (st < nk) {
-#pragma unroll
-        for (int x = 0; x < D; ++x) MM_DMA(x, st);
-      }
-    // stage 0 landed for every wave (the later stages may still be in flight)
-    if constexpr (S == 3) {
-      if (nk >= 3) vm_barrier<2 * D>(); else if (nk == 2) vm_barrier<D>(); else vm_barrier<0>();
-    } else {
-      if (nk >= 2) vm_barrier<D>(); else vm_barrier<0>();
-    }
+    // stage 0 landed for every wave (later stages, and the previous tile's
+    // epilogue stores, may still be in flight: counting them too only makes
+    // the wait stricter)
+    if (nk >= 3) vm_barrier<2 * D>(); else if (nk == 2) vm_barrier<D>(); else vm_barrier<0>();
 #pragma unroll
     for (int r = 0; r < 4 * NFR; ++r) read_frag(f, r, aoff, boff, 0u);
     // Every barrier below has a compile-time DMA count: stage kb+S refills
@@ -417,131 +462,132 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
     const std::integral_constant<bool, false> no;
     const std::integral_constant<int, D> vm_d;
     const std::integral_constant<int, 0> vm_0;
-    if constexpr (S == 3) {
-      if (nk >= 3) {
-        for (int kb = 0; kb < nk - 3; ++kb) step(kb, yes, yes, vm_d);
-        step(nk - 3, no, yes, vm_d);
-      }
-    } else {
-      for (int kb = 0; kb < nk - 2; ++kb) step(kb, yes, yes, vm_0);
+    if (nk >= 3) {
+      for (int kb = 0; kb < nk - 3; ++kb) step(kb, yes, yes, vm_d);
+      step(nk - 3, no, yes, vm_d);
     }
     if (nk >= 2) step(nk - 2, no, yes, vm_0);
     step(nk - 1, no, no, vm_0);
-#undef MM_DMA
-    // ------------------------------------------------------------ epilogue
-    // all waves are done reading the ring: it becomes the output band
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if constexpr (MODE == 0 && UC != UC_BF16) {
-      for (int r = t; r < BM; r += NT) orow[r] = r < valid ? a.x_scale[row0 + r] : 0.0f;
-    }
-    if constexpr (MODE == 1) {
-      // per-row route, A8W8 row scale s^A and the route's gate weight G[i,k]
-      for (int r = t; r < BM; r += NT) {
-        if (r < valid) {
-          const int64_t p = (int64_t)row0 + r;
-          int32_t route = a.pool_src[p];
-          if (route < 0 || route >= a.routes) route = -1;   // not a route of this call: row left out
-          oroute[r] = route;
-          ogw[r] = route >= 0 ? a.topk_w[route] : 0.0f;
-          orow[r] = (UC != UC_BF16) ? a.a_scale[p] : 1.0f;
+
+    // ------------------------------------------------ next tile, epilogue
+    // per-column scales (A8W8) of this wave's columns, loaded before the next
+    // tile's copies so that waiting for them does not wait for those
+    float cs0[NB], cs1[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      cs0[j] = 1.0f;
+      cs1[j] = 1.0f;
+      if constexpr (MODE == 0 && UC != UC_BF16) {
+        if (j < NB / 2) {
+          const int col = cur.n0 / 2 + wn * (WTN / 2) + j * 32 + lr;
+          cs0[j] = gp(a.w_scale)[(int64_t)cur.e * 2 * a.I + col];           // gate column
+          cs1[j] = gp(a.w_scale)[(int64_t)cur.e * 2 * a.I + a.I + col];     // up column
         }
       }
+      if constexpr (MODE == 1 && UC != UC_BF16) cs0[j] = gp(a.w_scale)[(int64_t)cur.e * a.H + cur.n0 + wn * WTN + j * 32 + lr];
     }
-    if constexpr (MODE != 2) __syncthreads();
+    // the scales are in registers before the next tile's copies go out (a
+    // wait the compiler sees, so it places none later that would also wait
+    // for those copies): s_waitcnt vmcnt(0)
+    if constexpr (UC != UC_BF16 && MODE != 2) __builtin_amdgcn_s_waitcnt(0x0F70);
+    // every wave is done reading the ring: the next tile's stages go out now
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    const int ntile = tile + per_x;
+    const bool nhave = ntile < t_end;
+    TileRef nxt{};
+    if (nhave) {
+      nxt = resolve_tile<BM>(a, off_s, cnt_s, ntile, n_tiles, kbytes);
+      start_tile(nxt, buf ^ 1);
+    }
 #pragma unroll
-    for (int pass = 0; pass < NPASS; ++pass) {
-      const int rlo = pass * EPR;   // rows rlo .. rlo + EPR - 1 of the tile
-      if (pass > 0) __syncthreads();   // the previous band has left LDS
+    for (int i = 0; i < MB; ++i) {
+      const int rb = wm * WTM + i * 32 + 4 * h;   // this lane's rows: rb + 8*(q/4) + q%4
+      // row data of the 16 rows, read outside the compiler's view (it would
+      // otherwise wait for the next tile's LDS copies first): Linear2 needs
+      // the whole entry, A8W8 Linear1 only s^X
+      u32x4 ri[MODE == 1 ? 16 : 1];
+      uint32_t sxr[(MODE == 0 && UC != UC_BF16) ? 16 : 1];
+      if constexpr (MODE == 1 || (MODE == 0 && UC != UC_BF16)) {
 #pragma unroll
-      for (int i = 0; i < MB; ++i) {
-        if ((wm * WTM + i * 32) / EPR != pass) continue;
-        const int rb = wm * WTM + i * 32 + 4 * h;
-        if constexpr (MODE == 0) {
-          // gate/up pair j -> 32 output columns
+        for (int q = 0; q < 16; ++q) {
+          const int r = rb + 8 * (q / 4) + (q % 4);
+          const uint32_t ad = rowinfo_base + (uint32_t)((buf * BM + r) * (int)sizeof(RowInfo));
+          if constexpr (MODE == 1) ri[q] = ds_read16<0>(ad);
+          else sxr[q] = ds_read4<8>(ad);
+        }
+        lgkm_wait<0>();
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          if constexpr (MODE == 1) tie(ri[q]);
+          else tie(sxr[q]);
+        }
+      }
+      if constexpr (MODE == 0) {
+        // tile bases are uniform; per-element offsets stay 32-bit (BM*I < 2^31)
+        uint16_t* const obase = static_cast<uint16_t*>(a.a_out) + (int64_t)cur.row0 * a.I + cur.n0 / 2;
+        float* const sbase = a.a_stage + (int64_t)cur.row0 * a.I + cur.n0 / 2;
+        // the lane's first row offset, laundered so that the compiler does not
+        // hoist the 16 per-row offsets out of the tile loop (they would stay
+        // live through the mainloop)
+        int lane_off = rb * a.I + wn * (WTN / 2) + lr;
+        asm volatile("" : "+v"(lane_off));
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int r = rb + 8 * (q / 4) + (q % 4);
 #pragma unroll
           for (int j = 0; j < NB / 2; ++j) {
-            const int oc = wn * (WTN / 2) + j * 32 + lr;
-            float gs = 1.0f, us = 1.0f;
+            const int oc = lane_off + (8 * (q / 4) + (q % 4)) * a.I + j * 32;
+            float g = acc_to_f32(acc[i][2 * j][q]);
+            float u = acc_to_f32(acc[i][2 * j + 1][q]);
             if constexpr (UC != UC_BF16) {
-              const int col = n0 / 2 + oc;
-              gs = a.w_scale[(int64_t)e * 2 * a.I + col];
-              us = a.w_scale[(int64_t)e * 2 * a.I + a.I + col];
+              const float sx = __uint_as_float(sxr[q]);
+              g = (g * cs0[j]) * sx;
+              u = (u * cs1[j]) * sx;
             }
-#pragma unroll
-            for (int q = 0; q < 16; ++q) {
-              const int r = rb + 8 * (q / 4) + (q % 4);
-              float g = acc_to_f32(acc[i][2 * j][q]);
-              float u = acc_to_f32(acc[i][2 * j + 1][q]);
-              if constexpr (UC != UC_BF16) {
-                const float sx = orow[r];
-                g = (g * gs) * sx;
-                u = (u * us) * sx;
-              }
-              otile[(r - rlo) * OPITCH + oc] = silu(g) * u;
-            }
-          }
-        } else {
-#pragma unroll
-          for (int j = 0; j < NB; ++j) {
-            const int oc = wn * WTN + j * 32 + lr;
-            float ws = 1.0f;
-            if constexpr (MODE == 1 && UC != UC_BF16) ws = a.w_scale[(int64_t)e * a.H + n0 + oc];
-#pragma unroll
-            for (int q = 0; q < 16; ++q) {
-              const int r = rb + 8 * (q / 4) + (q % 4);
-              if constexpr (MODE == 2) reinterpret_cast<int32_t*>(otile)[(r - rlo) * OPITCH + oc] = acc[i][j][q];
-              else otile[(r - rlo) * OPITCH + oc] = acc_to_f32(acc[i][j][q]) * ws;
+            const float v = silu(g) * u;
+            if (r < cur.valid) {
+              if constexpr (UC == UC_BF16) gp(obase)[oc] = f32_to_bf16_bits(v);
+              else gp(sbase)[oc] = v;
             }
           }
         }
-      }
-      __syncthreads();
-      // cooperative row-major pass over the band: 16-byte column chunks, one
-      // row per group of CPR consecutive threads (EPR * CPR is a multiple of
-      // the thread count, so every thread runs the same number of trips)
-      constexpr int CPR = OCOLS / 4;                     // float4 chunks per row
-      static_assert((EPR * CPR) % NT == 0 && CPR <= 64 && 64 % CPR == 0, "row groups stay inside a wave");
-      for (int idx = t; idx < EPR * CPR; idx += NT) {
-        const int rr = idx / CPR, c4 = idx % CPR;
-        const int r = rlo + rr;
-        const bool ok = r < valid;
-        const int64_t p = (int64_t)row0 + r;
-        const f32x4 v = *reinterpret_cast<const f32x4*>(otile + rr * OPITCH + c4 * 4);
-        if constexpr (MODE == 0) {
-          const int col = n0 / 2 + c4 * 4;
-          if constexpr (UC == UC_BF16) {
-            uint2 o;
-            o.x = pack_bf16x2(v[0], v[1]);
-            o.y = pack_bf16x2(v[2], v[3]);
-            if (ok) *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.a_out) + p * a.I + col) = o;
-          } else {
-            if (ok) *reinterpret_cast<f32x4*>(a.a_stage + p * a.I + col) = v;
-            // row amax of this tile's columns; the row's tiles combine by atomicMax
-            float m = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+      } else {
+        int32_t* const rbase = a.raw_out + (int64_t)cur.row0 * a.N;
+        int lane_row = rb;
+        asm volatile("" : "+v"(lane_row));   // keeps the row offsets inside the tile loop
 #pragma unroll
-            for (int o = CPR / 2; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-            if (ok && c4 == 0) atomicMax(&a.a_amax[p], __float_as_uint(m));
-          }
-        } else if constexpr (MODE == 1) {
-          // contribution of route i*K+k: ((D * s^W2) * s^A) * G[i,k]
-          const float rs = orow[r], gw = ogw[r];
-          f32x4 o;
+        for (int j = 0; j < NB; ++j) {
+          const int n = cur.n0 + wn * WTN + j * 32 + lr;
 #pragma unroll
-          for (int c = 0; c < 4; ++c) o[c] = (UC != UC_BF16) ? (v[c] * rs) * gw : v[c] * gw;
-          if (ok && oroute[r] >= 0) *reinterpret_cast<f32x4*>(a.contrib + (int64_t)oroute[r] * a.H + n0 + c4 * 4) = o;
-        } else {
-          const int n = n0 + c4 * 4;
-          int col = n;
-          if (a.gate_up_group > 0) {
-            const int g2 = 2 * a.gate_up_group;
-            const int qq = n / g2, m = n % g2;
-            col = (m < a.gate_up_group) ? qq * a.gate_up_group + m : a.I + qq * a.gate_up_group + (m - a.gate_up_group);
+          for (int q = 0; q < 16; ++q) {
+            const int r = rb + 8 * (q / 4) + (q % 4);
+            if constexpr (MODE == 1) {
+              // contribution of route i*K+k: ((D * s^W2) * s^A) * G[i,k]
+              const int32_t route = (int32_t)ri[q][0];
+              const float gw = __uint_as_float(ri[q][1]);
+              const float v = acc_to_f32(acc[i][j][q]) * cs0[j];
+              const float o = (UC != UC_BF16) ? (v * __uint_as_float(ri[q][2])) * gw : v * gw;
+              if (route >= 0) gp(a.contrib)[(int64_t)route * a.H + n] = o;
+            } else {
+              int col = n;
+              if (a.gate_up_group > 0) {
+                const int g2 = 2 * a.gate_up_group;
+                const int qq = n / g2, m = n % g2;
+                col = (m < a.gate_up_group) ? qq * a.gate_up_group + m : a.I + qq * a.gate_up_group + (m - a.gate_up_group);
+              }
+              if (r < cur.valid) gp(rbase)[(lane_row + 8 * (q / 4) + (q % 4)) * a.N + col] = acc[i][j][q];
+            }
           }
-          if (ok) *reinterpret_cast<i32x4*>(a.raw_out + p * a.N + col) = __builtin_bit_cast(i32x4, v);
         }
       }
     }
+    tile = ntile;
+    have = nhave;
+    cur = nxt;
+    buf ^= 1;
   }
+#undef MM_DMA
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
   __syncthreads();   // the block is done with LDS
 }
 
@@ -560,9 +606,16 @@ __device__ __forceinline__ void requant_row(const RequantArgs& a, int64_t p, con
     if (off_s[mid] <= p) lo = mid; else hi = mid;
   }
   if (p >= (int64_t)off_s[lo] + cnt_s[lo]) return;
-  const float qmax = (UC == UC_I8) ? 127.0f : 448.0f;
-  const float s = fmaxf(__uint_as_float(a.a_amax[p]) / qmax, 1e-8f);
   const float4* src = reinterpret_cast<const float4*>(a.a_stage + p * a.I);
+  // row amax over all I columns (exact: a max), then the codes
+  float m = 0.0f;
+  for (int c = l; c < a.I / 4; c += 64) {
+    const float4 v = src[c];
+    m = fmaxf(fmaxf(m, fmaxf(fabsf(v.x), fabsf(v.y))), fmaxf(fabsf(v.z), fabsf(v.w)));
+  }
+  m = wave_max(m);
+  const float qmax = (UC == UC_I8) ? 127.0f : 448.0f;
+  const float s = fmaxf(m / qmax, 1e-8f);
   uint2* dst = reinterpret_cast<uint2*>(static_cast<uint8_t*>(a.a_pool) + p * a.I);
   for (int c = l; c < a.I / 8; c += 64) {
     const float4 v0 = src[2 * c], v1 = src[2 * c + 1];

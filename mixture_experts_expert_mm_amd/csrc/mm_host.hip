@@ -36,7 +36,7 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 // ---------------------------------------------------------------- workspace
 struct WsLayout {
-  int64_t ctl, wave_base, a_amax, a_stage, contrib, end;                     // 3-call scratch
+  int64_t ctl, wave_base, a_stage, contrib, end;                             // 3-call scratch
   int64_t mega_args, offsets, pool_src, route_to_pool, x_pool, x_pool_scale, a_pool, a_pool_scale, fused_end;
 };
 
@@ -49,7 +49,6 @@ WsLayout ws_layout(const mm_plan& pl) {
   auto take = [&](int64_t bytes) { const int64_t at = o; o = align_up(o + bytes, kAlign); return at; };
   L.ctl = take(kCtlWords * 4);
   L.wave_base = take(dispatch_waves(p.num_tokens, (int)p.num_topk) * p.num_experts * 4);
-  L.a_amax = q ? take(P * 4) : -1;
   L.a_stage = q ? take(P * p.intermediate_hidden * 4) : -1;
   L.contrib = take(R * p.hidden * 4);
   L.end = o;
@@ -189,14 +188,12 @@ GemmArgs l1_args(const mm_plan& pl, const int32_t* offsets, const int32_t* count
   g.w_scale = w1_scale;
   g.a_out = a_pool;
   g.a_stage = at<float>(ws, L.a_stage);
-  g.a_amax = at<uint32_t>(ws, L.a_amax);
   return g;
 }
 
 RequantArgs requant_args(const mm_plan& pl, const GemmArgs& l1, void* a_pool, float* a_pool_scale) {
   RequantArgs r{};
   r.a_stage = l1.a_stage;
-  r.a_amax = l1.a_amax;
   r.offsets = l1.offsets;
   r.counts = l1.counts;
   r.E = l1.E;
@@ -252,7 +249,7 @@ mm_status do_dispatch(const mm_plan& pl, const int32_t* ids, const void* x, int3
                       int32_t* pool_src, int32_t* r2p, void* x_pool, float* x_pool_scale, void* ws, hipStream_t s) {
   const DispatchArgs d = dispatch_args(pl, ids, x, counts, offsets, pool_src, r2p, x_pool, x_pool_scale, ws);
   uint32_t* ctl = at<uint32_t>(ws, ws_layout(pl).ctl);
-  MM_TRY(run(MM_K_ZERO, s, [&] { return launch_zero(counts, d.E, nullptr, 0, ctl, s); }));
+  MM_TRY(run(MM_K_ZERO, s, [&] { return launch_zero(counts, d.E, ctl, s); }));
   MM_TRY(run(MM_K_COUNT, s, [&] { return launch_count(d, s); }));
   MM_TRY(run(MM_K_SCATTER, s, [&] { return launch_scatter(d, s); }));
   MM_TRY(run(MM_K_GATHER, s, [&] { return launch_gather(d, s); }));
@@ -265,8 +262,6 @@ mm_status do_l1(const mm_plan& pl, const int32_t* offsets, const int32_t* counts
   const mm_problem& p = pl.prob;
   const GemmArgs g = l1_args(pl, offsets, counts, x_pool, x_pool_scale, w1, w1_scale, a_pool, ws);
   const int grid = gemm_grid(pl.tile_l1, pl.pool_rows, g.N, num_cus());
-  if (p.usecase != MM_A16W16)
-    MM_TRY(run(MM_K_ZERO, s, [&] { return launch_zero(nullptr, 0, g.a_amax, pl.pool_rows, nullptr, s); }));
   MM_TRY(run(MM_K_L1, s, [&] { return launch_gemm(0, p.usecase, pl.tile_l1, g, grid, s); }));
   if (p.usecase != MM_A16W16) {
     const RequantArgs r = requant_args(pl, g, a_pool, a_pool_scale);

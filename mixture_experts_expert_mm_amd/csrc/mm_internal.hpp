@@ -54,7 +54,6 @@ struct GemmArgs {
   const float* w_scale;      // [E][N] formula order (A8W8)
   void* a_out;               // [P][I] bf16 (A16W16)
   float* a_stage;            // [P][I] f32 (A8W8)
-  uint32_t* a_amax;          // [P] (A8W8)
   // Linear2 (mode 1)
   const float* a_scale;      // [P] (A8W8)
   const float* topk_w;       // [T*K]
@@ -65,7 +64,6 @@ struct GemmArgs {
 
 struct RequantArgs {
   const float* a_stage;      // [P][I]
-  const uint32_t* a_amax;    // [P]
   const int32_t* offsets;    // [E+1]
   const int32_t* counts;     // [E]
   void* a_pool;              // [P][I] codes
@@ -99,7 +97,7 @@ struct MegaArgs {
 };
 
 // launchers (return hipError_t of the launch)
-hipError_t launch_zero(int32_t* counts, int E, uint32_t* a_amax, int64_t P, uint32_t* ctl, hipStream_t s);
+hipError_t launch_zero(int32_t* counts, int E, uint32_t* ctl, hipStream_t s);
 hipError_t launch_mega_prep(const MegaArgs& a, MegaArgs* dev_args, hipStream_t s);
 hipError_t launch_mega(int usecase, int tile, const MegaArgs* dev_args, int grid, hipStream_t s);
 int mega_grid(int tile, int num_cus);

@@ -79,7 +79,7 @@ __device__ bool grid_barrier(uint32_t* ctl, uint32_t n, uint32_t spin_limit, Bar
 
 template <int BM>
 constexpr int mega_lds_bytes() {
-  return lds_bytes_of<BM, 0>() > lds_bytes_of<BM, 1>() ? lds_bytes_of<BM, 0>() : lds_bytes_of<BM, 1>();
+  return lds_bytes_of<BM>();
 }
 
 template <int UC, int BM>
@@ -163,14 +163,11 @@ void k_mega(const MegaArgs* mp) {
 }
 
 // Pre-pass: clears the counters the fused kernel accumulates into (expert
-// counts, A8W8 row amax, control words) and stores the kernel's arguments
-// in the workspace.
-__global__ __launch_bounds__(256) void k_mega_prep(MegaArgs m, MegaArgs* out, int quantized) {
+// counts, control words) and stores the kernel's arguments in the workspace.
+__global__ __launch_bounds__(256) void k_mega_prep(MegaArgs m, MegaArgs* out) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t j = i; j < m.d.E; j += stride) m.d.counts[j] = 0;
-  if (quantized)
-    for (int64_t j = i; j < m.l1.P; j += stride) m.l1.a_amax[j] = 0u;
   if (i < kCtlWords) m.ctl[i] = 0u;
   constexpr int words = (int)(sizeof(MegaArgs) / 4);
   static_assert(sizeof(MegaArgs) % 4 == 0, "argument block copies as words");
@@ -212,12 +209,9 @@ static hipError_t launch_mega_bm(int tile, const MegaArgs* a, int grid, hipStrea
 }
 
 hipError_t launch_mega_prep(const MegaArgs& a, MegaArgs* dev_args, hipStream_t s) {
-  const int quantized = a.d.usecase != UC_BF16;
-  const int64_t n = quantized ? (a.l1.P > a.d.E ? a.l1.P : a.d.E) : a.d.E;
-  int grid = (int)((n + 255) / 256);
-  if (grid > 1024) grid = 1024;
+  int grid = (a.d.E + 255) / 256;
   if (grid < 1) grid = 1;
-  hipLaunchKernelGGL(k_mega_prep, dim3(grid), dim3(256), 0, s, a, dev_args, quantized);
+  hipLaunchKernelGGL(k_mega_prep, dim3(grid), dim3(256), 0, s, a, dev_args);
   return hipGetLastError();
 }
 
