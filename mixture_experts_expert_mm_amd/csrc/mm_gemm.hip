@@ -35,7 +35,7 @@ static hipError_t launch_one(const GemmArgs& a, int grid, hipStream_t s) {
 template <int UC, int MODE>
 static hipError_t launch_bm(int tile, const GemmArgs& a, int grid, hipStream_t s) {
   switch (tile) {
-    case TILE_M64_N256: return launch_one<UC, 64, MODE>(a, grid, s);
+    case TILE_M64_N128: return launch_one<UC, 64, MODE>(a, grid, s);
     default: return launch_one<UC, 128, MODE>(a, grid, s);
   }
 }
@@ -57,7 +57,7 @@ hipError_t launch_gemm(int mode, int usecase, int tile, const GemmArgs& a, int g
 }
 
 int gemm_grid(int tile, int64_t P, int N, int num_cus) {
-  const int64_t tiles = (P / tile_bm(tile)) * (int64_t)(N / kBN);
+  const int64_t tiles = (P / tile_bm(tile)) * (int64_t)(N / tile_bn(tile));
   int64_t g = num_cus;   // one resident workgroup per CU (LDS bound)
   if (tiles < g) g = tiles;
   return (int)(g < 1 ? 1 : g);

@@ -31,17 +31,19 @@
 
 namespace mm {
 
-constexpr int kBN = 256;
 constexpr int kRowBytes = 128;          // K bytes per stage row
 constexpr int kMaxExperts = 1024;
 
-// Workgroup shapes: WM waves along M x WN along N, one workgroup per CU (the
-// LDS ring fills it): four waves (one per SIMD) for 64-row tiles, eight (two
-// per SIMD) for 128-row tiles.  A wave's N range must hold whole 64-row
-// gate/up groups (WTN >= 64).
+// Tile shapes (BLOCK_M x BN, WM waves along M x WN along N), one workgroup
+// per CU:
+//  * 128 x 256, eight waves (two per SIMD), for the compute regime;
+//  * 64 x 128, four waves (one per SIMD), for the weight-streaming regime
+//    (few rows per expert): narrow tiles make four times as many tiles out
+//    of the same weights, so the last round of tiles leaves fewer CUs idle.
+// A wave's N range must hold whole 64-row gate/up groups (WTN >= 64).
 template <int BM> struct TileShape;
-template <> struct TileShape<64> { static constexpr int WM = 1, WN = 4; };
-template <> struct TileShape<128> { static constexpr int WM = 2, WN = 4; };
+template <> struct TileShape<64> { static constexpr int WM = 2, WN = 2, BN = 128; };
+template <> struct TileShape<128> { static constexpr int WM = 2, WN = 4, BN = 256; };
 template <int BM> constexpr int threads_of() { return 64 * TileShape<BM>::WM * TileShape<BM>::WN; }
 constexpr int kStages = 3;   // LDS ring slots
 // Per-row data of a tile for its epilogue, two tiles' worth (the next tile's
@@ -52,7 +54,9 @@ struct RowInfo {
   float rs;        // s^X (Linear1, A8W8) or s^A (Linear2, A8W8) of the row
   float pad;
 };
-template <int BM> constexpr int lds_bytes_of() { return kStages * (BM + 256) * 128 + 2 * BM * (int)sizeof(RowInfo); }
+template <int BM> constexpr int lds_bytes_of() {
+  return kStages * (BM + TileShape<BM>::BN) * kRowBytes + 2 * BM * (int)sizeof(RowInfo);
+}
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -225,7 +229,7 @@ __device__ __forceinline__ TileRef resolve_tile(const GemmArgs& a, const int32_t
   const int local = tile - mb0 * n_tiles;
   const int nblk = local / nmb, mblk = mb0 + local % nmb;
   r.row0 = mblk * BM;
-  r.n0 = nblk * kBN;
+  r.n0 = nblk * TileShape<BM>::BN;
   r.valid = min(BM, off_s[lo] + cnt_s[lo] - r.row0);
   r.abase = a.A + (int64_t)r.row0 * kbytes;
   r.bbase = a.B + ((int64_t)lo * a.N + r.n0) * kbytes;
@@ -237,9 +241,10 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
   const GemmArgs a = uniform_args(args);
   constexpr int WM = TileShape<BM>::WM, WN = TileShape<BM>::WN, S = kStages;
   constexpr int NT = threads_of<BM>(), NW = NT / 64;
-  constexpr int WTM = BM / WM, WTN = kBN / WN;
+  constexpr int BN = TileShape<BM>::BN;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int MB = WTM / 32, NB = WTN / 32;
-  constexpr int ROWS = BM + kBN;
+  constexpr int ROWS = BM + BN;
   constexpr int STAGE = ROWS * kRowBytes;
   constexpr int GROUPS = ROWS / 8;
   static_assert(GROUPS % NW == 0, "DMA groups must split evenly over the waves");
@@ -279,7 +284,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
 
   const int kbytes = a.Kdim * ESZ;
   const int nk = kbytes / kRowBytes;
-  const int n_tiles = a.N / kBN;
+  const int n_tiles = a.N / BN;
   const int total = offsets_ok ? (off_s[a.E] / BM) * n_tiles : 0;
   const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_ptr_t)lds;
   RowInfo* rowinfo = reinterpret_cast<RowInfo*>(lds + S * STAGE);   // [2][BM]
@@ -300,7 +305,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
   static_assert(NW % 2 == 0, "DMA swizzle assumes an even wave count");
   const uint32_t voff =
       (uint32_t)((8 * wv + l / 8) * kbytes + (((l & 7) ^ ((4 * (wv & 1) + l / 16) & 7)) << 4));
-  const int abytes = BM * kbytes, bbytes = kBN * kbytes;
+  const int abytes = BM * kbytes, bbytes = BN * kbytes;
 #define MM_DMA(tr_, i_, kb_) \
   dma_one<NW, BM, STAGE, S>(lds, (tr_).abase, abytes, (tr_).bbase, bbytes, voff, wv, kbytes, (i_), (kb_))
 

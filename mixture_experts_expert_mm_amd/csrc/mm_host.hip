@@ -318,7 +318,7 @@ mm_status mm_plan_create(const mm_problem* problem, mm_plan* plan) {
   pl.prob = p;
   // BLOCK_M from the expected rows per expert (small loads -> small blocks)
   const double expected = (double)R / (double)p.num_experts;
-  int tile = expected < 96 ? TILE_M64_N256 : TILE_M128_N256;
+  int tile = expected < 96 ? TILE_M64_N128 : TILE_M128_N256;
   // tuning override: MM_FORCE_TILE=<0..1> selects BLOCK_M 64/128
   if (const char* f = std::getenv("MM_FORCE_TILE")) {
     const int v = std::atoi(f);

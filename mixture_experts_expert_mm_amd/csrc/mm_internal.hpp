@@ -31,12 +31,12 @@ struct DispatchArgs {
 
 // Tile configurations of the grouped GEMMs (compile-time instances).
 enum TileCfg : int {
-  TILE_M64_N256 = 0,   // weight-streaming regime: few rows per expert
+  TILE_M64_N128 = 0,   // weight-streaming regime: few rows per expert
   TILE_M128_N256 = 1,  // compute regime
   TILE_COUNT = 2
 };
-inline int tile_bm(int t) { return t == TILE_M64_N256 ? 64 : 128; }
-constexpr int kTileBN = 256;
+inline int tile_bm(int t) { return t == TILE_M64_N128 ? 64 : 128; }
+inline int tile_bn(int t) { return t == TILE_M64_N128 ? 128 : 256; }
 
 struct GemmArgs {
   const uint8_t* A;          // pool rows [P][Kdim]

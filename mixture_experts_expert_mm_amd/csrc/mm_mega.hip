@@ -205,7 +205,7 @@ static hipError_t launch_mega_one(const MegaArgs* dev_args, int grid, hipStream_
 
 template <int UC>
 static hipError_t launch_mega_bm(int tile, const MegaArgs* a, int grid, hipStream_t s) {
-  return tile == TILE_M64_N256 ? launch_mega_one<UC, 64>(a, grid, s) : launch_mega_one<UC, 128>(a, grid, s);
+  return tile == TILE_M64_N128 ? launch_mega_one<UC, 64>(a, grid, s) : launch_mega_one<UC, 128>(a, grid, s);
 }
 
 hipError_t launch_mega_prep(const MegaArgs& a, MegaArgs* dev_args, hipStream_t s) {
