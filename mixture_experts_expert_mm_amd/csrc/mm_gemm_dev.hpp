@@ -14,10 +14,10 @@
 //   float32 combine slot i*K+k (Token Combine sums the slots in order).
 // Mode 2 stores the raw int32 accumulators (A8W8-INT exactness checks).
 //
-// Tiling: one workgroup per BLOCK_M x 256 output tile; each wave owns a
-// 64 x 64 grid of 32x32 MFMA blocks.  K advances 128
+// Tiling: one workgroup per BLOCK_M x BN output tile (128 x 256 or 64 x 128);
+// each wave owns a 64 x 64 grid of 32x32 MFMA blocks.  K advances 128
 // bytes per stage (64 bf16 or 128 int8/e4m3).  Stages are copied from HBM
-// straight into a three-slot LDS ring by buffer loads (no register staging),
+// straight into a ring of LDS slots by buffer loads (no register staging),
 // in a bank-conflict-free swizzled order; the fragment reads of the next
 // stage are interleaved with the MFMAs of the current one.  The grid is
 // persistent: workgroups stride over the tile list (expert M-blocks x
@@ -28,24 +28,27 @@
 #include "mm_internal.hpp"
 
 #include <type_traits>
+#include <utility>
 
 namespace mm {
 
 constexpr int kRowBytes = 128;          // K bytes per stage row
 constexpr int kMaxExperts = 1024;
 
-// Tile shapes (BLOCK_M x BN, WM waves along M x WN along N), one workgroup
-// per CU:
-//  * 128 x 256, eight waves (two per SIMD), for the compute regime;
+// Tile shapes (BLOCK_M x BN, WM waves along M x WN along N, S LDS ring
+// slots), one workgroup per CU:
+//  * 128 x 256, eight waves (two per SIMD), three slots (the LDS holds no
+//    more), for the compute regime;
 //  * 64 x 128, four waves (one per SIMD), for the weight-streaming regime
 //    (few rows per expert): narrow tiles make four times as many tiles out
-//    of the same weights, so the last round of tiles leaves fewer CUs idle.
+//    of the same weights, so the last round of tiles leaves fewer CUs idle,
+//    and the small stages leave room for six slots, five stages (120 KiB)
+//    in flight per CU to cover the HBM latency.
 // A wave's N range must hold whole 64-row gate/up groups (WTN >= 64).
 template <int BM> struct TileShape;
-template <> struct TileShape<64> { static constexpr int WM = 2, WN = 2, BN = 128; };
-template <> struct TileShape<128> { static constexpr int WM = 2, WN = 4, BN = 256; };
+template <> struct TileShape<64> { static constexpr int WM = 2, WN = 2, BN = 128, S = 6; };
+template <> struct TileShape<128> { static constexpr int WM = 2, WN = 4, BN = 256, S = 3; };
 template <int BM> constexpr int threads_of() { return 64 * TileShape<BM>::WM * TileShape<BM>::WN; }
-constexpr int kStages = 3;   // LDS ring slots
 // Per-row data of a tile for its epilogue, two tiles' worth (the next tile's
 // is written while the current one is still being stored): 16 bytes a row.
 struct RowInfo {
@@ -55,10 +58,20 @@ struct RowInfo {
   float pad;
 };
 template <int BM> constexpr int lds_bytes_of() {
-  return kStages * (BM + TileShape<BM>::BN) * kRowBytes + 2 * BM * (int)sizeof(RowInfo);
+  return TileShape<BM>::S * (BM + TileShape<BM>::BN) * kRowBytes + 2 * BM * (int)sizeof(RowInfo);
 }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// f(std::integral_constant<int, i>) for i = 0 .. N-1, unrolled at compile time
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 // LDS fragment read outside the compiler's view: the compiler would otherwise
 // wait for every in-flight LDS-DMA before any LDS read it cannot disambiguate.
@@ -239,7 +252,7 @@ __device__ __forceinline__ TileRef resolve_tile(const GemmArgs& a, const int32_t
 template <int UC, int BM, int MODE, bool WIDEN>
 __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, int32_t* off_s, int32_t* cnt_s) {
   const GemmArgs a = uniform_args(args);
-  constexpr int WM = TileShape<BM>::WM, WN = TileShape<BM>::WN, S = kStages;
+  constexpr int WM = TileShape<BM>::WM, WN = TileShape<BM>::WN, S = TileShape<BM>::S;
   constexpr int NT = threads_of<BM>(), NW = NT / 64;
   constexpr int BN = TileShape<BM>::BN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -455,24 +468,27 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
       __builtin_amdgcn_sched_barrier(0);
     };
 
-    // stage 0 landed for every wave (later stages, and the previous tile's
-    // epilogue stores, may still be in flight: counting them too only makes
-    // the wait stricter)
-    if (nk >= 3) vm_barrier<2 * D>(); else if (nk == 2) vm_barrier<D>(); else vm_barrier<0>();
+    // stage 0 landed for every wave: the tile's other min(nk, S) - 1 stages
+    // may still be in flight (the previous tile's epilogue stores were issued
+    // after them: counting them too only makes the wait stricter)
+    static_for<S>([&](auto cc) {
+      constexpr int c = S - 1 - decltype(cc)::value;   // S-1, ..., 0
+      if (min(nk, S) - 1 == c) vm_barrier<c * D>();
+    });
 #pragma unroll
     for (int r = 0; r < 4 * NFR; ++r) read_frag(f, r, aoff, boff, 0u);
-    // Every barrier below has a compile-time DMA count: stage kb+S refills
-    // while kb + S < nk, and the last stages drain the ring.
+    // Every barrier below has a compile-time DMA count.  At step kb's barrier
+    // stage kb+1 must have landed while stages kb+2 .. min(nk-1, kb+S-1) may
+    // be in flight; stage kb+S refills while kb + S < nk, and the last S
+    // steps drain the ring.
     const std::integral_constant<bool, true> yes;
     const std::integral_constant<bool, false> no;
-    const std::integral_constant<int, D> vm_d;
-    const std::integral_constant<int, 0> vm_0;
-    if (nk >= 3) {
-      for (int kb = 0; kb < nk - 3; ++kb) step(kb, yes, yes, vm_d);
-      step(nk - 3, no, yes, vm_d);
-    }
-    if (nk >= 2) step(nk - 2, no, yes, vm_0);
-    step(nk - 1, no, no, vm_0);
+    for (int kb = 0; kb < nk - S; ++kb) step(kb, yes, yes, std::integral_constant<int, (S - 2) * D>{});
+    static_for<S - 1>([&](auto jj) {
+      constexpr int j = S - decltype(jj)::value;   // S, ..., 2 steps before the end
+      if (nk >= j) step(nk - j, no, yes, std::integral_constant<int, (j - 2) * D>{});
+    });
+    step(nk - 1, no, no, std::integral_constant<int, 0>{});
 
     // ------------------------------------------------ next tile, epilogue
     // per-column scales (A8W8) of this wave's columns, loaded before the next
