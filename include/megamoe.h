@@ -33,8 +33,9 @@
  * - Route ids (topk_ids) must be in [0, E) and distinct within a token, as
  *   the Parameters table of the operator page requires; an id < 0 marks a
  *   masked route (DeepEP notes, section 5.2): it is skipped, counted for no
- *   expert and contributes 0.  Ids >= E or duplicated ids are not detected
- *   on the device and give undefined results.
+ *   expert and contributes 0.  An id >= E is skipped the same way and sets
+ *   MM_DEVERR_BAD_EXPERT in the workspace error word (mm_read_device_error);
+ *   duplicated ids are not detected and give undefined results.
  * - Workspace counters are reset by the library at the start of every
  *   call; the caller never clears them.
  * - Calls that share a workspace or intermediate buffers must be ordered
