@@ -32,13 +32,12 @@
 
 namespace mm {
 
-constexpr int kRowBytes = 128;          // K bytes per stage row
 constexpr int kMaxExperts = 1024;
 
 // Tile shapes (BLOCK_M x BN, WM waves along M x WN along N, S LDS ring
-// slots), one workgroup per CU:
-//  * 128 x 256, eight waves (two per SIMD), three slots (the LDS holds no
-//    more), for the compute regime;
+// slots of RB K-bytes per row), one workgroup per CU:
+//  * 128 x 256, eight waves (two per SIMD), three slots of 128 K-bytes (the
+//    LDS holds no more), for the compute regime;
 //  * 64 x 128, four waves (one per SIMD), for the weight-streaming regime
 //    (few rows per expert): narrow tiles make four times as many tiles out
 //    of the same weights, so the last round of tiles leaves fewer CUs idle,
@@ -46,8 +45,8 @@ constexpr int kMaxExperts = 1024;
 //    in flight per CU to cover the HBM latency.
 // A wave's N range must hold whole 64-row gate/up groups (WTN >= 64).
 template <int BM> struct TileShape;
-template <> struct TileShape<64> { static constexpr int WM = 2, WN = 2, BN = 128, S = 6; };
-template <> struct TileShape<128> { static constexpr int WM = 2, WN = 4, BN = 256, S = 3; };
+template <> struct TileShape<64> { static constexpr int WM = 2, WN = 2, BN = 128, S = 6, RB = 128; };
+template <> struct TileShape<128> { static constexpr int WM = 2, WN = 4, BN = 256, S = 3, RB = 128; };
 template <int BM> constexpr int threads_of() { return 64 * TileShape<BM>::WM * TileShape<BM>::WN; }
 // Per-row data of a tile for its epilogue, two tiles' worth (the next tile's
 // is written while the current one is still being stored): 16 bytes a row.
@@ -58,7 +57,7 @@ struct RowInfo {
   float pad;
 };
 template <int BM> constexpr int lds_bytes_of() {
-  return TileShape<BM>::S * (BM + TileShape<BM>::BN) * kRowBytes + 2 * BM * (int)sizeof(RowInfo);
+  return TileShape<BM>::S * (BM + TileShape<BM>::BN) * TileShape<BM>::RB + 2 * BM * (int)sizeof(RowInfo);
 }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -99,51 +98,52 @@ __device__ __forceinline__ void vm_barrier() {
 }
 
 // One LDS-DMA instruction of stage kb: instruction i of wave wv moves the
-// 8-row group g = wv + NW*i into slot kb % S (groups below BM/8 are A rows).
-// voff is the lane's byte offset inside its group; the group's row offset
-// and the stage's K offset are wave-uniform and go in the scalar offset.
-// The tile bases become buffer descriptors here: the descriptor type cannot
-// appear in a signature the host pass sees.
-template <int NW, int BM, int STAGE, int S>
+// group g = wv + NW*i of RPI = 1024 / RB rows into slot kb % S (groups
+// below BM / RPI are A rows).  voff is the lane's byte offset inside its
+// group; the group's row offset and the stage's K offset are wave-uniform
+// and go in the scalar offset.  The tile bases become buffer descriptors
+// here: the descriptor type cannot appear in a signature the host pass sees.
+template <int NW, int BM, int STAGE, int S, int RB>
 __device__ __forceinline__ void dma_one(uint8_t* lds, const uint8_t* abase, int abytes, const uint8_t* bbase,
                                         int bbytes, uint32_t voff, int wv, int kbytes, int i, int kb) {
-  const bool is_a = i < BM / (8 * NW);
+  constexpr int RPI = 1024 / RB;
+  const bool is_a = i < BM / (RPI * NW);
   const __amdgpu_buffer_rsrc_t rs =
       __builtin_amdgcn_make_buffer_rsrc((void*)(is_a ? abase : bbase), (short)0, is_a ? abytes : bbytes, 0x00020000);
-  const int rows = is_a ? 8 * NW * i : 8 * NW * i - BM;
-  const int soff = __builtin_amdgcn_readfirstlane(rows * kbytes + kb * kRowBytes);
+  const int rows = is_a ? RPI * NW * i : RPI * NW * i - BM;
+  const int soff = __builtin_amdgcn_readfirstlane(rows * kbytes + kb * RB);
   const int g = wv + NW * i;
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(lds + (kb % S) * STAGE + g * 1024), 16, voff, soff, 0, 0);
 }
 
-// The fragments of one K-stage held in registers: four 16-byte chunks of
-// the wave's MB A blocks and NB B blocks.
-template <int MB, int NB>
+// The fragments of one K-stage held in registers: NQ 16-byte chunks of the
+// wave's MB A blocks and NB B blocks.
+template <int MB, int NB, int NQ>
 struct Frags {
-  u32x4 a[MB][4];
-  u32x4 b[NB][4];
+  u32x4 a[MB][NQ];
+  u32x4 b[NB][NQ];
 };
 
 // Fragment read r of a stage (r = chunk * (MB + NB) + block; A blocks first),
-// 32 rows apart inside the wave's rows.  Only called with r known at compile
-// time after unrolling, so every branch folds away.
-template <int MB, int NB>
-__device__ __forceinline__ void read_frag(Frags<MB, NB>& f, int r, const uint32_t* aoff, const uint32_t* boff,
+// 32 rows (BOFF bytes) apart inside the wave's rows.  Only called with r
+// known at compile time after unrolling, so every branch folds away.
+template <int BOFF, int MB, int NB, int NQ>
+__device__ __forceinline__ void read_frag(Frags<MB, NB, NQ>& f, int r, const uint32_t* aoff, const uint32_t* boff,
                                           uint32_t so) {
   const int q = r / (MB + NB), x = r % (MB + NB);
   if (x < MB) {
     const uint32_t ad = aoff[q] + so;
     if (x == 0) f.a[0][q] = ds_read16<0>(ad);
-    if constexpr (MB > 1) if (x == 1) f.a[1][q] = ds_read16<4096>(ad);
-    if constexpr (MB > 2) if (x == 2) f.a[2][q] = ds_read16<8192>(ad);
-    if constexpr (MB > 3) if (x == 3) f.a[3][q] = ds_read16<12288>(ad);
+    if constexpr (MB > 1) if (x == 1) f.a[1][q] = ds_read16<BOFF>(ad);
+    if constexpr (MB > 2) if (x == 2) f.a[2][q] = ds_read16<2 * BOFF>(ad);
+    if constexpr (MB > 3) if (x == 3) f.a[3][q] = ds_read16<3 * BOFF>(ad);
   } else {
     const uint32_t ad = boff[q] + so;
     const int y = x - MB;
     if (y == 0) f.b[0][q] = ds_read16<0>(ad);
-    if constexpr (NB > 1) if (y == 1) f.b[1][q] = ds_read16<4096>(ad);
-    if constexpr (NB > 2) if (y == 2) f.b[2][q] = ds_read16<8192>(ad);
-    if constexpr (NB > 3) if (y == 3) f.b[3][q] = ds_read16<12288>(ad);
+    if constexpr (NB > 1) if (y == 1) f.b[1][q] = ds_read16<BOFF>(ad);
+    if constexpr (NB > 2) if (y == 2) f.b[2][q] = ds_read16<2 * BOFF>(ad);
+    if constexpr (NB > 3) if (y == 3) f.b[3][q] = ds_read16<3 * BOFF>(ad);
   }
 }
 
@@ -155,14 +155,15 @@ __device__ __forceinline__ void widen_e4m3(const u32x4& w, u32x4& lo, u32x4& hi)
 #undef CVT
 }
 
-// Mainloop data layout.  A stage holds BLOCK_M A rows then 256 B rows of 128
-// K-bytes (eight 16-byte chunks) each, filled by buffer loads straight into
-// LDS: one wave instruction moves 8 rows (64 lanes x 16 bytes, lane i -> byte
-// 16*i of the group).  Chunk c of row r sits at position c ^ ((r / 2) % 8):
-// LDS serves a 16-byte read of 16 lanes per pass over 64 banks, and 16
-// consecutive rows at one chunk then hit 16 distinct bank groups.  A lane's
-// MFMA operand covers chunks 4h..4h+3 of its row (h = lane / 32), the same
-// chunks for A and B, so every product pairs equal k.
+// Mainloop data layout.  A stage holds BLOCK_M A rows then BN B rows of RB
+// K-bytes (CH = RB/16 chunks of 16 bytes) each, filled by buffer loads
+// straight into LDS: one wave instruction moves 1 KiB = 1024/RB rows (64
+// lanes x 16 bytes, lane i -> byte 16*i of the group).  Chunk c of row r
+// sits at position c ^ ((r / (16/CH)) % CH): LDS serves a 16-byte read of 16
+// lanes per pass over 64 banks (16 groups of 16 bytes), and 16 consecutive
+// rows at one chunk then hit 16 distinct bank groups.  A lane's MFMA operand
+// covers chunks NQ*h .. NQ*h+NQ-1 of its row (h = lane / 32, NQ = CH/2),
+// the same chunks for A and B, so every product pairs equal k.
 //
 // Tiles run back to back: once a tile's last MFMAs are issued the ring is
 // free, so the first stages of the workgroup's next tile are issued at once
@@ -236,16 +237,19 @@ __device__ __forceinline__ TileRef resolve_tile(const GemmArgs& a, const int32_t
     const int mid = (lo + hi) >> 1;
     if ((off_s[mid] / BM) * n_tiles <= tile) lo = mid; else hi = mid;
   }
+  // every field is wave-uniform; saying so keeps them in scalar registers
+  // (a tile base the compiler cannot prove uniform would turn each buffer
+  // load into a loop over lanes)
   TileRef r;
-  r.e = lo;
+  r.e = uniform_int(lo);
   const int mb0 = off_s[lo] / BM, nmb = (off_s[lo + 1] - off_s[lo]) / BM;
   const int local = tile - mb0 * n_tiles;
   const int nblk = local / nmb, mblk = mb0 + local % nmb;
-  r.row0 = mblk * BM;
-  r.n0 = nblk * TileShape<BM>::BN;
-  r.valid = min(BM, off_s[lo] + cnt_s[lo] - r.row0);
-  r.abase = a.A + (int64_t)r.row0 * kbytes;
-  r.bbase = a.B + ((int64_t)lo * a.N + r.n0) * kbytes;
+  r.row0 = uniform_int(mblk * BM);
+  r.n0 = uniform_int(nblk * TileShape<BM>::BN);
+  r.valid = uniform_int(min(BM, off_s[lo] + cnt_s[lo] - r.row0));
+  r.abase = uniform_ptr(a.A + (int64_t)r.row0 * kbytes);
+  r.bbase = uniform_ptr(a.B + ((int64_t)r.e * a.N + r.n0) * kbytes);
   return r;
 }
 
@@ -254,12 +258,15 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
   const GemmArgs a = uniform_args(args);
   constexpr int WM = TileShape<BM>::WM, WN = TileShape<BM>::WN, S = TileShape<BM>::S;
   constexpr int NT = threads_of<BM>(), NW = NT / 64;
-  constexpr int BN = TileShape<BM>::BN;
+  constexpr int BN = TileShape<BM>::BN, RB = TileShape<BM>::RB;
+  constexpr int CH = RB / 16, NQ = CH / 2;                 // chunks per row; per lane and block
+  constexpr int RPI = 1024 / RB;                           // rows per DMA instruction
+  constexpr int RPS = 16 / CH;                             // rows per swizzle step
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int MB = WTM / 32, NB = WTN / 32;
   constexpr int ROWS = BM + BN;
-  constexpr int STAGE = ROWS * kRowBytes;
-  constexpr int GROUPS = ROWS / 8;
+  constexpr int STAGE = ROWS * RB;
+  constexpr int GROUPS = ROWS / RPI;
   static_assert(GROUPS % NW == 0, "DMA groups must split evenly over the waves");
   constexpr int D = GROUPS / NW;                           // DMA instructions per wave per stage
   static_assert((S - 1) * D <= 63, "vmcnt range");
@@ -267,12 +274,13 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
   constexpr int NFR = MB + NB;                             // fragment reads per chunk index
   // MFMA phases of a stage: one chunk each, or two for e4m3 MFMAs (K = 64)
   constexpr int CPP = (UC == UC_FP8 && !WIDEN) ? 2 : 1;
-  constexpr int NPH = 4 / CPP;
+  constexpr int NPH = NQ / CPP;
+  static_assert(NPH >= 2, "a stage needs MFMA phases after its barrier to hide the refill and the reads");
   constexpr int RPP = NFR * CPP;                           // fragment reads per phase
   constexpr int MPP = MB * NB * (WIDEN ? 2 : 1);           // MFMAs per phase
   // phase 0 may start once only the reads of the later phases are in flight
-  constexpr int P0WAIT = (4 * NFR - RPP) > 15 ? 15 : (4 * NFR - RPP);
-  static_assert(BM % (8 * NW) == 0, "A rows fill whole DMA instructions");
+  constexpr int P0WAIT = (NQ * NFR - RPP) > 15 ? 15 : (NQ * NFR - RPP);
+  static_assert(BM % (RPI * NW) == 0, "A rows fill whole DMA instructions");
   static_assert(MODE != 0 || NB % 2 == 0, "Linear1 waves hold whole gate/up pairs");
   typedef typename Acc<UC>::type AccT;
 
@@ -296,31 +304,34 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
   if (!offsets_ok && t == 0 && a.err) atomicOr(a.err, (uint32_t)MM_DEVERR_BAD_OFFSETS);
 
   const int kbytes = a.Kdim * ESZ;
-  const int nk = kbytes / kRowBytes;
+  const int nk = kbytes / RB;
   const int n_tiles = a.N / BN;
   const int total = offsets_ok ? (off_s[a.E] / BM) * n_tiles : 0;
   const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_ptr_t)lds;
   RowInfo* rowinfo = reinterpret_cast<RowInfo*>(lds + S * STAGE);   // [2][BM]
   const uint32_t rowinfo_base = lds_base + (uint32_t)(S * STAGE);
 
-  // per-lane LDS addresses of the four fragment chunks (stage slot added per stage)
-  uint32_t aoff[4], boff[4];
+  // per-lane LDS addresses of the NQ fragment chunks (stage slot added per
+  // stage); the wave's first rows are a multiple of 16, the swizzle period
+  uint32_t aoff[NQ], boff[NQ];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const uint32_t cpos = (uint32_t)(((4 * h + q) ^ ((lr >> 1) & 7)) << 4);
-    aoff[q] = lds_base + (uint32_t)(wm * WTM + lr) * kRowBytes + cpos;
-    boff[q] = lds_base + (uint32_t)(BM + wn * WTN + lr) * kRowBytes + cpos;
+  for (int q = 0; q < NQ; ++q) {
+    const uint32_t cpos = (uint32_t)(((NQ * h + q) ^ ((lr / RPS) % CH)) << 4);
+    aoff[q] = lds_base + (uint32_t)(wm * WTM + lr) * RB + cpos;
+    boff[q] = lds_base + (uint32_t)(BM + wn * WTN + lr) * RB + cpos;
   }
-  // per-lane byte offset of the DMA rows: group g covers rows 8g .. 8g+7, lane
-  // l row 8g + l/8, and lands its logical chunk (l%8) ^ ((row/2)%8) at
-  // position l%8.  With NW even, g and wv have the same parity, so the
-  // swizzle and the in-group offset are the same for all of a wave's groups.
-  static_assert(NW % 2 == 0, "DMA swizzle assumes an even wave count");
+  // per-lane byte offset of the DMA rows: group g covers rows RPI*g ..
+  // RPI*g + RPI-1, lane l row RPI*g + l/CH, and lands its logical chunk
+  // (l%CH) ^ swizzle(row) at position l%CH.  The swizzle of a lane's row is
+  // the same in all of a wave's groups g = wv + NW*i: their row offsets
+  // differ by RPI*NW*i, a multiple of the swizzle period RPS*CH (needs NW
+  // even when CH = 8).
+  static_assert((RPI * NW / RPS) % CH == 0, "DMA swizzle must repeat across a wave's groups");
   const uint32_t voff =
-      (uint32_t)((8 * wv + l / 8) * kbytes + (((l & 7) ^ ((4 * (wv & 1) + l / 16) & 7)) << 4));
+      (uint32_t)((RPI * wv + l / CH) * kbytes + (((l % CH) ^ (((RPI * wv + l / CH) / RPS) % CH)) << 4));
   const int abytes = BM * kbytes, bbytes = BN * kbytes;
 #define MM_DMA(tr_, i_, kb_) \
-  dma_one<NW, BM, STAGE, S>(lds, (tr_).abase, abytes, (tr_).bbase, bbytes, voff, wv, kbytes, (i_), (kb_))
+  dma_one<NW, BM, STAGE, S, RB>(lds, (tr_).abase, abytes, (tr_).bbase, bbytes, voff, wv, kbytes, (i_), (kb_))
 
   // Per-row epilogue data of tile `tr` into rowinfo[buf] (thread r: row r).
   auto fill_rowinfo = [&](const TileRef& tr, int buf) {
@@ -377,7 +388,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
 #pragma unroll
         for (int q = 0; q < 16; ++q) acc[i][j][q] = 0;
 
-    Frags<MB, NB> f;
+    Frags<MB, NB, NQ> f;
     // MFMA mi of phase p (chunks CPP*p .. CPP*p + CPP-1 of the stage in f)
     u32x4 wa_lo[MB], wa_hi[MB], wb_lo, wb_hi;   // e4m3 -> bf16 widened operands
     auto mfma_at = [&](int p, int mi) {
@@ -402,7 +413,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
     };
     auto tie_chunks = [&](int c0, int c1) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int q = 0; q < NQ; ++q) {
         if (q < c0 || q >= c1) continue;
 #pragma unroll
         for (int i = 0; i < MB; ++i) tie(f.a[i][q]);
@@ -432,7 +443,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
       } else {
         lgkm_wait<0>();
       }
-      tie_chunks(CPP, 4);
+      tie_chunks(CPP, NQ);
       __builtin_amdgcn_sched_barrier(0);
       const uint32_t so = (uint32_t)(((kb + 1) % S) * STAGE);
       constexpr int NMR = (NPH - 1) * MPP;   // MFMAs after the barrier: DMA issues spread over them
@@ -455,7 +466,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
             const int target = ((mi + 1) * RPP + MPP - 1) / MPP;
 #pragma unroll
             for (int r = 0; r < RPP; ++r)
-              if (r >= rd && r < target) read_frag(f, (p - 1) * RPP + r, aoff, boff, so);
+              if (r >= rd && r < target) read_frag<32 * RB>(f, (p - 1) * RPP + r, aoff, boff, so);
             rd = target < RPP ? target : RPP;
           }
           __builtin_amdgcn_sched_barrier(0);
@@ -463,7 +474,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
       }
       if constexpr (MORE) {
 #pragma unroll
-        for (int r = 0; r < RPP; ++r) read_frag(f, (NPH - 1) * RPP + r, aoff, boff, so);
+        for (int r = 0; r < RPP; ++r) read_frag<32 * RB>(f, (NPH - 1) * RPP + r, aoff, boff, so);
       }
       __builtin_amdgcn_sched_barrier(0);
     };
@@ -476,7 +487,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
       if (min(nk, S) - 1 == c) vm_barrier<c * D>();
     });
 #pragma unroll
-    for (int r = 0; r < 4 * NFR; ++r) read_frag(f, r, aoff, boff, 0u);
+    for (int r = 0; r < NQ * NFR; ++r) read_frag<32 * RB>(f, r, aoff, boff, 0u);
     // Every barrier below has a compile-time DMA count.  At step kb's barrier
     // stage kb+1 must have landed while stages kb+2 .. min(nk-1, kb+S-1) may
     // be in flight; stage kb+S refills while kb + S < nk, and the last S
