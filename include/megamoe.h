@@ -234,7 +234,9 @@ mm_status mega_moe(const mm_plan* plan, const void* x, const int32_t* topk_ids,
 typedef enum mm_device_error {
   MM_DEVERR_NONE = 0,
   MM_DEVERR_BAD_EXPERT = 1,      /* a route named an expert id >= E (skipped like a masked route) */
-  MM_DEVERR_BARRIER_TIMEOUT = 2, /* a grid barrier of mega_moe gave up waiting; y is unspecified */
+  MM_DEVERR_BARRIER_TIMEOUT = 2, /* a wait inside a kernel gave up (a grid barrier of mega_moe, or a GEMM
+                                    waiting for another workgroup's partial sums of a split tile);
+                                    y is unspecified */
   MM_DEVERR_BAD_OFFSETS = 4      /* a GEMM got offsets/counts that do not describe a padded pool
                                     of at most P rows: it ran no tile (its outputs are unspecified) */
 } mm_device_error;

@@ -13,7 +13,8 @@ __global__ void k_zero(int32_t* __restrict__ counts, int E, uint32_t* __restrict
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   if (counts)
     for (int64_t j = i; j < E; j += stride) counts[j] = 0;
-  if (ctl && i < kCtlWords) ctl[i] = 0u;
+  if (ctl)
+    for (int64_t j = i; j < kCtlWords; j += stride) ctl[j] = 0u;
 }
 
 __global__ __launch_bounds__(256) void k_count(DispatchArgs a, int64_t nwaves) {

@@ -105,13 +105,13 @@ __device__ __forceinline__ void vm_barrier() {
 // here: the descriptor type cannot appear in a signature the host pass sees.
 template <int NW, int BM, int STAGE, int S, int RB>
 __device__ __forceinline__ void dma_one(uint8_t* lds, const uint8_t* abase, int abytes, const uint8_t* bbase,
-                                        int bbytes, uint32_t voff, int wv, int kbytes, int i, int kb) {
+                                        int bbytes, uint32_t voff, int wv, int kbytes, int i, int kb, int kbase) {
   constexpr int RPI = 1024 / RB;
   const bool is_a = i < BM / (RPI * NW);
   const __amdgpu_buffer_rsrc_t rs =
       __builtin_amdgcn_make_buffer_rsrc((void*)(is_a ? abase : bbase), (short)0, is_a ? abytes : bbytes, 0x00020000);
   const int rows = is_a ? RPI * NW * i : RPI * NW * i - BM;
-  const int soff = __builtin_amdgcn_readfirstlane(rows * kbytes + kb * RB);
+  const int soff = __builtin_amdgcn_readfirstlane(rows * kbytes + (kb + kbase) * RB);
   const int g = wv + NW * i;
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(lds + (kb % S) * STAGE + g * 1024), 16, voff, soff, 0, 0);
 }
@@ -215,15 +215,61 @@ __device__ __forceinline__ GemmArgs uniform_args(const GemmArgs& in) {
   a.H = uniform_int(in.H);
   a.K = uniform_int(in.K);
   a.gate_up_group = uniform_int(in.gate_up_group);
+  a.partials = uniform_ptr(in.partials);
+  a.split_flags = uniform_ptr(in.split_flags);
+  a.max_split = uniform_int(in.max_split);
+  a.spin_limit = (uint32_t)uniform_int((int)in.spin_limit);
   return a;
 }
 
-// One entry of the workgroup's tile list, resolved.
+// One item of the workgroup's work list: a tile, or a K piece of a split
+// tail tile, resolved.
+enum TileRole : int { kRoleFull = 0, kRoleReduce = 1, kRoleProduce = 2 };
 struct TileRef {
   int e, row0, n0, valid;
   const uint8_t* abase;   // first A row of the tile
   const uint8_t* bbase;   // first B row (prepared weights) of the tile
+  int kbase, nkl;         // K stages kbase .. kbase + nkl - 1
+  int role;               // TileRole: whole tile, or piece 0 (adds the others' partials), or a later piece
+  int slot;               // partial slot of a piece (piece 0: the later pieces use slot + 1 ..)
 };
+
+constexpr int kMinSplitStages = 4;   // shortest K piece of a split tile
+
+// K pieces per tail tile.  A slice of n tiles on G workgroups runs n / G full
+// rounds and then `tail` tiles; split in c pieces they take ceil(tail*c/G)
+// rounds of 1/c of a tile.  c divides G (the pieces of one tile run in the
+// same round) and tail*c <= 2G (two partial slots per workgroup).  Depends
+// only on the arguments, so every launch shape that has the same grid splits
+// the same way.
+__device__ __forceinline__ int split_factor(int tail, int G, int nk, int max_split, int grid) {
+  if (max_split < 2 || tail <= 0 || 2 * grid > kSplitSlots) return 1;
+  int best = 1;
+  for (int c = 2; c <= 8 && c <= max_split; c *= 2) {
+    if (G % c != 0 || nk / c < kMinSplitStages || tail * c > 2 * G) continue;
+    const int rc = (tail * c + G - 1) / G, rb = (tail * best + G - 1) / G;
+    if (rc * best < rb * c) best = c;
+  }
+  return best;
+}
+
+// An accumulator element as a 32-bit word and back.  The element is passed
+// by value: a bit cast applied directly to a vector element expression was
+// compiled into a read of element 0.
+__device__ __forceinline__ uint32_t word_of(float x) { return __float_as_uint(x); }
+__device__ __forceinline__ uint32_t word_of(int32_t x) { return (uint32_t)x; }
+template <typename E> __device__ __forceinline__ E from_word(uint32_t w);
+template <> __device__ __forceinline__ float from_word<float>(uint32_t w) { return __uint_as_float(w); }
+template <> __device__ __forceinline__ int32_t from_word<int32_t>(uint32_t w) { return (int32_t)w; }
+
+__device__ __forceinline__ bool poll_flag(uint32_t* p, uint32_t spin_limit) {
+  uint32_t polls = 0;
+  while (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+    if (++polls > spin_limit) return false;
+    __builtin_amdgcn_s_sleep(2);
+  }
+  return true;
+}
 
 // Tile order: expert-major, then N-block, then M-block, so tiles that run
 // together share weight tiles (same expert and N-block) and activation tiles
@@ -283,6 +329,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
   static_assert(BM % (RPI * NW) == 0, "A rows fill whole DMA instructions");
   static_assert(MODE != 0 || NB % 2 == 0, "Linear1 waves hold whole gate/up pairs");
   typedef typename Acc<UC>::type AccT;
+  typedef std::conditional_t<UC == UC_I8, int32_t, float> AccE;   // one accumulator element
 
   const int t = threadIdx.x, l = lane_id();
   const int wv = __builtin_amdgcn_readfirstlane(t / 64);
@@ -331,7 +378,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
       (uint32_t)((RPI * wv + l / CH) * kbytes + (((l % CH) ^ (((RPI * wv + l / CH) / RPS) % CH)) << 4));
   const int abytes = BM * kbytes, bbytes = BN * kbytes;
 #define MM_DMA(tr_, i_, kb_) \
-  dma_one<NW, BM, STAGE, S, RB>(lds, (tr_).abase, abytes, (tr_).bbase, bbytes, voff, wv, kbytes, (i_), (kb_))
+  dma_one<NW, BM, STAGE, S, RB>(lds, (tr_).abase, abytes, (tr_).bbase, bbytes, voff, wv, kbytes, (i_), (kb_), (tr_).kbase)
 
   // Per-row epilogue data of tile `tr` into rowinfo[buf] (thread r: row r).
   auto fill_rowinfo = [&](const TileRef& tr, int buf) {
@@ -357,7 +404,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
     fill_rowinfo(tr, buf);
 #pragma unroll
     for (int st = 0; st < S; ++st)
-      if (st < nk) {
+      if (st < tr.nkl) {
 #pragma unroll
         for (int x = 0; x < D; ++x) MM_DMA(tr, x, st);
       }
@@ -371,12 +418,41 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
   const int t_beg = xcd * slice, t_end = min(total, t_beg + slice);
   const bool in_grid = (int)blockIdx.x < per_x * nxcd;   // a tail beyond a multiple of 8 stays idle
 
-  int tile = t_beg + wgx;
-  bool have = in_grid && tile < t_end;
+  // Work list of this workgroup: the slice's full rounds of tiles round
+  // robin, then its tail tiles (fewer than one per workgroup) split along K
+  // into sk pieces each, so that the last round ends sooner.  Piece p of the
+  // tail goes to workgroup p % G; piece 0 of a tile adds the partial sums of
+  // the tile's later pieces (in piece order) and runs the epilogue.
+  const int n_s = in_grid ? max(0, t_end - t_beg) : 0;
+  const int full = n_s / per_x, tail = n_s - full * per_x;
+  const int sk = split_factor(tail, per_x, nk, a.max_split, (int)gridDim.x);
+  const int pieces = tail * sk;
+  const int n_items = full + (pieces > wgx ? (pieces - wgx + per_x - 1) / per_x : 0);
+  auto make_item = [&](int j) {
+    TileRef r;
+    if (j < full) {
+      r = resolve_tile<BM>(a, off_s, cnt_s, t_beg + wgx + j * per_x, n_tiles, kbytes);
+      r.kbase = 0;
+      r.nkl = nk;
+      r.role = kRoleFull;
+      r.slot = 0;
+    } else {
+      const int p = wgx + (j - full) * per_x, sub = p % sk;
+      r = resolve_tile<BM>(a, off_s, cnt_s, t_beg + full * per_x + p / sk, n_tiles, kbytes);
+      r.kbase = uniform_int(sub * nk / sk);
+      r.nkl = uniform_int((sub + 1) * nk / sk - sub * nk / sk);
+      r.role = sk == 1 ? kRoleFull : (sub == 0 ? kRoleReduce : kRoleProduce);
+      r.slot = uniform_int(xcd * 2 * per_x + p);
+    }
+    return r;
+  };
+
+  int item = 0;
+  bool have = item < n_items;
   TileRef cur{};
   int buf = 0;
   if (have) {
-    cur = resolve_tile<BM>(a, off_s, cnt_s, tile, n_tiles, kbytes);
+    cur = make_item(0);
     start_tile(cur, buf);
   }
   while (have) {
@@ -482,9 +558,10 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
     // stage 0 landed for every wave: the tile's other min(nk, S) - 1 stages
     // may still be in flight (the previous tile's epilogue stores were issued
     // after them: counting them too only makes the wait stricter)
+    const int nkl = cur.nkl;
     static_for<S>([&](auto cc) {
       constexpr int c = S - 1 - decltype(cc)::value;   // S-1, ..., 0
-      if (min(nk, S) - 1 == c) vm_barrier<c * D>();
+      if (min(nkl, S) - 1 == c) vm_barrier<c * D>();
     });
 #pragma unroll
     for (int r = 0; r < NQ * NFR; ++r) read_frag<32 * RB>(f, r, aoff, boff, 0u);
@@ -494,12 +571,12 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
     // steps drain the ring.
     const std::integral_constant<bool, true> yes;
     const std::integral_constant<bool, false> no;
-    for (int kb = 0; kb < nk - S; ++kb) step(kb, yes, yes, std::integral_constant<int, (S - 2) * D>{});
+    for (int kb = 0; kb < nkl - S; ++kb) step(kb, yes, yes, std::integral_constant<int, (S - 2) * D>{});
     static_for<S - 1>([&](auto jj) {
       constexpr int j = S - decltype(jj)::value;   // S, ..., 2 steps before the end
-      if (nk >= j) step(nk - j, no, yes, std::integral_constant<int, (j - 2) * D>{});
+      if (nkl >= j) step(nkl - j, no, yes, std::integral_constant<int, (j - 2) * D>{});
     });
-    step(nk - 1, no, no, std::integral_constant<int, 0>{});
+    step(nkl - 1, no, no, std::integral_constant<int, 0>{});
 
     // ------------------------------------------------ next tile, epilogue
     // per-column scales (A8W8) of this wave's columns, loaded before the next
@@ -522,98 +599,157 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
     // wait the compiler sees, so it places none later that would also wait
     // for those copies): s_waitcnt vmcnt(0)
     if constexpr (UC != UC_BF16 && MODE != 2) __builtin_amdgcn_s_waitcnt(0x0F70);
-    // every wave is done reading the ring: the next tile's stages go out now
+    // every wave is done reading the ring
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    const int ntile = tile + per_x;
-    const bool nhave = ntile < t_end;
+    const int nitem = item + 1;
+    const bool nhave = nitem < n_items;
     TileRef nxt{};
-    if (nhave) {
-      nxt = resolve_tile<BM>(a, off_s, cnt_s, ntile, n_tiles, kbytes);
-      start_tile(nxt, buf ^ 1);
-    }
+    // A K piece of a split tile: a later piece hands its partial sums to
+    // piece 0 through its slot and moves on; piece 0 adds them in piece
+    // order.  Both finish this exchange before the next item's stages go out
+    // (the waits for the exchange would otherwise wait for those too).
+    if (cur.role != kRoleFull) {
+      uint32_t* const pslot = a.partials + (size_t)cur.slot * (BM * BN);
+      const int lane_words = ((wv * MB * NB) * 64 + l) * 16;   // [wave][block][lane][16]
+      if (cur.role == kRoleProduce) {
 #pragma unroll
-    for (int i = 0; i < MB; ++i) {
-      const int rb = wm * WTM + i * 32 + 4 * h;   // this lane's rows: rb + 8*(q/4) + q%4
-      // row data of the 16 rows, read outside the compiler's view (it would
-      // otherwise wait for the next tile's LDS copies first): Linear2 needs
-      // the whole entry, A8W8 Linear1 only s^X
-      u32x4 ri[MODE == 1 ? 16 : 1];
-      uint32_t sxr[(MODE == 0 && UC != UC_BF16) ? 16 : 1];
-      if constexpr (MODE == 1 || (MODE == 0 && UC != UC_BF16)) {
+        for (int i = 0; i < MB; ++i)
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int r = rb + 8 * (q / 4) + (q % 4);
-          const uint32_t ad = rowinfo_base + (uint32_t)((buf * BM + r) * (int)sizeof(RowInfo));
-          if constexpr (MODE == 1) ri[q] = ds_read16<0>(ad);
-          else sxr[q] = ds_read4<8>(ad);
-        }
-        lgkm_wait<0>();
+          for (int j = 0; j < NB; ++j) {
+            u32x4* dst = reinterpret_cast<u32x4*>(pslot + lane_words + (i * NB + j) * 64 * 16);
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          if constexpr (MODE == 1) tie(ri[q]);
-          else tie(sxr[q]);
-        }
-      }
-      if constexpr (MODE == 0) {
-        // tile bases are uniform; per-element offsets stay 32-bit (BM*I < 2^31)
-        uint16_t* const obase = static_cast<uint16_t*>(a.a_out) + (int64_t)cur.row0 * a.I + cur.n0 / 2;
-        float* const sbase = a.a_stage + (int64_t)cur.row0 * a.I + cur.n0 / 2;
-        // the lane's first row offset, laundered so that the compiler does not
-        // hoist the 16 per-row offsets out of the tile loop (they would stay
-        // live through the mainloop)
-        int lane_off = rb * a.I + wn * (WTN / 2) + lr;
-        asm volatile("" : "+v"(lane_off));
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int r = rb + 8 * (q / 4) + (q % 4);
-#pragma unroll
-          for (int j = 0; j < NB / 2; ++j) {
-            const int oc = lane_off + (8 * (q / 4) + (q % 4)) * a.I + j * 32;
-            float g = acc_to_f32(acc[i][2 * j][q]);
-            float u = acc_to_f32(acc[i][2 * j + 1][q]);
-            if constexpr (UC != UC_BF16) {
-              const float sx = __uint_as_float(sxr[q]);
-              g = (g * cs0[j]) * sx;
-              u = (u * cs1[j]) * sx;
-            }
-            const float v = silu(g) * u;
-            if (r < cur.valid) {
-              if constexpr (UC == UC_BF16) gp(obase)[oc] = f32_to_bf16_bits(v);
-              else gp(sbase)[oc] = v;
-            }
+            for (int v = 0; v < 4; ++v)
+              gp(dst)[v] = u32x4{word_of(acc[i][j][4 * v]), word_of(acc[i][j][4 * v + 1]), word_of(acc[i][j][4 * v + 2]),
+                                 word_of(acc[i][j][4 * v + 3])};
           }
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the partial sums are in L2
+        __syncthreads();
+        if (t == 0) {
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+          __hip_atomic_store(&a.split_flags[cur.slot], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
       } else {
-        int32_t* const rbase = a.raw_out + (int64_t)cur.row0 * a.N;
-        int lane_row = rb;
-        asm volatile("" : "+v"(lane_row));   // keeps the row offsets inside the tile loop
+        __shared__ int32_t ready;
+        if (t == 0) {
+          bool ok = true;
+          for (int q = 1; q < sk; ++q) ok = ok && poll_flag(&a.split_flags[cur.slot + q], a.spin_limit);
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+          if (!ok && a.err) atomicOr(a.err, (uint32_t)MM_DEVERR_BARRIER_TIMEOUT);
+          ready = ok ? 1 : 0;
+        }
+        __syncthreads();
+        if (ready) {
+          for (int q = 1; q < sk; ++q) {
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
-          const int n = cur.n0 + wn * WTN + j * 32 + lr;
+            for (int i = 0; i < MB; ++i)
+#pragma unroll
+              for (int j = 0; j < NB; ++j) {
+                const u32x4* src = reinterpret_cast<const u32x4*>(pslot + (size_t)q * (BM * BN) + lane_words + (i * NB + j) * 64 * 16);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                  const u32x4 w = gp(src)[v];
+#pragma unroll
+                  for (int e = 0; e < 4; ++e) acc[i][j][4 * v + e] += from_word<AccE>(w[e]);
+                }
+              }
+          }
+        }
+        __syncthreads();   // every partial has been read: the flags go back to zero
+        if (t == 0)
+          for (int q = 1; q < sk; ++q)
+            __hip_atomic_store(&a.split_flags[cur.slot + q], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    // the next item's first stages go out now, ahead of this tile's epilogue
+    if (nhave) {
+      nxt = make_item(nitem);
+      start_tile(nxt, buf ^ 1);
+    }
+    if (cur.role != kRoleProduce) {   // a later piece has no epilogue
+#pragma unroll
+      for (int i = 0; i < MB; ++i) {
+        const int rb = wm * WTM + i * 32 + 4 * h;   // this lane's rows: rb + 8*(q/4) + q%4
+        // row data of the 16 rows, read outside the compiler's view (it would
+        // otherwise wait for the next tile's LDS copies first): Linear2 needs
+        // the whole entry, A8W8 Linear1 only s^X
+        u32x4 ri[MODE == 1 ? 16 : 1];
+        uint32_t sxr[(MODE == 0 && UC != UC_BF16) ? 16 : 1];
+        if constexpr (MODE == 1 || (MODE == 0 && UC != UC_BF16)) {
 #pragma unroll
           for (int q = 0; q < 16; ++q) {
             const int r = rb + 8 * (q / 4) + (q % 4);
-            if constexpr (MODE == 1) {
-              // contribution of route i*K+k: ((D * s^W2) * s^A) * G[i,k]
-              const int32_t route = (int32_t)ri[q][0];
-              const float gw = __uint_as_float(ri[q][1]);
-              const float v = acc_to_f32(acc[i][j][q]) * cs0[j];
-              const float o = (UC != UC_BF16) ? (v * __uint_as_float(ri[q][2])) * gw : v * gw;
-              if (route >= 0) gp(a.contrib)[(int64_t)route * a.H + n] = o;
-            } else {
-              int col = n;
-              if (a.gate_up_group > 0) {
-                const int g2 = 2 * a.gate_up_group;
-                const int qq = n / g2, m = n % g2;
-                col = (m < a.gate_up_group) ? qq * a.gate_up_group + m : a.I + qq * a.gate_up_group + (m - a.gate_up_group);
+            const uint32_t ad = rowinfo_base + (uint32_t)((buf * BM + r) * (int)sizeof(RowInfo));
+            if constexpr (MODE == 1) ri[q] = ds_read16<0>(ad);
+            else sxr[q] = ds_read4<8>(ad);
+          }
+          lgkm_wait<0>();
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            if constexpr (MODE == 1) tie(ri[q]);
+            else tie(sxr[q]);
+          }
+        }
+        if constexpr (MODE == 0) {
+          // tile bases are uniform; per-element offsets stay 32-bit (BM*I < 2^31)
+          uint16_t* const obase = static_cast<uint16_t*>(a.a_out) + (int64_t)cur.row0 * a.I + cur.n0 / 2;
+          float* const sbase = a.a_stage + (int64_t)cur.row0 * a.I + cur.n0 / 2;
+          // the lane's first row offset, laundered so that the compiler does not
+          // hoist the 16 per-row offsets out of the tile loop (they would stay
+          // live through the mainloop)
+          int lane_off = rb * a.I + wn * (WTN / 2) + lr;
+          asm volatile("" : "+v"(lane_off));
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            const int r = rb + 8 * (q / 4) + (q % 4);
+#pragma unroll
+            for (int j = 0; j < NB / 2; ++j) {
+              const int oc = lane_off + (8 * (q / 4) + (q % 4)) * a.I + j * 32;
+              float g = acc_to_f32(acc[i][2 * j][q]);
+              float u = acc_to_f32(acc[i][2 * j + 1][q]);
+              if constexpr (UC != UC_BF16) {
+                const float sx = __uint_as_float(sxr[q]);
+                g = (g * cs0[j]) * sx;
+                u = (u * cs1[j]) * sx;
               }
-              if (r < cur.valid) gp(rbase)[(lane_row + 8 * (q / 4) + (q % 4)) * a.N + col] = acc[i][j][q];
+              const float v = silu(g) * u;
+              if (r < cur.valid) {
+                if constexpr (UC == UC_BF16) gp(obase)[oc] = f32_to_bf16_bits(v);
+                else gp(sbase)[oc] = v;
+              }
+            }
+          }
+        } else {
+          int32_t* const rbase = a.raw_out + (int64_t)cur.row0 * a.N;
+          int lane_row = rb;
+          asm volatile("" : "+v"(lane_row));   // keeps the row offsets inside the tile loop
+#pragma unroll
+          for (int j = 0; j < NB; ++j) {
+            const int n = cur.n0 + wn * WTN + j * 32 + lr;
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+              const int r = rb + 8 * (q / 4) + (q % 4);
+              if constexpr (MODE == 1) {
+                // contribution of route i*K+k: ((D * s^W2) * s^A) * G[i,k]
+                const int32_t route = (int32_t)ri[q][0];
+                const float gw = __uint_as_float(ri[q][1]);
+                const float v = acc_to_f32(acc[i][j][q]) * cs0[j];
+                const float o = (UC != UC_BF16) ? (v * __uint_as_float(ri[q][2])) * gw : v * gw;
+                if (route >= 0) gp(a.contrib)[(int64_t)route * a.H + n] = o;
+              } else {
+                int col = n;
+                if (a.gate_up_group > 0) {
+                  const int g2 = 2 * a.gate_up_group;
+                  const int qq = n / g2, m = n % g2;
+                  col = (m < a.gate_up_group) ? qq * a.gate_up_group + m : a.I + qq * a.gate_up_group + (m - a.gate_up_group);
+                }
+                if (r < cur.valid) gp(rbase)[(lane_row + 8 * (q / 4) + (q % 4)) * a.N + col] = acc[i][j][q];
+              }
             }
           }
         }
       }
     }
-    tile = ntile;
+    item = nitem;
     have = nhave;
     cur = nxt;
     buf ^= 1;
@@ -639,18 +775,41 @@ __device__ __forceinline__ void requant_row(const RequantArgs& a, int64_t p, con
   }
   if (p >= (int64_t)off_s[lo] + cnt_s[lo]) return;
   const float4* src = reinterpret_cast<const float4*>(a.a_stage + p * a.I);
-  // row amax over all I columns (exact: a max), then the codes
+  // row amax over all I columns (exact: a max), then the codes.  Rows of up
+  // to kRequantRegChunks float8 chunks stay in registers between the two
+  // (every load of the row in flight at once); longer rows are read twice.
+  constexpr int kRequantRegChunks = 8;                       // I <= 64*8*8 = 4096
+  const int nch = a.I / 8;
+  const bool in_regs = nch <= 64 * kRequantRegChunks;
+  float4 keep[2 * kRequantRegChunks];
   float m = 0.0f;
-  for (int c = l; c < a.I / 4; c += 64) {
-    const float4 v = src[c];
-    m = fmaxf(fmaxf(m, fmaxf(fabsf(v.x), fabsf(v.y))), fmaxf(fabsf(v.z), fabsf(v.w)));
+  if (in_regs) {
+#pragma unroll
+    for (int j = 0; j < kRequantRegChunks; ++j) {
+      const int c = j * 64 + l;
+      if (c < nch) {
+        keep[2 * j] = src[2 * c];
+        keep[2 * j + 1] = src[2 * c + 1];
+      } else {
+        keep[2 * j] = keep[2 * j + 1] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 2 * kRequantRegChunks; ++j) {
+      const float4 v = keep[j];
+      m = fmaxf(fmaxf(m, fmaxf(fabsf(v.x), fabsf(v.y))), fmaxf(fabsf(v.z), fabsf(v.w)));
+    }
+  } else {
+    for (int c = l; c < a.I / 4; c += 64) {
+      const float4 v = src[c];
+      m = fmaxf(fmaxf(m, fmaxf(fabsf(v.x), fabsf(v.y))), fmaxf(fabsf(v.z), fabsf(v.w)));
+    }
   }
   m = wave_max(m);
   const float qmax = (UC == UC_I8) ? 127.0f : 448.0f;
   const float s = fmaxf(m / qmax, 1e-8f);
   uint2* dst = reinterpret_cast<uint2*>(static_cast<uint8_t*>(a.a_pool) + p * a.I);
-  for (int c = l; c < a.I / 8; c += 64) {
-    const float4 v0 = src[2 * c], v1 = src[2 * c + 1];
+  auto codes = [&](const float4& v0, const float4& v1) {
     const float f[8] = {v0.x / s, v0.y / s, v0.z / s, v0.w / s, v1.x / s, v1.y / s, v1.z / s, v1.w / s};
     uint32_t o[2];
 #pragma unroll
@@ -662,7 +821,16 @@ __device__ __forceinline__ void requant_row(const RequantArgs& a, int64_t p, con
         o[q] = f32x2_to_e4m3x2(f[4 * q], f[4 * q + 1]) | (f32x2_to_e4m3x2(f[4 * q + 2], f[4 * q + 3]) << 16);
       }
     }
-    dst[c] = make_uint2(o[0], o[1]);
+    return make_uint2(o[0], o[1]);
+  };
+  if (in_regs) {
+#pragma unroll
+    for (int j = 0; j < kRequantRegChunks; ++j) {
+      const int c = j * 64 + l;
+      if (c < nch) dst[c] = codes(keep[2 * j], keep[2 * j + 1]);
+    }
+  } else {
+    for (int c = l; c < nch; c += 64) dst[c] = codes(src[2 * c], src[2 * c + 1]);
   }
   if (l == 0) a.a_scale[p] = s;
 }

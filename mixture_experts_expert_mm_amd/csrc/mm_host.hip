@@ -36,7 +36,7 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 // ---------------------------------------------------------------- workspace
 struct WsLayout {
-  int64_t ctl, wave_base, a_stage, contrib, end;                             // 3-call scratch
+  int64_t ctl, wave_base, a_stage, contrib, partials, end;                   // 3-call scratch
   int64_t mega_args, offsets, pool_src, route_to_pool, x_pool, x_pool_scale, a_pool, a_pool_scale, fused_end;
 };
 
@@ -51,6 +51,8 @@ WsLayout ws_layout(const mm_plan& pl) {
   L.wave_base = take(dispatch_waves(p.num_tokens, (int)p.num_topk) * p.num_experts * 4);
   L.a_stage = q ? take(P * p.intermediate_hidden * 4) : -1;
   L.contrib = take(R * p.hidden * 4);
+  // partial sums of split tail tiles: one slot per piece in flight
+  L.partials = take((int64_t)kSplitSlots * tile_bm(pl.tile_l1) * tile_bn(pl.tile_l1) * 4);
   L.end = o;
   L.mega_args = take(sizeof(MegaArgs));
   L.offsets = take((p.num_experts + 1) * 4);
@@ -165,6 +167,33 @@ DispatchArgs dispatch_args(const mm_plan& pl, const int32_t* ids, const void* x,
   return d;
 }
 
+// Polls a wait inside a kernel (a fused-kernel grid barrier, a GEMM waiting
+// for a partial tile) makes before giving up (about seconds); MM_BARRIER_SPIN
+// overrides it, which tests use to exercise the time-out.
+uint32_t barrier_spin_limit() {
+  if (const char* v = std::getenv("MM_BARRIER_SPIN")) {
+    const long n = std::atol(v);
+    if (n > 0) return (uint32_t)n;
+  }
+  return 1u << 21;
+}
+
+// Largest K split of a tail tile (MM_MAX_SPLIT overrides: 1 turns it off).
+int max_split() {
+  if (const char* v = std::getenv("MM_MAX_SPLIT")) {
+    const int n = std::atoi(v);
+    if (n >= 1 && n <= 8) return n;
+  }
+  return 8;
+}
+
+void set_split(GemmArgs& g, const WsLayout& L, void* ws) {
+  g.partials = at<uint32_t>(ws, L.partials);
+  g.split_flags = at<uint32_t>(ws, L.ctl) + kSplitFlag0;
+  g.max_split = max_split();
+  g.spin_limit = barrier_spin_limit();
+}
+
 GemmArgs l1_args(const mm_plan& pl, const int32_t* offsets, const int32_t* counts, const void* x_pool,
                  const float* x_pool_scale, const void* w1, const float* w1_scale, void* a_pool, void* ws) {
   const mm_problem& p = pl.prob;
@@ -188,6 +217,7 @@ GemmArgs l1_args(const mm_plan& pl, const int32_t* offsets, const int32_t* count
   g.w_scale = w1_scale;
   g.a_out = a_pool;
   g.a_stage = at<float>(ws, L.a_stage);
+  set_split(g, L, ws);
   return g;
 }
 
@@ -229,6 +259,7 @@ GemmArgs l2_args(const mm_plan& pl, const int32_t* offsets, const int32_t* count
   g.w_scale = w2_scale;
   g.topk_w = topk_w;
   g.contrib = at<float>(ws, L.contrib);
+  set_split(g, L, ws);
   return g;
 }
 
@@ -280,16 +311,6 @@ mm_status do_l2(const mm_plan& pl, const int32_t* offsets, const int32_t* counts
   const CombineArgs c = combine_args(pl, g.contrib, r2p, y);
   MM_TRY(run(MM_K_COMBINE, s, [&] { return launch_combine(c, s); }));
   return MM_OK;
-}
-
-// Polls a fused-kernel grid barrier makes before giving up (about seconds);
-// MM_BARRIER_SPIN overrides it, which tests use to exercise the time-out.
-uint32_t barrier_spin_limit() {
-  if (const char* v = std::getenv("MM_BARRIER_SPIN")) {
-    const long n = std::atol(v);
-    if (n > 0) return (uint32_t)n;
-  }
-  return 1u << 21;
 }
 
 bool ok16(const void* p) { return p && aligned(p, 16); }

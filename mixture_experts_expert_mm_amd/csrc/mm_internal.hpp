@@ -60,6 +60,11 @@ struct GemmArgs {
   float* contrib;            // [T*K][H]
   // debug (mode 2: raw int32 accumulators)
   int32_t* raw_out;
+  // split tail tiles (partial accumulators of K pieces, their ready flags)
+  uint32_t* partials;        // [kSplitSlots][BM*BN] words
+  uint32_t* split_flags;     // [kSplitSlots], zero between calls
+  int max_split;             // largest K split of a tail tile (<= 1: none)
+  uint32_t spin_limit;       // polls before a wait for a partial gives up
 };
 
 struct RequantArgs {
@@ -82,8 +87,12 @@ struct CombineArgs {
 
 // Control words at the start of the workspace, cleared by the pre-pass of
 // every call: [1] is the device error word (mm_device_error bits); the fused
-// kernel's grid barriers use [0], [2] and [16..47].
-constexpr int kCtlWords = 64;
+// kernel's grid barriers use [0], [2] and [16..47]; [kSplitFlag0 ..] are the
+// ready flags of split tail tiles (each flag is reset by its consumer, so
+// they are zero again when a GEMM ends).
+constexpr int kSplitSlots = 512;
+constexpr int kSplitFlag0 = 64;
+constexpr int kCtlWords = kSplitFlag0 + kSplitSlots;
 
 // Everything the fused persistent kernel needs: the arguments of each phase.
 struct MegaArgs {

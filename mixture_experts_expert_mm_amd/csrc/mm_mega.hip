@@ -168,7 +168,7 @@ __global__ __launch_bounds__(256) void k_mega_prep(MegaArgs m, MegaArgs* out) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t j = i; j < m.d.E; j += stride) m.d.counts[j] = 0;
-  if (i < kCtlWords) m.ctl[i] = 0u;
+  for (int64_t j = i; j < kCtlWords; j += stride) m.ctl[j] = 0u;
   constexpr int words = (int)(sizeof(MegaArgs) / 4);
   static_assert(sizeof(MegaArgs) % 4 == 0, "argument block copies as words");
   if (blockIdx.x == 0) {

@@ -225,6 +225,36 @@ def test_fused_equals_three_call_and_is_deterministic(usecase):
     assert layer.device_error(fused=True) == 0 and layer.device_error(fused=False) == 0
 
 
+@pytest.mark.parametrize("usecase", ["int8", "bf16", "fp8"])
+def test_split_tail_tiles(usecase, monkeypatch):
+    """Few tiles on many workgroups: the tail tiles are split along K (eight
+    pieces in Linear1, two in Linear2 here) and piece 0 adds the others'
+    partial sums in piece order.  int8 accumulators are exact, so the split
+    result equals the unsplit one bit for bit; every use case stays within
+    the oracle tolerance, and fused == three-call."""
+    cfg = wl.Config(f"split_{usecase}", usecase, 64, 4096, 1024, 4, 2, 0.5, 77)
+    inp = wl.make_inputs(cfg)
+    x, ids, wts = device_inputs(inp)
+    layer = make_layer(inp, "f32")
+    monkeypatch.setenv("MM_MAX_SPLIT", "1")
+    y_one, _ = layer.forward(x, ids, wts)
+    y_one = y_one.clone()
+    monkeypatch.setenv("MM_MAX_SPLIT", "8")
+    log(f"[split] {usecase}: unsplit vs split tail tiles")
+    y_f, _ = layer.forward(x, ids, wts)
+    y_3, _ = layer.forward_3call(x, ids, wts)
+    torch.cuda.synchronize()
+    assert layer.device_error(fused=True) == 0 and layer.device_error(fused=False) == 0
+    assert torch.equal(y_f.view(torch.int32), y_3.view(torch.int32))
+    if usecase == "int8":
+        assert torch.equal(y_f.view(torch.int32), y_one.view(torch.int32))
+    y_or = oracle_y(inp)
+    for y in (y_one, y_f):
+        err = rel_err(y.cpu().double().numpy(), y_or)
+        log(f"    max|dY|/rms = {err:.3e}")
+        assert err <= TOL[usecase], err
+
+
 def test_fused_barrier_timeout_is_reported_and_recovers(monkeypatch):
     """A grid barrier that gives up (forced from the host with a one-poll
     limit) sets its error bit and every block still leaves the kernel; the
