@@ -140,18 +140,22 @@ __device__ void scatter_block(const DispatchArgs& a, int64_t vb, int64_t nvb, in
 // [-127,127] or e4m3fn ties-to-even saturated to +-448.
 constexpr int kMaxHidden = 16384;
 
-template <int UC, int NT>
+// TOK: write row i of a [T][H] buffer (x_pool, x_pool_scale indexed by
+// token) instead of the K pool rows of token i: the fused kernel's A8W8
+// quantisation of the tokens, whose Linear1 reads token rows in place.
+template <int UC, int NT, bool TOK = false>
 __device__ void gather_token(const DispatchArgs& a, int64_t i, int32_t* dst, float* red) {
   constexpr int NW = NT / 64, MAXC = kMaxHidden / 8 / NT;
   const int t = threadIdx.x;
-  if (t < a.K) dst[t] = a.route_to_pool[i * a.K + t];
+  const int nrows = TOK ? 1 : a.K;
+  if (t < nrows) dst[t] = TOK ? (int32_t)i : a.route_to_pool[i * a.K + t];
   const int nchunk = (int)(a.H / 8);
   const uint4* xr = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + i * a.H);
   if constexpr (UC == UC_BF16) {
     __syncthreads();
     for (int c = t; c < nchunk; c += NT) {
       const uint4 v = xr[c];
-      for (int k = 0; k < a.K; ++k) {
+      for (int k = 0; k < nrows; ++k) {
         const int p = dst[k];
         if (p >= 0) reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.x_pool) + (int64_t)p * a.H)[c] = v;
       }
@@ -199,13 +203,13 @@ __device__ void gather_token(const DispatchArgs& a, int64_t i, int32_t* dst, flo
           }
         }
         const uint2 ov = make_uint2(o[0], o[1]);
-        for (int k = 0; k < a.K; ++k) {
+        for (int k = 0; k < nrows; ++k) {
           const int p = dst[k];
           if (p >= 0) reinterpret_cast<uint2*>(static_cast<uint8_t*>(a.x_pool) + (int64_t)p * a.H)[c] = ov;
         }
       }
     }
-    if (t < a.K && dst[t] >= 0) a.x_pool_scale[dst[t]] = s;
+    if (t < nrows && dst[t] >= 0) a.x_pool_scale[dst[t]] = s;
   }
   __syncthreads();   // dst / red are reused by the next token
 }

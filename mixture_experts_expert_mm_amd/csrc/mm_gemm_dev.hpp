@@ -103,17 +103,21 @@ __device__ __forceinline__ void vm_barrier() {
 // group; the group's row offset and the stage's K offset are wave-uniform
 // and go in the scalar offset.  The tile bases become buffer descriptors
 // here: the descriptor type cannot appear in a signature the host pass sees.
+// A rows read by token (by_tok): the lane's own row offset voff_a replaces
+// the group's row offset, which then stays out of the scalar offset.
 template <int NW, int BM, int STAGE, int S, int RB>
 __device__ __forceinline__ void dma_one(uint8_t* lds, const uint8_t* abase, int abytes, const uint8_t* bbase,
-                                        int bbytes, uint32_t voff, int wv, int kbytes, int i, int kb, int kbase) {
+                                        int bbytes, uint32_t voff, int wv, int kbytes, int i, int kb, int kbase,
+                                        bool by_tok, uint32_t voff_a) {
   constexpr int RPI = 1024 / RB;
   const bool is_a = i < BM / (RPI * NW);
   const __amdgpu_buffer_rsrc_t rs =
       __builtin_amdgcn_make_buffer_rsrc((void*)(is_a ? abase : bbase), (short)0, is_a ? abytes : bbytes, 0x00020000);
-  const int rows = is_a ? RPI * NW * i : RPI * NW * i - BM;
+  const int rows = is_a ? (by_tok ? 0 : RPI * NW * i) : RPI * NW * i - BM;
   const int soff = __builtin_amdgcn_readfirstlane(rows * kbytes + (kb + kbase) * RB);
   const int g = wv + NW * i;
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(lds + (kb % S) * STAGE + g * 1024), 16, voff, soff, 0, 0);
+  const uint32_t vo = (is_a && by_tok) ? voff_a : voff;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(lds + (kb % S) * STAGE + g * 1024), 16, vo, soff, 0, 0);
 }
 
 // The fragments of one K-stage held in registers: NQ 16-byte chunks of the
@@ -215,6 +219,8 @@ __device__ __forceinline__ GemmArgs uniform_args(const GemmArgs& in) {
   a.H = uniform_int(in.H);
   a.K = uniform_int(in.K);
   a.gate_up_group = uniform_int(in.gate_up_group);
+  a.a_route = uniform_ptr(in.a_route);
+  a.a_rows = (int64_t)uniform_int((int)in.a_rows);   // < 2^31 (checked by the host)
   a.partials = uniform_ptr(in.partials);
   a.split_flags = uniform_ptr(in.split_flags);
   a.max_split = uniform_int(in.max_split);
@@ -230,6 +236,7 @@ struct TileRef {
   const uint8_t* abase;   // first A row of the tile
   const uint8_t* bbase;   // first B row (prepared weights) of the tile
   int kbase, nkl;         // K stages kbase .. kbase + nkl - 1
+  uint32_t aoa[2];        // per lane: byte offsets of its A rows' chunks (A read by token)
   int role;               // TileRole: whole tile, or piece 0 (adds the others' partials), or a later piece
   int slot;               // partial slot of a piece (piece 0: the later pieces use slot + 1 ..)
 };
@@ -294,7 +301,7 @@ __device__ __forceinline__ TileRef resolve_tile(const GemmArgs& a, const int32_t
   r.row0 = uniform_int(mblk * BM);
   r.n0 = uniform_int(nblk * TileShape<BM>::BN);
   r.valid = uniform_int(min(BM, off_s[lo] + cnt_s[lo] - r.row0));
-  r.abase = uniform_ptr(a.A + (int64_t)r.row0 * kbytes);
+  r.abase = uniform_ptr(a.a_route ? a.A : a.A + (int64_t)r.row0 * kbytes);
   r.bbase = uniform_ptr(a.B + ((int64_t)r.e * a.N + r.n0) * kbytes);
   return r;
 }
@@ -374,11 +381,17 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
   // differ by RPI*NW*i, a multiple of the swizzle period RPS*CH (needs NW
   // even when CH = 8).
   static_assert((RPI * NW / RPS) % CH == 0, "DMA swizzle must repeat across a wave's groups");
-  const uint32_t voff =
-      (uint32_t)((RPI * wv + l / CH) * kbytes + (((l % CH) ^ (((RPI * wv + l / CH) / RPS) % CH)) << 4));
-  const int abytes = BM * kbytes, bbytes = BN * kbytes;
-#define MM_DMA(tr_, i_, kb_) \
-  dma_one<NW, BM, STAGE, S, RB>(lds, (tr_).abase, abytes, (tr_).bbase, bbytes, voff, wv, kbytes, (i_), (kb_), (tr_).kbase)
+  const uint32_t vchunk = (uint32_t)(((l % CH) ^ (((RPI * wv + l / CH) / RPS) % CH)) << 4);
+  const uint32_t voff = (uint32_t)((RPI * wv + l / CH) * kbytes) + vchunk;
+  // A read by token: the A buffer is the T token rows, each lane's rows come
+  // from the route of their pool row (padding rows read token 0, unused)
+  const bool by_tok = a.a_route != nullptr;
+  constexpr int DA = BM / (RPI * NW);                      // A instructions per wave and stage
+  static_assert(DA <= 2, "per-lane A row offsets of at most two instructions");
+  const int abytes = by_tok ? (int)(a.a_rows * kbytes) : BM * kbytes, bbytes = BN * kbytes;
+#define MM_DMA(tr_, i_, kb_)                                                                                    \
+  dma_one<NW, BM, STAGE, S, RB>(lds, (tr_).abase, abytes, (tr_).bbase, bbytes, voff, wv, kbytes, (i_), (kb_), \
+                                (tr_).kbase, by_tok, (tr_).aoa[(i_) < DA ? (i_) : 0])
 
   // Per-row epilogue data of tile `tr` into rowinfo[buf] (thread r: row r).
   auto fill_rowinfo = [&](const TileRef& tr, int buf) {
@@ -386,7 +399,14 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
       RowInfo ri{-1, 0.0f, 1.0f, 0.0f};
       if (r < tr.valid) {
         const int64_t p = (int64_t)tr.row0 + r;
-        if constexpr (MODE == 0 && UC != UC_BF16) ri.rs = gp(a.x_scale)[p];
+        if constexpr (MODE == 0 && UC != UC_BF16) {
+          if (by_tok) {
+            const int32_t route = gp(a.a_route)[p];
+            ri.rs = route >= 0 ? gp(a.x_scale)[route / a.K] : 1.0f;
+          } else {
+            ri.rs = gp(a.x_scale)[p];
+          }
+        }
         if constexpr (MODE == 1) {
           int32_t route = gp(a.pool_src)[p];
           if (route < 0 || route >= a.routes) route = -1;   // not a route of this call: row left out
@@ -443,6 +463,15 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
       r.nkl = uniform_int((sub + 1) * nk / sk - sub * nk / sk);
       r.role = sk == 1 ? kRoleFull : (sub == 0 ? kRoleReduce : kRoleProduce);
       r.slot = uniform_int(xcd * 2 * per_x + p);
+    }
+    r.aoa[0] = r.aoa[1] = 0;
+    if (by_tok) {
+#pragma unroll
+      for (int x = 0; x < DA; ++x) {
+        const int64_t p = (int64_t)r.row0 + RPI * (wv + NW * x) + l / CH;
+        const int32_t route = gp(a.a_route)[p];
+        r.aoa[x] = (uint32_t)((route >= 0 ? route / a.K : 0) * kbytes) + vchunk;
+      }
     }
     return r;
   };

@@ -37,7 +37,8 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 // ---------------------------------------------------------------- workspace
 struct WsLayout {
   int64_t ctl, wave_base, a_stage, contrib, partials, end;                   // 3-call scratch
-  int64_t mega_args, offsets, pool_src, route_to_pool, x_pool, x_pool_scale, a_pool, a_pool_scale, fused_end;
+  int64_t mega_args, offsets, pool_src, route_to_pool, x_pool, x_pool_scale, a_pool, a_pool_scale, x_tok, x_tok_scale,
+      fused_end;
 };
 
 WsLayout ws_layout(const mm_plan& pl) {
@@ -62,6 +63,9 @@ WsLayout ws_layout(const mm_plan& pl) {
   L.x_pool_scale = take(P * 4);
   L.a_pool = take(pl.a_pool_bytes);
   L.a_pool_scale = take(P * 4);
+  // A8W8 codes and scales of the T tokens (the fused kernel's Linear1 reads token rows in place)
+  L.x_tok = q ? take(p.num_tokens * p.hidden) : -1;
+  L.x_tok_scale = q ? take(p.num_tokens * 4) : -1;
   L.fused_end = o;
   return L;
 }
@@ -185,6 +189,13 @@ int max_split() {
     if (n >= 1 && n <= 8) return n;
   }
   return 8;
+}
+
+// Fused kernel: Linear1 reads token rows in place (MM_L1_BY_TOKEN=0 gathers
+// the pool rows instead; a tuning switch).
+bool by_token_enabled() {
+  const char* v = std::getenv("MM_L1_BY_TOKEN");
+  return !(v && v[0] == '0');
 }
 
 void set_split(GemmArgs& g, const WsLayout& L, void* ws) {
@@ -450,6 +461,18 @@ mm_status mega_moe(const mm_plan* plan, const void* x, const int32_t* topk_ids, 
   m.cb = combine_args(pl, m.l2.contrib, r2p, y);
   m.ctl = at<uint32_t>(workspace, L.ctl);
   m.nwaves = dispatch_waves(pl.prob.num_tokens, (int)pl.prob.num_topk);
+  // Linear1 reads the token rows in place (x, or the token codes) through
+  // pool_src when the token matrix fits one buffer descriptor
+  const int64_t tok_bytes = pl.prob.num_tokens * pl.prob.hidden * elem_size(pl.prob.usecase);
+  if (tok_bytes < ((int64_t)1 << 31) && by_token_enabled()) {
+    m.l1_by_token = 1;
+    m.x_tok = q ? at<uint8_t>(workspace, L.x_tok) : nullptr;
+    m.x_tok_scale = q ? at<float>(workspace, L.x_tok_scale) : nullptr;
+    m.l1.A = static_cast<const uint8_t*>(q ? m.x_tok : x);
+    m.l1.x_scale = m.x_tok_scale;
+    m.l1.a_route = pool_src;
+    m.l1.a_rows = pl.prob.num_tokens;
+  }
   m.spin_limit = barrier_spin_limit();
   MegaArgs* dev_args = at<MegaArgs>(workspace, L.mega_args);
   MM_TRY(run(MM_K_ZERO, s, [&] { return launch_mega_prep(m, dev_args, s); }));

@@ -60,6 +60,10 @@ struct GemmArgs {
   float* contrib;            // [T*K][H]
   // debug (mode 2: raw int32 accumulators)
   int32_t* raw_out;
+  // Linear1 of the fused kernel: A row p of a tile is the token row
+  // a_route[p] / K of A (a_rows token rows) instead of pool row p
+  const int32_t* a_route;    // [P] route i*K+k of pool row p (-1: padding), or null
+  int64_t a_rows;            // T when a_route is set
   // split tail tiles (partial accumulators of K pieces, their ready flags)
   uint32_t* partials;        // [kSplitSlots][BM*BN] words
   uint32_t* split_flags;     // [kSplitSlots], zero between calls
@@ -102,6 +106,11 @@ struct MegaArgs {
   CombineArgs cb;
   uint32_t* ctl;             // [kCtlWords]
   int64_t nwaves;            // dispatch waves
+  // Linear1 reads the token rows in place (l1.a_route set): A8W8 codes and
+  // scales of the T tokens are made here, no pool rows are gathered
+  void* x_tok;               // [T][H] codes (A8W8)
+  float* x_tok_scale;        // [T] (A8W8)
+  int l1_by_token;
   uint32_t spin_limit;       // polls before a grid barrier gives up
 };
 

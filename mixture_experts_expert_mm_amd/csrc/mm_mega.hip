@@ -127,12 +127,23 @@ void k_mega(const MegaArgs* mp) {
   }
   if (!grid_barrier(ctl, ++nb, spin, bs, &ok)) return;
 
-  // gather (+ A8W8 activation quantisation), one token per block at a time
-  {
+  // gather (+ A8W8 activation quantisation), one token per block at a time.
+  // When Linear1 reads the token rows in place there is nothing to gather
+  // for A16W16, and A8W8 quantises each token once into a [T][H] buffer
+  // instead of writing its K pool rows.
+  if (m.l1_by_token) {
+    if constexpr (UC != UC_BF16) {
+      DispatchArgs d = m.d;
+      d.x_pool = m.x_tok;
+      d.x_pool_scale = m.x_tok_scale;
+      for (int64_t tok = blockIdx.x; tok < d.T; tok += gridDim.x) gather_token<UC, NT, true>(d, tok, dst, red);
+      if (!grid_barrier(ctl, ++nb, spin, bs, &ok)) return;
+    }
+  } else {
     const DispatchArgs d = m.d;
     for (int64_t tok = blockIdx.x; tok < d.T; tok += gridDim.x) gather_token<UC, NT>(d, tok, dst, red);
+    if (!grid_barrier(ctl, ++nb, spin, bs, &ok)) return;
   }
-  if (!grid_barrier(ctl, ++nb, spin, bs, &ok)) return;
 
   // Linear1 + SwiGLU (gemm_tiles leaves the offsets and counts in off_s / cnt_s)
   {
