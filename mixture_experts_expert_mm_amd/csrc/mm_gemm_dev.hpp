@@ -393,41 +393,53 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
   dma_one<NW, BM, STAGE, S, RB>(lds, (tr_).abase, abytes, (tr_).bbase, bbytes, voff, wv, kbytes, (i_), (kb_), \
                                 (tr_).kbase, by_tok, (tr_).aoa[(i_) < DA ? (i_) : 0])
 
-  // Per-row epilogue data of tile `tr` into rowinfo[buf] (thread r: row r).
-  auto fill_rowinfo = [&](const TileRef& tr, int buf) {
-    for (int r = t; r < BM; r += NT) {
-      RowInfo ri{-1, 0.0f, 1.0f, 0.0f};
-      if (r < tr.valid) {
-        const int64_t p = (int64_t)tr.row0 + r;
-        if constexpr (MODE == 0 && UC != UC_BF16) {
-          if (by_tok) {
-            const int32_t route = gp(a.a_route)[p];
-            ri.rs = route >= 0 ? gp(a.x_scale)[route / a.K] : 1.0f;
-          } else {
-            ri.rs = gp(a.x_scale)[p];
-          }
-        }
-        if constexpr (MODE == 1) {
-          int32_t route = gp(a.pool_src)[p];
-          if (route < 0 || route >= a.routes) route = -1;   // not a route of this call: row left out
-          ri.route = route;
-          ri.gw = route >= 0 ? gp(a.topk_w)[route] : 0.0f;
-          if constexpr (UC != UC_BF16) ri.rs = gp(a.a_scale)[p];
-        }
+  // Per-row epilogue data of a tile, thread t holding row t: loaded into
+  // registers when the tile's stages go out (the loads that need the route
+  // once the tile's first stage has landed, by then the route has arrived),
+  // written to rowinfo[buf] when the tile's mainloop is done.  No wait for
+  // row data holds back the tile's stages.
+  static_assert(BM <= NT, "one row per thread");
+  struct RowRegs {
+    int32_t route;
+    float gw, rs;
+  };
+  auto row_first = [&](const TileRef& tr) {
+    RowRegs rr{-1, 0.0f, 1.0f};
+    if (t < tr.valid) {
+      const int64_t p = (int64_t)tr.row0 + t;
+      if constexpr (MODE == 0 && UC != UC_BF16) {
+        if (by_tok) rr.route = gp(a.a_route)[p];
+        else rr.rs = gp(a.x_scale)[p];
       }
-      rowinfo[buf * BM + r] = ri;
+      if constexpr (MODE == 1) {
+        rr.route = gp(a.pool_src)[p];
+        if constexpr (UC != UC_BF16) rr.rs = gp(a.a_scale)[p];
+      }
+    }
+    return rr;
+  };
+  auto row_second = [&](RowRegs& rr) {
+    if constexpr (MODE == 0 && UC != UC_BF16) {
+      if (by_tok) rr.rs = rr.route >= 0 ? gp(a.x_scale)[rr.route / a.K] : 1.0f;
+    }
+    if constexpr (MODE == 1) {
+      if (rr.route < 0 || rr.route >= a.routes) rr.route = -1;   // not a route of this call: row left out
+      rr.gw = rr.route >= 0 ? gp(a.topk_w)[rr.route] : 0.0f;
     }
   };
-  // The first S stages of tile `tr` (its row data goes first: no DMA is in
-  // flight yet, so the compiler's waits for those loads cost nothing).
-  auto start_tile = [&](const TileRef& tr, int buf) {
-    fill_rowinfo(tr, buf);
+  auto row_commit = [&](const RowRegs& rr, int buf) {
+    if (t < BM) rowinfo[buf * BM + t] = RowInfo{MODE == 1 ? rr.route : -1, rr.gw, rr.rs, 0.0f};
+  };
+  // The first S stages of tile `tr`, after its row data loads.
+  auto start_tile = [&](const TileRef& tr) {
+    const RowRegs rr = row_first(tr);
 #pragma unroll
     for (int st = 0; st < S; ++st)
       if (st < tr.nkl) {
 #pragma unroll
         for (int x = 0; x < D; ++x) MM_DMA(tr, x, st);
       }
+    return rr;
   };
 
   // Workgroup w runs on XCD w % 8 (round-robin dispatch); each XCD walks its
@@ -479,10 +491,11 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
   int item = 0;
   bool have = item < n_items;
   TileRef cur{};
+  RowRegs rr_cur{-1, 0.0f, 1.0f};
   int buf = 0;
   if (have) {
     cur = make_item(0);
-    start_tile(cur, buf);
+    rr_cur = start_tile(cur);
   }
   while (have) {
     AccT acc[MB][NB];
@@ -592,6 +605,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
       constexpr int c = S - 1 - decltype(cc)::value;   // S-1, ..., 0
       if (min(nkl, S) - 1 == c) vm_barrier<c * D>();
     });
+    row_second(rr_cur);
 #pragma unroll
     for (int r = 0; r < NQ * NFR; ++r) read_frag<32 * RB>(f, r, aoff, boff, 0u);
     // Every barrier below has a compile-time DMA count.  At step kb's barrier
@@ -628,11 +642,13 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
     // wait the compiler sees, so it places none later that would also wait
     // for those copies): s_waitcnt vmcnt(0)
     if constexpr (UC != UC_BF16 && MODE != 2) __builtin_amdgcn_s_waitcnt(0x0F70);
-    // every wave is done reading the ring
+    // this tile's row data goes to LDS; every wave is done reading the ring
+    row_commit(rr_cur, buf);
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     const int nitem = item + 1;
     const bool nhave = nitem < n_items;
     TileRef nxt{};
+    RowRegs rr_nxt{-1, 0.0f, 1.0f};
     // A K piece of a split tile: a later piece hands its partial sums to
     // piece 0 through its slot and moves on; piece 0 adds them in piece
     // order.  Both finish this exchange before the next item's stages go out
@@ -692,7 +708,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
     // the next item's first stages go out now, ahead of this tile's epilogue
     if (nhave) {
       nxt = make_item(nitem);
-      start_tile(nxt, buf ^ 1);
+      rr_nxt = start_tile(nxt);
     }
     if (cur.role != kRoleProduce) {   // a later piece has no epilogue
 #pragma unroll
@@ -781,6 +797,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
     item = nitem;
     have = nhave;
     cur = nxt;
+    rr_cur = rr_nxt;
     buf ^= 1;
   }
 #undef MM_DMA
