@@ -13,13 +13,8 @@ void k_gemm(GemmArgs a) {
   gemm_tiles<UC, BM, MODE, WIDEN>(a, lds, off_s, cnt_s);
 }
 
-template <int UC, int BM, int MODE>
+template <int UC, int BM, int MODE, bool WIDEN>
 static hipError_t launch_one(const GemmArgs& a, int grid, hipStream_t s) {
-  // e4m3 Linear1 runs on bf16 MFMA with exact e4m3 -> bf16 widening: the
-  // e4m3 MFMAs round inside their dot products, and the per-row e4m3
-  // requantisation that follows Linear1 would turn that rounding into code
-  // changes.  Linear2 keeps the e4m3 MFMA (nothing is quantised after it).
-  constexpr bool WIDEN = (UC == UC_FP8) && (MODE == 0);
   constexpr size_t lds = (size_t)lds_bytes_of<BM>();
   static bool attr_set = false;
   if (!attr_set) {
@@ -32,26 +27,33 @@ static hipError_t launch_one(const GemmArgs& a, int grid, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int UC, int MODE>
+template <int UC, int MODE, bool WIDEN = false>
 static hipError_t launch_bm(int tile, const GemmArgs& a, int grid, hipStream_t s) {
   switch (tile) {
-    case TILE_M64_N128: return launch_one<UC, 64, MODE>(a, grid, s);
-    default: return launch_one<UC, 128, MODE>(a, grid, s);
+    case TILE_M64_N128: return launch_one<UC, 64, MODE, WIDEN>(a, grid, s);
+    default: return launch_one<UC, 128, MODE, WIDEN>(a, grid, s);
   }
 }
 
+// e4m3 Linear1 either on the e4m3 MFMA, or (exact_l1) on the bf16 MFMA after
+// an exact e4m3 -> bf16 widening: the e4m3 MFMAs round inside their dot
+// products, and the per-row requantisation after Linear1 can turn that into
+// code changes, which move Y visibly when I is small.  Linear2 always keeps
+// the e4m3 MFMA (nothing is quantised after it).
 template <int MODE>
-static hipError_t launch_uc(int usecase, int tile, const GemmArgs& a, int grid, hipStream_t s) {
+static hipError_t launch_uc(int usecase, int tile, bool exact_l1, const GemmArgs& a, int grid, hipStream_t s) {
   switch (usecase) {
     case UC_BF16: return launch_bm<UC_BF16, MODE>(tile, a, grid, s);
-    case UC_FP8: return launch_bm<UC_FP8, MODE>(tile, a, grid, s);
+    case UC_FP8:
+      if (MODE == 0 && exact_l1) return launch_bm<UC_FP8, MODE, MODE == 0>(tile, a, grid, s);
+      return launch_bm<UC_FP8, MODE>(tile, a, grid, s);
     default: return launch_bm<UC_I8, MODE>(tile, a, grid, s);
   }
 }
 
-hipError_t launch_gemm(int mode, int usecase, int tile, const GemmArgs& a, int grid, hipStream_t s) {
-  if (mode == 0) return launch_uc<0>(usecase, tile, a, grid, s);
-  if (mode == 1) return launch_uc<1>(usecase, tile, a, grid, s);
+hipError_t launch_gemm(int mode, int usecase, int tile, bool exact_l1, const GemmArgs& a, int grid, hipStream_t s) {
+  if (mode == 0) return launch_uc<0>(usecase, tile, exact_l1, a, grid, s);
+  if (mode == 1) return launch_uc<1>(usecase, tile, exact_l1, a, grid, s);
   if (usecase != UC_I8) return hipErrorInvalidValue;
   return launch_bm<UC_I8, 2>(tile, a, grid, s);
 }

@@ -117,14 +117,15 @@ struct MegaArgs {
 // launchers (return hipError_t of the launch)
 hipError_t launch_zero(int32_t* counts, int E, uint32_t* ctl, hipStream_t s);
 hipError_t launch_mega_prep(const MegaArgs& a, MegaArgs* dev_args, hipStream_t s);
-hipError_t launch_mega(int usecase, int tile, const MegaArgs* dev_args, int grid, hipStream_t s);
+hipError_t launch_mega(int usecase, int tile, bool exact_l1, const MegaArgs* dev_args, int grid, hipStream_t s);
 int mega_grid(int tile, int num_cus);
 hipError_t launch_count(const DispatchArgs& a, hipStream_t s);
 hipError_t launch_scatter(const DispatchArgs& a, hipStream_t s);
 hipError_t launch_gather(const DispatchArgs& a, hipStream_t s);
 hipError_t launch_prepare(const void* w1, const void* w2, void* w1o, void* w2o, int E, int H, int I,
                           int esz, int group, hipStream_t s);
-hipError_t launch_gemm(int mode, int usecase, int tile, const GemmArgs& a, int grid, hipStream_t s);
+// exact_l1: e4m3 Linear1 on bf16 MFMA with exact widening (else on the e4m3 MFMA)
+hipError_t launch_gemm(int mode, int usecase, int tile, bool exact_l1, const GemmArgs& a, int grid, hipStream_t s);
 int gemm_grid(int tile, int64_t P, int N, int num_cus);
 hipError_t launch_requant(const RequantArgs& a, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);

@@ -82,7 +82,7 @@ constexpr int mega_lds_bytes() {
   return lds_bytes_of<BM>();
 }
 
-template <int UC, int BM>
+template <int UC, int BM, bool WIDEN>
 __global__ __launch_bounds__(threads_of<BM>()) __attribute__((amdgpu_waves_per_eu(threads_of<BM>() / 256, threads_of<BM>() / 256)))
 void k_mega(const MegaArgs* mp) {
   // The arguments sit in device memory (written by the pre-pass) rather than
@@ -91,7 +91,6 @@ void k_mega(const MegaArgs* mp) {
   // for the whole kernel.
   const MegaArgs& m = *mp;
   constexpr int NT = threads_of<BM>(), NW = NT / 64;
-  constexpr bool WIDEN = (UC == UC_FP8);   // e4m3 Linear1 on bf16 MFMA, as in the three-call path
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   __shared__ int32_t off_s[kMaxExperts + 1];
   __shared__ int32_t cnt_s[kMaxExperts];
@@ -194,15 +193,15 @@ __global__ __launch_bounds__(256) void k_mega_prep(MegaArgs m, MegaArgs* out) {
 // cooperative launch guarantees the same on an idle device but costs tens of
 // microseconds more per call).  Work of other streams that holds CUs only
 // delays the late workgroups, which the barriers wait for (bounded).
-template <int UC, int BM>
+template <int UC, int BM, bool WIDEN>
 static hipError_t launch_mega_one(const MegaArgs* dev_args, int grid, hipStream_t s) {
   constexpr size_t lds = (size_t)mega_lds_bytes<BM>();
   static int per_cu = -1;
   if (per_cu < 0) {
-    hipError_t err = hipFuncSetAttribute((const void*)k_mega<UC, BM>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t err = hipFuncSetAttribute((const void*)k_mega<UC, BM, WIDEN>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (err != hipSuccess) return err;
     int n = 0;
-    err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_mega<UC, BM>, threads_of<BM>(), lds);
+    err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_mega<UC, BM, WIDEN>, threads_of<BM>(), lds);
     if (err != hipSuccess) return err;
     per_cu = n;
   }
@@ -210,13 +209,13 @@ static hipError_t launch_mega_one(const MegaArgs* dev_args, int grid, hipStream_
   if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return hipErrorInvalidDevice;
   if (per_cu < 1 || grid > per_cu * cus) return hipErrorCooperativeLaunchTooLarge;
-  hipLaunchKernelGGL((k_mega<UC, BM>), dim3(grid), dim3(threads_of<BM>()), lds, s, dev_args);
+  hipLaunchKernelGGL((k_mega<UC, BM, WIDEN>), dim3(grid), dim3(threads_of<BM>()), lds, s, dev_args);
   return hipGetLastError();
 }
 
-template <int UC>
+template <int UC, bool WIDEN = false>
 static hipError_t launch_mega_bm(int tile, const MegaArgs* a, int grid, hipStream_t s) {
-  return tile == TILE_M64_N128 ? launch_mega_one<UC, 64>(a, grid, s) : launch_mega_one<UC, 128>(a, grid, s);
+  return tile == TILE_M64_N128 ? launch_mega_one<UC, 64, WIDEN>(a, grid, s) : launch_mega_one<UC, 128, WIDEN>(a, grid, s);
 }
 
 hipError_t launch_mega_prep(const MegaArgs& a, MegaArgs* dev_args, hipStream_t s) {
@@ -226,10 +225,11 @@ hipError_t launch_mega_prep(const MegaArgs& a, MegaArgs* dev_args, hipStream_t s
   return hipGetLastError();
 }
 
-hipError_t launch_mega(int usecase, int tile, const MegaArgs* dev_args, int grid, hipStream_t s) {
+hipError_t launch_mega(int usecase, int tile, bool exact_l1, const MegaArgs* dev_args, int grid, hipStream_t s) {
   switch (usecase) {
     case UC_BF16: return launch_mega_bm<UC_BF16>(tile, dev_args, grid, s);
-    case UC_FP8: return launch_mega_bm<UC_FP8>(tile, dev_args, grid, s);
+    case UC_FP8:
+      return exact_l1 ? launch_mega_bm<UC_FP8, true>(tile, dev_args, grid, s) : launch_mega_bm<UC_FP8>(tile, dev_args, grid, s);
     default: return launch_mega_bm<UC_I8>(tile, dev_args, grid, s);
   }
 }

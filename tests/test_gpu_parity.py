@@ -255,6 +255,27 @@ def test_split_tail_tiles(usecase, monkeypatch):
         assert err <= TOL[usecase], err
 
 
+@pytest.mark.parametrize("mode", ["exact", "fast"])
+def test_fp8_linear1_modes(mode, monkeypatch):
+    """e4m3 Linear1 on the e4m3 MFMA (fast, the default for I >= 1024) or on
+    the bf16 MFMA after exact widening (exact, the default below): both stay
+    within the fp8 bar at I = 1024, and fused == three-call in each mode."""
+    cfg = wl.Config(f"fp8_l1_{mode}", "fp8", 256, 1024, 1024, 8, 4, 0.5, 31)
+    inp = wl.make_inputs(cfg)
+    x, ids, wts = device_inputs(inp)
+    layer = make_layer(inp, "f32")
+    monkeypatch.setenv("MM_FP8_L1", mode)
+    log(f"[fp8 Linear1] {mode}")
+    y_f, _ = layer.forward(x, ids, wts)
+    y_3, _ = layer.forward_3call(x, ids, wts)
+    torch.cuda.synchronize()
+    assert layer.device_error(fused=True) == 0
+    assert torch.equal(y_f.view(torch.int32), y_3.view(torch.int32))
+    err = rel_err(y_f.cpu().double().numpy(), oracle_y(inp))
+    log(f"    max|dY|/rms = {err:.3e}")
+    assert err <= TOL["fp8"], err
+
+
 def test_fused_barrier_timeout_is_reported_and_recovers(monkeypatch):
     """A grid barrier that gives up (forced from the host with a one-poll
     limit) sets its error bit and every block still leaves the kernel; the
