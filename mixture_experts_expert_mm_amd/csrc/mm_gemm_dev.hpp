@@ -219,6 +219,7 @@ __device__ __forceinline__ GemmArgs uniform_args(const GemmArgs& in) {
   a.H = uniform_int(in.H);
   a.K = uniform_int(in.K);
   a.gate_up_group = uniform_int(in.gate_up_group);
+  a.group_m = uniform_int(in.group_m);
   a.a_route = uniform_ptr(in.a_route);
   a.a_rows = (int64_t)uniform_int((int)in.a_rows);   // < 2^31 (checked by the host)
   a.partials = uniform_ptr(in.partials);
@@ -278,10 +279,13 @@ __device__ __forceinline__ bool poll_flag(uint32_t* p, uint32_t spin_limit) {
   return true;
 }
 
-// Tile order: expert-major, then N-block, then M-block, so tiles that run
-// together share weight tiles (same expert and N-block) and activation tiles
-// (same M-block).  The expert of a tile is the largest e with
-// (off[e] / BM) * n_tiles <= tile.
+// Tile order: expert-major; inside an expert, groups of group_m M-blocks
+// (0: all of them), and in a group N-block-major, M-block fastest.  With
+// group_m = 8 the 32 workgroups of an XCD run 8 M-blocks x 4 N-blocks of one
+// expert at a time and per K-stage read 8 activation and 4 weight stages
+// (the fewest bytes for 32 tiles when activation rows come from the pool);
+// without groups they read one weight stage and up to 32 activation stages.
+// The expert of a tile is the largest e with (off[e] / BM) * n_tiles <= tile.
 template <int BM>
 __device__ __forceinline__ TileRef resolve_tile(const GemmArgs& a, const int32_t* off_s, const int32_t* cnt_s,
                                                int tile, int n_tiles, int kbytes) {
@@ -297,7 +301,10 @@ __device__ __forceinline__ TileRef resolve_tile(const GemmArgs& a, const int32_t
   r.e = uniform_int(lo);
   const int mb0 = off_s[lo] / BM, nmb = (off_s[lo + 1] - off_s[lo]) / BM;
   const int local = tile - mb0 * n_tiles;
-  const int nblk = local / nmb, mblk = mb0 + local % nmb;
+  const int GM = a.group_m > 0 ? a.group_m : nmb;   // M-blocks per group (0: the whole expert)
+  const int g = local / (GM * n_tiles), gm = min(GM, nmb - g * GM);
+  const int idx = local - g * GM * n_tiles;
+  const int nblk = idx / gm, mblk = mb0 + g * GM + idx % gm;
   r.row0 = uniform_int(mblk * BM);
   r.n0 = uniform_int(nblk * TileShape<BM>::BN);
   r.valid = uniform_int(min(BM, off_s[lo] + cnt_s[lo] - r.row0));

@@ -243,6 +243,9 @@ GemmArgs l1_args(const mm_plan& pl, const int32_t* offsets, const int32_t* count
   g.a_out = a_pool;
   g.a_stage = at<float>(ws, L.a_stage);
   set_split(g, L, ws);
+  // pool rows are read once per group of N-blocks: group 8 M-blocks (with 4
+  // N-blocks per XCD round) to read each activation stage a quarter as often
+  g.group_m = 8;
   return g;
 }
 
@@ -285,6 +288,7 @@ GemmArgs l2_args(const mm_plan& pl, const int32_t* offsets, const int32_t* count
   g.topk_w = topk_w;
   g.contrib = at<float>(ws, L.contrib);
   set_split(g, L, ws);
+  g.group_m = 0;   // measured: grouping slows Linear2 (its weight tiles are re-read per group)
   return g;
 }
 
@@ -486,6 +490,7 @@ mm_status mega_moe(const mm_plan* plan, const void* x, const int32_t* topk_ids, 
     m.l1.x_scale = m.x_tok_scale;
     m.l1.a_route = pool_src;
     m.l1.a_rows = pl.prob.num_tokens;
+    m.l1.group_m = 0;   // token rows are shared K-fold and stay cached: weight reuse order (measured)
   }
   m.spin_limit = barrier_spin_limit();
   MegaArgs* dev_args = at<MegaArgs>(workspace, L.mega_args);

@@ -49,6 +49,7 @@ struct GemmArgs {
   uint32_t* err;             // device error word (mm_device_error bits)
   int E, N, Kdim, I, H, K;
   int gate_up_group;
+  int group_m;               // M-blocks per tile group of an expert (0: all of them)
   // Linear1 (mode 0)
   const float* x_scale;      // [P] (A8W8)
   const float* w_scale;      // [E][N] formula order (A8W8)
