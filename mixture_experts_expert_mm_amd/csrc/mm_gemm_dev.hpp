@@ -786,7 +786,10 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
                 const float gw = __uint_as_float(ri[q][1]);
                 const float v = acc_to_f32(acc[i][j][q]) * cs0[j];
                 const float o = (UC != UC_BF16) ? (v * __uint_as_float(ri[q][2])) * gw : v * gw;
-                if (route >= 0) gp(a.contrib)[(int64_t)route * a.H + n] = o;
+                if (route >= 0) {
+                  if constexpr (UC == UC_BF16) gp(static_cast<float*>(a.contrib))[(int64_t)route * a.H + n] = o;
+                  else gp(static_cast<uint16_t*>(a.contrib))[(int64_t)route * a.H + n] = f32_to_bf16_bits(o);
+                }
               } else {
                 int col = n;
                 if (a.gate_up_group > 0) {
@@ -891,7 +894,26 @@ __device__ __forceinline__ void requant_row(const RequantArgs& a, int64_t p, con
 // ---------------------------------------------------------------------------
 // Token Combine: y_i = sum_{k=0..K-1} slot[i*K+k] in slot order, float32;
 // masked routes (route_to_pool < 0) contribute nothing.  One thread makes 8
-// consecutive columns c .. c+7 of token i.
+// consecutive columns c .. c+7 of token i.  Slots are float32, or bf16 for
+// the A8W8 use cases.
+
+// 8 consecutive slot values of route r from column c, as float32
+__device__ __forceinline__ void load_slot8(const CombineArgs& a, int64_t r, int c, float* v) {
+  if (a.slot_bf16) {
+    const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.contrib) + r * a.H + c);
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v[2 * q] = bf16_bits_to_f32(ww[q] & 0xffffu);
+      v[2 * q + 1] = bf16_bits_to_f32(ww[q] >> 16);
+    }
+  } else {
+    const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(a.contrib) + r * a.H + c);
+    const float4 v0 = src[0], v1 = src[1];
+    v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w;
+    v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
+  }
+}
 // ---------------------------------------------------------------------------
 // U work items idx0, idx0 + stride, ... (item = token idx / (H/8), columns
 // 8 * (idx % (H/8)) ..) at once, so a thread keeps U loads in flight; the
@@ -911,23 +933,19 @@ __device__ __forceinline__ void combine_8u(const CombineArgs& a, int64_t idx0, i
     for (int c = 0; c < 8; ++c) acc[u][c] = 0.0f;
   }
   for (int k = 0; k < a.K; ++k) {
-    float4 v[U][2];
+    float v[U][8];
     bool on[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t r = tok[u] * a.K + k;
       on[u] = tok[u] >= 0 && a.route_to_pool[r] >= 0;
-      if (on[u]) {
-        const float4* src = reinterpret_cast<const float4*>(a.contrib + r * a.H + col[u]);
-        v[u][0] = src[0];
-        v[u][1] = src[1];
-      }
+      if (on[u]) load_slot8(a, r, col[u], v[u]);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (!on[u]) continue;
-      acc[u][0] += v[u][0].x; acc[u][1] += v[u][0].y; acc[u][2] += v[u][0].z; acc[u][3] += v[u][0].w;
-      acc[u][4] += v[u][1].x; acc[u][5] += v[u][1].y; acc[u][6] += v[u][1].z; acc[u][7] += v[u][1].w;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acc[u][c] += v[u][c];
     }
   }
 #pragma unroll
@@ -953,10 +971,10 @@ __device__ __forceinline__ void combine_8(const CombineArgs& a, int64_t i, int c
   for (int k = 0; k < a.K; ++k) {
     const int64_t r = i * a.K + k;
     if (a.route_to_pool[r] < 0) continue;
-    const float4* src = reinterpret_cast<const float4*>(a.contrib + r * a.H + c);
-    const float4 v0 = src[0], v1 = src[1];
-    acc[0] += v0.x; acc[1] += v0.y; acc[2] += v0.z; acc[3] += v0.w;
-    acc[4] += v1.x; acc[5] += v1.y; acc[6] += v1.z; acc[7] += v1.w;
+    float v[8];
+    load_slot8(a, r, c, v);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] += v[q];
   }
   if (a.y_f32) {
     float4* dst = reinterpret_cast<float4*>(static_cast<float*>(a.y) + i * a.H + c);

@@ -51,7 +51,7 @@ WsLayout ws_layout(const mm_plan& pl) {
   L.ctl = take(kCtlWords * 4);
   L.wave_base = take(dispatch_waves(p.num_tokens, (int)p.num_topk) * p.num_experts * 4);
   L.a_stage = q ? take(P * p.intermediate_hidden * 4) : -1;
-  L.contrib = take(R * p.hidden * 4);
+  L.contrib = take(R * p.hidden * (q ? 2 : 4));   // combine slots: bf16 for A8W8, float32 for A16W16
   // partial sums of split tail tiles: one slot per piece in flight
   L.partials = take((int64_t)kSplitSlots * tile_bm(pl.tile_l1) * tile_bn(pl.tile_l1) * 4);
   L.end = o;
@@ -286,13 +286,13 @@ GemmArgs l2_args(const mm_plan& pl, const int32_t* offsets, const int32_t* count
   g.a_scale = a_pool_scale;
   g.w_scale = w2_scale;
   g.topk_w = topk_w;
-  g.contrib = at<float>(ws, L.contrib);
+  g.contrib = at<uint8_t>(ws, L.contrib);
   set_split(g, L, ws);
   g.group_m = 0;   // measured: grouping slows Linear2 (its weight tiles are re-read per group)
   return g;
 }
 
-CombineArgs combine_args(const mm_plan& pl, const float* contrib, const int32_t* r2p, void* y) {
+CombineArgs combine_args(const mm_plan& pl, const void* contrib, const int32_t* r2p, void* y) {
   const mm_problem& p = pl.prob;
   CombineArgs c{};
   c.contrib = contrib;
@@ -302,6 +302,7 @@ CombineArgs combine_args(const mm_plan& pl, const float* contrib, const int32_t*
   c.H = (int)p.hidden;
   c.K = (int)p.num_topk;
   c.y_f32 = p.y_dtype == MM_OUT_F32;
+  c.slot_bf16 = p.usecase != MM_A16W16;
   return c;
 }
 

@@ -58,7 +58,7 @@ struct GemmArgs {
   // Linear2 (mode 1)
   const float* a_scale;      // [P] (A8W8)
   const float* topk_w;       // [T*K]
-  float* contrib;            // [T*K][H]
+  void* contrib;             // [T*K][H] float32 (A16W16) or bf16 (A8W8)
   // debug (mode 2: raw int32 accumulators)
   int32_t* raw_out;
   // Linear1 of the fused kernel: A row p of a tile is the token row
@@ -83,11 +83,11 @@ struct RequantArgs {
 };
 
 struct CombineArgs {
-  const float* contrib;        // [T*K][H]
+  const void* contrib;         // [T*K][H] float32, or bf16 when slot_bf16
   const int32_t* route_to_pool;// [T*K]
   void* y;                     // [T][H]
   int64_t T;
-  int H, K, y_f32;
+  int H, K, y_f32, slot_bf16;
 };
 
 // Control words at the start of the workspace, cleared by the pre-pass of
