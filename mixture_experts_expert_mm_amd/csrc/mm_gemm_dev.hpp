@@ -438,14 +438,27 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
     if (t < BM) rowinfo[buf * BM + t] = RowInfo{MODE == 1 ? rr.route : -1, rr.gw, rr.rs, 0.0f};
   };
   // The first S stages of tile `tr`, after its row data loads.
-  auto start_tile = [&](const TileRef& tr) {
+  // Between tiles the first stage goes out before the finished tile's
+  // epilogue and the others after it: the epilogue's stores, counted with
+  // the loads in order, then complete with stage 0 and do not hold up the
+  // next tile's first wait.
+  auto start_first = [&](const TileRef& tr) {
     const RowRegs rr = row_first(tr);
 #pragma unroll
-    for (int st = 0; st < S; ++st)
+    for (int x = 0; x < D; ++x) MM_DMA(tr, x, 0);
+    return rr;
+  };
+  auto start_rest = [&](const TileRef& tr) {
+#pragma unroll
+    for (int st = 1; st < S; ++st)
       if (st < tr.nkl) {
 #pragma unroll
         for (int x = 0; x < D; ++x) MM_DMA(tr, x, st);
       }
+  };
+  auto start_tile = [&](const TileRef& tr) {
+    const RowRegs rr = start_first(tr);
+    start_rest(tr);
     return rr;
   };
 
@@ -605,8 +618,8 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
     };
 
     // stage 0 landed for every wave: the tile's other min(nk, S) - 1 stages
-    // may still be in flight (the previous tile's epilogue stores were issued
-    // after them: counting them too only makes the wait stricter)
+    // may still be in flight (the previous tile's epilogue stores, issued
+    // between stage 0 and them, complete before them)
     const int nkl = cur.nkl;
     static_for<S>([&](auto cc) {
       constexpr int c = S - 1 - decltype(cc)::value;   // S-1, ..., 0
@@ -715,7 +728,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
     // the next item's first stages go out now, ahead of this tile's epilogue
     if (nhave) {
       nxt = make_item(nitem);
-      rr_nxt = start_tile(nxt);
+      rr_nxt = start_first(nxt);
     }
     if (cur.role != kRoleProduce) {   // a later piece has no epilogue
 #pragma unroll
@@ -804,6 +817,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
         }
       }
     }
+    if (nhave) start_rest(nxt);
     item = nitem;
     have = nhave;
     cur = nxt;
