@@ -336,11 +336,21 @@ def _edge_inputs(T, H, I, E, K, ids_np, usecase="bf16", seed=77):
     return wl.Inputs(cfg, wl.tokens(cfg), ids, wts, wl.all_weights(cfg))
 
 
-@pytest.mark.parametrize("case", ["one_expert", "empty_expert", "single_token", "topk1", "odd_tokens", "ids_out_of_range"])
+@pytest.mark.parametrize("case", ["one_expert", "empty_expert", "single_token", "topk1", "odd_tokens", "ids_out_of_range",
+                                  "many_experts", "topk64", "all_masked"])
 def test_edge_cases(case):
     H, I = 256, 128
     rng = np.random.default_rng(3)
-    if case == "one_expert":
+    if case == "many_experts":   # the largest expert count, almost all of them empty
+        T, E, K = 64, 1024, 8
+        ids = np.stack([rng.choice(E, K, replace=False) for _ in range(T)])
+    elif case == "topk64":       # the largest top-k
+        T, E, K = 20, 64, 64
+        ids = np.stack([rng.permutation(E) for _ in range(T)])
+    elif case == "all_masked":   # no route at all: y = 0, no tile runs
+        T, E, K = 33, 4, 2
+        ids = np.full((T, K), -1)
+    elif case == "one_expert":
         T, E, K = 150, 4, 1
         ids = np.full((T, 1), 2)
     elif case == "empty_expert":
@@ -368,7 +378,10 @@ def test_edge_cases(case):
     ids_or = ids.copy()
     ids_or[ids_or >= E] = -1
     y_or, _ = oracle.moe_forward(inp.x.float().numpy(), ids_or, inp.topk_weights.numpy(), expert_fn(inp), "bf16")
-    assert rel_err(y.cpu().double().numpy(), y_or) <= TOL["bf16"]
+    if case == "all_masked":
+        assert not y_or.any() and not y.cpu().numpy().any()
+    else:
+        assert rel_err(y.cpu().double().numpy(), y_or) <= TOL["bf16"]
     np.testing.assert_array_equal(counts.cpu().numpy(), np.bincount(ids_or[ids_or >= 0], minlength=E))
     assert layer.device_error() == (B.MM_DEVERR_BAD_EXPERT if case == "ids_out_of_range" else 0)
 
