@@ -133,22 +133,97 @@ __device__ void scatter_block(const DispatchArgs& a, int64_t vb, int64_t nvb, in
   __syncthreads();
 }
 
-// Gather of token i by the whole block: reads x_i once, writes its K pool
-// rows (dst: 64 ints of LDS, red: NT/64 floats of LDS).
-// A8W8: s_i = max(max|x_i| / Qmax, 1e-8) and q = round(x_i / s_i) in IEEE
-// float32 (correctly rounded division), int8 ties-to-even clamped to
-// [-127,127] or e4m3fn ties-to-even saturated to +-448.
+// A8W8 activation quantisation: s_i = max(max|x_i| / Qmax, 1e-8) and
+// q = round(x_i / s_i) in IEEE float32 (correctly rounded division), int8
+// ties-to-even clamped to [-127,127] or e4m3fn ties-to-even saturated to
+// +-448.
 constexpr int kMaxHidden = 16384;
 
-// TOK: write row i of a [T][H] buffer (x_pool, x_pool_scale indexed by
-// token) instead of the K pool rows of token i: the fused kernel's A8W8
-// quantisation of the tokens, whose Linear1 reads token rows in place.
-template <int UC, int NT, bool TOK = false>
+// The 8 codes of 8 bf16 activations (one 16-byte chunk) at scale s.
+template <int UC>
+__device__ __forceinline__ uint2 codes8_of_bf16(const uint4& v, float s) {
+  const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+  uint32_t o[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const float f0 = bf16_bits_to_f32(wv[2 * q] & 0xffffu) / s;
+    const float f1 = bf16_bits_to_f32(wv[2 * q] >> 16) / s;
+    const float f2 = bf16_bits_to_f32(wv[2 * q + 1] & 0xffffu) / s;
+    const float f3 = bf16_bits_to_f32(wv[2 * q + 1] >> 16) / s;
+    if constexpr (UC == UC_I8) {
+      o[q] = (uint32_t)(f32_to_i8sym(f0) & 0xff) | ((uint32_t)(f32_to_i8sym(f1) & 0xff) << 8) |
+             ((uint32_t)(f32_to_i8sym(f2) & 0xff) << 16) | ((uint32_t)(f32_to_i8sym(f3) & 0xff) << 24);
+    } else {
+      o[q] = f32x2_to_e4m3x2(f0, f1) | (f32x2_to_e4m3x2(f2, f3) << 16);
+    }
+  }
+  return make_uint2(o[0], o[1]);
+}
+
+__device__ __forceinline__ float amax8_of_bf16(const uint4& v, float m) {
+  const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    m = fmaxf(m, fabsf(bf16_bits_to_f32(wv[q] & 0xffffu)));
+    m = fmaxf(m, fabsf(bf16_bits_to_f32(wv[q] >> 16)));
+  }
+  return m;
+}
+
+// A8W8 quantisation of token i by one wave into row i of a [T][H] code
+// buffer (x_pool, x_pool_scale indexed by token): the fused kernel's step
+// for a Linear1 that reads token rows in place.  A block runs one token per
+// wave, so the loads of several tokens are in flight without block
+// barriers.  Rows of up to 64 * kTokRegChunks chunks stay in registers
+// between the amax and the codes; longer rows are read twice.  Same
+// arithmetic, so the same codes and scale, as the block gather below.
+template <int UC>
+__device__ void quant_token_wave(const DispatchArgs& a, int64_t i) {
+  constexpr int kTokRegChunks = 16;   // H <= 64 * 16 * 8 = 8192
+  const int l = lane_id();
+  const int nchunk = (int)(a.H / 8);
+  const uint4* xr = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + i * a.H);
+  uint2* dst = reinterpret_cast<uint2*>(static_cast<uint8_t*>(a.x_pool) + i * a.H);
+  const float qmax = (UC == UC_I8) ? 127.0f : 448.0f;
+  float m = 0.0f;
+  if (nchunk <= 64 * kTokRegChunks) {
+    // registers cleared first, then loads that only fill them, then the
+    // amax (a cleared chunk adds |0|): every load is issued before the first
+    // wait
+    uint4 v[kTokRegChunks];
+#pragma unroll
+    for (int j = 0; j < kTokRegChunks; ++j) v[j] = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int j = 0; j < kTokRegChunks; ++j) {
+      const int c = j * 64 + l;
+      if (c < nchunk) v[j] = xr[c];
+    }
+#pragma unroll
+    for (int j = 0; j < kTokRegChunks; ++j) m = amax8_of_bf16(v[j], m);
+    const float s = fmaxf(wave_max(m) / qmax, 1e-8f);
+#pragma unroll
+    for (int j = 0; j < kTokRegChunks; ++j) {
+      const int c = j * 64 + l;
+      if (c < nchunk) dst[c] = codes8_of_bf16<UC>(v[j], s);
+    }
+    if (l == 0) a.x_pool_scale[i] = s;
+  } else {
+    for (int c = l; c < nchunk; c += 64) m = amax8_of_bf16(xr[c], m);
+    const float s = fmaxf(wave_max(m) / qmax, 1e-8f);
+    for (int c = l; c < nchunk; c += 64) dst[c] = codes8_of_bf16<UC>(xr[c], s);
+    if (l == 0) a.x_pool_scale[i] = s;
+  }
+}
+
+// Gather of token i by the whole block: reads x_i once, writes its K pool
+// rows (A8W8: their codes and scales) (dst: 64 ints of LDS, red: NT/64
+// floats of LDS).
+template <int UC, int NT>
 __device__ void gather_token(const DispatchArgs& a, int64_t i, int32_t* dst, float* red) {
   constexpr int NW = NT / 64, MAXC = kMaxHidden / 8 / NT;
   const int t = threadIdx.x;
-  const int nrows = TOK ? 1 : a.K;
-  if (t < nrows) dst[t] = TOK ? (int32_t)i : a.route_to_pool[i * a.K + t];
+  const int nrows = a.K;
+  if (t < nrows) dst[t] = a.route_to_pool[i * a.K + t];
   const int nchunk = (int)(a.H / 8);
   const uint4* xr = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + i * a.H);
   if constexpr (UC == UC_BF16) {
@@ -164,18 +239,14 @@ __device__ void gather_token(const DispatchArgs& a, int64_t i, int32_t* dst, flo
     uint4 v[MAXC];
     float m = 0.0f;
 #pragma unroll
+    for (int j = 0; j < MAXC; ++j) v[j] = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
     for (int j = 0; j < MAXC; ++j) {
       const int c = t + j * NT;
-      if (c < nchunk) {
-        v[j] = xr[c];
-        const uint32_t wv[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          m = fmaxf(m, fabsf(bf16_bits_to_f32(wv[q] & 0xffffu)));
-          m = fmaxf(m, fabsf(bf16_bits_to_f32(wv[q] >> 16)));
-        }
-      }
+      if (c < nchunk) v[j] = xr[c];
     }
+#pragma unroll
+    for (int j = 0; j < MAXC; ++j) m = amax8_of_bf16(v[j], m);
     m = wave_max(m);
     if (lane_id() == 0) red[t / 64] = m;
     __syncthreads();
@@ -187,22 +258,7 @@ __device__ void gather_token(const DispatchArgs& a, int64_t i, int32_t* dst, flo
     for (int j = 0; j < MAXC; ++j) {
       const int c = t + j * NT;
       if (c < nchunk) {
-        const uint32_t wv[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
-        uint32_t o[2];
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const float f0 = bf16_bits_to_f32(wv[2 * q] & 0xffffu) / s;
-          const float f1 = bf16_bits_to_f32(wv[2 * q] >> 16) / s;
-          const float f2 = bf16_bits_to_f32(wv[2 * q + 1] & 0xffffu) / s;
-          const float f3 = bf16_bits_to_f32(wv[2 * q + 1] >> 16) / s;
-          if constexpr (UC == UC_I8) {
-            o[q] = (uint32_t)(f32_to_i8sym(f0) & 0xff) | ((uint32_t)(f32_to_i8sym(f1) & 0xff) << 8) |
-                   ((uint32_t)(f32_to_i8sym(f2) & 0xff) << 16) | ((uint32_t)(f32_to_i8sym(f3) & 0xff) << 24);
-          } else {
-            o[q] = f32x2_to_e4m3x2(f0, f1) | (f32x2_to_e4m3x2(f2, f3) << 16);
-          }
-        }
-        const uint2 ov = make_uint2(o[0], o[1]);
+        const uint2 ov = codes8_of_bf16<UC>(v[j], s);
         for (int k = 0; k < nrows; ++k) {
           const int p = dst[k];
           if (p >= 0) reinterpret_cast<uint2*>(static_cast<uint8_t*>(a.x_pool) + (int64_t)p * a.H)[c] = ov;

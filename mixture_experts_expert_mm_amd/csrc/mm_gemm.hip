@@ -70,7 +70,7 @@ __global__ __launch_bounds__(256) void k_requant(RequantArgs a) {
   for (int e = threadIdx.x; e <= a.E; e += 256) off_s[e] = a.offsets[e];
   for (int e = threadIdx.x; e < a.E; e += 256) cnt_s[e] = a.counts[e];
   __syncthreads();
-  requant_row<UC>(a, (int64_t)blockIdx.x * 4 + threadIdx.x / 64, off_s, cnt_s);
+  requant_rows<UC, 1>(a, (int64_t)blockIdx.x * 4 + threadIdx.x / 64, 0, off_s, cnt_s);
 }
 
 hipError_t launch_requant(const RequantArgs& a, hipStream_t s) {
@@ -81,12 +81,13 @@ hipError_t launch_requant(const RequantArgs& a, hipStream_t s) {
 }
 
 __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
-  const int c = (blockIdx.y * 256 + threadIdx.x) * 8;
-  if (c < a.H) combine_8(a, blockIdx.x, c);
+  const int64_t work = a.T * (a.H / 8), idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (a.slot_bf16) combine_items<1, true>(a, idx, 0, work);
+  else combine_items<1, false>(a, idx, 0, work);
 }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)a.T, (unsigned)((a.H + 2047) / 2048));
+  const dim3 grid((unsigned)((a.T * (a.H / 8) + 255) / 256));
   hipLaunchKernelGGL(k_combine, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }

@@ -831,78 +831,103 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
 
 // ---------------------------------------------------------------------------
 // per-row requantisation of A (A8W8): s^A = max(amax/Qmax, 1e-8), IEEE f32.
-// One wave per pool row p; rows past their expert's count (padding) carry no
+// One wave per pool row; rows past their expert's count (padding) carry no
 // route and are skipped.  off_s / cnt_s: the dispatch offsets and counts.
 // ---------------------------------------------------------------------------
-template <int UC>
-__device__ __forceinline__ void requant_row(const RequantArgs& a, int64_t p, const int32_t* off_s, const int32_t* cnt_s) {
-  const int l = lane_id();
-  if (p >= off_s[a.E] || p >= a.P) return;
+__device__ __forceinline__ bool requant_row_live(const RequantArgs& a, int64_t p, const int32_t* off_s, const int32_t* cnt_s) {
+  if (p >= off_s[a.E] || p >= a.P) return false;
   int lo = 0, hi = a.E;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
     if (off_s[mid] <= p) lo = mid; else hi = mid;
   }
-  if (p >= (int64_t)off_s[lo] + cnt_s[lo]) return;
-  const float4* src = reinterpret_cast<const float4*>(a.a_stage + p * a.I);
-  // row amax over all I columns (exact: a max), then the codes.  Rows of up
-  // to kRequantRegChunks float8 chunks stay in registers between the two
-  // (every load of the row in flight at once); longer rows are read twice.
-  constexpr int kRequantRegChunks = 8;                       // I <= 64*8*8 = 4096
+  return p < (int64_t)off_s[lo] + cnt_s[lo];
+}
+
+template <int UC>
+__device__ __forceinline__ uint2 requant_codes8(const float4& v0, const float4& v1, float s) {
+  const float f[8] = {v0.x / s, v0.y / s, v0.z / s, v0.w / s, v1.x / s, v1.y / s, v1.z / s, v1.w / s};
+  uint32_t o[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    if constexpr (UC == UC_I8) {
+      o[q] = (uint32_t)(f32_to_i8sym(f[4 * q]) & 0xff) | ((uint32_t)(f32_to_i8sym(f[4 * q + 1]) & 0xff) << 8) |
+             ((uint32_t)(f32_to_i8sym(f[4 * q + 2]) & 0xff) << 16) | ((uint32_t)(f32_to_i8sym(f[4 * q + 3]) & 0xff) << 24);
+    } else {
+      o[q] = f32x2_to_e4m3x2(f[4 * q], f[4 * q + 1]) | (f32x2_to_e4m3x2(f[4 * q + 2], f[4 * q + 3]) << 16);
+    }
+  }
+  return make_uint2(o[0], o[1]);
+}
+
+__device__ __forceinline__ float amax4(const float4& v, float m) {
+  return fmaxf(fmaxf(m, fmaxf(fabsf(v.x), fabsf(v.y))), fmaxf(fabsf(v.z), fabsf(v.w)));
+}
+
+// Rows p0, p0 + pstride, ... (U of them) by one wave.  Rows of up to RC
+// float8 chunks per lane (I <= 64*8*RC) stay in registers between the amax
+// (exact: a max) and the codes, with the loads of all U rows in flight at
+// once; longer rows are read twice, one at a time.
+template <int UC, int U, int RC = 8>
+__device__ __forceinline__ void requant_rows(const RequantArgs& a, int64_t p0, int64_t pstride, const int32_t* off_s,
+                                             const int32_t* cnt_s) {
+  constexpr int kRequantRegChunks = RC;
+  const int l = lane_id();
   const int nch = a.I / 8;
-  const bool in_regs = nch <= 64 * kRequantRegChunks;
-  float4 keep[2 * kRequantRegChunks];
-  float m = 0.0f;
-  if (in_regs) {
-#pragma unroll
-    for (int j = 0; j < kRequantRegChunks; ++j) {
-      const int c = j * 64 + l;
-      if (c < nch) {
-        keep[2 * j] = src[2 * c];
-        keep[2 * j + 1] = src[2 * c + 1];
-      } else {
-        keep[2 * j] = keep[2 * j + 1] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 2 * kRequantRegChunks; ++j) {
-      const float4 v = keep[j];
-      m = fmaxf(fmaxf(m, fmaxf(fabsf(v.x), fabsf(v.y))), fmaxf(fabsf(v.z), fabsf(v.w)));
-    }
-  } else {
-    for (int c = l; c < a.I / 4; c += 64) {
-      const float4 v = src[c];
-      m = fmaxf(fmaxf(m, fmaxf(fabsf(v.x), fabsf(v.y))), fmaxf(fabsf(v.z), fabsf(v.w)));
-    }
-  }
-  m = wave_max(m);
   const float qmax = (UC == UC_I8) ? 127.0f : 448.0f;
-  const float s = fmaxf(m / qmax, 1e-8f);
-  uint2* dst = reinterpret_cast<uint2*>(static_cast<uint8_t*>(a.a_pool) + p * a.I);
-  auto codes = [&](const float4& v0, const float4& v1) {
-    const float f[8] = {v0.x / s, v0.y / s, v0.z / s, v0.w / s, v1.x / s, v1.y / s, v1.z / s, v1.w / s};
-    uint32_t o[2];
+  bool live[U];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      if constexpr (UC == UC_I8) {
-        o[q] = (uint32_t)(f32_to_i8sym(f[4 * q]) & 0xff) | ((uint32_t)(f32_to_i8sym(f[4 * q + 1]) & 0xff) << 8) |
-               ((uint32_t)(f32_to_i8sym(f[4 * q + 2]) & 0xff) << 16) | ((uint32_t)(f32_to_i8sym(f[4 * q + 3]) & 0xff) << 24);
-      } else {
-        o[q] = f32x2_to_e4m3x2(f[4 * q], f[4 * q + 1]) | (f32x2_to_e4m3x2(f[4 * q + 2], f[4 * q + 3]) << 16);
+  for (int u = 0; u < U; ++u) live[u] = requant_row_live(a, p0 + u * pstride, off_s, cnt_s);
+  if (nch <= 64 * kRequantRegChunks) {
+    // registers cleared first, then loads that only fill them: no branch
+    // writes a register a load in flight targets, so every load of the U
+    // rows is issued before the first wait
+    float4 keep[U][2 * kRequantRegChunks];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int j = 0; j < 2 * kRequantRegChunks; ++j) keep[u][j] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float4* src = reinterpret_cast<const float4*>(a.a_stage + (p0 + u * pstride) * a.I);
+#pragma unroll
+      for (int j = 0; j < kRequantRegChunks; ++j) {
+        const int c = j * 64 + l;
+        if (live[u] && c < nch) {
+          keep[u][2 * j] = src[2 * c];
+          keep[u][2 * j + 1] = src[2 * c + 1];
+        }
       }
     }
-    return make_uint2(o[0], o[1]);
-  };
-  if (in_regs) {
 #pragma unroll
-    for (int j = 0; j < kRequantRegChunks; ++j) {
-      const int c = j * 64 + l;
-      if (c < nch) dst[c] = codes(keep[2 * j], keep[2 * j + 1]);
+    for (int u = 0; u < U; ++u) {
+      if (!live[u]) continue;
+      float m = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 2 * kRequantRegChunks; ++j) m = amax4(keep[u][j], m);
+      const float s = fmaxf(wave_max(m) / qmax, 1e-8f);
+      const int64_t p = p0 + u * pstride;
+      uint2* dst = reinterpret_cast<uint2*>(static_cast<uint8_t*>(a.a_pool) + p * a.I);
+#pragma unroll
+      for (int j = 0; j < kRequantRegChunks; ++j) {
+        const int c = j * 64 + l;
+        if (c < nch) dst[c] = requant_codes8<UC>(keep[u][2 * j], keep[u][2 * j + 1], s);
+      }
+      if (l == 0) a.a_scale[p] = s;
     }
   } else {
-    for (int c = l; c < nch; c += 64) dst[c] = codes(src[2 * c], src[2 * c + 1]);
+    for (int u = 0; u < U; ++u) {
+      if (!live[u]) continue;
+      const int64_t p = p0 + u * pstride;
+      const float4* src = reinterpret_cast<const float4*>(a.a_stage + p * a.I);
+      float m = 0.0f;
+      for (int c = l; c < a.I / 4; c += 64) m = amax4(src[c], m);
+      const float s = fmaxf(wave_max(m) / qmax, 1e-8f);
+      uint2* dst = reinterpret_cast<uint2*>(static_cast<uint8_t*>(a.a_pool) + p * a.I);
+      for (int c = l; c < nch; c += 64) dst[c] = requant_codes8<UC>(src[2 * c], src[2 * c + 1], s);
+      if (l == 0) a.a_scale[p] = s;
+    }
   }
-  if (l == 0) a.a_scale[p] = s;
 }
 
 // ---------------------------------------------------------------------------
@@ -911,29 +936,15 @@ __device__ __forceinline__ void requant_row(const RequantArgs& a, int64_t p, con
 // consecutive columns c .. c+7 of token i.  Slots are float32, or bf16 for
 // the A8W8 use cases.
 
-// 8 consecutive slot values of route r from column c, as float32
-__device__ __forceinline__ void load_slot8(const CombineArgs& a, int64_t r, int c, float* v) {
-  if (a.slot_bf16) {
-    const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.contrib) + r * a.H + c);
-    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      v[2 * q] = bf16_bits_to_f32(ww[q] & 0xffffu);
-      v[2 * q + 1] = bf16_bits_to_f32(ww[q] >> 16);
-    }
-  } else {
-    const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(a.contrib) + r * a.H + c);
-    const float4 v0 = src[0], v1 = src[1];
-    v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w;
-    v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
-  }
-}
-// ---------------------------------------------------------------------------
-// U work items idx0, idx0 + stride, ... (item = token idx / (H/8), columns
-// 8 * (idx % (H/8)) ..) at once, so a thread keeps U loads in flight; the
-// K contributions of each element are still added in slot order.
-template <int U>
-__device__ __forceinline__ void combine_8u(const CombineArgs& a, int64_t idx0, int64_t stride, int64_t work) {
+// U work items idx0, idx0 + stride, ... at once (item = token idx / (H/8),
+// columns 8 * (idx % (H/8)) .. +7).  For each group of up to 8 routes of a
+// token the route indices are loaded together and then all the slot rows
+// together, so a thread keeps 8U slot loads in flight; the additions still
+// run in slot order and a masked route adds nothing.  BF16: the slots are
+// bf16 (the A8W8 use cases), else float32.
+template <int U, bool BF16>
+__device__ __forceinline__ void combine_items(const CombineArgs& a, int64_t idx0, int64_t stride, int64_t work) {
+  constexpr int KC = 8;
   const int64_t nch = a.H / 8;
   float acc[U][8];
   int64_t tok[U];
@@ -946,20 +957,67 @@ __device__ __forceinline__ void combine_8u(const CombineArgs& a, int64_t idx0, i
 #pragma unroll
     for (int c = 0; c < 8; ++c) acc[u][c] = 0.0f;
   }
-  for (int k = 0; k < a.K; ++k) {
-    float v[U][8];
-    bool on[U];
+  // The route-index loads are unconditional (a clamped, in-bounds index)
+  // and a slot load only fills a register cleared beforehand, so no branch
+  // of the unrolled loops writes a register a load in flight still targets
+  // (which would make the compiler wait for every load in turn).
+  for (int k0 = 0; k0 < a.K; k0 += KC) {
+    bool on[U][KC];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t r = tok[u] * a.K + k;
-      on[u] = tok[u] >= 0 && a.route_to_pool[r] >= 0;
-      if (on[u]) load_slot8(a, r, col[u], v[u]);
+      const int64_t tu = tok[u] >= 0 ? tok[u] : 0;
+      int32_t pi[KC];
+#pragma unroll
+      for (int kk = 0; kk < KC; ++kk) pi[kk] = a.route_to_pool[tu * a.K + min(k0 + kk, a.K - 1)];
+#pragma unroll
+      for (int kk = 0; kk < KC; ++kk) on[u][kk] = tok[u] >= 0 && k0 + kk < a.K && pi[kk] >= 0;
     }
+    if constexpr (BF16) {
+      uint4 w[U][KC];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (!on[u]) continue;
+      for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int c = 0; c < 8; ++c) acc[u][c] += v[u][c];
+        for (int kk = 0; kk < KC; ++kk) {
+          w[u][kk] = make_uint4(0u, 0u, 0u, 0u);
+          if (on[u][kk])
+            w[u][kk] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.contrib) +
+                                                       (tok[u] * a.K + k0 + kk) * a.H + col[u]);
+        }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int kk = 0; kk < KC; ++kk) {
+          if (!on[u][kk]) continue;
+          const uint32_t ww[4] = {w[u][kk].x, w[u][kk].y, w[u][kk].z, w[u][kk].w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            acc[u][2 * q] += bf16_bits_to_f32(ww[q] & 0xffffu);
+            acc[u][2 * q + 1] += bf16_bits_to_f32(ww[q] >> 16);
+          }
+        }
+    } else {
+      float4 v[U][KC][2];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int kk = 0; kk < KC; ++kk) {
+          v[u][kk][0] = v[u][kk][1] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+          if (on[u][kk]) {
+            const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(a.contrib) +
+                                                                (tok[u] * a.K + k0 + kk) * a.H + col[u]);
+            v[u][kk][0] = src[0];
+            v[u][kk][1] = src[1];
+          }
+        }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int kk = 0; kk < KC; ++kk) {
+          if (!on[u][kk]) continue;
+          const float4 v0 = v[u][kk][0], v1 = v[u][kk][1];
+          acc[u][0] += v0.x; acc[u][1] += v0.y; acc[u][2] += v0.z; acc[u][3] += v0.w;
+          acc[u][4] += v1.x; acc[u][5] += v1.y; acc[u][6] += v1.z; acc[u][7] += v1.w;
+        }
     }
   }
 #pragma unroll
@@ -977,30 +1035,6 @@ __device__ __forceinline__ void combine_8u(const CombineArgs& a, int64_t idx0, i
       o.w = pack_bf16x2(acc[u][6], acc[u][7]);
       *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.y) + tok[u] * a.H + col[u]) = o;
     }
-  }
-}
-
-__device__ __forceinline__ void combine_8(const CombineArgs& a, int64_t i, int c) {
-  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int k = 0; k < a.K; ++k) {
-    const int64_t r = i * a.K + k;
-    if (a.route_to_pool[r] < 0) continue;
-    float v[8];
-    load_slot8(a, r, c, v);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) acc[q] += v[q];
-  }
-  if (a.y_f32) {
-    float4* dst = reinterpret_cast<float4*>(static_cast<float*>(a.y) + i * a.H + c);
-    dst[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-    dst[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
-  } else {
-    uint4 o;
-    o.x = pack_bf16x2(acc[0], acc[1]);
-    o.y = pack_bf16x2(acc[2], acc[3]);
-    o.z = pack_bf16x2(acc[4], acc[5]);
-    o.w = pack_bf16x2(acc[6], acc[7]);
-    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.y) + i * a.H + c) = o;
   }
 }
 

@@ -126,16 +126,17 @@ void k_mega(const MegaArgs* mp) {
   }
   if (!grid_barrier(ctl, ++nb, spin, bs, &ok)) return;
 
-  // gather (+ A8W8 activation quantisation), one token per block at a time.
-  // When Linear1 reads the token rows in place there is nothing to gather
-  // for A16W16, and A8W8 quantises each token once into a [T][H] buffer
-  // instead of writing its K pool rows.
+  // gather (+ A8W8 activation quantisation).  When Linear1 reads the token
+  // rows in place there is nothing to gather for A16W16, and A8W8 quantises
+  // each token once (one wave per token) into a [T][H] buffer instead of
+  // writing its K pool rows; otherwise one token per block at a time.
   if (m.l1_by_token) {
     if constexpr (UC != UC_BF16) {
       DispatchArgs d = m.d;
       d.x_pool = m.x_tok;
       d.x_pool_scale = m.x_tok_scale;
-      for (int64_t tok = blockIdx.x; tok < d.T; tok += gridDim.x) gather_token<UC, NT, true>(d, tok, dst, red);
+      const int64_t nwv = (int64_t)gridDim.x * NW;
+      for (int64_t tok = (int64_t)blockIdx.x * NW + t / 64; tok < d.T; tok += nwv) quant_token_wave<UC>(d, tok);
       if (!grid_barrier(ctl, ++nb, spin, bs, &ok)) return;
     }
   } else {
@@ -152,10 +153,16 @@ void k_mega(const MegaArgs* mp) {
   if (!grid_barrier(ctl, ++nb, spin, bs, &ok)) return;
 
   if constexpr (UC != UC_BF16) {
-    // per-row requantisation of A, one wave per pool row
+    // per-row requantisation of A, one wave per pool row (two rows at a time
+    // when I <= 2048)
     const RequantArgs r = m.rq;
     const int64_t used = off_s[r.E], nwv = (int64_t)gridDim.x * NW;
-    for (int64_t p = (int64_t)blockIdx.x * NW + t / 64; p < used; p += nwv) requant_row<UC>(r, p, off_s, cnt_s);
+    const int64_t p0 = (int64_t)blockIdx.x * NW + t / 64;
+    if (r.I <= 2048) {
+      for (int64_t p = p0; p < used; p += 2 * nwv) requant_rows<UC, 2, 4>(r, p, nwv, off_s, cnt_s);
+    } else {
+      for (int64_t p = p0; p < used; p += nwv) requant_rows<UC, 1>(r, p, 0, off_s, cnt_s);
+    }
     if (!grid_barrier(ctl, ++nb, spin, bs, &ok)) return;
   }
 
@@ -166,10 +173,13 @@ void k_mega(const MegaArgs* mp) {
   }
   if (!grid_barrier(ctl, ++nb, spin, bs, &ok)) return;
 
-  // combine: 8 columns of one token per item, four items per thread at a time
+  // combine: 8 columns of one token per item; two items per thread at a time
+  // with bf16 slots (A8W8), one with float32 slots
   const CombineArgs c = m.cb;
   const int64_t work = c.T * (c.H / 8), stride = (int64_t)gridDim.x * NT;
-  for (int64_t idx = (int64_t)blockIdx.x * NT + t; idx < work; idx += 4 * stride) combine_8u<4>(c, idx, stride, work);
+  constexpr int CU = UC == UC_BF16 ? 1 : 2;
+  for (int64_t idx = (int64_t)blockIdx.x * NT + t; idx < work; idx += CU * stride)
+    combine_items<CU, UC != UC_BF16>(c, idx, stride, work);
 }
 
 // Pre-pass: clears the counters the fused kernel accumulates into (expert
