@@ -34,7 +34,7 @@ __device__ __forceinline__ int read_route(const DispatchArgs& a, int64_t gw, int
 // block: LDS histogram per wave (smem: NW * E ints), then one global atomic
 // per (wave, expert) with a nonzero count.
 template <int NW>
-__device__ void count_block(const DispatchArgs& a, int64_t vb, int64_t nwaves, int32_t* smem) {
+__device__ __forceinline__ void count_block(const DispatchArgs& a, int64_t vb, int64_t nwaves, int32_t* smem) {
   const int w = threadIdx.x / 64, l = lane_id();
   int32_t* hist = smem + w * a.E;
   const int64_t gw = vb * NW + w;
@@ -56,7 +56,7 @@ __device__ void count_block(const DispatchArgs& a, int64_t vb, int64_t nwaves, i
 // Block-wide exclusive scan of the BLOCK_M-padded counts into off[0..E]
 // (wsum: NT/64 ints of LDS).
 template <int NT>
-__device__ void padded_prefix(const DispatchArgs& a, int32_t* off, int32_t* wsum) {
+__device__ __forceinline__ void padded_prefix(const DispatchArgs& a, int32_t* off, int32_t* wsum) {
   constexpr int NW = NT / 64;
   const int t = threadIdx.x, w = t / 64, l = lane_id();
   const int per = (a.E + NT - 1) / NT;
@@ -95,7 +95,7 @@ __device__ void padded_prefix(const DispatchArgs& a, int32_t* off, int32_t* wsum
 // NW * E ints of LDS).  Virtual block vb of nvb also marks the padding rows
 // of experts vb, vb + nvb, ... with pool_src = -1.
 template <int NW>
-__device__ void scatter_block(const DispatchArgs& a, int64_t vb, int64_t nvb, int64_t nwaves, const int32_t* off,
+__device__ __forceinline__ void scatter_block(const DispatchArgs& a, int64_t vb, int64_t nvb, int64_t nwaves, const int32_t* off,
                               int32_t* run) {
   constexpr int NT = NW * 64;
   const int t = threadIdx.x, w = t / 64, l = lane_id();
@@ -178,7 +178,7 @@ __device__ __forceinline__ float amax8_of_bf16(const uint4& v, float m) {
 // between the amax and the codes; longer rows are read twice.  Same
 // arithmetic, so the same codes and scale, as the block gather below.
 template <int UC>
-__device__ void quant_token_wave(const DispatchArgs& a, int64_t i) {
+__device__ __forceinline__ void quant_token_wave(const DispatchArgs& a, int64_t i) {
   constexpr int kTokRegChunks = 16;   // H <= 64 * 16 * 8 = 8192
   const int l = lane_id();
   const int nchunk = (int)(a.H / 8);
@@ -219,7 +219,7 @@ __device__ void quant_token_wave(const DispatchArgs& a, int64_t i) {
 // rows (A8W8: their codes and scales) (dst: 64 ints of LDS, red: NT/64
 // floats of LDS).
 template <int UC, int NT>
-__device__ void gather_token(const DispatchArgs& a, int64_t i, int32_t* dst, float* red) {
+__device__ __forceinline__ void gather_token(const DispatchArgs& a, int64_t i, int32_t* dst, float* red) {
   constexpr int NW = NT / 64, MAXC = kMaxHidden / 8 / NT;
   const int t = threadIdx.x;
   const int nrows = a.K;

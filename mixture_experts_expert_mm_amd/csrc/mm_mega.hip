@@ -34,7 +34,7 @@ __device__ __forceinline__ uint32_t xcc_id() {
   return __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 15u;
 }
 
-__device__ bool poll_until(uint32_t* p, uint32_t target, uint32_t spin_limit) {
+__device__ __forceinline__ bool poll_until(uint32_t* p, uint32_t target, uint32_t spin_limit) {
   uint32_t polls = 0;
   while (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
     if (++polls > spin_limit) return false;
@@ -43,7 +43,7 @@ __device__ bool poll_until(uint32_t* p, uint32_t target, uint32_t spin_limit) {
   return true;
 }
 
-__device__ void barrier_register(uint32_t* ctl, BarState& bs) {
+__device__ __forceinline__ void barrier_register(uint32_t* ctl, BarState& bs) {
   bs = BarState{xcc_id(), 0u, 0u};
   if (threadIdx.x == 0) {
     __hip_atomic_fetch_add(&ctl[32 + bs.xcd], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -51,7 +51,7 @@ __device__ void barrier_register(uint32_t* ctl, BarState& bs) {
   }
 }
 
-__device__ bool grid_barrier(uint32_t* ctl, uint32_t n, uint32_t spin_limit, BarState& bs, int32_t* ok_lds) {
+__device__ __forceinline__ bool grid_barrier(uint32_t* ctl, uint32_t n, uint32_t spin_limit, BarState& bs, int32_t* ok_lds) {
   __syncthreads();
   if (threadIdx.x == 0) {
     bool ok = true;
