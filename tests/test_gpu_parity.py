@@ -225,6 +225,30 @@ def test_fused_equals_three_call_and_is_deterministic(usecase):
     assert layer.device_error(fused=True) == 0 and layer.device_error(fused=False) == 0
 
 
+@pytest.mark.parametrize("usecase", ["bf16", "fp8", "int8"])
+@pytest.mark.parametrize("shape", ["max_hidden", "max_intermediate"])
+def test_largest_hidden_and_intermediate(shape, usecase):
+    """The largest hidden size (16384: the fused kernel quantises a token row
+    in two passes, the combine spans 2048 column groups) and the largest
+    intermediate size (16384: requantisation rows read twice, 128 Linear1
+    column tiles per M-block): oracle tolerance, fused == three-call."""
+    T, E, K = 24, 3, 2
+    H, I = (16384, 256) if shape == "max_hidden" else (256, 16384)
+    cfg = wl.Config(f"{shape}_{usecase}", usecase, T, H, I, E, K, 0.5, 91)
+    inp = wl.make_inputs(cfg)
+    log(f"[max] {shape} {usecase}")
+    layer = make_layer(inp, "f32")
+    x, ids, wts = device_inputs(inp)
+    y_f, _ = layer.forward(x, ids, wts)
+    y_3, _ = layer.forward_3call(x, ids, wts)
+    torch.cuda.synchronize()
+    err = rel_err(y_f.cpu().double().numpy(), oracle_y(inp))
+    log(f"    max|dY|/rms = {err:.3e}")
+    assert err <= TOL[usecase], err
+    assert torch.equal(y_f.view(torch.int32), y_3.view(torch.int32))
+    assert layer.device_error(fused=True) == 0 and layer.device_error(fused=False) == 0
+
+
 @pytest.mark.parametrize("usecase", ["int8", "bf16", "fp8"])
 def test_split_tail_tiles(usecase, monkeypatch):
     """Few tiles on many workgroups: the tail tiles are split along K (eight
