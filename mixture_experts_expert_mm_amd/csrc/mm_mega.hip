@@ -135,8 +135,9 @@ void k_mega(const MegaArgs* mp) {
       DispatchArgs d = m.d;
       d.x_pool = m.x_tok;
       d.x_pool_scale = m.x_tok_scale;
+      // token i to wave i / G of block i % G: a short batch spreads over all CUs
       const int64_t nwv = (int64_t)gridDim.x * NW;
-      for (int64_t tok = (int64_t)blockIdx.x * NW + t / 64; tok < d.T; tok += nwv) quant_token_wave<UC>(d, tok);
+      for (int64_t tok = (int64_t)(t / 64) * gridDim.x + blockIdx.x; tok < d.T; tok += nwv) quant_token_wave<UC>(d, tok);
       if (!grid_barrier(ctl, ++nb, spin, bs, &ok)) return;
     }
   } else {

@@ -57,7 +57,9 @@ def test_plan_sizes_and_block_m():
     assert p.x_pool_bytes == p.pool_rows * 7168 * 2
     assert p.w1_bytes == 32 * 7168 * 4096 * 2
     assert p.fused_workspace_bytes > p.workspace_bytes > 0
-    small = B.mm_plan_create(128, 7168, 2048, 32, 8, "fp8")
+    t128 = B.mm_plan_create(128, 7168, 2048, 32, 8, "fp8")   # 32 rows per expert
+    assert t128.block_m == 128
+    small = B.mm_plan_create(64, 7168, 2048, 32, 8, "fp8")    # 16 rows per expert
     assert small.block_m == 64 and small.x_pool_bytes == small.pool_rows * 7168
     tiny = B.mm_plan_create(20, 256, 128, 16, 2, "int8")
     assert tiny.block_m == 64

@@ -25,17 +25,19 @@ from gpu_helpers import (TOL, bf16_bits_of_f32, cpu_inputs, device_inputs, exper
 
 pytestmark = pytest.mark.gpu
 
-# shapes that span several tiles and a ragged tail in every GEMM dimension
+# shapes that span several tiles and a ragged tail in every GEMM dimension;
+# bm64 has 17 rows per expert on average (BLOCK_M 64) and, from a strong
+# router bias, two experts of more than one M-block and seven empty ones
 SMALL = {
-    "bm32": dict(T=20, H=256, I=128, E=16, K=2),
-    "bm64": dict(T=200, H=512, I=256, E=8, K=2),
-    "bm128": dict(T=333, H=768, I=384, E=6, K=3),
+    "bm32": dict(T=20, H=256, I=128, E=16, K=2, bias=0.5),
+    "bm64": dict(T=200, H=512, I=256, E=24, K=2, bias=2.0),
+    "bm128": dict(T=333, H=768, I=384, E=6, K=3, bias=0.5),
 }
 
 
 def small_cfg(shape: str, usecase: str, **kw) -> wl.Config:
     s = SMALL[shape]
-    return wl.Config(f"{shape}_{usecase}", usecase, s["T"], s["H"], s["I"], s["E"], s["K"], 0.5, 2024, **kw)
+    return wl.Config(f"{shape}_{usecase}", usecase, s["T"], s["H"], s["I"], s["E"], s["K"], s["bias"], 2024, **kw)
 
 
 def check_dispatch(layer: moe.ExpertLayer, inp: wl.Inputs, im, sample_rows=None):
@@ -259,6 +261,7 @@ def test_split_tail_tiles(usecase, monkeypatch):
     cfg = wl.Config(f"split_{usecase}", usecase, 64, 4096, 1024, 4, 2, 0.5, 77)
     inp = wl.make_inputs(cfg)
     x, ids, wts = device_inputs(inp)
+    monkeypatch.setenv("MM_FORCE_TILE", "0")   # BLOCK_M 64: the piece counts above
     layer = make_layer(inp, "f32")
     monkeypatch.setenv("MM_MAX_SPLIT", "1")
     y_one, _ = layer.forward(x, ids, wts)
