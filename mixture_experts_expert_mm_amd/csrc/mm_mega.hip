@@ -1,11 +1,13 @@
 // The fused persistent kernel of mega_moe: every step of the routed-expert
 // path in one launch.  One workgroup per compute unit, the whole grid
-// resident at once; the phases run in order
+// resident at once; the phases run in order, separated by grid-wide
+// barriers:
 //   count + claim | prefix + scatter | gather | Linear1 + SwiGLU |
 //   (A8W8) requantisation | Linear2 + gate | combine
-// separated by grid-wide barriers, and each phase is the same device code
-// the three-call path runs as separate kernels, so the results are bitwise
-// those of that path.  The counters it relies on (expert counts, A8W8 row
+// When Linear1 reads the token rows in place there is no gather phase and
+// the A8W8 token quantisation runs beside the count.  Each phase computes
+// exactly what the three-call path's kernels compute, so the results are
+// bitwise those of that path.  The counters it relies on (expert counts, A8W8 row
 // amax, barrier arrivals, error word) are cleared by a small pre-pass.
 #include "mm_dispatch_dev.hpp"
 #include "mm_gemm_dev.hpp"
@@ -109,10 +111,23 @@ void k_mega(const MegaArgs* mp) {
   uint32_t nb = 0;
   const int64_t nvb = (nwaves + NW - 1) / NW;   // virtual dispatch blocks of NW waves
 
-  // count + claim (each phase copies the arguments it needs into registers)
+  // count + claim (each phase copies the arguments it needs into registers).
+  // When Linear1 reads the token rows in place, A8W8 quantises each token
+  // once (one wave per token) into a [T][H] buffer: that needs no routing,
+  // so it runs here too, beside the count.
   {
     const DispatchArgs d = m.d;
     for (int64_t vb = blockIdx.x; vb < nvb; vb += gridDim.x) count_block<NW>(d, vb, nwaves, smem);
+  }
+  if constexpr (UC != UC_BF16) {
+    if (m.l1_by_token) {
+      DispatchArgs d = m.d;
+      d.x_pool = m.x_tok;
+      d.x_pool_scale = m.x_tok_scale;
+      // token i to wave i / G of block i % G: a short batch spreads over all CUs
+      const int64_t nwv = (int64_t)gridDim.x * NW;
+      for (int64_t tok = (int64_t)(t / 64) * gridDim.x + blockIdx.x; tok < d.T; tok += nwv) quant_token_wave<UC>(d, tok);
+    }
   }
   if (!grid_barrier(ctl, ++nb, spin, bs, &ok)) return;
 
@@ -126,21 +141,9 @@ void k_mega(const MegaArgs* mp) {
   }
   if (!grid_barrier(ctl, ++nb, spin, bs, &ok)) return;
 
-  // gather (+ A8W8 activation quantisation).  When Linear1 reads the token
-  // rows in place there is nothing to gather for A16W16, and A8W8 quantises
-  // each token once (one wave per token) into a [T][H] buffer instead of
-  // writing its K pool rows; otherwise one token per block at a time.
-  if (m.l1_by_token) {
-    if constexpr (UC != UC_BF16) {
-      DispatchArgs d = m.d;
-      d.x_pool = m.x_tok;
-      d.x_pool_scale = m.x_tok_scale;
-      // token i to wave i / G of block i % G: a short batch spreads over all CUs
-      const int64_t nwv = (int64_t)gridDim.x * NW;
-      for (int64_t tok = (int64_t)(t / 64) * gridDim.x + blockIdx.x; tok < d.T; tok += nwv) quant_token_wave<UC>(d, tok);
-      if (!grid_barrier(ctl, ++nb, spin, bs, &ok)) return;
-    }
-  } else {
+  // gather (+ A8W8 activation quantisation) of the pool rows, one token per
+  // block at a time, unless Linear1 reads the token rows in place
+  if (!m.l1_by_token) {
     const DispatchArgs d = m.d;
     for (int64_t tok = blockIdx.x; tok < d.T; tok += gridDim.x) gather_token<UC, NT>(d, tok, dst, red);
     if (!grid_barrier(ctl, ++nb, spin, bs, &ok)) return;
