@@ -103,8 +103,13 @@ __device__ __forceinline__ void vm_barrier() {
 // group; the group's row offset and the stage's K offset are wave-uniform
 // and go in the scalar offset.  The tile bases become buffer descriptors
 // here: the descriptor type cannot appear in a signature the host pass sees.
-// A rows read by token (by_tok): the lane's own row offset voff_a replaces
-// the group's row offset, which then stays out of the scalar offset.
+// A rows take the lane's offset voff_a: its row-in-group offset, or, when
+// read by token (by_tok), its token row's offset (the group's row offset then
+// stays out of the scalar offset); a lane whose row is past the tile's valid
+// rows gets an offset beyond the descriptor's range, which loads zeros
+// without a memory access.
+constexpr uint32_t kOffRange = 0x7fff0000u;   // past any A descriptor's range (< 2^31 bytes)
+
 template <int NW, int BM, int STAGE, int S, int RB>
 __device__ __forceinline__ void dma_one(uint8_t* lds, const uint8_t* abase, int abytes, const uint8_t* bbase,
                                         int bbytes, uint32_t voff, int wv, int kbytes, int i, int kb, int kbase,
@@ -116,7 +121,7 @@ __device__ __forceinline__ void dma_one(uint8_t* lds, const uint8_t* abase, int 
   const int rows = is_a ? (by_tok ? 0 : RPI * NW * i) : RPI * NW * i - BM;
   const int soff = __builtin_amdgcn_readfirstlane(rows * kbytes + (kb + kbase) * RB);
   const int g = wv + NW * i;
-  const uint32_t vo = (is_a && by_tok) ? voff_a : voff;
+  const uint32_t vo = is_a ? voff_a : voff;
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(lds + (kb % S) * STAGE + g * 1024), 16, vo, soff, 0, 0);
 }
 
@@ -497,12 +502,14 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
       r.slot = uniform_int(xcd * 2 * per_x + p);
     }
     r.aoa[0] = r.aoa[1] = 0;
-    if (by_tok) {
 #pragma unroll
-      for (int x = 0; x < DA; ++x) {
-        const int64_t p = (int64_t)r.row0 + RPI * (wv + NW * x) + l / CH;
-        const int32_t route = gp(a.a_route)[p];
-        r.aoa[x] = (uint32_t)((route >= 0 ? route / a.K : 0) * kbytes) + vchunk;
+    for (int x = 0; x < DA; ++x) {
+      const int row = RPI * (wv + NW * x) + l / CH;   // the lane's A row in the tile
+      if (by_tok) {
+        const int32_t route = gp(a.a_route)[(int64_t)r.row0 + row];
+        r.aoa[x] = route >= 0 ? (uint32_t)((route / a.K) * kbytes) + vchunk : kOffRange;
+      } else {
+        r.aoa[x] = row < r.valid ? voff : kOffRange;
       }
     }
     return r;
