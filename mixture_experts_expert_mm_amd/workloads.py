@@ -77,6 +77,11 @@ CONFIGS = {
     "dsv3_fp8_t128": Config("dsv3_fp8_t128", "fp8", 128, 7168, 2048, 32, 8, 0.5, 1003),
     "dsv3_fp8_t16384": Config("dsv3_fp8_t16384", "fp8", 16384, 7168, 2048, 32, 8, 0.5, 1003),
     "dsv3_int8": Config("dsv3_int8", "int8", 8192, 7168, 2048, 32, 8, 0.0, 1004),
+    # the bf16 layer at the two token counts the throughput targets name
+    # (16K tokens: MFMA-bound; 128 tokens: weight streaming); same weights
+    # as dsv3_bf16
+    "dsv3_bf16_t16384": Config("dsv3_bf16_t16384", "bf16", 16384, 7168, 2048, 32, 8, 0.5, 1002),
+    "dsv3_bf16_t128": Config("dsv3_bf16_t128", "bf16", 128, 7168, 2048, 32, 8, 0.5, 1002),
 }
 
 

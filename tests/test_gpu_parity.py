@@ -435,7 +435,8 @@ def test_prepare_weights_layout(usecase):
 # sampled tokens against the per-token oracle
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("name", ["mid_bf16", "dsv3_bf16", "dsv3_fp8_t128", "dsv3_fp8_t16384", "dsv3_int8"])
+@pytest.mark.parametrize("name", ["mid_bf16", "dsv3_bf16", "dsv3_fp8_t128", "dsv3_fp8_t16384", "dsv3_int8",
+                                  "dsv3_bf16_t16384", "dsv3_bf16_t128"])
 def test_full_config_sampled_tokens(name):
     cfg = wl.CONFIGS[name]
     log(f"[full] {name}: generating inputs")

@@ -10,9 +10,11 @@ def test_configs_match_stated_shapes():
     c = wl.CONFIGS
     assert (c["tiny_bf16"].T, c["tiny_bf16"].H, c["tiny_bf16"].I, c["tiny_bf16"].E, c["tiny_bf16"].K) == (64, 256, 128, 8, 2)
     assert (c["mid_bf16"].T, c["mid_bf16"].H, c["mid_bf16"].I, c["mid_bf16"].E, c["mid_bf16"].K) == (2048, 4096, 1408, 16, 4)
-    for n in ("dsv3_bf16", "dsv3_fp8_t128", "dsv3_fp8_t16384", "dsv3_int8"):
+    for n in ("dsv3_bf16", "dsv3_fp8_t128", "dsv3_fp8_t16384", "dsv3_int8", "dsv3_bf16_t16384", "dsv3_bf16_t128"):
         assert (c[n].H, c[n].I, c[n].E, c[n].K) == (7168, 2048, 32, 8)
     assert c["dsv3_fp8_t128"].seed == c["dsv3_fp8_t16384"].seed      # one weight set for the sweep
+    assert c["dsv3_bf16_t128"].seed == c["dsv3_bf16_t16384"].seed == c["dsv3_bf16"].seed
+    assert (c["dsv3_bf16_t16384"].T, c["dsv3_bf16_t128"].T) == (16384, 128)
 
 
 def test_routing_is_deterministic_distinct_and_normalised():
