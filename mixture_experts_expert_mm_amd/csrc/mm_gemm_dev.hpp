@@ -681,19 +681,32 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
     // order.  Both finish this exchange before the next item's stages go out
     // (the waits for the exchange would otherwise wait for those too).
     if (cur.role != kRoleFull) {
-      uint32_t* const pslot = a.partials + (size_t)cur.slot * (BM * BN);
-      const int lane_words = ((wv * MB * NB) * 64 + l) * 16;   // [wave][block][lane][16]
+      // Slots [slot, slot + sk) as one buffer.  Only rows below the tile's
+      // valid count are exchanged: word group v of block (i, j) holds rows
+      // rb0 + 32i + 8v .. + 3 of one column; a group past the valid rows gets
+      // an offset beyond the descriptor's range, so its store is dropped and
+      // its load returns zeros, neither touching memory.  (The epilogue never
+      // stores those rows, and their A rows are zero in every piece.)
+      const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(a.partials + (size_t)cur.slot * (BM * BN)), (short)0, 8 * BM * BN * 4, 0x00020000);
+      const uint32_t lane_bytes = (uint32_t)(((wv * MB * NB) * 64 + l) * 16 * 4);   // [wave][block][lane][16] words
+      const int rb0 = wm * WTM + 4 * h;
+      uint32_t vo[MB][4];
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) vo[i][v] = rb0 + i * 32 + 8 * v < cur.valid ? lane_bytes : kOffRange;
       if (cur.role == kRoleProduce) {
 #pragma unroll
         for (int i = 0; i < MB; ++i)
 #pragma unroll
-          for (int j = 0; j < NB; ++j) {
-            u32x4* dst = reinterpret_cast<u32x4*>(pslot + lane_words + (i * NB + j) * 64 * 16);
+          for (int j = 0; j < NB; ++j)
 #pragma unroll
             for (int v = 0; v < 4; ++v)
-              gp(dst)[v] = u32x4{word_of(acc[i][j][4 * v]), word_of(acc[i][j][4 * v + 1]), word_of(acc[i][j][4 * v + 2]),
-                                 word_of(acc[i][j][4 * v + 3])};
-          }
+              __builtin_amdgcn_raw_buffer_store_b128(
+                  u32x4{word_of(acc[i][j][4 * v]), word_of(acc[i][j][4 * v + 1]), word_of(acc[i][j][4 * v + 2]),
+                        word_of(acc[i][j][4 * v + 3])},
+                  prs, vo[i][v], ((i * NB + j) * 64 * 16 + 4 * v) * 4, 0);
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the partial sums are in L2
         __syncthreads();
         if (t == 0) {
@@ -715,15 +728,14 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
 #pragma unroll
             for (int i = 0; i < MB; ++i)
 #pragma unroll
-              for (int j = 0; j < NB; ++j) {
-                const u32x4* src = reinterpret_cast<const u32x4*>(pslot + (size_t)q * (BM * BN) + lane_words + (i * NB + j) * 64 * 16);
+              for (int j = 0; j < NB; ++j)
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
-                  const u32x4 w = gp(src)[v];
+                  const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(
+                      prs, vo[i][v], (q * (BM * BN) + (i * NB + j) * 64 * 16 + 4 * v) * 4, 0);
 #pragma unroll
                   for (int e = 0; e < 4; ++e) acc[i][j][4 * v + e] += from_word<AccE>(w[e]);
                 }
-              }
           }
         }
         __syncthreads();   // every partial has been read: the flags go back to zero

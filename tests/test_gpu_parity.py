@@ -251,23 +251,26 @@ def test_largest_hidden_and_intermediate(shape, usecase):
     assert layer.device_error(fused=True) == 0 and layer.device_error(fused=False) == 0
 
 
+@pytest.mark.parametrize("tile", ["0", "1"])
 @pytest.mark.parametrize("usecase", ["int8", "bf16", "fp8"])
-def test_split_tail_tiles(usecase, monkeypatch):
-    """Few tiles on many workgroups: the tail tiles are split along K (eight
-    pieces in Linear1, two in Linear2 here) and piece 0 adds the others'
-    partial sums in piece order.  int8 accumulators are exact, so the split
-    result equals the unsplit one bit for bit; every use case stays within
-    the oracle tolerance, and fused == three-call."""
+def test_split_tail_tiles(usecase, tile, monkeypatch):
+    """Few tiles on many workgroups: the tail tiles are split along K (with
+    BLOCK_M 64: eight pieces in Linear1, two in Linear2; with BLOCK_M 128:
+    eight and four) and piece 0 adds the others' partial sums in piece order.
+    About 32 routes per expert, so every tile has padding rows, whose partial
+    sums are not exchanged.  int8 accumulators are exact, so the split result
+    equals the unsplit one bit for bit; every use case stays within the
+    oracle tolerance, and fused == three-call."""
     cfg = wl.Config(f"split_{usecase}", usecase, 64, 4096, 1024, 4, 2, 0.5, 77)
     inp = wl.make_inputs(cfg)
     x, ids, wts = device_inputs(inp)
-    monkeypatch.setenv("MM_FORCE_TILE", "0")   # BLOCK_M 64: the piece counts above
+    monkeypatch.setenv("MM_FORCE_TILE", tile)   # the piece counts above
     layer = make_layer(inp, "f32")
     monkeypatch.setenv("MM_MAX_SPLIT", "1")
     y_one, _ = layer.forward(x, ids, wts)
     y_one = y_one.clone()
     monkeypatch.setenv("MM_MAX_SPLIT", "8")
-    log(f"[split] {usecase}: unsplit vs split tail tiles")
+    log(f"[split] {usecase}, BLOCK_M {64 << int(tile)}: unsplit vs split tail tiles")
     y_f, _ = layer.forward(x, ids, wts)
     y_3, _ = layer.forward_3call(x, ids, wts)
     torch.cuda.synchronize()
