@@ -27,7 +27,7 @@ __global__ __launch_bounds__(256) void k_scatter(DispatchArgs a, int64_t nwaves)
   int32_t* off = smem;                     // [E+1]
   int32_t* run = smem + a.E + 1;           // [4][E]
   __shared__ int32_t wsum[kDispatchWavesPerBlock];
-  padded_prefix<256>(a, off, wsum);
+  padded_prefix<256>(a, a.counts, off, wsum);
   if (blockIdx.x == 0)
     for (int e = threadIdx.x; e <= a.E; e += 256) a.offsets[e] = off[e];
   scatter_block<kDispatchWavesPerBlock>(a, blockIdx.x, gridDim.x, nwaves, off, run);

@@ -53,10 +53,10 @@ __device__ __forceinline__ void count_block(const DispatchArgs& a, int64_t vb, i
   __syncthreads();
 }
 
-// Block-wide exclusive scan of the BLOCK_M-padded counts into off[0..E]
-// (wsum: NT/64 ints of LDS).
+// Block-wide exclusive scan of the BLOCK_M-padded counts cnt[0..E-1] (the
+// global counts, or an LDS copy) into off[0..E] (wsum: NT/64 ints of LDS).
 template <int NT>
-__device__ __forceinline__ void padded_prefix(const DispatchArgs& a, int32_t* off, int32_t* wsum) {
+__device__ __forceinline__ void padded_prefix(const DispatchArgs& a, const int32_t* cnt, int32_t* off, int32_t* wsum) {
   constexpr int NW = NT / 64;
   const int t = threadIdx.x, w = t / 64, l = lane_id();
   const int per = (a.E + NT - 1) / NT;
@@ -64,7 +64,7 @@ __device__ __forceinline__ void padded_prefix(const DispatchArgs& a, int32_t* of
   int local = 0;
   for (int j = 0; j < per; ++j) {
     const int e = e0 + j;
-    if (e < a.E) local += (a.counts[e] + a.block_m - 1) / a.block_m * a.block_m;
+    if (e < a.E) local += (cnt[e] + a.block_m - 1) / a.block_m * a.block_m;
   }
   int incl = local;
 #pragma unroll
@@ -80,7 +80,7 @@ __device__ __forceinline__ void padded_prefix(const DispatchArgs& a, int32_t* of
     const int e = e0 + j;
     if (e < a.E) {
       off[e] = excl;
-      excl += (a.counts[e] + a.block_m - 1) / a.block_m * a.block_m;
+      excl += (cnt[e] + a.block_m - 1) / a.block_m * a.block_m;
     }
   }
   if (t == 0) {
@@ -88,6 +88,56 @@ __device__ __forceinline__ void padded_prefix(const DispatchArgs& a, int32_t* of
     for (int ww = 0; ww < NW; ++ww) total += wsum[ww];
     off[a.E] = total;
   }
+  __syncthreads();
+}
+
+// The whole dispatch of a small batch (at most MAXR * NT routes) by one
+// block, with no grid-wide step between count and scatter.  Thread t takes
+// routes t, t + NT, ...; a route's rank inside its expert is the old value
+// of an LDS atomic add on that expert's count (hist: E ints of LDS).  Then,
+// as in the multi-block path: the padded prefix, counts and offsets out,
+// pool_src / route_to_pool, and pool_src = -1 on every expert's padding
+// rows.  The order of the routes inside an expert is arbitrary here as it
+// is with the per-wave claims; every later step computes a route's result
+// from its own row alone, so the output does not depend on that order.
+template <int NT, int MAXR>
+__device__ __forceinline__ void dispatch_one_block(const DispatchArgs& a, int32_t* hist, int32_t* off, int32_t* wsum) {
+  const int t = threadIdx.x;
+  const int64_t R = a.T * a.K;
+  for (int e = t; e < a.E; e += NT) hist[e] = 0;
+  __syncthreads();
+  int ex[MAXR], rk[MAXR];
+  // registers set first and loads that only fill them: every load goes out
+  // before the first wait
+#pragma unroll
+  for (int j = 0; j < MAXR; ++j) {
+    const int64_t r = t + (int64_t)NT * j;
+    ex[j] = -1;
+    if (r < R) ex[j] = a.topk_ids[r];
+  }
+#pragma unroll
+  for (int j = 0; j < MAXR; ++j) {
+    const int64_t r = t + (int64_t)NT * j;
+    if (r < R && ex[j] >= a.E && a.err) atomicOr(a.err, (uint32_t)MM_DEVERR_BAD_EXPERT);
+    const int e = (r < R && ex[j] >= 0 && ex[j] < a.E) ? ex[j] : -1;
+    ex[j] = e;
+    rk[j] = e >= 0 ? atomicAdd(&hist[e], 1) : 0;
+  }
+  __syncthreads();
+  padded_prefix<NT>(a, hist, off, wsum);
+  for (int e = t; e < a.E; e += NT) a.counts[e] = hist[e];
+  for (int e = t; e <= a.E; e += NT) a.offsets[e] = off[e];
+#pragma unroll
+  for (int j = 0; j < MAXR; ++j) {
+    const int64_t r = t + (int64_t)NT * j;
+    if (r < R) {
+      const int32_t p = ex[j] >= 0 ? off[ex[j]] + rk[j] : -1;
+      a.route_to_pool[r] = p;
+      if (p >= 0) a.pool_src[p] = (int32_t)r;
+    }
+  }
+  for (int e = 0; e < a.E; ++e)
+    for (int64_t p = (int64_t)off[e] + hist[e] + t; p < off[e + 1]; p += NT) a.pool_src[p] = -1;
   __syncthreads();
 }
 

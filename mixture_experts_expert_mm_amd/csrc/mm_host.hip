@@ -183,15 +183,22 @@ uint32_t barrier_spin_limit() {
 }
 
 // Largest K split of a tail tile (MM_MAX_SPLIT overrides: 1 turns it off).
-// Split only in the compute regime: measured, splitting the last round's
-// tiles makes the 2048 x 4096 layer 2-3% faster and costs the 128-token
-// 7168 x 2048 layers 3-5% (the partial sums add traffic to a step that is
-// already bound by streaming the weights); neutral in between.
+// Only int8 splits by default: its partial sums are exact int32.  With
+// float accumulators a split tile rounds differently from an unsplit one,
+// and which M-block of its expert (so which tile) a route lands in depends
+// on the order in which the dispatch's atomics claim pool rows; unsplit,
+// every route's result depends on its own row alone, so the output is the
+// same on every call and in both paths.  Split only in the compute regime:
+// measured, splitting the last round's tiles makes the 2048 x 4096 layer
+// 2-3% faster and costs the 128-token 7168 x 2048 layers 3-5% (the partial
+// sums add traffic to a step that is already bound by streaming the
+// weights); neutral in between.
 int max_split(const mm_plan& pl) {
   if (const char* v = std::getenv("MM_MAX_SPLIT")) {
     const int n = std::atoi(v);
     if (n >= 1 && n <= 8) return n;
   }
+  if (pl.prob.usecase != MM_A8W8_INT8) return 1;
   const double expected = (double)(pl.prob.num_tokens * pl.prob.num_topk) / (double)pl.prob.num_experts;
   return expected >= 96 ? 8 : 1;
 }

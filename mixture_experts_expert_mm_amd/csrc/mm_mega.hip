@@ -5,7 +5,9 @@
 //   count + claim | prefix + scatter | gather | Linear1 + SwiGLU |
 //   (A8W8) requantisation | Linear2 + gate | combine
 // When Linear1 reads the token rows in place there is no gather phase and
-// the A8W8 token quantisation runs beside the count.  Each phase computes
+// the A8W8 token quantisation runs beside the count; a small batch is
+// dispatched whole by one block in the first phase (no prefix + scatter
+// phase).  Each phase computes
 // exactly what the three-call path's kernels compute, so the results are
 // bitwise those of that path.  The counters it relies on (expert counts, A8W8 row
 // amax, barrier arrivals, error word) are cleared by a small pre-pass.
@@ -19,10 +21,12 @@ namespace mm {
 // registered, ctl[16 + x] arrivals on XCD x, ctl[32 + x] workgroups on XCD x.
 //
 // Every workgroup registers its XCD at kernel start.  At barrier n each wave
-// has its stores in L2 (workgroup barrier); thread 0 adds one arrival for its
-// XCD, and the last workgroup of an XCD to arrive writes that XCD's L2 back
-// (one device-scope release per XCD, not one per workgroup) and releases the
-// XCD; every workgroup then waits for all active XCDs and acquires.  Polls
+// waits for its own stores to complete (be in L2), then the workgroup
+// barrier (which alone does not wait for them); thread 0 adds one arrival
+// for its XCD, and the last workgroup of an XCD to arrive writes that XCD's
+// L2 back (one device-scope release per XCD, not one per workgroup) and
+// releases the XCD; every workgroup then waits for all active XCDs and
+// acquires.  Polls
 // are relaxed device-scope loads with a sleep between them.  After spin_limit
 // polls a wait gives up: it sets MM_DEVERR_BARRIER_TIMEOUT and the block
 // leaves the kernel, so no phase runs on data another block may not have
@@ -54,6 +58,9 @@ __device__ __forceinline__ void barrier_register(uint32_t* ctl, BarState& bs) {
 }
 
 __device__ __forceinline__ bool grid_barrier(uint32_t* ctl, uint32_t n, uint32_t spin_limit, BarState& bs, int32_t* ok_lds) {
+  // s_waitcnt vmcnt(0): the write-back below covers only stores already in
+  // L2, and a wave's stores may still be in flight at the workgroup barrier
+  __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
   if (threadIdx.x == 0) {
     bool ok = true;
@@ -114,10 +121,18 @@ void k_mega(const MegaArgs* mp) {
   // count + claim (each phase copies the arguments it needs into registers).
   // When Linear1 reads the token rows in place, A8W8 quantises each token
   // once (one wave per token) into a [T][H] buffer: that needs no routing,
-  // so it runs here too, beside the count.
+  // so it runs here too, beside the count.  A small batch (at most
+  // kOneBlockRoutes routes per thread of a block) is dispatched whole by
+  // block 0 here, which saves the prefix + scatter phase and its barrier.
+  constexpr int kOneBlockRoutes = 16;
+  const bool one_block = m.d.T * m.d.K <= (int64_t)kOneBlockRoutes * NT;
   {
     const DispatchArgs d = m.d;
-    for (int64_t vb = blockIdx.x; vb < nvb; vb += gridDim.x) count_block<NW>(d, vb, nwaves, smem);
+    if (one_block) {
+      if (blockIdx.x == 0) dispatch_one_block<NT, kOneBlockRoutes>(d, smem, off_s, wsum);
+    } else {
+      for (int64_t vb = blockIdx.x; vb < nvb; vb += gridDim.x) count_block<NW>(d, vb, nwaves, smem);
+    }
   }
   if constexpr (UC != UC_BF16) {
     if (m.l1_by_token) {
@@ -132,14 +147,14 @@ void k_mega(const MegaArgs* mp) {
   if (!grid_barrier(ctl, ++nb, spin, bs, &ok)) return;
 
   // padded prefix (every block, into LDS) + scatter
-  {
+  if (!one_block) {
     const DispatchArgs d = m.d;
-    padded_prefix<NT>(d, off_s, wsum);
+    padded_prefix<NT>(d, d.counts, off_s, wsum);
     if (blockIdx.x == 0)
       for (int e = t; e <= d.E; e += NT) d.offsets[e] = off_s[e];
     for (int64_t vb = blockIdx.x; vb < nvb; vb += gridDim.x) scatter_block<NW>(d, vb, nvb, nwaves, off_s, smem);
+    if (!grid_barrier(ctl, ++nb, spin, bs, &ok)) return;
   }
-  if (!grid_barrier(ctl, ++nb, spin, bs, &ok)) return;
 
   // gather (+ A8W8 activation quantisation) of the pool rows, one token per
   // block at a time, unless Linear1 reads the token rows in place
