@@ -802,6 +802,28 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
               }
             }
           }
+        } else if constexpr (MODE == 1) {
+          // contribution of route i*K+k: ((D * s^W2) * s^A) * G[i,k].  Row
+          // outer, so that a row's slot offset (one 32 x 32 -> 64-bit
+          // multiply) serves all of the lane's columns in it and one mask
+          // covers them.
+          const int ncol = cur.n0 + wn * WTN + lr;
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            const int32_t route = (int32_t)ri[q][0];
+            const float gw = __uint_as_float(ri[q][1]);
+            const float rs = __uint_as_float(ri[q][2]);
+            if (route >= 0) {
+              const uint64_t off = (uint64_t)(uint32_t)route * (uint32_t)a.H + (uint32_t)ncol;
+#pragma unroll
+              for (int j = 0; j < NB; ++j) {
+                const float v = acc_to_f32(acc[i][j][q]) * cs0[j];
+                const float o = (UC != UC_BF16) ? (v * rs) * gw : v * gw;
+                if constexpr (UC == UC_BF16) gp(static_cast<float*>(a.contrib))[off + j * 32] = o;
+                else gp(static_cast<uint16_t*>(a.contrib))[off + j * 32] = f32_to_bf16_bits(o);
+              }
+            }
+          }
         } else {
           int32_t* const rbase = a.raw_out + (int64_t)cur.row0 * a.N;
           int lane_row = rb;
@@ -812,25 +834,13 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
 #pragma unroll
             for (int q = 0; q < 16; ++q) {
               const int r = rb + 8 * (q / 4) + (q % 4);
-              if constexpr (MODE == 1) {
-                // contribution of route i*K+k: ((D * s^W2) * s^A) * G[i,k]
-                const int32_t route = (int32_t)ri[q][0];
-                const float gw = __uint_as_float(ri[q][1]);
-                const float v = acc_to_f32(acc[i][j][q]) * cs0[j];
-                const float o = (UC != UC_BF16) ? (v * __uint_as_float(ri[q][2])) * gw : v * gw;
-                if (route >= 0) {
-                  if constexpr (UC == UC_BF16) gp(static_cast<float*>(a.contrib))[(int64_t)route * a.H + n] = o;
-                  else gp(static_cast<uint16_t*>(a.contrib))[(int64_t)route * a.H + n] = f32_to_bf16_bits(o);
-                }
-              } else {
-                int col = n;
-                if (a.gate_up_group > 0) {
-                  const int g2 = 2 * a.gate_up_group;
-                  const int qq = n / g2, m = n % g2;
-                  col = (m < a.gate_up_group) ? qq * a.gate_up_group + m : a.I + qq * a.gate_up_group + (m - a.gate_up_group);
-                }
-                if (r < cur.valid) gp(rbase)[(lane_row + 8 * (q / 4) + (q % 4)) * a.N + col] = acc[i][j][q];
+              int col = n;
+              if (a.gate_up_group > 0) {
+                const int g2 = 2 * a.gate_up_group;
+                const int qq = n / g2, m = n % g2;
+                col = (m < a.gate_up_group) ? qq * a.gate_up_group + m : a.I + qq * a.gate_up_group + (m - a.gate_up_group);
               }
+              if (r < cur.valid) gp(rbase)[(lane_row + 8 * (q / 4) + (q % 4)) * a.N + col] = acc[i][j][q];
             }
           }
         }
