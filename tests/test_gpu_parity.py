@@ -228,19 +228,19 @@ def test_fused_equals_three_call_and_is_deterministic(usecase):
 
 
 @pytest.mark.parametrize("usecase", ["bf16", "fp8"])
-@pytest.mark.parametrize("T", [1024, 1025])
-def test_fused_one_block_dispatch_boundary(T, usecase):
+@pytest.mark.parametrize("T,E,block_m", [(1024, 32, 128), (1025, 32, 128), (512, 256, 64), (513, 256, 64)])
+def test_fused_one_block_dispatch_boundary(T, E, block_m, usecase):
     """The fused kernel dispatches a batch of at most 16 routes per thread
-    of a block (8192 with BLOCK_M 128) in one block, a larger one over the
-    grid: at 8192 and 8200 routes, with masked routes, the fused result
-    equals the three-call one bit for bit, the counts match, and Y is within
-    the oracle tolerance."""
-    cfg = wl.Config(f"dispatch_boundary_{usecase}", usecase, T, 512, 256, 32, 8, 0.5, 91, masked_ratio=0.1)
+    of a block (8192 with BLOCK_M 128, 4096 with BLOCK_M 64) in one block,
+    a larger one over the grid: at and just past each limit, with masked
+    routes, the fused result equals the three-call one bit for bit, the
+    counts match, and Y is within the oracle tolerance."""
+    cfg = wl.Config(f"dispatch_boundary_{usecase}", usecase, T, 512, 256, E, 8, 0.5, 91, masked_ratio=0.1)
     inp = wl.make_inputs(cfg)
     layer = make_layer(inp, "f32")
-    assert layer.plan.block_m == 128
+    assert layer.plan.block_m == block_m
     x, ids, wts = device_inputs(inp)
-    log(f"[one-block dispatch] {usecase}: {T * 8} routes")
+    log(f"[one-block dispatch] {usecase}: {T * 8} routes over {E} experts, BLOCK_M {block_m}")
     y_f, c_f = layer.forward(x, ids, wts)
     y_3, im = layer.forward_3call(x, ids, wts)
     torch.cuda.synchronize()
