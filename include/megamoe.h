@@ -41,7 +41,11 @@
  * - Calls that share a workspace or intermediate buffers must be ordered
  *   on one stream; overlapping calls on the same buffers race.
  * - Results are deterministic: the top-k sum runs in slot order k = 0..K-1
- *   in float32 (operator page, "Deterministic Computation").
+ *   in float32 (operator page, "Deterministic Computation"), and a route's
+ *   result depends on its own pool row alone, not on where in its expert's
+ *   range the dispatch placed it.  (Setting MM_MAX_SPLIT above 1 for the
+ *   bf16 or fp8 use case, a tuning knob, gives that up: a K-split tile
+ *   rounds its float32 sums differently.)
  */
 #ifndef MEGAMOE_H
 #define MEGAMOE_H
