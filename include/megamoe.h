@@ -85,6 +85,14 @@ typedef struct mm_problem {
   int64_t num_topk;            /* K in [1, min(E, 64)] */
   int32_t usecase;             /* mm_usecase */
   int32_t y_dtype;             /* mm_out_dtype */
+  /* The operator's activation_clamp (mega_moe, Parameters): with
+   * clamp_activation = 1, every element of Linear1's output H (gate and up
+   * halves, after A8W8 dequantisation) is clamped to [-activation_clamp,
+   * activation_clamp] before SwiGLU; activation_clamp must then be >= 0 (not
+   * NaN).  clamp_activation = 0 (a zeroed struct) is the operator's None: no
+   * clamp, activation_clamp ignored.  Other values: MM_ERR_INVALID_ARG. */
+  int32_t clamp_activation;
+  float activation_clamp;
 } mm_problem;
 
 /* A plan is plain host data filled by mm_plan_create.  Callers read the

@@ -31,6 +31,8 @@ class MMProblem(ctypes.Structure):
         ("num_topk", ctypes.c_int64),
         ("usecase", ctypes.c_int32),
         ("y_dtype", ctypes.c_int32),
+        ("clamp_activation", ctypes.c_int32),
+        ("activation_clamp", ctypes.c_float),
     ]
 
 
@@ -130,9 +132,11 @@ def _check(fn, st):
 
 # ------------------------------------------------------------------ entries
 
-def mm_plan_create(T, H, I, E, K, usecase="bf16", y_dtype="bf16") -> MMPlan:
+def mm_plan_create(T, H, I, E, K, usecase="bf16", y_dtype="bf16", activation_clamp=None) -> MMPlan:
+    """activation_clamp: None (no clamp) or c >= 0 (H clamped to [-c, c] before SwiGLU)."""
     prob = MMProblem(T, H, I, E, K, USECASE.get(usecase, usecase) if isinstance(usecase, str) else usecase,
-                     MM_OUT_F32 if y_dtype in ("f32", "fp32", MM_OUT_F32) else MM_OUT_BF16)
+                     MM_OUT_F32 if y_dtype in ("f32", "fp32", MM_OUT_F32) else MM_OUT_BF16,
+                     0 if activation_clamp is None else 1, 0.0 if activation_clamp is None else float(activation_clamp))
     plan = MMPlan()
     _check("mm_plan_create", load().mm_plan_create(ctypes.byref(prob), ctypes.byref(plan)))
     return plan

@@ -230,6 +230,7 @@ __device__ __forceinline__ GemmArgs uniform_args(const GemmArgs& in) {
   a.partials = uniform_ptr(in.partials);
   a.split_flags = uniform_ptr(in.split_flags);
   a.max_split = uniform_int(in.max_split);
+  a.clamp = __builtin_bit_cast(float, uniform_int(__builtin_bit_cast(int, in.clamp)));
   a.spin_limit = (uint32_t)uniform_int((int)in.spin_limit);
   return a;
 }
@@ -795,6 +796,9 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
                 g = (g * cs0[j]) * sx;
                 u = (u * cs1[j]) * sx;
               }
+              // the operator's activation_clamp (+inf: none; identity on finite H)
+              g = __builtin_amdgcn_fmed3f(g, -a.clamp, a.clamp);
+              u = __builtin_amdgcn_fmed3f(u, -a.clamp, a.clamp);
               const float v = silu(g) * u;
               if (r < cur.valid) {
                 if constexpr (UC == UC_BF16) gp(obase)[oc] = f32_to_bf16_bits(v);

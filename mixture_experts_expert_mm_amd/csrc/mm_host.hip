@@ -2,6 +2,7 @@
 // kernel timing.  No entry point allocates, frees or synchronises.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstddef>
 #include <cstdlib>
 #include <cstring>
@@ -248,6 +249,7 @@ GemmArgs l1_args(const mm_plan& pl, const int32_t* offsets, const int32_t* count
   g.H = (int)p.hidden;
   g.K = (int)p.num_topk;
   g.gate_up_group = pl.gate_up_group;
+  g.clamp = p.clamp_activation ? p.activation_clamp : INFINITY;
   g.routes = p.num_tokens * p.num_topk;
   g.err = at<uint32_t>(ws, L.ctl) + 1;
   g.x_scale = x_pool_scale;
@@ -367,6 +369,8 @@ mm_status mm_plan_create(const mm_problem* problem, mm_plan* plan) {
   const mm_problem p = *problem;
   if (p.usecase < MM_A16W16 || p.usecase > MM_A8W8_INT8) return MM_ERR_UNSUPPORTED;
   if (p.y_dtype != MM_OUT_BF16 && p.y_dtype != MM_OUT_F32) return MM_ERR_UNSUPPORTED;
+  if (p.clamp_activation != 0 && p.clamp_activation != 1) return MM_ERR_INVALID_ARG;
+  if (p.clamp_activation && !(p.activation_clamp >= 0.0f)) return MM_ERR_INVALID_ARG;   // negative or NaN
   if (p.num_tokens < 1 || p.num_tokens > (1 << 24)) return MM_ERR_INVALID_ARG;
   if (p.hidden < 256 || p.hidden > 16384 || p.hidden % 256) return MM_ERR_INVALID_ARG;
   if (p.intermediate_hidden < 128 || p.intermediate_hidden > 16384 || p.intermediate_hidden % 128)

@@ -69,6 +69,7 @@ struct GemmArgs {
   uint32_t* partials;        // [kSplitSlots][BM*BN] words
   uint32_t* split_flags;     // [kSplitSlots], zero between calls
   int max_split;             // largest K split of a tail tile (<= 1: none)
+  float clamp;               // Linear1: H clamped to [-clamp, clamp] before SwiGLU (+inf: none)
   uint32_t spin_limit;       // polls before a wait for a partial gives up
 };
 

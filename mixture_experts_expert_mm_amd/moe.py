@@ -29,12 +29,12 @@ class Intermediates:
 
 
 class ExpertLayer:
-    def __init__(self, T, H, I, E, K, usecase="bf16", y_dtype="bf16", device="cuda"):
+    def __init__(self, T, H, I, E, K, usecase="bf16", y_dtype="bf16", device="cuda", activation_clamp=None):
         self.T, self.H, self.I, self.E, self.K = T, H, I, E, K
         self.usecase = usecase
         self.y_dtype = y_dtype
         self.device = torch.device(device)
-        self.plan = B.mm_plan_create(T, H, I, E, K, usecase, y_dtype)
+        self.plan = B.mm_plan_create(T, H, I, E, K, usecase, y_dtype, activation_clamp)
         self.w1 = self.w2 = self.s1 = self.s2 = None
         self._ws = None
         self._fused_ws = None

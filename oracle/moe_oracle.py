@@ -231,7 +231,7 @@ def _expert_f64(expert, e, usecase):
 
 
 def moe_forward(x_f32, topk_ids, topk_weights, expert, usecase: str,
-                tokens=None, requant_fp32: bool = False):
+                tokens=None, requant_fp32: bool = False, activation_clamp=None):
     """y_i = sum_k G[i,k] * SwiGLU-FFN_{E[i,k]}(x_i), float64.
 
     [ASC] Computation Process: EP Dispatch groups the tokens per expert,
@@ -246,7 +246,10 @@ def moe_forward(x_f32, topk_ids, topk_weights, expert, usecase: str,
     uint8) and per-channel scales.  ``tokens`` optionally restricts the
     result to those token indices (rows are independent, so each is the same
     as in the full computation).  Returns ``(y float64 [T or len(tokens), H],
-    counts)``.
+    counts)``.  ``activation_clamp`` (None or c >= 0): [ASC] Parameters,
+    activation_clamp — the activation function's input, the whole Linear1
+    output H (gate and up halves, after dequantisation), is clamped to
+    [-c, c] before SwiGLU.
 
     Rows are grouped per expert and multiplied with float64 BLAS, which
     changes no definition: every GEMM row is independent of the others.
@@ -285,11 +288,15 @@ def moe_forward(x_f32, topk_ids, topk_weights, expert, usecase: str,
         if usecase == "bf16":
             xe = x[i].astype(np.float64)
             h = xe @ w1
+            if activation_clamp is not None:
+                h = np.clip(h, -activation_clamp, activation_clamp)
             a = bf16_round(swiglu(h))
             o = a @ w2
         else:
             c = xin_sub[rows] @ w1
             h = (c * s1[None, :]) * sx_sub[rows].astype(np.float64)[:, None]
+            if activation_clamp is not None:
+                h = np.clip(h, -activation_clamp, activation_clamp)
             a = swiglu(h)
             aq, sa = requantize_rows(a, usecase, emulate_fp32=requant_fp32)
             d = aq @ w2
@@ -298,7 +305,7 @@ def moe_forward(x_f32, topk_ids, topk_weights, expert, usecase: str,
     return y, counts
 
 
-def moe_forward_bruteforce(x_f32, topk_ids, topk_weights, expert, usecase: str):
+def moe_forward_bruteforce(x_f32, topk_ids, topk_weights, expert, usecase: str, activation_clamp=None):
     """Literal per-token, per-slot scalar loops (tiny inputs only).
 
     Follows [ASC] Computation Process one scalar at a time: for token i and
@@ -334,6 +341,8 @@ def moe_forward_bruteforce(x_f32, topk_ids, topk_weights, expert, usecase: str):
                     acc += xv * float(w1[j, c])
                 if usecase != "bf16":
                     acc = acc * float(s1[c]) * float(sx[i])
+                if activation_clamp is not None:
+                    acc = min(float(activation_clamp), max(-float(activation_clamp), acc))
                 h.append(acc)
             a = []
             for c in range(inter):

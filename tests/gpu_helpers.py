@@ -42,9 +42,9 @@ def expert_fn(inp: wl.Inputs):
     return expert
 
 
-def make_layer(inp: wl.Inputs, y_dtype="f32"):
+def make_layer(inp: wl.Inputs, y_dtype="f32", activation_clamp=None):
     c = inp.cfg
-    layer = moe.ExpertLayer(c.T, c.H, c.I, c.E, c.K, c.usecase, y_dtype, "cuda")
+    layer = moe.ExpertLayer(c.T, c.H, c.I, c.E, c.K, c.usecase, y_dtype, "cuda", activation_clamp=activation_clamp)
     layer.load_weights(inp.weights.w1, inp.weights.w2, inp.weights.s1, inp.weights.s2)
     return layer
 
@@ -53,9 +53,9 @@ def device_inputs(inp: wl.Inputs):
     return inp.x.cuda(), inp.topk_ids.cuda(), inp.topk_weights.cuda()
 
 
-def oracle_y(inp: wl.Inputs, tokens=None):
+def oracle_y(inp: wl.Inputs, tokens=None, activation_clamp=None):
     y, _ = oracle.moe_forward(inp.x.float().numpy(), inp.topk_ids.numpy(), inp.topk_weights.numpy(),
-                              expert_fn(inp), inp.cfg.usecase, tokens=tokens)
+                              expert_fn(inp), inp.cfg.usecase, tokens=tokens, activation_clamp=activation_clamp)
     return y
 
 

@@ -42,9 +42,9 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_struct_sizes_match_header():
-    # mm_problem: 5 int64 + 2 int32; mm_plan: problem + 4 int32 + 7 int64 + u64 + 8 int64
-    assert ctypes.sizeof(B.MMProblem) == 48
-    assert ctypes.sizeof(B.MMPlan) == 48 + 16 + 56 + 8 + 64
+    # mm_problem: 5 int64 + 3 int32 + float; mm_plan: problem + 4 int32 + 7 int64 + u64 + 8 int64
+    assert ctypes.sizeof(B.MMProblem) == 56
+    assert ctypes.sizeof(B.MMPlan) == 56 + 16 + 56 + 8 + 64
 
 
 def test_plan_sizes_and_block_m():
@@ -74,6 +74,21 @@ def test_plan_rejects_bad_dimensions(dims):
     with pytest.raises(B.MMError) as ei:
         B.mm_plan_create(*dims, "bf16")
     assert ei.value.status == 1
+
+
+@pytest.mark.parametrize("flag,clamp", [(1, -0.5), (1, float("nan")), (2, 1.0)])
+def test_plan_rejects_bad_activation_clamp(flag, clamp):
+    lib = _lib()
+    prob = B.MMProblem(64, 256, 128, 8, 2, B.MM_A16W16, B.MM_OUT_BF16, flag, clamp)
+    plan = B.MMPlan()
+    assert lib.mm_plan_create(ctypes.byref(prob), ctypes.byref(plan)) == 1   # MM_ERR_INVALID_ARG
+
+
+def test_plan_accepts_activation_clamp():
+    _lib()
+    for c in (None, 0.0, 2.5):
+        plan = B.mm_plan_create(64, 256, 128, 8, 2, "bf16", activation_clamp=c)
+        assert plan.prob.clamp_activation == (0 if c is None else 1)
 
 
 def test_plan_rejects_unknown_usecase():

@@ -253,6 +253,32 @@ def test_fused_one_block_dispatch_boundary(T, E, block_m, usecase):
 
 
 @pytest.mark.parametrize("usecase", ["bf16", "fp8", "int8"])
+@pytest.mark.parametrize("shape", ["bm64", "bm128"])
+def test_activation_clamp(shape, usecase):
+    """The operator's activation_clamp: H (both halves, after dequantisation)
+    clamped to [-c, c] before SwiGLU.  With c small enough to clip most of H
+    (|H| is about 1 here), Y matches the oracle with the same clamp, differs
+    from the unclamped Y by far more than the tolerance, and fused ==
+    three-call."""
+    cfg = small_cfg(shape, usecase)
+    inp = wl.make_inputs(cfg)
+    x, ids, wts = device_inputs(inp)
+    c = 0.3
+    layer = make_layer(inp, "f32", activation_clamp=c)
+    log(f"[clamp] {cfg.name}: c = {c}")
+    y_f, _ = layer.forward(x, ids, wts)
+    y_3, _ = layer.forward_3call(x, ids, wts)
+    torch.cuda.synchronize()
+    assert layer.device_error(fused=True) == 0 and layer.device_error(fused=False) == 0
+    assert torch.equal(y_f.view(torch.int32), y_3.view(torch.int32))
+    y_or = oracle_y(inp, activation_clamp=c)
+    err = rel_err(y_f.cpu().double().numpy(), y_or)
+    log(f"    max|dY|/rms = {err:.3e}")
+    assert err <= TOL[usecase], err
+    assert rel_err(oracle_y(inp), y_or) > 10 * TOL[usecase]
+
+
+@pytest.mark.parametrize("usecase", ["bf16", "fp8", "int8"])
 def test_fused_deterministic_with_experts_of_several_m_blocks(usecase):
     """Experts of about 500 routes (four M-blocks each, tail tiles in every
     GEMM): the dispatch's atomics place a route in any M-block of its expert,

@@ -248,6 +248,26 @@ def test_forward_matches_bruteforce(usecase, masked):
     np.testing.assert_array_equal(ys, y[[3, 0]])
 
 
+@pytest.mark.parametrize("usecase", ["bf16", "int8", "fp8"])
+def test_activation_clamp(usecase):
+    """[ASC] Parameters, activation_clamp: the literal scalar loops with the
+    clamp agree with the grouped oracle; a clamp at or above max|H| changes
+    nothing; c = 0 makes every SwiGLU output, so Y, zero; and a small clamp
+    does change Y (so the clamp is applied at all)."""
+    cfg, x, ids, wts, expert = _tiny_problem(usecase, masked=True)
+    y0, _ = oracle.moe_forward(x, ids, wts, expert, usecase)
+    scale = np.sqrt(np.mean(y0 ** 2))
+    for c in (0.05, 0.3):
+        y, _ = oracle.moe_forward(x, ids, wts, expert, usecase, activation_clamp=c)
+        yb = oracle.moe_forward_bruteforce(x, ids, wts, expert, usecase, activation_clamp=c)
+        np.testing.assert_allclose(y, yb, rtol=0, atol=1e-12 * scale)
+        assert np.abs(y - y0).max() > 1e-3 * scale
+    y_big, _ = oracle.moe_forward(x, ids, wts, expert, usecase, activation_clamp=1e30)
+    np.testing.assert_array_equal(y_big, y0)
+    y_zero, _ = oracle.moe_forward(x, ids, wts, expert, usecase, activation_clamp=0.0)
+    assert np.all(y_zero == 0.0)
+
+
 def test_topk1_unit_gate_is_dense_swiglu_ffn():
     """K = 1, g = 1: every token passes through one dense SwiGLU FFN (torch reference)."""
     rng = np.random.default_rng(7)
