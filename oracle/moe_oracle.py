@@ -10,7 +10,7 @@ Sources, cited by page title and section:
   Section 1 (Count -> Prefix Sum -> Scatter), section 3.5 (pool block
   offset), section 5.2 (masked routes).
 * [DG]  "DeepGEMM MegaMoE: Fused Communication and Expert Compute".
-  Section 2 (token identities).
+  Section 2 (token identities), section 6 (optional shared experts).
 
 Readings taken where the pages are silent or ambiguous (each one is listed
 with its reason in the design notes of the repository):
@@ -25,7 +25,13 @@ with its reason in the design notes of the repository):
   are the same on both sides;
 * the Linear2 operand A is rounded to the Linear's activation dtype of the
   use case table (bf16 for A16W16);
-* route ids < 0 are masked: skipped, counted nowhere, contribute 0 ([MD] 5.2).
+* route ids < 0 are masked: skipped, counted nowhere, contribute 0 ([MD] 5.2);
+* a token whose x_active_mask entry is 0 ([ASC] Parameters: the token does
+  not take part in the communication) sends nothing to any expert, routed or
+  shared, so its output row is 0;
+* a shared expert ([DG] section 6: an always-local MLP on every token, its
+  output in the extra combine slot num_topk, summed with the routed slots)
+  enters with weight 1, after the routed slots.
 """
 
 from __future__ import annotations
@@ -230,8 +236,29 @@ def _expert_f64(expert, e, usecase):
     return w1, w2, s1, s2
 
 
+def _route_table(topk_ids, topk_weights, shared_expert, active):
+    """Routes of every token as ``(ids [T, K+S], weights [T, K+S])``.
+
+    The K routed slots come first; with ``shared_expert`` (an expert index)
+    every token gets one more slot on that expert with weight 1 ([DG]
+    section 6).  Tokens with ``active[i] == 0`` get id -1 in every slot
+    ([ASC] Parameters, x_active_mask).
+    """
+    ids = np.asarray(topk_ids).astype(np.int64)
+    g = np.asarray(topk_weights, dtype=np.float64)
+    T = ids.shape[0]
+    if shared_expert is not None:
+        ids = np.concatenate([ids, np.full((T, 1), int(shared_expert), dtype=np.int64)], axis=1)
+        g = np.concatenate([g, np.ones((T, 1))], axis=1)
+    if active is not None:
+        on = np.asarray(active).reshape(-1) != 0
+        ids = np.where(on[:, None], ids, -1)
+    return ids, g
+
+
 def moe_forward(x_f32, topk_ids, topk_weights, expert, usecase: str,
-                tokens=None, requant_fp32: bool = False, activation_clamp=None):
+                tokens=None, requant_fp32: bool = False, activation_clamp=None,
+                shared_expert=None, active=None):
     """y_i = sum_k G[i,k] * SwiGLU-FFN_{E[i,k]}(x_i), float64.
 
     [ASC] Computation Process: EP Dispatch groups the tokens per expert,
@@ -251,14 +278,19 @@ def moe_forward(x_f32, topk_ids, topk_weights, expert, usecase: str,
     output H (gate and up halves, after dequantisation), is clamped to
     [-c, c] before SwiGLU.
 
+    ``shared_expert`` (None or an expert index): every token also goes
+    through that expert with weight 1 ([DG] section 6).  ``active`` (None or
+    [T]): tokens whose entry is 0 contribute nothing, their rows of y are 0
+    ([ASC] Parameters, x_active_mask).  The returned counts cover every
+    expert index used, the shared expert's included.
+
     Rows are grouped per expert and multiplied with float64 BLAS, which
     changes no definition: every GEMM row is independent of the others.
     The float64 sum over the top-k slots is independent of order at the
     tolerances used.
     """
     x = np.asarray(x_f32, dtype=np.float32)
-    ids = np.asarray(topk_ids).astype(np.int64)
-    g = np.asarray(topk_weights, dtype=np.float64)
+    ids, g = _route_table(topk_ids, topk_weights, shared_expert, active)
     T, K = ids.shape
     if tokens is None:
         tok = np.arange(T)
@@ -305,7 +337,8 @@ def moe_forward(x_f32, topk_ids, topk_weights, expert, usecase: str,
     return y, counts
 
 
-def moe_forward_bruteforce(x_f32, topk_ids, topk_weights, expert, usecase: str, activation_clamp=None):
+def moe_forward_bruteforce(x_f32, topk_ids, topk_weights, expert, usecase: str, activation_clamp=None,
+                           shared_expert=None, active=None):
     """Literal per-token, per-slot scalar loops (tiny inputs only).
 
     Follows [ASC] Computation Process one scalar at a time: for token i and
@@ -313,6 +346,8 @@ def moe_forward_bruteforce(x_f32, topk_ids, topk_weights, expert, usecase: str, 
     SiLU(h_c) * h_{I+c}; o_n = sum_c a_c W2[e][c,n]; y_in += G[i,k] o_n.
     Quantised use cases take the quantised tokens, dequantise h per element,
     requantise a per route with its own amax, and dequantise o per element.
+    An inactive token (active[i] == 0) is skipped whole; a shared expert is
+    one more slot after the routed ones, with weight 1.
     """
     x = np.asarray(x_f32, dtype=np.float32)
     ids = np.asarray(topk_ids).astype(np.int64)
@@ -324,8 +359,12 @@ def moe_forward_bruteforce(x_f32, topk_ids, topk_weights, expert, usecase: str, 
     y = [[0.0] * H for _ in range(T)]
     cache = {}
     for i in range(T):
-        for k in range(K):
-            e = int(ids[i, k])
+        if active is not None and int(np.asarray(active).reshape(-1)[i]) == 0:
+            continue
+        slots = [(int(ids[i, k]), float(g[i, k])) for k in range(K)]
+        if shared_expert is not None:
+            slots.append((int(shared_expert), 1.0))
+        for e, gw in slots:
             if e < 0:
                 continue
             if e not in cache:
@@ -364,5 +403,5 @@ def moe_forward_bruteforce(x_f32, topk_ids, topk_weights, expert, usecase: str, 
                     acc += a[c] * float(w2[c, n])
                 if usecase != "bf16":
                     acc = acc * float(s2[n]) * sa
-                y[i][n] += float(g[i, k]) * acc
+                y[i][n] += gw * acc
     return np.array(y, dtype=np.float64)
