@@ -25,6 +25,7 @@ from .moe_oracle import (  # noqa: F401
     quantize_tokens,
     requantize_rows,
     dispatch_layout,
+    route_table,
     moe_forward,
     moe_forward_bruteforce,
 )

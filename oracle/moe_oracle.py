@@ -219,14 +219,25 @@ def dispatch_layout(topk_ids: np.ndarray, num_experts: int, block_m: int):
 # forward
 # --------------------------------------------------------------------------
 
+def _e4m3_table() -> np.ndarray:
+    """float64 value of each of the 256 e4m3fn codes (``e4m3_decode`` itself)."""
+    return e4m3_decode(np.arange(256, dtype=np.uint8))
+
+
 def _expert_f64(expert, e, usecase):
-    """Decode expert ``e`` to float64 ``(W1 [H,2I], W2 [I,H], s1, s2)``."""
+    """Decode expert ``e`` to float64 ``(W1 [H,2I], W2 [I,H], s1, s2)``.
+
+    e4m3 weights are decoded by looking each code up in the 256 values
+    ``e4m3_decode`` gives for the 256 codes: the same values, without
+    re-deriving the format for every one of the H*3I weights.
+    """
     w1, w2, s1, s2 = expert(e)
     w1 = np.asarray(w1)
     w2 = np.asarray(w2)
     if usecase == "fp8":
-        w1 = e4m3_decode(w1.view(np.uint8))
-        w2 = e4m3_decode(w2.view(np.uint8))
+        table = _e4m3_table()
+        w1 = table[w1.view(np.uint8)]
+        w2 = table[w2.view(np.uint8)]
     else:
         w1 = w1.astype(np.float64)
         w2 = w2.astype(np.float64)
@@ -236,7 +247,7 @@ def _expert_f64(expert, e, usecase):
     return w1, w2, s1, s2
 
 
-def _route_table(topk_ids, topk_weights, shared_expert, active):
+def route_table(topk_ids, topk_weights, shared_expert=None, active=None):
     """Routes of every token as ``(ids [T, K+S], weights [T, K+S])``.
 
     The K routed slots come first; with ``shared_expert`` (an expert index)
@@ -290,7 +301,7 @@ def moe_forward(x_f32, topk_ids, topk_weights, expert, usecase: str,
     tolerances used.
     """
     x = np.asarray(x_f32, dtype=np.float32)
-    ids, g = _route_table(topk_ids, topk_weights, shared_expert, active)
+    ids, g = route_table(topk_ids, topk_weights, shared_expert, active)
     T, K = ids.shape
     if tokens is None:
         tok = np.arange(T)
