@@ -4,14 +4,18 @@
 One step = one ``mega_moe`` call (dispatch -> Linear1 + SwiGLU -> Linear2 ->
 combine, one persistent kernel after a zeroing pre-pass) over one batch of
 seeded synthetic inputs already resident in HBM.  The default workload is
-the mid-size bf16 layer (T=2048, hidden=4096, intermediate=1408, 16 experts,
-top-4).
+the A8W8 fp8 layer at 16384 tokens (hidden 7168, intermediate 2048, 32
+experts, top-8): the MFMA-bound point.  The same run also times the same
+layer at 128 tokens (the HBM-bound, weight-streaming point) and reports it
+under "hbm_point".
 
 Prints one JSON line: throughput in TFLOP/s (FLOP = 6 * routes * hidden *
 intermediate), the roofline of the dominant kernel (the fused kernel, timed
-with HIP events on its stream inside the timed region), a per-phase
-breakdown from the three-call path, and the CPU oracle timed on a bounded
-sample of the same workload.
+with HIP events on its stream inside the timed region) against the
+datasheet peak, against the MFMA peak at the shader clock the kernel ran at
+(sampled inside the kernel) and against a measured device-copy bandwidth, a
+per-phase breakdown from the three-call path, and the CPU oracle timed on a
+bounded sample of the same workload.
 """
 
 from __future__ import annotations
@@ -36,12 +40,18 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="mid_bf16")
+    ap.add_argument("--workload", default="dsv3_fp8_t16384")
+    ap.add_argument("--hbm-workload", default="dsv3_fp8_t128",
+                    help="weight-streaming point timed in the same run ('' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-phases", action="store_true", help="skip the three-call per-kernel breakdown")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU oracle time")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one plain 1 GiB device copy (counter calibration) and exit")
     return ap.parse_args()
+
+
+CLOCK_DATASHEET_HZ = 2.4e9   # the MI355X peak clock the datasheet peaks assume
 
 
 def algorithmic(cfg, counts):
@@ -92,6 +102,26 @@ def measured_traffic(workload, kernel="mega"):
     return None if ent is None else ent["traffic_bytes"]
 
 
+def copy_bandwidth(dev, nbytes=1 << 30, reps=10):
+    """Read + write bytes per second of a plain device-to-device copy."""
+    import torch
+    a = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    a.fill_(1)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b
+    torch.cuda.empty_cache()
+    return 2 * nbytes / (ms * 1e-3), ms
+
+
 def phase_breakdown(layer, x, ids, wts, steps):
     """Per-kernel milliseconds of the three-call path (same device code as
     the phases of the fused kernel), averaged over `steps` calls."""
@@ -113,7 +143,94 @@ def phase_breakdown(layer, x, ids, wts, steps):
     torch.cuda.synchronize()
     B.mm_trace_enable(False)
     tr = B.mm_trace_collect()
+    del im, y
+    layer._ws = None
+    torch.cuda.empty_cache()
     return {k: v[1] / steps for k, v in tr.items() if v[0]}
+
+
+def time_layer(cfg, dev, steps, warmup, with_phases):
+    """Build the layer of `cfg`, warm up, time `steps` mega_moe calls.
+
+    Returns the measurements and the inputs.  The fused kernel's duration
+    comes from HIP events recorded around each of its launches on its stream
+    inside the timed region; the clock from its own clock sample.
+    """
+    import torch
+    from mixture_experts_expert_mm_amd import binding as B
+    from mixture_experts_expert_mm_amd import moe
+    from mixture_experts_expert_mm_amd import workloads as wl
+    inp = wl.make_inputs(cfg)
+    layer = moe.ExpertLayer(cfg.T, cfg.H, cfg.I, cfg.E, cfg.K, cfg.usecase, "bf16", dev)
+    layer.load_weights(inp.weights.w1, inp.weights.w2, inp.weights.s1, inp.weights.s2)
+    x, ids, wts = inp.x.to(dev), inp.topk_ids.to(dev), inp.topk_weights.to(dev)
+    y = layer.new_y()
+    counts = torch.empty(cfg.E, dtype=torch.int32, device=dev)
+    layer.workspace(True)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(warmup):
+        layer.forward(x, ids, wts, y, counts)
+    torch.cuda.synchronize()
+    B.mm_trace_collect()
+    B.mm_trace_enable(True)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(steps):
+        layer.forward(x, ids, wts, y, counts)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    B.mm_trace_enable(False)
+    trace = B.mm_trace_collect()
+    clocks, ticks = B.mm_read_kernel_clock(layer.plan, layer.workspace(True))
+    n_k, t_k = trace["mega"]
+    res = dict(ms_per_step=ev0.elapsed_time(ev1) / steps, wall=wall, kernel_ms=t_k / max(n_k, 1),
+               kernels={k: v[1] / steps for k, v in trace.items() if v[0]},
+               clock_hz=(clocks / ticks * 100e6) if ticks > 0 else None, counts=counts.cpu().numpy())
+    if with_phases:
+        res["phases"] = phase_breakdown(layer, x, ids, wts, max(2, min(steps, 10)))
+    del layer, x, ids, wts, y
+    torch.cuda.empty_cache()
+    return res, inp
+
+
+def roofline(cfg, res, copy_bps):
+    """Roofline of the fused kernel: bound by MFMA when the step's arithmetic
+    intensity is above the dtype's ridge, else by HBM."""
+    al = algorithmic(cfg, res["counts"])
+    k_s = res["kernel_ms"] * 1e-3
+    peak_mfma = PEAK[cfg.usecase]
+    if al["flop"] / al["step_bytes"] > peak_mfma / PEAK["hbm"]:
+        ach = al["flop"] / k_s
+        roof = {"bound": "mfma", "achieved": ach / 1e12, "peak": peak_mfma / 1e12, "unit": "TFLOP/s",
+                "frac": ach / peak_mfma, "traffic": None}
+        if res["clock_hz"]:
+            roof["frac_vs_clock_peak"] = ach / (peak_mfma * res["clock_hz"] / CLOCK_DATASHEET_HZ)
+    else:
+        ach = al["step_bytes"] / k_s
+        roof = {"bound": "hbm", "achieved": ach / 1e9, "peak": PEAK["hbm"] / 1e9, "unit": "GB/s",
+                "frac": ach / PEAK["hbm"], "traffic": None}
+        roof["frac_vs_copy"] = ach / copy_bps
+    roof["traffic"] = measured_traffic(cfg.name)
+    roof["algorithmic_bytes"] = al["step_bytes"]
+    roof["algorithmic_flop"] = al["flop"]
+    roof["kernel"] = "mega (fused persistent kernel: dispatch, Linear1 + SwiGLU, Linear2, combine)"
+    roof["kernel_ms"] = res["kernel_ms"]
+    roof["shader_clock_ghz"] = None if res["clock_hz"] is None else res["clock_hz"] / 1e9
+    return roof, al
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(inp, target_s):
@@ -149,10 +266,12 @@ def cpu_baseline(inp, target_s):
         n = min(cfg.T, max(n * 2, int(n * target_s / max(elapsed, 1e-3) / 2)))
     R = int(np.sum(ids[toks] >= 0))
     flop = 6.0 * R * cfg.H * cfg.I
-    threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
-    return {"value": flop / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{n} of {cfg.T} tokens ({R} routes), float64 numpy/BLAS, {elapsed:.1f} s",
-            "tokens_per_s": n / elapsed}
+    blas = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+    return {"value": flop / elapsed / 1e12, "unit": "TFLOP/s", "cores": len(os.sched_getaffinity(0)),
+            "kind": "oracle",
+            "sample": f"{n} of {cfg.T} tokens ({R} routes), float64 numpy/BLAS, {elapsed:.1f} s "
+                      f"(includes decoding the experts' weights)",
+            "blas_threads": int(blas), "cpu_model": cpu_model(), "tokens_per_s": n / elapsed}
 
 
 def main():
@@ -161,85 +280,25 @@ def main():
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (the expert path here "
               f"runs with all experts local on a single MI355X).", file=sys.stderr)
         sys.exit(2)
-    import numpy as np
     import torch
     from mixture_experts_expert_mm_amd import binding as B
-    from mixture_experts_expert_mm_amd import moe
     from mixture_experts_expert_mm_amd import workloads as wl
 
     B.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.copy_calibration:
-        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        b = torch.empty_like(a)
-        a.fill_(1)
-        torch.cuda.synchronize()
-        b.copy_(a)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(10):
-            b.copy_(a)
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / 10
-        print(json.dumps({"copy_bytes": 1 << 30, "copy_ms": ms,
-                          "copy_GBps_read_plus_write": 2 * (1 << 30) / (ms * 1e-3) / 1e9}))
+        bps, ms = copy_bandwidth(dev)
+        print(json.dumps({"copy_bytes": 1 << 30, "copy_ms": ms, "copy_GBps_read_plus_write": bps / 1e9}))
         return
+    copy_bps, _ = copy_bandwidth(dev)
 
     cfg = wl.CONFIGS[args.workload]
-    inp = wl.make_inputs(cfg)
-    layer = moe.ExpertLayer(cfg.T, cfg.H, cfg.I, cfg.E, cfg.K, cfg.usecase, "bf16", dev)
-    layer.load_weights(inp.weights.w1, inp.weights.w2, inp.weights.s1, inp.weights.s2)
-    x, ids, wts = inp.x.to(dev), inp.topk_ids.to(dev), inp.topk_weights.to(dev)
-    y = layer.new_y()
-    counts = torch.empty(cfg.E, dtype=torch.int32, device=dev)
-    layer.workspace(True)
-    stream = torch.cuda.current_stream(dev)
-
-    for _ in range(args.warmup):
-        layer.forward(x, ids, wts, y, counts)
-    torch.cuda.synchronize()
-
-    B.mm_trace_enable(True)
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        layer.forward(x, ids, wts, y, counts)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    B.mm_trace_enable(False)
-    trace = B.mm_trace_collect()
-    gpu_ms = ev0.elapsed_time(ev1)
-    ms_per_step = gpu_ms / args.steps
-
-    al = algorithmic(cfg, counts.cpu().numpy())
+    res, inp = time_layer(cfg, dev, args.steps, args.warmup, not args.no_phases)
+    roof, al = roofline(cfg, res, copy_bps)
+    ms_per_step = res["ms_per_step"]
     tflops = al["flop"] / (ms_per_step * 1e-3) / 1e12
-    n_k, t_k = trace["mega"]
-    k_ms = t_k / max(n_k, 1)
     peak_mfma = PEAK[cfg.usecase]
-    # the fused kernel does the whole step: its algorithmic work is the step's
-    mfma_bound = al["flop"] / al["step_bytes"] > peak_mfma / PEAK["hbm"]
-    if mfma_bound:
-        ach = al["flop"] / (k_ms * 1e-3)
-        roof = {"bound": "mfma", "achieved": ach / 1e12, "peak": peak_mfma / 1e12, "unit": "TFLOP/s",
-                "frac": ach / peak_mfma, "traffic": None}
-    else:
-        ach = al["step_bytes"] / (k_ms * 1e-3)
-        roof = {"bound": "hbm", "achieved": ach / 1e9, "peak": PEAK["hbm"] / 1e9, "unit": "GB/s",
-                "frac": ach / PEAK["hbm"], "traffic": None}
-    roof["traffic"] = measured_traffic(cfg.name)
-    roof["algorithmic_bytes"] = al["step_bytes"]
-    roof["algorithmic_flop"] = al["flop"]
-    roof["kernel"] = "mega (fused persistent kernel: dispatch, Linear1 + SwiGLU, Linear2, combine)"
-    roof["kernel_ms"] = k_ms
-    phases = phase_breakdown(layer, x, ids, wts, max(2, min(args.steps, 10)))
-
     out = {
         "metric": METRIC,
         "value": tflops,
@@ -254,15 +313,30 @@ def main():
         "dtype": {"bf16": "bf16", "fp8": "fp8_e4m3", "int8": "int8"}[cfg.usecase],
         "data": "synthetic (seeded randn tokens and weights, top-k of randn router scores)",
         "config": {"workload": cfg.name, "tokens": cfg.T, "hidden": cfg.H, "intermediate_hidden": cfg.I,
-                   "num_experts": cfg.E, "topk": cfg.K, "usecase": cfg.usecase, "parallelism": "none (1 GPU, all experts local)"},
+                   "num_experts": cfg.E, "topk": cfg.K, "usecase": cfg.usecase,
+                   "parallelism": "none (1 GPU, all experts local)"},
         "tokens_per_s": cfg.T / (ms_per_step * 1e-3),
         "hbm_frac_step": al["step_bytes"] / (ms_per_step * 1e-3) / PEAK["hbm"],
         "mfma_frac_step": al["flop"] / (ms_per_step * 1e-3) / peak_mfma,
-        "wall_s_timed": wall,
-        "kernels_ms_per_step": {k: v[1] / args.steps for k, v in trace.items() if v[0]},
-        "three_call_phases_ms": phases,
+        "hbm_copy_GBps": copy_bps / 1e9,
+        "wall_s_timed": res["wall"],
+        "kernels_ms_per_step": res["kernels"],
+        "three_call_phases_ms": res.get("phases"),
         "roofline": roof,
     }
+    if args.hbm_workload:
+        hcfg = wl.CONFIGS[args.hbm_workload]
+        hres, _ = time_layer(hcfg, dev, max(args.steps, 20), args.warmup, False)
+        hroof, hal = roofline(hcfg, hres, copy_bps)
+        out["hbm_point"] = {
+            "workload": hcfg.name, "tokens": hcfg.T, "usecase": hcfg.usecase,
+            "ms_per_step": hres["ms_per_step"],
+            "tokens_per_s": hcfg.T / (hres["ms_per_step"] * 1e-3),
+            "TFLOP_s": hal["flop"] / (hres["ms_per_step"] * 1e-3) / 1e12,
+            "hbm_frac_step": hal["step_bytes"] / (hres["ms_per_step"] * 1e-3) / PEAK["hbm"],
+            "kernels_ms_per_step": hres["kernels"],
+            "roofline": hroof,
+        }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
     print(json.dumps(out))

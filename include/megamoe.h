@@ -14,7 +14,16 @@
  * (token, top-k slot) identity of every row, sections 1, 3 and 4).
  *
  * Symbols: T = num_tokens, H = hidden, I = intermediate_hidden,
- * E = num_experts, K = num_topk, P = plan.pool_rows.
+ * E = num_experts, K = num_topk, S = num_shared_experts (0 or 1),
+ * P = plan.pool_rows.
+ *
+ * Shared expert (DeepGEMM MegaMoE page, section 6 "Optional Shared
+ * Experts"): with S = 1 every active token also goes through one always-local
+ * SwiGLU FFN, expert index E in the weight arrays, whose output is added
+ * after the K routed contributions (combine slot K) with weight 1:
+ *     y_i = sum_k G[i,k] * FFN_{E[i,k]}(x_i) + FFN_E(x_i).
+ * Internally a token then has K + S slots; route r = i*(K+S) + k names slot
+ * k of token i, k = K being the shared expert's.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -36,11 +45,15 @@
  *   expert and contributes 0.  An id >= E is skipped the same way and sets
  *   MM_DEVERR_BAD_EXPERT in the workspace error word (mm_read_device_error);
  *   duplicated ids are not detected and give undefined results.
+ * - x_active_mask (operator page, Parameters: whether a token takes part in
+ *   the layer's communication): device int8 [T] or NULL (every token
+ *   active).  A token whose entry is 0 dispatches no route (routed or
+ *   shared), is counted for no expert, and its row of y is 0.
  * - Workspace counters are reset by the library at the start of every
  *   call; the caller never clears them.
  * - Calls that share a workspace or intermediate buffers must be ordered
  *   on one stream; overlapping calls on the same buffers race.
- * - Results are deterministic: the top-k sum runs in slot order k = 0..K-1
+ * - Results are deterministic: the top-k sum runs in slot order k = 0..K+S-1
  *   in float32 (operator page, "Deterministic Computation"), and a route's
  *   result depends on its own pool row alone, not on where in its expert's
  *   range the dispatch placed it.  (Setting MM_MAX_SPLIT above 1 for the
@@ -93,6 +106,10 @@ typedef struct mm_problem {
    * clamp, activation_clamp ignored.  Other values: MM_ERR_INVALID_ARG. */
   int32_t clamp_activation;
   float activation_clamp;
+  /* S: 0, or 1 for one shared expert (index E of the weight arrays, which
+   * then hold E + 1 experts); K + S <= 64 and E + S <= 1024. */
+  int32_t num_shared_experts;
+  int32_t reserved0;          /* must be 0 */
 } mm_problem;
 
 /* A plan is plain host data filled by mm_plan_create.  Callers read the
@@ -106,8 +123,8 @@ typedef struct mm_plan {
   int64_t pool_rows;          /* P = capacity of the padded pool, a multiple of block_m */
   int64_t x_pool_bytes;       /* P * H * elem(usecase) */
   int64_t a_pool_bytes;       /* P * I * elem(usecase) */
-  int64_t w1_bytes;           /* E * H * 2I * elem(usecase) (formula and prepared) */
-  int64_t w2_bytes;           /* E * I * H * elem(usecase) */
+  int64_t w1_bytes;           /* (E+S) * H * 2I * elem(usecase) (formula and prepared) */
+  int64_t w2_bytes;           /* (E+S) * I * H * elem(usecase) */
   int64_t workspace_bytes;    /* scratch of the three-call path */
   int64_t fused_workspace_bytes; /* scratch of mega_moe (holds the pool too) */
   uint64_t checksum;          /* guards against a modified plan */
@@ -120,8 +137,8 @@ typedef struct mm_plan {
  * mm_plan_create -- validate a problem and choose BLOCK_M and tiles.
  * Host only, no HIP call.  BLOCK_M follows the expected rows per expert,
  * T*K/E (DeepGEMM MegaMoE page, section 3.3 shape heuristic): small loads
- * take a small BLOCK_M.  P = T*K + E*(BLOCK_M-1) rounded up to BLOCK_M,
- * enough for any routing.
+ * take a small BLOCK_M.  P = R + (E+S)*(BLOCK_M-1) rounded up to BLOCK_M,
+ * with R = T*(K+S) routes: enough for any routing.
  * Errors: MM_ERR_INVALID_ARG for NULL pointers or dimensions outside the
  * ranges stated in mm_problem; MM_ERR_UNSUPPORTED for an unknown use case
  * or output dtype.
@@ -132,15 +149,15 @@ mm_status mm_plan_create(const mm_problem* problem, mm_plan* plan);
  * mm_prepare_weights -- one-time relayout of the expert weights into the
  * layout the GEMM kernels stream (DeepGEMM MegaMoE page, section 3.2: done
  * once by the caller before repeated launches; not part of the timed path).
- *   w1     device [E][H][2I]  formula layout of the operator page (Formula)
- *   w2     device [E][I][H]   formula layout
- *   w1_out device [E][2I][H]  K-contiguous rows; row n of expert e holds the
+ *   w1     device [E+S][H][2I]  formula layout of the operator page (Formula)
+ *   w2     device [E+S][I][H]   formula layout
+ *   w1_out device [E+S][2I][H] K-contiguous rows; row n of expert e holds the
  *                             W1 column c(n) with gate and up columns
  *                             interleaved in groups of g = gate_up_group:
  *                             c(n) = (n/2g)*g + n%g            if n%2g <  g
  *                                    I + (n/2g)*g + n%g - g    otherwise
- *   w2_out device [E][H][I]   K-contiguous (transposed)
- * Scales stay in formula layout ([E][2I] and [E][H]).  Buffers must not
+ *   w2_out device [E+S][H][I] K-contiguous (transposed)
+ * Scales stay in formula layout ([E+S][2I] and [E+S][H]).  Buffers must not
  * overlap.
  */
 mm_status mm_prepare_weights(const mm_plan* plan, const void* w1, const void* w2,
@@ -154,12 +171,14 @@ mm_status mm_prepare_weights(const mm_plan* plan, const void* w1, const void* w2
  * DeepEP notes sections 3.2-3.5 (count in LDS, one claim atomic, scatter,
  * pool block offsets).
  *   topk_ids       device int32 [T][K]
+ *   x_active_mask  device int8 [T] or NULL (see the conventions above)
  *   x              device bf16  [T][H]
- *   expert_counts  device int32 [E]    out: N_e (the operator's expert_token_nums)
- *   expert_offsets device int32 [E+1]  out: padded exclusive prefix,
+ *   expert_counts  device int32 [E+S]  out: N_e (the operator's expert_token_nums;
+ *                                      entry E: the shared expert's count)
+ *   expert_offsets device int32 [E+S+1] out: padded exclusive prefix,
  *                                      off[e+1] = off[e] + BLOCK_M*ceil(N_e/BLOCK_M)
- *   pool_src       device int32 [P]    out: i*K+k of pool row p, -1 on padding
- *   route_to_pool  device int32 [T*K]  out: pool row of route i*K+k, -1 if masked
+ *   pool_src       device int32 [P]    out: route i*(K+S)+k of pool row p, -1 on padding
+ *   route_to_pool  device int32 [T*(K+S)] out: pool row of each route, -1 if skipped
  *   x_pool         device [P][H]       out: row p = x_i (bf16) or q_i (A8W8);
  *                                      padding rows are unspecified
  *   x_pool_scale   device f32 [P]      out: s_i of row p (A8W8); may be NULL for A16W16
@@ -167,7 +186,8 @@ mm_status mm_prepare_weights(const mm_plan* plan, const void* w1, const void* w2
  * The order of the rows of one expert inside its pool range is unspecified
  * (the operator page stacks them "in any fixed order").
  */
-mm_status mm_dispatch_layout(const mm_plan* plan, const int32_t* topk_ids, const void* x,
+mm_status mm_dispatch_layout(const mm_plan* plan, const int32_t* topk_ids, const int8_t* x_active_mask,
+                             const void* x,
                              int32_t* expert_counts, int32_t* expert_offsets,
                              int32_t* pool_src, int32_t* route_to_pool,
                              void* x_pool, float* x_pool_scale,
@@ -182,7 +202,7 @@ mm_status mm_dispatch_layout(const mm_plan* plan, const int32_t* topk_ids, const
  *   expert_offsets, expert_counts  as written by mm_dispatch_layout
  *   x_pool, x_pool_scale           as written by mm_dispatch_layout
  *   w1        device, prepared by mm_prepare_weights
- *   w1_scale  device f32 [E][2I] formula order (A8W8), NULL for A16W16
+ *   w1_scale  device f32 [E+S][2I] formula order (A8W8), NULL for A16W16
  *   a_pool    device [P][I] out: bf16 A (A16W16) or its int8 / e4m3 codes
  *   a_pool_scale device f32 [P] out: s^A (A8W8), may be NULL for A16W16
  */
@@ -196,13 +216,15 @@ mm_status mm_grouped_l1_swiglu(const mm_plan* plan, const int32_t* expert_offset
  * mm_grouped_l2_combine -- Linear2 per expert, gate weighting, Token Combine.
  * Operator page, Expert Compute step 3 (Y_e = A_e . W2[e]; A8W8:
  * Y_e = (D * s^W2_e) * s^A_e) and Token Combine
- * (y_i = sum_k G[i,k] * Y_{e_ik}[row(i,k)], stacked in token order).  Each
- * weighted contribution is kept in float32 and the K of a token are summed
- * in slot order.
+ * (y_i = sum_k G[i,k] * Y_{e_ik}[row(i,k)], stacked in token order; a
+ * shared-expert slot has weight 1).  Each weighted contribution is stored in
+ * float32 for A16W16 and in bf16 for the A8W8 use cases (whose y is bf16,
+ * as the DeepGEMM page's combine slots are, section 4 step 7); the K + S
+ * contributions of a token are summed in float32 in slot order.
  *   pool_src, route_to_pool        as written by mm_dispatch_layout
  *   a_pool, a_pool_scale           as written by mm_grouped_l1_swiglu
  *   w2        device, prepared by mm_prepare_weights
- *   w2_scale  device f32 [E][H] (A8W8), NULL for A16W16
+ *   w2_scale  device f32 [E+S][H] (A8W8), NULL for A16W16
  *   topk_weights device f32 [T][K]
  *   y         device [T][H] out, bf16 or f32 per plan.prob.y_dtype
  */
@@ -226,19 +248,27 @@ mm_status mm_grouped_l2_combine(const mm_plan* plan, const int32_t* expert_offse
  * Device-side conditions (an expert id >= E, a barrier that timed out) are
  * recorded in the workspace error word, see mm_read_device_error.  A device
  * that cannot hold one workgroup per compute unit makes the call fail with
- * MM_ERR_HIP before anything runs; work on other streams that occupies
- * compute units only delays the kernel.
+ * MM_ERR_HIP before anything runs.
+ * Co-residency: the grid barriers need every workgroup of the grid running
+ * at once.  Work on other streams that holds compute units only delays the
+ * late workgroups, but if it holds them longer than the barriers' bounded
+ * wait (about a second), the barrier gives up: the call has already
+ * returned MM_OK, y is then unspecified, and only the error word
+ * (MM_DEVERR_BARRIER_TIMEOUT) reports it.  Callers that share the GPU with
+ * long-running concurrent kernels must read the error word.
  *   x              device bf16 [T][H]
  *   topk_ids       device int32 [T][K]
  *   topk_weights   device f32 [T][K]
+ *   x_active_mask  device int8 [T] or NULL
  *   w1, w2         device, prepared by mm_prepare_weights
  *   w1_scale, w2_scale  device f32 (A8W8) or NULL (A16W16)
  *   y              device [T][H] out (bf16 or f32 per plan)
- *   expert_token_nums device int32 [E] out: N_e
+ *   expert_token_nums device int32 [E] out: N_e of the routed experts
  *   workspace      device, plan.fused_workspace_bytes
  */
 mm_status mega_moe(const mm_plan* plan, const void* x, const int32_t* topk_ids,
-                   const float* topk_weights, const void* w1, const float* w1_scale,
+                   const float* topk_weights, const int8_t* x_active_mask,
+                   const void* w1, const float* w1_scale,
                    const void* w2, const float* w2_scale, void* y, int32_t* expert_token_nums,
                    void* workspace, uint64_t workspace_bytes, void* stream);
 
@@ -267,16 +297,43 @@ mm_status mm_read_device_error(const mm_plan* plan, const void* workspace, int32
  * mm_debug_raw_accumulators -- the integer GEMM accumulators before any
  * scaling, for checking that the A8W8-INT products are exact (operator
  * page, A8W8-INT: C = Q_e . W1[e] and D = A^int8 . W2[e] in Z_32).
- * Runs the same mainloop as the entry points with an epilogue that stores
- * the raw int32 accumulators (A8W8_INT8 plans only).
+ * Runs the same mainloop, tile shape and tail-tile K split as the entry
+ * points with an epilogue that stores the raw int32 accumulators
+ * (A8W8_INT8 plans only).
  *   which = 1: c_out int32 [P][2I], column order of the formula (gate then up),
  *              from x_pool and the prepared w1;
  *   which = 2: c_out int32 [P][H] from a_pool and the prepared w2.
+ *   workspace  device, plan.workspace_bytes (partial sums of split tiles)
  * Padding rows of c_out are unspecified.
  */
 mm_status mm_debug_raw_accumulators(const mm_plan* plan, int which, const int32_t* expert_offsets,
                                     const int32_t* expert_counts, const void* act_pool,
-                                    const void* w_prepared, int32_t* c_out, void* stream);
+                                    const void* w_prepared, int32_t* c_out,
+                                    void* workspace, uint64_t workspace_bytes, void* stream);
+
+/*
+ * mm_debug_fused_layout -- copies the dispatch metadata that the last
+ * mega_moe call on `workspace` built inside it (DeepEP notes, sections 1
+ * and 3.5: the padded per-expert offsets and the (token, slot) identity of
+ * every pool row), asynchronously on `stream`, so that it can be checked
+ * like mm_dispatch_layout's outputs.  Diagnostics only.
+ *   offsets_out        device int32 [E+S+1]
+ *   pool_src_out       device int32 [P]
+ *   route_to_pool_out  device int32 [T*(K+S)]
+ */
+mm_status mm_debug_fused_layout(const mm_plan* plan, const void* workspace, int32_t* offsets_out,
+                                int32_t* pool_src_out, int32_t* route_to_pool_out, void* stream);
+
+/*
+ * mm_read_kernel_clock -- the clock sample of the last mega_moe call on
+ * `workspace`: its workgroup 0 reads the shader-clock counter (s_memtime)
+ * and the constant 100 MHz counter (s_memrealtime) when it starts and when
+ * it is done.  host_out[0], [1]: shader clocks at start and end; [2], [3]:
+ * 100 MHz ticks at start and end, so the mean shader clock over the run is
+ * 100 MHz * (out[1] - out[0]) / (out[3] - out[2]).  Copied asynchronously on
+ * `stream`; read it after the stream has synchronised.  Diagnostics only.
+ */
+mm_status mm_read_kernel_clock(const mm_plan* plan, const void* workspace, uint64_t* host_out, void* stream);
 
 /* Kernel timing (diagnostics).  While enabled, every kernel the library
  * launches is bracketed by two HIP events on its stream; mm_trace_collect

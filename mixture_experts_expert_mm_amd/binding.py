@@ -33,6 +33,8 @@ class MMProblem(ctypes.Structure):
         ("y_dtype", ctypes.c_int32),
         ("clamp_activation", ctypes.c_int32),
         ("activation_clamp", ctypes.c_float),
+        ("num_shared_experts", ctypes.c_int32),
+        ("reserved0", ctypes.c_int32),
     ]
 
 
@@ -58,7 +60,7 @@ class MMPlan(ctypes.Structure):
 EXPORTS = [
     "mm_plan_create", "mm_prepare_weights", "mm_dispatch_layout", "mm_grouped_l1_swiglu",
     "mm_grouped_l2_combine", "mega_moe", "mm_read_device_error", "mm_debug_raw_accumulators",
-    "mm_trace_enable", "mm_trace_collect", "mm_kernel_name", "mm_status_string",
+    "mm_debug_fused_layout", "mm_read_kernel_clock", "mm_trace_enable", "mm_trace_collect", "mm_kernel_name", "mm_status_string",
 ]
 
 _lib = None
@@ -86,12 +88,14 @@ def load() -> ctypes.CDLL:
     P = ctypes.POINTER(MMPlan)
     lib.mm_plan_create.argtypes = [ctypes.POINTER(MMProblem), P]
     lib.mm_prepare_weights.argtypes = [P, vp, vp, vp, vp, vp]
-    lib.mm_dispatch_layout.argtypes = [P, i32p, vp, i32p, i32p, i32p, i32p, vp, f32p, vp, u64, vp]
+    lib.mm_dispatch_layout.argtypes = [P, i32p, vp, vp, i32p, i32p, i32p, i32p, vp, f32p, vp, u64, vp]
     lib.mm_grouped_l1_swiglu.argtypes = [P, i32p, i32p, vp, f32p, vp, f32p, vp, f32p, vp, u64, vp]
     lib.mm_grouped_l2_combine.argtypes = [P, i32p, i32p, i32p, i32p, vp, f32p, vp, f32p, f32p, vp, vp, u64, vp]
-    lib.mega_moe.argtypes = [P, vp, i32p, f32p, vp, f32p, vp, f32p, vp, i32p, vp, u64, vp]
+    lib.mega_moe.argtypes = [P, vp, i32p, f32p, vp, vp, f32p, vp, f32p, vp, i32p, vp, u64, vp]
     lib.mm_read_device_error.argtypes = [P, vp, ctypes.POINTER(ctypes.c_int32), vp]
-    lib.mm_debug_raw_accumulators.argtypes = [P, ctypes.c_int, i32p, i32p, vp, vp, i32p, vp]
+    lib.mm_debug_raw_accumulators.argtypes = [P, ctypes.c_int, i32p, i32p, vp, vp, i32p, vp, u64, vp]
+    lib.mm_debug_fused_layout.argtypes = [P, vp, i32p, i32p, i32p, vp]
+    lib.mm_read_kernel_clock.argtypes = [P, vp, ctypes.POINTER(ctypes.c_uint64), vp]
     lib.mm_trace_enable.argtypes = [ctypes.c_int]
     lib.mm_trace_collect.argtypes = [ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_double)]
     lib.mm_kernel_name.argtypes = [ctypes.c_int]
@@ -132,11 +136,14 @@ def _check(fn, st):
 
 # ------------------------------------------------------------------ entries
 
-def mm_plan_create(T, H, I, E, K, usecase="bf16", y_dtype="bf16", activation_clamp=None) -> MMPlan:
-    """activation_clamp: None (no clamp) or c >= 0 (H clamped to [-c, c] before SwiGLU)."""
+def mm_plan_create(T, H, I, E, K, usecase="bf16", y_dtype="bf16", activation_clamp=None,
+                   num_shared_experts=0) -> MMPlan:
+    """activation_clamp: None (no clamp) or c >= 0 (H clamped to [-c, c] before SwiGLU);
+    num_shared_experts: 0 or 1 (expert index E of the weight arrays)."""
     prob = MMProblem(T, H, I, E, K, USECASE.get(usecase, usecase) if isinstance(usecase, str) else usecase,
                      MM_OUT_F32 if y_dtype in ("f32", "fp32", MM_OUT_F32) else MM_OUT_BF16,
-                     0 if activation_clamp is None else 1, 0.0 if activation_clamp is None else float(activation_clamp))
+                     0 if activation_clamp is None else 1, 0.0 if activation_clamp is None else float(activation_clamp),
+                     int(num_shared_experts), 0)
     plan = MMPlan()
     _check("mm_plan_create", load().mm_plan_create(ctypes.byref(prob), ctypes.byref(plan)))
     return plan
@@ -147,10 +154,10 @@ def mm_prepare_weights(plan, w1, w2, w1_out, w2_out, stream=None):
         ctypes.byref(plan), _ptr(w1), _ptr(w2), _ptr(w1_out), _ptr(w2_out), _stream(stream)))
 
 
-def mm_dispatch_layout(plan, topk_ids, x, expert_counts, expert_offsets, pool_src, route_to_pool,
+def mm_dispatch_layout(plan, topk_ids, x_active_mask, x, expert_counts, expert_offsets, pool_src, route_to_pool,
                        x_pool, x_pool_scale, workspace, stream=None):
     _check("mm_dispatch_layout", load().mm_dispatch_layout(
-        ctypes.byref(plan), _ptr(topk_ids), _ptr(x), _ptr(expert_counts), _ptr(expert_offsets),
+        ctypes.byref(plan), _ptr(topk_ids), _ptr(x_active_mask), _ptr(x), _ptr(expert_counts), _ptr(expert_offsets),
         _ptr(pool_src), _ptr(route_to_pool), _ptr(x_pool), _ptr(x_pool_scale), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
 
@@ -171,10 +178,10 @@ def mm_grouped_l2_combine(plan, expert_offsets, expert_counts, pool_src, route_t
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
-def mega_moe(plan, x, topk_ids, topk_weights, w1, w1_scale, w2, w2_scale, y, expert_token_nums,
+def mega_moe(plan, x, topk_ids, topk_weights, x_active_mask, w1, w1_scale, w2, w2_scale, y, expert_token_nums,
              workspace, stream=None):
     _check("mega_moe", load().mega_moe(
-        ctypes.byref(plan), _ptr(x), _ptr(topk_ids), _ptr(topk_weights), _ptr(w1), _ptr(w1_scale),
+        ctypes.byref(plan), _ptr(x), _ptr(topk_ids), _ptr(topk_weights), _ptr(x_active_mask), _ptr(w1), _ptr(w1_scale),
         _ptr(w2), _ptr(w2_scale), _ptr(y), _ptr(expert_token_nums), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
 
@@ -188,11 +195,27 @@ def mm_read_device_error(plan, workspace, stream=None) -> int:
     return out.value
 
 
+def mm_read_kernel_clock(plan, workspace, stream=None):
+    """(shader clocks, 100 MHz ticks) spanned by workgroup 0 of the last mega_moe call; waits for the device."""
+    out = (ctypes.c_uint64 * 4)()
+    _check("mm_read_kernel_clock", load().mm_read_kernel_clock(ctypes.byref(plan), _ptr(workspace), out,
+                                                                _stream(stream)))
+    torch.cuda.synchronize()
+    return out[1] - out[0], out[3] - out[2]
+
+
 def mm_debug_raw_accumulators(plan, which, expert_offsets, expert_counts, act_pool, w_prepared, c_out,
-                              stream=None):
+                              workspace, stream=None):
     _check("mm_debug_raw_accumulators", load().mm_debug_raw_accumulators(
         ctypes.byref(plan), which, _ptr(expert_offsets), _ptr(expert_counts), _ptr(act_pool),
-        _ptr(w_prepared), _ptr(c_out), _stream(stream)))
+        _ptr(w_prepared), _ptr(c_out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+
+
+def mm_debug_fused_layout(plan, workspace, offsets_out, pool_src_out, route_to_pool_out, stream=None):
+    _check("mm_debug_fused_layout", load().mm_debug_fused_layout(
+        ctypes.byref(plan), _ptr(workspace), _ptr(offsets_out), _ptr(pool_src_out), _ptr(route_to_pool_out),
+        _stream(stream)))
 
 
 def mm_trace_enable(on: bool):

@@ -8,13 +8,13 @@ namespace mm {
 // ---------------------------------------------------------------------------
 // reset of the per-call counters and control words
 // ---------------------------------------------------------------------------
-__global__ void k_zero(int32_t* __restrict__ counts, int E, uint32_t* __restrict__ ctl) {
+__global__ void k_zero(int32_t* __restrict__ counts, int E, uint32_t* __restrict__ ctl, int ctl_first, int ctl_n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   if (counts)
     for (int64_t j = i; j < E; j += stride) counts[j] = 0;
   if (ctl)
-    for (int64_t j = i; j < kCtlWords; j += stride) ctl[j] = 0u;
+    for (int64_t j = i; j < ctl_n; j += stride) ctl[ctl_first + j] = 0u;
 }
 
 __global__ __launch_bounds__(256) void k_count(DispatchArgs a, int64_t nwaves) {
@@ -75,10 +75,10 @@ __global__ __launch_bounds__(256) void k_transpose(const T* __restrict__ in, T* 
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-hipError_t launch_zero(int32_t* counts, int E, uint32_t* ctl, hipStream_t s) {
-  int grid = (E + 255) / 256;
+hipError_t launch_zero(int32_t* counts, int E, uint32_t* ctl, int ctl_first, int ctl_n, hipStream_t s) {
+  int grid = ((E > ctl_n ? E : ctl_n) + 255) / 256;
   if (grid < 1) grid = 1;
-  hipLaunchKernelGGL(k_zero, dim3(grid), dim3(256), 0, s, counts, E, ctl);
+  hipLaunchKernelGGL(k_zero, dim3(grid), dim3(256), 0, s, counts, E, ctl, ctl_first, ctl_n);
   return hipGetLastError();
 }
 

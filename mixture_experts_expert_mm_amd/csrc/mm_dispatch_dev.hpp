@@ -15,9 +15,21 @@
 
 namespace mm {
 
+// Expert of route (tok, slot): a routed slot (slot < Kr) reads topk_ids, a
+// shared-expert slot names expert Er + (slot - Kr).  -1 for masked routes
+// (id < 0), ids >= Er (which also raise MM_DEVERR_BAD_EXPERT) and every
+// slot of a token whose x_active_mask entry is 0 (the token takes part in
+// nothing, so its output row is 0).
+__device__ __forceinline__ int route_expert(const DispatchArgs& a, int64_t tok, int slot) {
+  if (a.active && a.active[tok] == 0) return -1;
+  if (slot >= a.Kr) return a.Er + (slot - a.Kr);
+  const int e = a.topk_ids[tok * a.Kr + slot];
+  if (e >= a.Er && a.err) atomicOr(a.err, (uint32_t)MM_DEVERR_BAD_EXPERT);
+  return (e >= 0 && e < a.Er) ? e : -1;
+}
+
 // Route of lane l of global wave gw: token gw*tpw + l/K, slot l%K.  Returns
-// the expert id, or -1 for idle lanes, masked routes (id < 0) and ids >= E
-// (an id >= E also raises MM_DEVERR_BAD_EXPERT in the error word).
+// the expert id (route_expert), or -1 for idle lanes and skipped routes.
 __device__ __forceinline__ int read_route(const DispatchArgs& a, int64_t gw, int l, int64_t* route) {
   const int tpw = 64 / a.K;
   const int64_t tok = gw * tpw + l / a.K;
@@ -25,9 +37,7 @@ __device__ __forceinline__ int read_route(const DispatchArgs& a, int64_t gw, int
   *route = -1;
   if (l >= tpw * a.K || tok >= a.T) return -1;
   *route = tok * a.K + slot;
-  const int e = a.topk_ids[*route];
-  if (e >= a.E && a.err) atomicOr(a.err, (uint32_t)MM_DEVERR_BAD_EXPERT);
-  return (e >= 0 && e < a.E) ? e : -1;
+  return route_expert(a, tok, slot);
 }
 
 // Count + claim for dispatch waves vb*NW .. vb*NW+NW-1, one per wave of the
@@ -112,17 +122,10 @@ __device__ __forceinline__ void dispatch_one_block(const DispatchArgs& a, int32_
 #pragma unroll
   for (int j = 0; j < MAXR; ++j) {
     const int64_t r = t + (int64_t)NT * j;
-    ex[j] = -1;
-    if (r < R) ex[j] = a.topk_ids[r];
+    ex[j] = r < R ? route_expert(a, r / a.K, (int)(r % a.K)) : -1;
   }
 #pragma unroll
-  for (int j = 0; j < MAXR; ++j) {
-    const int64_t r = t + (int64_t)NT * j;
-    if (r < R && ex[j] >= a.E && a.err) atomicOr(a.err, (uint32_t)MM_DEVERR_BAD_EXPERT);
-    const int e = (r < R && ex[j] >= 0 && ex[j] < a.E) ? ex[j] : -1;
-    ex[j] = e;
-    rk[j] = e >= 0 ? atomicAdd(&hist[e], 1) : 0;
-  }
+  for (int j = 0; j < MAXR; ++j) rk[j] = ex[j] >= 0 ? atomicAdd(&hist[ex[j]], 1) : 0;
   __syncthreads();
   padded_prefix<NT>(a, hist, off, wsum);
   for (int e = t; e < a.E; e += NT) a.counts[e] = hist[e];

@@ -223,6 +223,7 @@ __device__ __forceinline__ GemmArgs uniform_args(const GemmArgs& in) {
   a.I = uniform_int(in.I);
   a.H = uniform_int(in.H);
   a.K = uniform_int(in.K);
+  a.Kr = uniform_int(in.Kr);
   a.gate_up_group = uniform_int(in.gate_up_group);
   a.group_m = uniform_int(in.group_m);
   a.a_route = uniform_ptr(in.a_route);
@@ -437,7 +438,9 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
     }
     if constexpr (MODE == 1) {
       if (rr.route < 0 || rr.route >= a.routes) rr.route = -1;   // not a route of this call: row left out
-      rr.gw = rr.route >= 0 ? gp(a.topk_w)[rr.route] : 0.0f;
+      // routed slot k < Kr: G[i,k]; a shared-expert slot: weight 1
+      const int slot = rr.route >= 0 ? rr.route % a.K : 0;
+      rr.gw = rr.route < 0 ? 0.0f : slot < a.Kr ? gp(a.topk_w)[(rr.route / a.K) * a.Kr + slot] : 1.0f;
     }
   };
   auto row_commit = [&](const RowRegs& rr, int buf) {

@@ -21,6 +21,10 @@ inline int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 
 int elem_size(int usecase) { return usecase == MM_A16W16 ? 2 : 1; }
 
+// experts with weights (routed + shared) and slots per token (top-k + shared)
+int64_t all_experts(const mm_problem& p) { return p.num_experts + p.num_shared_experts; }
+int64_t slots_per_token(const mm_problem& p) { return p.num_topk + p.num_shared_experts; }
+
 uint64_t plan_checksum(const mm_plan* p) {
   // FNV-1a over every field except the checksum itself
   const uint8_t* b = reinterpret_cast<const uint8_t*>(p);
@@ -38,26 +42,27 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 // ---------------------------------------------------------------- workspace
 struct WsLayout {
   int64_t ctl, wave_base, a_stage, contrib, partials, end;                   // 3-call scratch
-  int64_t mega_args, offsets, pool_src, route_to_pool, x_pool, x_pool_scale, a_pool, a_pool_scale, x_tok, x_tok_scale,
-      fused_end;
+  int64_t mega_args, counts, offsets, pool_src, route_to_pool, x_pool, x_pool_scale, a_pool, a_pool_scale, x_tok,
+      x_tok_scale, fused_end;
 };
 
 WsLayout ws_layout(const mm_plan& pl) {
   const mm_problem& p = pl.prob;
   const bool q = p.usecase != MM_A16W16;
-  const int64_t P = pl.pool_rows, R = p.num_tokens * p.num_topk;
+  const int64_t P = pl.pool_rows, R = p.num_tokens * slots_per_token(p), Et = all_experts(p);
   WsLayout L{};
   int64_t o = 0;
   auto take = [&](int64_t bytes) { const int64_t at = o; o = align_up(o + bytes, kAlign); return at; };
   L.ctl = take(kCtlWords * 4);
-  L.wave_base = take(dispatch_waves(p.num_tokens, (int)p.num_topk) * p.num_experts * 4);
+  L.wave_base = take(dispatch_waves(p.num_tokens, (int)slots_per_token(p)) * Et * 4);
   L.a_stage = q ? take(P * p.intermediate_hidden * 4) : -1;
   L.contrib = take(R * p.hidden * (q ? 2 : 4));   // combine slots: bf16 for A8W8, float32 for A16W16
   // partial sums of split tail tiles: one slot per piece in flight
   L.partials = take((int64_t)kSplitSlots * tile_bm(pl.tile_l1) * tile_bn(pl.tile_l1) * 4);
   L.end = o;
   L.mega_args = take(sizeof(MegaArgs));
-  L.offsets = take((p.num_experts + 1) * 4);
+  L.counts = take(Et * 4);
+  L.offsets = take((Et + 1) * 4);
   L.pool_src = take(P * 4);
   L.route_to_pool = take(R * 4);
   L.x_pool = take(pl.x_pool_bytes);
@@ -147,12 +152,14 @@ mm_status check_plan(const mm_plan* pl) {
 // ---------------------------------------------------------------- stages
 // Argument blocks of each step; the three-call path launches them as
 // separate kernels, mega_moe hands all of them to the fused kernel.
-DispatchArgs dispatch_args(const mm_plan& pl, const int32_t* ids, const void* x, int32_t* counts, int32_t* offsets,
-                           int32_t* pool_src, int32_t* r2p, void* x_pool, float* x_pool_scale, void* ws) {
+DispatchArgs dispatch_args(const mm_plan& pl, const int32_t* ids, const int8_t* active, const void* x, int32_t* counts,
+                           int32_t* offsets, int32_t* pool_src, int32_t* r2p, void* x_pool, float* x_pool_scale,
+                           void* ws) {
   const mm_problem& p = pl.prob;
   const WsLayout L = ws_layout(pl);
   DispatchArgs d{};
   d.topk_ids = ids;
+  d.active = active;
   d.x = x;
   d.counts = counts;
   d.offsets = offsets;
@@ -165,8 +172,10 @@ DispatchArgs dispatch_args(const mm_plan& pl, const int32_t* ids, const void* x,
   d.T = p.num_tokens;
   d.H = p.hidden;
   d.P = pl.pool_rows;
-  d.E = (int)p.num_experts;
-  d.K = (int)p.num_topk;
+  d.E = (int)all_experts(p);
+  d.K = (int)slots_per_token(p);
+  d.Er = (int)p.num_experts;
+  d.Kr = (int)p.num_topk;
   d.block_m = pl.block_m;
   d.usecase = p.usecase;
   return d;
@@ -242,15 +251,16 @@ GemmArgs l1_args(const mm_plan& pl, const int32_t* offsets, const int32_t* count
   g.offsets = offsets;
   g.counts = counts;
   g.P = pl.pool_rows;
-  g.E = (int)p.num_experts;
+  g.E = (int)all_experts(p);
   g.N = (int)(2 * p.intermediate_hidden);
   g.Kdim = (int)p.hidden;
   g.I = (int)p.intermediate_hidden;
   g.H = (int)p.hidden;
-  g.K = (int)p.num_topk;
+  g.K = (int)slots_per_token(p);
+  g.Kr = (int)p.num_topk;
   g.gate_up_group = pl.gate_up_group;
   g.clamp = p.clamp_activation ? p.activation_clamp : INFINITY;
-  g.routes = p.num_tokens * p.num_topk;
+  g.routes = p.num_tokens * slots_per_token(p);
   g.err = at<uint32_t>(ws, L.ctl) + 1;
   g.x_scale = x_pool_scale;
   g.w_scale = w1_scale;
@@ -289,13 +299,14 @@ GemmArgs l2_args(const mm_plan& pl, const int32_t* offsets, const int32_t* count
   g.counts = counts;
   g.pool_src = pool_src;
   g.P = pl.pool_rows;
-  g.E = (int)p.num_experts;
+  g.E = (int)all_experts(p);
   g.N = (int)p.hidden;
   g.Kdim = (int)p.intermediate_hidden;
   g.I = (int)p.intermediate_hidden;
   g.H = (int)p.hidden;
-  g.K = (int)p.num_topk;
-  g.routes = p.num_tokens * p.num_topk;
+  g.K = (int)slots_per_token(p);
+  g.Kr = (int)p.num_topk;
+  g.routes = p.num_tokens * slots_per_token(p);
   g.err = at<uint32_t>(ws, L.ctl) + 1;
   g.a_scale = a_pool_scale;
   g.w_scale = w2_scale;
@@ -314,21 +325,31 @@ CombineArgs combine_args(const mm_plan& pl, const void* contrib, const int32_t* 
   c.y = y;
   c.T = p.num_tokens;
   c.H = (int)p.hidden;
-  c.K = (int)p.num_topk;
+  c.K = (int)slots_per_token(p);
   c.y_f32 = p.y_dtype == MM_OUT_F32;
   c.slot_bf16 = p.usecase != MM_A16W16;
   return c;
 }
 
-mm_status do_dispatch(const mm_plan& pl, const int32_t* ids, const void* x, int32_t* counts, int32_t* offsets,
-                      int32_t* pool_src, int32_t* r2p, void* x_pool, float* x_pool_scale, void* ws, hipStream_t s) {
-  const DispatchArgs d = dispatch_args(pl, ids, x, counts, offsets, pool_src, r2p, x_pool, x_pool_scale, ws);
+mm_status do_dispatch(const mm_plan& pl, const int32_t* ids, const int8_t* active, const void* x, int32_t* counts,
+                      int32_t* offsets, int32_t* pool_src, int32_t* r2p, void* x_pool, float* x_pool_scale, void* ws,
+                      hipStream_t s) {
+  const DispatchArgs d = dispatch_args(pl, ids, active, x, counts, offsets, pool_src, r2p, x_pool, x_pool_scale, ws);
   uint32_t* ctl = at<uint32_t>(ws, ws_layout(pl).ctl);
-  MM_TRY(run(MM_K_ZERO, s, [&] { return launch_zero(counts, d.E, ctl, s); }));
+  MM_TRY(run(MM_K_ZERO, s, [&] { return launch_zero(counts, d.E, ctl, 0, kCtlWords, s); }));
   MM_TRY(run(MM_K_COUNT, s, [&] { return launch_count(d, s); }));
   MM_TRY(run(MM_K_SCATTER, s, [&] { return launch_scatter(d, s); }));
   MM_TRY(run(MM_K_GATHER, s, [&] { return launch_gather(d, s); }));
   return MM_OK;
+}
+
+// The ready flags of split tail tiles start at zero: a GEMM entry point may
+// get a workspace no dispatch has cleared, or one where a waiter gave up
+// before a late producer set its flag.  Only when tiles can split.
+mm_status clear_split_flags(const GemmArgs& g, hipStream_t s) {
+  if (g.max_split < 2) return MM_OK;
+  uint32_t* ctl = g.split_flags - kSplitFlag0;
+  return run(MM_K_ZERO, s, [&] { return launch_zero(nullptr, 0, ctl, kSplitFlag0, kSplitSlots, s); });
 }
 
 mm_status do_l1(const mm_plan& pl, const int32_t* offsets, const int32_t* counts, const void* x_pool,
@@ -337,6 +358,7 @@ mm_status do_l1(const mm_plan& pl, const int32_t* offsets, const int32_t* counts
   const mm_problem& p = pl.prob;
   const GemmArgs g = l1_args(pl, offsets, counts, x_pool, x_pool_scale, w1, w1_scale, a_pool, ws);
   const int grid = gemm_grid(pl.tile_l1, pl.pool_rows, g.N, num_cus());
+  MM_TRY(clear_split_flags(g, s));
   MM_TRY(run(MM_K_L1, s, [&] { return launch_gemm(0, p.usecase, pl.tile_l1, fp8_l1_exact(pl), g, grid, s); }));
   if (p.usecase != MM_A16W16) {
     const RequantArgs r = requant_args(pl, g, a_pool, a_pool_scale);
@@ -351,6 +373,7 @@ mm_status do_l2(const mm_plan& pl, const int32_t* offsets, const int32_t* counts
   const mm_problem& p = pl.prob;
   const GemmArgs g = l2_args(pl, offsets, counts, pool_src, a_pool, a_pool_scale, w2, w2_scale, topk_w, ws);
   const int grid = gemm_grid(pl.tile_l2, pl.pool_rows, g.N, num_cus());
+  MM_TRY(clear_split_flags(g, s));
   MM_TRY(run(MM_K_L2, s, [&] { return launch_gemm(1, p.usecase, pl.tile_l2, false, g, grid, s); }));
   const CombineArgs c = combine_args(pl, g.contrib, r2p, y);
   MM_TRY(run(MM_K_COMBINE, s, [&] { return launch_combine(c, s); }));
@@ -377,7 +400,9 @@ mm_status mm_plan_create(const mm_problem* problem, mm_plan* plan) {
     return MM_ERR_INVALID_ARG;
   if (p.num_experts < 1 || p.num_experts > 1024) return MM_ERR_INVALID_ARG;
   if (p.num_topk < 1 || p.num_topk > 64 || p.num_topk > p.num_experts) return MM_ERR_INVALID_ARG;
-  const int64_t R = p.num_tokens * p.num_topk;
+  if (p.num_shared_experts < 0 || p.num_shared_experts > 1 || p.reserved0 != 0) return MM_ERR_INVALID_ARG;
+  if (slots_per_token(p) > 64 || all_experts(p) > 1024) return MM_ERR_INVALID_ARG;
+  const int64_t R = p.num_tokens * slots_per_token(p);
   if (R > (int64_t)1 << 30) return MM_ERR_INVALID_ARG;
 
   mm_plan pl;
@@ -398,14 +423,14 @@ mm_status mm_plan_create(const mm_problem* problem, mm_plan* plan) {
   pl.tile_l2 = tile;
   pl.block_m = tile_bm(tile);
   pl.gate_up_group = 32;
-  const int64_t P = align_up(R + p.num_experts * (pl.block_m - 1), pl.block_m);
+  const int64_t P = align_up(R + all_experts(p) * (pl.block_m - 1), pl.block_m);
   if (P > ((int64_t)1 << 31) - 1) return MM_ERR_INVALID_ARG;
   pl.pool_rows = P;
   const int es = elem_size(p.usecase);
   pl.x_pool_bytes = P * p.hidden * es;
   pl.a_pool_bytes = P * p.intermediate_hidden * es;
-  pl.w1_bytes = p.num_experts * p.hidden * 2 * p.intermediate_hidden * es;
-  pl.w2_bytes = p.num_experts * p.intermediate_hidden * p.hidden * es;
+  pl.w1_bytes = all_experts(p) * p.hidden * 2 * p.intermediate_hidden * es;
+  pl.w2_bytes = all_experts(p) * p.intermediate_hidden * p.hidden * es;
   const WsLayout L = ws_layout(pl);
   pl.workspace_bytes = L.end;
   pl.fused_workspace_bytes = L.fused_end;
@@ -421,14 +446,15 @@ mm_status mm_prepare_weights(const mm_plan* plan, const void* w1, const void* w2
   const mm_problem& p = plan->prob;
   hipStream_t s = static_cast<hipStream_t>(stream);
   return run(MM_K_PREPARE, s, [&] {
-    return launch_prepare(w1, w2, w1_out, w2_out, (int)p.num_experts, (int)p.hidden, (int)p.intermediate_hidden,
+    return launch_prepare(w1, w2, w1_out, w2_out, (int)all_experts(p), (int)p.hidden, (int)p.intermediate_hidden,
                           elem_size(p.usecase), plan->gate_up_group, s);
   });
 }
 
-mm_status mm_dispatch_layout(const mm_plan* plan, const int32_t* topk_ids, const void* x, int32_t* expert_counts,
-                             int32_t* expert_offsets, int32_t* pool_src, int32_t* route_to_pool, void* x_pool,
-                             float* x_pool_scale, void* workspace, uint64_t workspace_bytes, void* stream) {
+mm_status mm_dispatch_layout(const mm_plan* plan, const int32_t* topk_ids, const int8_t* x_active_mask, const void* x,
+                             int32_t* expert_counts, int32_t* expert_offsets, int32_t* pool_src, int32_t* route_to_pool,
+                             void* x_pool, float* x_pool_scale, void* workspace, uint64_t workspace_bytes,
+                             void* stream) {
   MM_TRY(check_plan(plan));
   const bool q = plan->prob.usecase != MM_A16W16;
   if (!ok4(topk_ids) || !ok16(x) || !ok4(expert_counts) || !ok4(expert_offsets) || !ok4(pool_src) ||
@@ -436,7 +462,7 @@ mm_status mm_dispatch_layout(const mm_plan* plan, const int32_t* topk_ids, const
     return MM_ERR_INVALID_ARG;
   if (q && !ok4(x_pool_scale)) return MM_ERR_INVALID_ARG;
   if ((int64_t)workspace_bytes < plan->workspace_bytes) return MM_ERR_WORKSPACE;
-  return do_dispatch(*plan, topk_ids, x, expert_counts, expert_offsets, pool_src, route_to_pool, x_pool,
+  return do_dispatch(*plan, topk_ids, x_active_mask, x, expert_counts, expert_offsets, pool_src, route_to_pool, x_pool,
                      q ? x_pool_scale : nullptr, workspace, static_cast<hipStream_t>(stream));
 }
 
@@ -472,8 +498,9 @@ mm_status mm_grouped_l2_combine(const mm_plan* plan, const int32_t* expert_offse
 }
 
 mm_status mega_moe(const mm_plan* plan, const void* x, const int32_t* topk_ids, const float* topk_weights,
-                   const void* w1, const float* w1_scale, const void* w2, const float* w2_scale, void* y,
-                   int32_t* expert_token_nums, void* workspace, uint64_t workspace_bytes, void* stream) {
+                   const int8_t* x_active_mask, const void* w1, const float* w1_scale, const void* w2,
+                   const float* w2_scale, void* y, int32_t* expert_token_nums, void* workspace,
+                   uint64_t workspace_bytes, void* stream) {
   MM_TRY(check_plan(plan));
   const bool q = plan->prob.usecase != MM_A16W16;
   if (!ok16(x) || !ok4(topk_ids) || !ok4(topk_weights) || !ok16(w1) || !ok16(w2) || !ok16(y) ||
@@ -483,6 +510,7 @@ mm_status mega_moe(const mm_plan* plan, const void* x, const int32_t* topk_ids, 
   if ((int64_t)workspace_bytes < plan->fused_workspace_bytes) return MM_ERR_WORKSPACE;
   const WsLayout L = ws_layout(*plan);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t* counts = at<int32_t>(workspace, L.counts);
   int32_t* offsets = at<int32_t>(workspace, L.offsets);
   int32_t* pool_src = at<int32_t>(workspace, L.pool_src);
   int32_t* r2p = at<int32_t>(workspace, L.route_to_pool);
@@ -492,13 +520,14 @@ mm_status mega_moe(const mm_plan* plan, const void* x, const int32_t* topk_ids, 
   float* as = q ? at<float>(workspace, L.a_pool_scale) : nullptr;
   const mm_plan& pl = *plan;
   MegaArgs m{};
-  m.d = dispatch_args(pl, topk_ids, x, expert_token_nums, offsets, pool_src, r2p, x_pool, xs, workspace);
-  m.l1 = l1_args(pl, offsets, expert_token_nums, x_pool, xs, w1, w1_scale, a_pool, workspace);
+  m.d = dispatch_args(pl, topk_ids, x_active_mask, x, counts, offsets, pool_src, r2p, x_pool, xs, workspace);
+  m.l1 = l1_args(pl, offsets, counts, x_pool, xs, w1, w1_scale, a_pool, workspace);
   m.rq = requant_args(pl, m.l1, a_pool, as);
-  m.l2 = l2_args(pl, offsets, expert_token_nums, pool_src, a_pool, as, w2, w2_scale, topk_weights, workspace);
+  m.l2 = l2_args(pl, offsets, counts, pool_src, a_pool, as, w2, w2_scale, topk_weights, workspace);
+  m.counts_out = expert_token_nums;
   m.cb = combine_args(pl, m.l2.contrib, r2p, y);
   m.ctl = at<uint32_t>(workspace, L.ctl);
-  m.nwaves = dispatch_waves(pl.prob.num_tokens, (int)pl.prob.num_topk);
+  m.nwaves = dispatch_waves(pl.prob.num_tokens, (int)slots_per_token(pl.prob));
   // Linear1 reads the token rows in place (x, or the token codes) through
   // pool_src when the token matrix fits one buffer descriptor
   const int64_t tok_bytes = pl.prob.num_tokens * pl.prob.hidden * elem_size(pl.prob.usecase);
@@ -532,24 +561,29 @@ mm_status mm_read_device_error(const mm_plan* plan, const void* workspace, int32
 
 mm_status mm_debug_raw_accumulators(const mm_plan* plan, int which, const int32_t* expert_offsets,
                                     const int32_t* expert_counts, const void* act_pool, const void* w_prepared,
-                                    int32_t* c_out, void* stream) {
+                                    int32_t* c_out, void* workspace, uint64_t workspace_bytes, void* stream) {
   MM_TRY(check_plan(plan));
   const mm_problem& p = plan->prob;
   if (p.usecase != MM_A8W8_INT8) return MM_ERR_UNSUPPORTED;
   if ((which != 1 && which != 2) || !ok4(expert_offsets) || !ok4(expert_counts) || !ok16(act_pool) ||
-      !ok16(w_prepared) || !ok4(c_out))
+      !ok16(w_prepared) || !ok4(c_out) || !ok16(workspace))
     return MM_ERR_INVALID_ARG;
+  if ((int64_t)workspace_bytes < plan->workspace_bytes) return MM_ERR_WORKSPACE;
+  const WsLayout L = ws_layout(*plan);
   GemmArgs g{};
   g.A = static_cast<const uint8_t*>(act_pool);
   g.B = static_cast<const uint8_t*>(w_prepared);
   g.offsets = expert_offsets;
   g.counts = expert_counts;
   g.P = plan->pool_rows;
-  g.E = (int)p.num_experts;
+  g.E = (int)all_experts(p);
   g.I = (int)p.intermediate_hidden;
   g.H = (int)p.hidden;
-  g.K = (int)p.num_topk;
+  g.K = (int)slots_per_token(p);
+  g.Kr = (int)p.num_topk;
   g.raw_out = c_out;
+  g.err = at<uint32_t>(workspace, L.ctl) + 1;
+  set_split(g, *plan, L, workspace);   // tail tiles split along K as in the entry points
   if (which == 1) {
     g.N = (int)(2 * p.intermediate_hidden);
     g.Kdim = (int)p.hidden;
@@ -562,7 +596,35 @@ mm_status mm_debug_raw_accumulators(const mm_plan* plan, int which, const int32_
   const int tile = which == 1 ? plan->tile_l1 : plan->tile_l2;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int grid = gemm_grid(tile, plan->pool_rows, g.N, num_cus());
+  MM_TRY(clear_split_flags(g, s));
   return run(which == 1 ? MM_K_L1 : MM_K_L2, s, [&] { return launch_gemm(2, p.usecase, tile, false, g, grid, s); });
+}
+
+mm_status mm_read_kernel_clock(const mm_plan* plan, const void* workspace, uint64_t* host_out, void* stream) {
+  MM_TRY(check_plan(plan));
+  if (!ok16(workspace) || !host_out) return MM_ERR_INVALID_ARG;
+  const uint8_t* words = static_cast<const uint8_t*>(workspace) + ws_layout(*plan).ctl + kClockWord0 * 4;
+  if (hipMemcpyAsync(host_out, words, 32, hipMemcpyDeviceToHost, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return MM_ERR_HIP;
+  return MM_OK;
+}
+
+mm_status mm_debug_fused_layout(const mm_plan* plan, const void* workspace, int32_t* offsets_out,
+                                int32_t* pool_src_out, int32_t* route_to_pool_out, void* stream) {
+  MM_TRY(check_plan(plan));
+  if (!ok16(workspace) || !ok4(offsets_out) || !ok4(pool_src_out) || !ok4(route_to_pool_out))
+    return MM_ERR_INVALID_ARG;
+  const mm_problem& p = plan->prob;
+  const WsLayout L = ws_layout(*plan);
+  const uint8_t* ws = static_cast<const uint8_t*>(workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const struct { void* dst; int64_t off, bytes; } parts[3] = {
+      {offsets_out, L.offsets, (all_experts(p) + 1) * 4},
+      {pool_src_out, L.pool_src, plan->pool_rows * 4},
+      {route_to_pool_out, L.route_to_pool, p.num_tokens * slots_per_token(p) * 4}};
+  for (const auto& c : parts)
+    if (hipMemcpyAsync(c.dst, ws + c.off, (size_t)c.bytes, hipMemcpyDeviceToDevice, s) != hipSuccess) return MM_ERR_HIP;
+  return MM_OK;
 }
 
 mm_status mm_trace_enable(int on) {

@@ -7,6 +7,11 @@
 
 namespace mm {
 
+// Route numbering.  A token has K = Kr + S slots: its Kr routed top-k
+// choices, then S (0 or 1) shared-expert slots; route r = i*K + k.  Experts
+// 0 .. Er-1 are the routed ones, expert Er + s is shared expert s, which
+// every active token visits with gate weight 1.
+//
 // Wavefront-to-route mapping shared by the count and scatter kernels: one
 // wave owns floor(64/K) consecutive tokens (its lanes hold (token, slot)
 // pairs, lane = t*K + k; the remaining lanes idle).
@@ -15,7 +20,8 @@ inline int64_t dispatch_waves(int64_t T, int K) { return (T + tokens_per_wave(K)
 constexpr int kDispatchWavesPerBlock = 4;
 
 struct DispatchArgs {
-  const int32_t* topk_ids;   // [T][K]
+  const int32_t* topk_ids;   // [T][Kr]
+  const int8_t* active;      // [T] x_active_mask (0: token inactive), or null (all active)
   const void* x;             // bf16 [T][H]
   int32_t* counts;           // [E]
   int32_t* offsets;          // [E+1]
@@ -27,6 +33,7 @@ struct DispatchArgs {
   uint32_t* err;             // ws: device error word (mm_device_error bits)
   int64_t T, H, P;
   int E, K, block_m, usecase;
+  int Er, Kr;                // routed experts and routed top-k (E = Er + S, K = Kr + S)
 };
 
 // Tile configurations of the grouped GEMMs (compile-time instances).
@@ -48,6 +55,7 @@ struct GemmArgs {
   int64_t routes;            // T*K
   uint32_t* err;             // device error word (mm_device_error bits)
   int E, N, Kdim, I, H, K;
+  int Kr;                    // routed slots per token (slots Kr .. K-1: shared experts, gate weight 1)
   int gate_up_group;
   int group_m;               // M-blocks per tile group of an expert (0: all of them)
   // Linear1 (mode 0)
@@ -57,7 +65,7 @@ struct GemmArgs {
   float* a_stage;            // [P][I] f32 (A8W8)
   // Linear2 (mode 1)
   const float* a_scale;      // [P] (A8W8)
-  const float* topk_w;       // [T*K]
+  const float* topk_w;       // [T][Kr]
   void* contrib;             // [T*K][H] float32 (A16W16) or bf16 (A8W8)
   // debug (mode 2: raw int32 accumulators)
   int32_t* raw_out;
@@ -98,6 +106,9 @@ struct CombineArgs {
 // they are zero again when a GEMM ends).
 constexpr int kSplitSlots = 512;
 constexpr int kSplitFlag0 = 64;
+// [kClockWord0, +8): the fused kernel's clock sample, four 64-bit words:
+// shader-clock counter at start and end, 100 MHz counter at start and end
+constexpr int kClockWord0 = 48;
 constexpr int kCtlWords = kSplitFlag0 + kSplitSlots;
 
 // Everything the fused persistent kernel needs: the arguments of each phase.
@@ -114,10 +125,14 @@ struct MegaArgs {
   float* x_tok_scale;        // [T] (A8W8)
   int l1_by_token;
   uint32_t spin_limit;       // polls before a grid barrier gives up
+  // the routed experts' counts for the caller (expert_token_nums [Er]);
+  // d.counts is the workspace's own [E] array (shared experts included)
+  int32_t* counts_out;
 };
 
 // launchers (return hipError_t of the launch)
-hipError_t launch_zero(int32_t* counts, int E, uint32_t* ctl, hipStream_t s);
+// clears counts[0..E) and ctl words [ctl_first, ctl_first + ctl_n)
+hipError_t launch_zero(int32_t* counts, int E, uint32_t* ctl, int ctl_first, int ctl_n, hipStream_t s);
 hipError_t launch_mega_prep(const MegaArgs& a, MegaArgs* dev_args, hipStream_t s);
 hipError_t launch_mega(int usecase, int tile, bool exact_l1, const MegaArgs* dev_args, int grid, hipStream_t s);
 int mega_grid(int tile, int num_cus);

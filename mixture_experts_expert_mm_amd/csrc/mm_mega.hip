@@ -113,6 +113,13 @@ void k_mega(const MegaArgs* mp) {
   uint32_t* const ctl = m.ctl;
   const uint32_t spin = m.spin_limit;
   const int64_t nwaves = m.nwaves;
+  // clock sample of this run: shader-clock counter and the constant 100 MHz
+  // counter, read by workgroup 0 when it starts and when it is done
+  if (blockIdx.x == 0 && t == 0) {
+    uint64_t* clk = reinterpret_cast<uint64_t*>(ctl + kClockWord0);
+    clk[0] = __builtin_amdgcn_s_memtime();
+    clk[2] = __builtin_amdgcn_s_memrealtime();
+  }
   BarState bs;
   barrier_register(ctl, bs);
   uint32_t nb = 0;
@@ -145,6 +152,9 @@ void k_mega(const MegaArgs* mp) {
     }
   }
   if (!grid_barrier(ctl, ++nb, spin, bs, &ok)) return;
+  // the counts are final: the routed experts' ones go to the caller
+  if (blockIdx.x == 0)
+    for (int e = t; e < m.d.Er; e += NT) m.counts_out[e] = m.d.counts[e];
 
   // padded prefix (every block, into LDS) + scatter
   if (!one_block) {
@@ -199,6 +209,12 @@ void k_mega(const MegaArgs* mp) {
   constexpr int CU = UC == UC_BF16 ? 1 : 2;
   for (int64_t idx = (int64_t)blockIdx.x * NT + t; idx < work; idx += CU * stride)
     combine_items<CU, UC != UC_BF16>(c, idx, stride, work);
+  __syncthreads();
+  if (blockIdx.x == 0 && t == 0) {
+    uint64_t* clk = reinterpret_cast<uint64_t*>(ctl + kClockWord0);
+    clk[1] = __builtin_amdgcn_s_memtime();
+    clk[3] = __builtin_amdgcn_s_memrealtime();
+  }
 }
 
 // Pre-pass: clears the counters the fused kernel accumulates into (expert

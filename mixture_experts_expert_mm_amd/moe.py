@@ -29,26 +29,30 @@ class Intermediates:
 
 
 class ExpertLayer:
-    def __init__(self, T, H, I, E, K, usecase="bf16", y_dtype="bf16", device="cuda", activation_clamp=None):
+    def __init__(self, T, H, I, E, K, usecase="bf16", y_dtype="bf16", device="cuda", activation_clamp=None,
+                 num_shared_experts=0):
         self.T, self.H, self.I, self.E, self.K = T, H, I, E, K
+        self.S = int(num_shared_experts)
+        self.Et, self.Ks = E + self.S, K + self.S      # experts with weights; slots per token
         self.usecase = usecase
         self.y_dtype = y_dtype
         self.device = torch.device(device)
-        self.plan = B.mm_plan_create(T, H, I, E, K, usecase, y_dtype, activation_clamp)
+        self.plan = B.mm_plan_create(T, H, I, E, K, usecase, y_dtype, activation_clamp, self.S)
         self.w1 = self.w2 = self.s1 = self.s2 = None
         self._ws = None
         self._fused_ws = None
 
     # ---------------------------------------------------------------- weights
     def load_weights(self, w1, w2, s1=None, s2=None, stream=None):
-        """Upload formula-layout weights ([E,H,2I], [E,I,H]) and relayout them once."""
+        """Upload formula-layout weights ([E+S,H,2I], [E+S,I,H]; a shared expert last) and relayout them once."""
         dt = _DT[self.usecase]
         w1d = w1.to(self.device).contiguous()
         w2d = w2.to(self.device).contiguous()
         assert w1d.dtype == dt and w2d.dtype == dt
-        assert tuple(w1d.shape) == (self.E, self.H, 2 * self.I) and tuple(w2d.shape) == (self.E, self.I, self.H)
-        self.w1 = torch.empty((self.E, 2 * self.I, self.H), dtype=dt, device=self.device)
-        self.w2 = torch.empty((self.E, self.H, self.I), dtype=dt, device=self.device)
+        Et = self.Et
+        assert tuple(w1d.shape) == (Et, self.H, 2 * self.I) and tuple(w2d.shape) == (Et, self.I, self.H)
+        self.w1 = torch.empty((Et, 2 * self.I, self.H), dtype=dt, device=self.device)
+        self.w2 = torch.empty((Et, self.H, self.I), dtype=dt, device=self.device)
         B.mm_prepare_weights(self.plan, w1d, w2d, self.w1, self.w2, stream)
         if self.usecase != "bf16":
             self.s1 = s1.to(self.device, torch.float32).contiguous()
@@ -72,10 +76,10 @@ class ExpertLayer:
         es = 2 if self.usecase == "bf16" else 1
         i32 = dict(dtype=torch.int32, device=dev)
         return Intermediates(
-            expert_counts=torch.empty(self.E, **i32),
-            expert_offsets=torch.empty(self.E + 1, **i32),
+            expert_counts=torch.empty(self.Et, **i32),
+            expert_offsets=torch.empty(self.Et + 1, **i32),
             pool_src=torch.empty(P, **i32),
-            route_to_pool=torch.empty(self.T * self.K, **i32),
+            route_to_pool=torch.empty(self.T * self.Ks, **i32),
             x_pool=torch.empty(P * self.H * es, dtype=torch.uint8, device=dev),
             x_pool_scale=torch.empty(P, dtype=torch.float32, device=dev) if q else None,
             a_pool=torch.empty(P * self.I * es, dtype=torch.uint8, device=dev),
@@ -87,21 +91,30 @@ class ExpertLayer:
         return torch.empty((self.T, self.H), dtype=dt, device=self.device)
 
     # -------------------------------------------------------------- entries
-    def forward(self, x, topk_ids, topk_weights, y=None, counts=None, stream=None):
-        """mega_moe: returns (y, expert_token_nums)."""
+    def forward(self, x, topk_ids, topk_weights, y=None, counts=None, stream=None, active=None):
+        """mega_moe: returns (y, expert_token_nums).  active: int8 [T] x_active_mask or None."""
         y = self.new_y() if y is None else y
         counts = torch.empty(self.E, dtype=torch.int32, device=self.device) if counts is None else counts
-        B.mega_moe(self.plan, x, topk_ids, topk_weights, self.w1, self.s1, self.w2, self.s2, y, counts,
+        B.mega_moe(self.plan, x, topk_ids, topk_weights, active, self.w1, self.s1, self.w2, self.s2, y, counts,
                    self.workspace(True), stream)
         return y, counts
+
+    def fused_layout(self):
+        """Dispatch metadata the last forward() built in its workspace: (offsets, pool_src, route_to_pool)."""
+        i32 = dict(dtype=torch.int32, device=self.device)
+        off = torch.empty(self.Et + 1, **i32)
+        psrc = torch.empty(self.plan.pool_rows, **i32)
+        r2p = torch.empty(self.T * self.Ks, **i32)
+        B.mm_debug_fused_layout(self.plan, self.workspace(True), off, psrc, r2p)
+        return off, psrc, r2p
 
     def device_error(self, fused: bool = True) -> int:
         """The device error word of the last call on this layer's workspace
         (mm_device_error bits; waits for the device)."""
         return B.mm_read_device_error(self.plan, self.workspace(fused))
 
-    def dispatch(self, x, topk_ids, im: Intermediates, stream=None):
-        B.mm_dispatch_layout(self.plan, topk_ids, x, im.expert_counts, im.expert_offsets, im.pool_src,
+    def dispatch(self, x, topk_ids, im: Intermediates, stream=None, active=None):
+        B.mm_dispatch_layout(self.plan, topk_ids, active, x, im.expert_counts, im.expert_offsets, im.pool_src,
                              im.route_to_pool, im.x_pool, im.x_pool_scale, self.workspace(False), stream)
 
     def linear1(self, im: Intermediates, stream=None):
@@ -113,10 +126,10 @@ class ExpertLayer:
                                 im.a_pool, im.a_pool_scale, self.w2, self.s2, topk_weights, y,
                                 self.workspace(False), stream)
 
-    def forward_3call(self, x, topk_ids, topk_weights, stream=None):
+    def forward_3call(self, x, topk_ids, topk_weights, stream=None, active=None):
         im = self.new_intermediates()
         y = self.new_y()
-        self.dispatch(x, topk_ids, im, stream)
+        self.dispatch(x, topk_ids, im, stream, active)
         self.linear1(im, stream)
         self.linear2_combine(im, topk_weights, y, stream)
         return y, im

@@ -24,6 +24,12 @@ Recipe (all draws are numpy PCG64, float32):
 * Optional masked routes (DeepEP metadata notes, section 5.2): each route is
   set to id -1 with probability ``masked_ratio`` (stream
   ``default_rng([seed, 4, T])``) and its weight to 0.
+* Optional shared expert (DeepGEMM MegaMoE page, section 6): ``shared = 1``
+  adds expert index ``E`` to the weight arrays, drawn like a routed expert
+  (stream ``default_rng([seed, 0, E])``).
+* Optional x_active_mask (Ascend page, Parameters): each token is inactive
+  with probability ``inactive_ratio`` (stream ``default_rng([seed, 5, T])``);
+  ``active_mask`` returns int8 [T] (1 active, 0 inactive) or None.
 
 Quantised use cases take the weights offline to the use case's dtype, as the
 Ascend page's A2/A3 example does before calling the operator: per output
@@ -59,6 +65,8 @@ class Config:
     bias_std: float
     seed: int
     masked_ratio: float = 0.0
+    shared: int = 0
+    inactive_ratio: float = 0.0
 
     @property
     def routes(self) -> int:
@@ -114,6 +122,14 @@ def routing(cfg: Config):
         ids = np.where(m, np.int32(-1), ids)
         wts = np.where(m, np.float32(0.0), wts)
     return torch.from_numpy(np.ascontiguousarray(ids)), torch.from_numpy(np.ascontiguousarray(wts))
+
+
+def active_mask(cfg: Config):
+    """x_active_mask as an int8 torch CPU tensor ``[T]``, or None when every token is active."""
+    if cfg.inactive_ratio <= 0:
+        return None
+    off = np.random.default_rng([cfg.seed, 5, cfg.T]).random(cfg.T) < cfg.inactive_ratio
+    return torch.from_numpy((~off).astype(np.int8))
 
 
 def tokens(cfg: Config) -> torch.Tensor:
@@ -182,19 +198,20 @@ def expert_weights(cfg: Config, e: int):
 
 @dataclasses.dataclass
 class Weights:
-    w1: torch.Tensor            # [E, H, 2I]
-    w2: torch.Tensor            # [E, I, H]
-    s1: torch.Tensor | None     # [E, 2I] float32
-    s2: torch.Tensor | None     # [E, H] float32
+    w1: torch.Tensor            # [E+S, H, 2I] (a shared expert last)
+    w2: torch.Tensor            # [E+S, I, H]
+    s1: torch.Tensor | None     # [E+S, 2I] float32
+    s2: torch.Tensor | None     # [E+S, H] float32
 
 
 def all_weights(cfg: Config) -> Weights:
     dt = {"bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn, "int8": torch.int8}[cfg.usecase]
-    w1 = torch.empty((cfg.E, cfg.H, 2 * cfg.I), dtype=dt)
-    w2 = torch.empty((cfg.E, cfg.I, cfg.H), dtype=dt)
+    n = cfg.E + cfg.shared
+    w1 = torch.empty((n, cfg.H, 2 * cfg.I), dtype=dt)
+    w2 = torch.empty((n, cfg.I, cfg.H), dtype=dt)
     q = cfg.usecase != "bf16"
-    s1 = torch.empty((cfg.E, 2 * cfg.I), dtype=torch.float32) if q else None
-    s2 = torch.empty((cfg.E, cfg.H), dtype=torch.float32) if q else None
+    s1 = torch.empty((n, 2 * cfg.I), dtype=torch.float32) if q else None
+    s2 = torch.empty((n, cfg.H), dtype=torch.float32) if q else None
 
     def one(e):
         a, b, c, d = expert_weights(cfg, e)
@@ -205,7 +222,7 @@ def all_weights(cfg: Config) -> Weights:
             s2[e] = d
 
     with ThreadPoolExecutor(_threads()) as ex:
-        list(ex.map(one, range(cfg.E)))
+        list(ex.map(one, range(n)))
     return Weights(w1, w2, s1, s2)
 
 
@@ -216,8 +233,9 @@ class Inputs:
     topk_ids: torch.Tensor
     topk_weights: torch.Tensor
     weights: Weights
+    active: torch.Tensor | None = None   # x_active_mask int8 [T], None: every token active
 
 
 def make_inputs(cfg: Config) -> Inputs:
     ids, wts = routing(cfg)
-    return Inputs(cfg, tokens(cfg), ids, wts, all_weights(cfg))
+    return Inputs(cfg, tokens(cfg), ids, wts, all_weights(cfg), active_mask(cfg))

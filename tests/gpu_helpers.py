@@ -44,7 +44,8 @@ def expert_fn(inp: wl.Inputs):
 
 def make_layer(inp: wl.Inputs, y_dtype="f32", activation_clamp=None):
     c = inp.cfg
-    layer = moe.ExpertLayer(c.T, c.H, c.I, c.E, c.K, c.usecase, y_dtype, "cuda", activation_clamp=activation_clamp)
+    layer = moe.ExpertLayer(c.T, c.H, c.I, c.E, c.K, c.usecase, y_dtype, "cuda", activation_clamp=activation_clamp,
+                            num_shared_experts=c.shared)
     layer.load_weights(inp.weights.w1, inp.weights.w2, inp.weights.s1, inp.weights.s2)
     return layer
 
@@ -53,10 +54,47 @@ def device_inputs(inp: wl.Inputs):
     return inp.x.cuda(), inp.topk_ids.cuda(), inp.topk_weights.cuda()
 
 
+def device_active(inp: wl.Inputs):
+    return None if inp.active is None else inp.active.cuda()
+
+
 def oracle_y(inp: wl.Inputs, tokens=None, activation_clamp=None):
+    c = inp.cfg
     y, _ = oracle.moe_forward(inp.x.float().numpy(), inp.topk_ids.numpy(), inp.topk_weights.numpy(),
-                              expert_fn(inp), inp.cfg.usecase, tokens=tokens, activation_clamp=activation_clamp)
+                              expert_fn(inp), c.usecase, tokens=tokens, activation_clamp=activation_clamp,
+                              shared_expert=c.E if c.shared else None,
+                              active=None if inp.active is None else inp.active.numpy())
     return y
+
+
+def oracle_routes(inp: wl.Inputs) -> np.ndarray:
+    """Route table [T, K+S] (shared slot, inactive tokens -1) from the oracle."""
+    c = inp.cfg
+    ids, _ = oracle.route_table(inp.topk_ids.numpy(), inp.topk_weights.numpy(), c.E if c.shared else None,
+                                None if inp.active is None else inp.active.numpy())
+    return ids
+
+
+def check_layout(inp: wl.Inputs, block_m: int, counts, offs, psrc, r2p):
+    """Bit-exact dispatch metadata against the oracle: counts, padded offsets,
+    per-expert (token, slot) multisets, -1 padding, inverse map, skipped
+    routes.  Returns the valid pool rows."""
+    c = inp.cfg
+    ids = oracle_routes(inp)
+    Et = c.E + c.shared
+    d = oracle.dispatch_layout(ids, Et, block_m)
+    np.testing.assert_array_equal(np.asarray(counts), d["counts"][:len(counts)])
+    np.testing.assert_array_equal(offs, d["offsets"])
+    for e in range(Et):
+        o, n, o1 = offs[e], d["counts"][e], offs[e + 1]
+        np.testing.assert_array_equal(np.sort(psrc[o:o + n]), d["routes"][e])
+        assert np.all(psrc[o + n:o1] == -1)
+    flat = ids.reshape(-1)
+    valid = flat >= 0
+    assert np.all(r2p[~valid] == -1)
+    rv = np.nonzero(valid)[0]
+    np.testing.assert_array_equal(psrc[r2p[rv]], rv)
+    return np.concatenate([np.arange(offs[e], offs[e] + d["counts"][e]) for e in range(Et)])
 
 
 def rel_err(y_gpu: np.ndarray, y_or: np.ndarray) -> float:

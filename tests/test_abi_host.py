@@ -42,9 +42,9 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_struct_sizes_match_header():
-    # mm_problem: 5 int64 + 3 int32 + float; mm_plan: problem + 4 int32 + 7 int64 + u64 + 8 int64
-    assert ctypes.sizeof(B.MMProblem) == 56
-    assert ctypes.sizeof(B.MMPlan) == 56 + 16 + 56 + 8 + 64
+    # mm_problem: 5 int64 + 3 int32 + float + 2 int32; mm_plan: problem + 4 int32 + 7 int64 + u64 + 8 int64
+    assert ctypes.sizeof(B.MMProblem) == 64
+    assert ctypes.sizeof(B.MMPlan) == 64 + 16 + 56 + 8 + 64
 
 
 def test_plan_sizes_and_block_m():
@@ -76,6 +76,33 @@ def test_plan_rejects_bad_dimensions(dims):
     assert ei.value.status == 1
 
 
+def test_plan_with_shared_expert():
+    _lib()
+    p0 = B.mm_plan_create(4096, 7168, 2048, 32, 8, "fp8")
+    p1 = B.mm_plan_create(4096, 7168, 2048, 32, 8, "fp8", num_shared_experts=1)
+    assert p1.prob.num_shared_experts == 1
+    R1 = 4096 * 9                        # one shared slot per token
+    assert p1.pool_rows % p1.block_m == 0 and p1.pool_rows >= R1 + 33 * (p1.block_m - 1)
+    assert p1.w1_bytes == 33 * 7168 * 4096 and p1.w2_bytes == 33 * 2048 * 7168
+    assert p1.fused_workspace_bytes > p0.fused_workspace_bytes
+    B.mm_plan_create(64, 256, 128, 64, 63, "bf16", num_shared_experts=1)      # 64 slots: the limit
+
+
+@pytest.mark.parametrize("dims,shared", [((64, 256, 128, 8, 2), 2), ((64, 256, 128, 8, 2), -1),
+                                         ((64, 256, 128, 64, 64), 1), ((64, 256, 128, 1024, 2), 1)])
+def test_plan_rejects_bad_shared_experts(dims, shared):
+    _lib()
+    with pytest.raises(B.MMError) as ei:
+        B.mm_plan_create(*dims, "bf16", num_shared_experts=shared)
+    assert ei.value.status == 1
+
+
+def test_plan_rejects_nonzero_reserved():
+    lib = _lib()
+    prob = B.MMProblem(64, 256, 128, 8, 2, B.MM_A16W16, B.MM_OUT_BF16, 0, 0.0, 0, 5)
+    assert lib.mm_plan_create(ctypes.byref(prob), ctypes.byref(B.MMPlan())) == 1
+
+
 @pytest.mark.parametrize("flag,clamp", [(1, -0.5), (1, float("nan")), (2, 1.0)])
 def test_plan_rejects_bad_activation_clamp(flag, clamp):
     lib = _lib()
@@ -103,27 +130,30 @@ def test_entry_points_validate_before_any_hip_call():
     plan = B.mm_plan_create(64, 256, 128, 8, 2, "bf16")
     good = 1 << 20          # an aligned fake address; never dereferenced on these paths
     P = ctypes.byref(plan)
-    # NULL pointer
-    assert lib.mega_moe(P, None, good, good, good, None, good, None, good, good, good, 1 << 40, None) == 1
+    # NULL pointer (x_active_mask, the fifth argument, may be NULL)
+    assert lib.mega_moe(P, None, good, good, None, good, None, good, None, good, good, good, 1 << 40, None) == 1
     # misaligned pointer
-    assert lib.mega_moe(P, good + 2, good, good, good, None, good, None, good, good, good, 1 << 40, None) == 1
+    assert lib.mega_moe(P, good + 2, good, good, None, good, None, good, None, good, good, good, 1 << 40, None) == 1
     # workspace too small
-    assert lib.mega_moe(P, good, good, good, good, None, good, None, good, good, good, 16, None) == 3
-    assert lib.mm_dispatch_layout(P, good, good, good, good, good, good, good, None, good, 16, None) == 3
+    assert lib.mega_moe(P, good, good, good, None, good, None, good, None, good, good, good, 16, None) == 3
+    assert lib.mm_dispatch_layout(P, good, None, good, good, good, good, good, good, None, good, 16, None) == 3
     # a modified plan is rejected
     bad = B.MMPlan.from_buffer_copy(plan)
     bad.pool_rows += 1
-    assert lib.mega_moe(ctypes.byref(bad), good, good, good, good, None, good, None, good, good, good,
+    assert lib.mega_moe(ctypes.byref(bad), good, good, good, None, good, None, good, None, good, good, good,
                         1 << 40, None) == 1
     # quantised plans need the scales
     q = B.mm_plan_create(64, 256, 128, 8, 2, "int8")
-    assert lib.mega_moe(ctypes.byref(q), good, good, good, good, None, good, None, good, good, good,
+    assert lib.mega_moe(ctypes.byref(q), good, good, good, None, good, None, good, None, good, good, good,
                         1 << 40, None) == 1
     # the error word needs a host destination
     assert lib.mm_read_device_error(P, good, None, None) == 1
-    # raw accumulators exist for int8 only
-    assert lib.mm_debug_raw_accumulators(P, 1, good, good, good, good, good, None) == 2
-    assert lib.mm_debug_raw_accumulators(ctypes.byref(q), 3, good, good, good, good, good, None) == 1
+    # raw accumulators exist for int8 only, and need a large enough workspace
+    assert lib.mm_debug_raw_accumulators(P, 1, good, good, good, good, good, good, 1 << 40, None) == 2
+    assert lib.mm_debug_raw_accumulators(ctypes.byref(q), 3, good, good, good, good, good, good, 1 << 40, None) == 1
+    assert lib.mm_debug_raw_accumulators(ctypes.byref(q), 1, good, good, good, good, good, good, 16, None) == 3
+    # the fused-layout reader needs its three destinations
+    assert lib.mm_debug_fused_layout(P, good, good, None, good, None) == 1
 
 
 def test_names():

@@ -20,8 +20,8 @@ from mixture_experts_expert_mm_amd import binding as B
 from mixture_experts_expert_mm_amd import moe
 from mixture_experts_expert_mm_amd import workloads as wl
 
-from gpu_helpers import (TOL, bf16_bits_of_f32, cpu_inputs, device_inputs, expert_fn, log, make_layer, oracle_y,
-                         rel_err)
+from gpu_helpers import (TOL, bf16_bits_of_f32, check_layout, cpu_inputs, device_active, device_inputs, expert_fn,
+                         log, make_layer, oracle_routes, oracle_y, rel_err)
 
 pytestmark = pytest.mark.gpu
 
@@ -36,6 +36,7 @@ SMALL = {
 
 
 def small_cfg(shape: str, usecase: str, **kw) -> wl.Config:
+    """A SMALL shape with the use case's dtype (extra Config fields in kw)."""
     s = SMALL[shape]
     return wl.Config(f"{shape}_{usecase}", usecase, s["T"], s["H"], s["I"], s["E"], s["K"], s["bias"], 2024, **kw)
 
@@ -43,29 +44,14 @@ def small_cfg(shape: str, usecase: str, **kw) -> wl.Config:
 def check_dispatch(layer: moe.ExpertLayer, inp: wl.Inputs, im, sample_rows=None):
     """Bit-exact dispatch metadata and pool rows against the oracle."""
     c = inp.cfg
-    ids = inp.topk_ids.numpy()
-    d = oracle.dispatch_layout(ids, c.E, layer.plan.block_m)
     counts = im.expert_counts.cpu().numpy()
-    offs = im.expert_offsets.cpu().numpy()
+    rows = check_layout(inp, layer.plan.block_m, counts, im.expert_offsets.cpu().numpy(), im.pool_src.cpu().numpy(),
+                        im.route_to_pool.cpu().numpy())
     psrc = im.pool_src.cpu().numpy()
-    r2p = im.route_to_pool.cpu().numpy()
-    np.testing.assert_array_equal(counts, d["counts"])
-    np.testing.assert_array_equal(offs, d["offsets"])
-    assert counts.sum() == int(((ids >= 0) & (ids < c.E)).sum())
-    for e in range(c.E):
-        o, n, o1 = offs[e], counts[e], offs[e + 1]
-        np.testing.assert_array_equal(np.sort(psrc[o:o + n]), d["routes"][e])
-        assert np.all(psrc[o + n:o1] == -1)
-    flat = ids.reshape(-1)
-    valid = (flat >= 0) & (flat < c.E)
-    assert np.all(r2p[~valid] == -1)
-    rv = np.nonzero(valid)[0]
-    np.testing.assert_array_equal(psrc[r2p[rv]], rv)
     # pool rows: x_i itself (bf16) or its quantised codes and scale
-    rows = np.concatenate([np.arange(offs[e], offs[e] + counts[e]) for e in range(c.E)])
     if sample_rows is not None and rows.size > sample_rows:
         rows = np.random.default_rng(0).choice(rows, sample_rows, replace=False)
-    tok = psrc[rows] // c.K
+    tok = psrc[rows] // (c.K + c.shared)
     rows_t = torch.from_numpy(rows).cuda()
     if c.usecase == "bf16":
         xp = im.x_pool.view(torch.int16).view(-1, c.H)[rows_t].cpu()
@@ -175,20 +161,34 @@ def test_tiny_config_all_elements():
 # exact integer accumulators (A8W8-INT)
 # ---------------------------------------------------------------------------
 
-def test_int8_accumulators_exact():
-    cfg = small_cfg("bm64", "int8")
+@pytest.mark.parametrize("shape", ["bm64", "split128", "split64"])
+def test_int8_accumulators_exact(shape, monkeypatch):
+    """int32 accumulators before any scaling equal numpy's int64 products on
+    every valid row.  bm64: the 64 x 128 tile, no split.  split128 / split64:
+    256 routes per expert, so the tail tiles of both GEMMs are split along K
+    (BLOCK_M 128: Linear1 in up to 4 pieces, Linear2 in 2; BLOCK_M 64 forced:
+    more pieces) and piece 0 adds the others' partial sums."""
+    if shape == "bm64":
+        cfg = small_cfg("bm64", "int8")
+    else:
+        cfg = wl.Config(f"{shape}_int8", "int8", 512, 2048, 1024, 8, 4, 0.3, 61)
+        if shape == "split64":
+            monkeypatch.setenv("MM_FORCE_TILE", "0")
     inp = wl.make_inputs(cfg)
     layer = make_layer(inp, "f32")
+    log(f"[int8 exact] {shape}: BLOCK_M {layer.plan.block_m}")
     x, ids, wts = device_inputs(inp)
     im = layer.new_intermediates()
     layer.dispatch(x, ids, im)
     layer.linear1(im)
     P = layer.plan.pool_rows
+    ws = layer.workspace(False)
     c1 = torch.empty((P, 2 * cfg.I), dtype=torch.int32, device="cuda")
     c2 = torch.empty((P, cfg.H), dtype=torch.int32, device="cuda")
-    B.mm_debug_raw_accumulators(layer.plan, 1, im.expert_offsets, im.expert_counts, im.x_pool, layer.w1, c1)
-    B.mm_debug_raw_accumulators(layer.plan, 2, im.expert_offsets, im.expert_counts, im.a_pool, layer.w2, c2)
+    B.mm_debug_raw_accumulators(layer.plan, 1, im.expert_offsets, im.expert_counts, im.x_pool, layer.w1, c1, ws)
+    B.mm_debug_raw_accumulators(layer.plan, 2, im.expert_offsets, im.expert_counts, im.a_pool, layer.w2, c2, ws)
     torch.cuda.synchronize()
+    assert layer.device_error(fused=False) == 0
     offs = im.expert_offsets.cpu().numpy()
     counts = im.expert_counts.cpu().numpy()
     psrc = im.pool_src.cpu().numpy()
@@ -205,6 +205,68 @@ def test_int8_accumulators_exact():
         np.testing.assert_array_equal(c1[rows], q[psrc[rows] // cfg.K].astype(np.int64) @ w1)
         np.testing.assert_array_equal(c2[rows], a_codes[rows] @ w2)
         assert np.all(np.abs(a_codes[rows]) <= 127)
+
+
+def test_gemm_entry_points_on_a_dirty_workspace():
+    """The GEMM entry points clear the split-tile flags themselves: Linear1
+    and Linear2 run on a separate workspace filled with 0xFF (as a fresh
+    allocation may be) give Y bit-equal to a clean run, on an int8 shape
+    whose tail tiles are split along K."""
+    cfg = wl.Config("dirty_ws_int8", "int8", 512, 2048, 1024, 8, 4, 0.3, 62)
+    inp = wl.make_inputs(cfg)
+    layer = make_layer(inp, "f32")
+    x, ids, wts = device_inputs(inp)
+    y_ref, _ = layer.forward_3call(x, ids, wts)
+    im = layer.new_intermediates()
+    layer.dispatch(x, ids, im)
+    dirty = torch.full((layer.plan.workspace_bytes,), 255, dtype=torch.uint8, device="cuda")
+    y = layer.new_y()
+    log("[dirty workspace] int8 L1 + L2 on a 0xFF workspace")
+    B.mm_grouped_l1_swiglu(layer.plan, im.expert_offsets, im.expert_counts, im.x_pool, im.x_pool_scale, layer.w1,
+                           layer.s1, im.a_pool, im.a_pool_scale, dirty)
+    B.mm_grouped_l2_combine(layer.plan, im.expert_offsets, im.expert_counts, im.pool_src, im.route_to_pool, im.a_pool,
+                            im.a_pool_scale, layer.w2, layer.s2, wts, y, dirty)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int32), y_ref.view(torch.int32))
+
+
+# ---------------------------------------------------------------------------
+# shared expert and x_active_mask
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("shape", ["bm64", "bm128"])
+@pytest.mark.parametrize("usecase", ["bf16", "fp8", "int8"])
+@pytest.mark.parametrize("variant", ["shared", "active", "shared_active"])
+def test_shared_expert_and_active_mask(shape, usecase, variant):
+    """A shared expert (one more slot per token, weight 1) and/or an
+    x_active_mask with about a third of the tokens inactive: Y within the
+    oracle tolerance, inactive rows exactly 0, fused == three-call bit for
+    bit, the dispatch metadata of both paths bit-exact, expert_token_nums
+    the routed experts' counts."""
+    cfg = small_cfg(shape, usecase, masked_ratio=0.1, shared=int("shared" in variant),
+                    inactive_ratio=0.35 if "active" in variant else 0.0)
+    inp = wl.make_inputs(cfg)
+    log(f"[{variant}] {cfg.name}")
+    layer = make_layer(inp, "f32")
+    x, ids, wts = device_inputs(inp)
+    act = device_active(inp)
+    y_f, c_f = layer.forward(x, ids, wts, active=act)
+    y_f = y_f.clone()
+    off, psrc, r2p = (t.cpu().numpy() for t in layer.fused_layout())
+    y_3, im = layer.forward_3call(x, ids, wts, active=act)
+    torch.cuda.synchronize()
+    assert layer.device_error(fused=True) == 0 and layer.device_error(fused=False) == 0
+    assert torch.equal(y_f.view(torch.int32), y_3.view(torch.int32))
+    check_dispatch(layer, inp, im)
+    check_layout(inp, layer.plan.block_m, c_f.cpu().numpy(), off, psrc, r2p)
+    np.testing.assert_array_equal(c_f.cpu().numpy(), im.expert_counts.cpu().numpy()[:cfg.E])
+    y_or = oracle_y(inp)
+    err = rel_err(y_f.cpu().double().numpy(), y_or)
+    log(f"    max|dY|/rms = {err:.3e}")
+    assert err <= TOL[usecase], err
+    if inp.active is not None:
+        off_rows = (inp.active.numpy() == 0)
+        assert off_rows.any() and not y_f.cpu().numpy()[off_rows].any()
 
 
 # ---------------------------------------------------------------------------
@@ -508,15 +570,40 @@ def test_prepare_weights_layout(usecase):
 
 
 # ---------------------------------------------------------------------------
-# full-size configurations, the launch configuration the benchmark times,
-# sampled tokens against the per-token oracle
+# full-size configurations, in the launch configuration the benchmark times
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("name", ["mid_bf16", "dsv3_bf16", "dsv3_fp8_t128", "dsv3_fp8_t16384", "dsv3_int8",
-                                  "dsv3_bf16_t16384", "dsv3_bf16_t128"])
-def test_full_config_sampled_tokens(name):
-    """Every workload at its full size: two fused calls agree bit for bit, Y on
-    12 sampled tokens is within the oracle tolerance, counts match."""
+def _tokens_covering_every_m_block(inp, offs, psrc, block_m, extra, seed=11):
+    """One token of the first and of the last valid row of every M-block of
+    every expert (so every tile row-block and every ragged tail is compared),
+    plus `extra` random tokens."""
+    c = inp.cfg
+    Ks = c.K + c.shared
+    ids = oracle_routes(inp)
+    counts = np.bincount(ids[ids >= 0].ravel(), minlength=c.E + c.shared)
+    toks = set()
+    for e in range(c.E + c.shared):
+        for j in range(0, counts[e], block_m):
+            for r in (j, min(counts[e], j + block_m) - 1):
+                toks.add(int(psrc[offs[e] + r]) // Ks)
+    rng = np.random.default_rng(seed)
+    toks.update(rng.choice(c.T, min(c.T, extra), replace=False).tolist())
+    return np.array(sorted(toks))
+
+
+FULL = ["tiny_bf16", "mid_bf16", "dsv3_bf16", "dsv3_fp8_t128", "dsv3_bf16_t128", "dsv3_fp8_t16384", "dsv3_int8",
+        "dsv3_bf16_t16384"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_config(name):
+    """Every workload at its full size, through mega_moe as the benchmark
+    times it: the fused kernel's own dispatch metadata (offsets, pool rows,
+    inverse map) bit-exact against the oracle; two fused calls and the
+    three-call path agree bit for bit; the three-call dispatch bit-exact too
+    (pool rows sampled); Y within the oracle tolerance on every token up to
+    4096 tokens, else on a token of the first and last row of every M-block
+    of every expert plus 512 random ones."""
     cfg = wl.CONFIGS[name]
     log(f"[full] {name}: generating inputs")
     inp = cpu_inputs(cfg)
@@ -524,18 +611,30 @@ def test_full_config_sampled_tokens(name):
     layer = make_layer(inp, "f32")
     y32, counts = layer.forward(x, ids, wts)
     y32 = y32.clone()
+    off, psrc, r2p = (t.cpu().numpy() for t in layer.fused_layout())
     y_again, _ = layer.forward(x, ids, wts)
     torch.cuda.synchronize()
+    assert layer.device_error(fused=True) == 0
     assert torch.equal(y32.view(torch.int32), y_again.view(torch.int32)), "two calls differ"
     del y_again
-    rng = np.random.default_rng(11)
-    tokens = np.sort(rng.choice(cfg.T, min(cfg.T, 12), replace=False))
+    log(f"[full] {name}: fused metadata")
+    check_layout(inp, layer.plan.block_m, counts.cpu().numpy(), off, psrc, r2p)
+    y3, im = layer.forward_3call(x, ids, wts)
+    torch.cuda.synchronize()
+    assert layer.device_error(fused=False) == 0
+    assert torch.equal(y32.view(torch.int32), y3.view(torch.int32)), "fused != three-call"
+    log(f"[full] {name}: three-call metadata")
+    check_dispatch(layer, inp, im, sample_rows=4096)
+    del y3, im
+    layer._ws = None
+    if cfg.T <= 4096:
+        tokens = np.arange(cfg.T)
+    else:
+        tokens = _tokens_covering_every_m_block(inp, off, psrc, layer.plan.block_m, extra=512)
     log(f"[full] {name}: oracle on {tokens.size} tokens")
     y_or = oracle_y(inp, tokens=tokens)
     err = rel_err(y32[torch.from_numpy(tokens).cuda()].cpu().double().numpy(), y_or)
     log(f"[full] {name}: max|dY|/rms = {err:.3e}")
     assert err <= TOL[cfg.usecase], err
-    ids_np = inp.topk_ids.numpy()
-    np.testing.assert_array_equal(counts.cpu().numpy(), np.bincount(ids_np.ravel(), minlength=cfg.E))
     del layer
     torch.cuda.empty_cache()

@@ -65,3 +65,16 @@ def test_quantised_weights_per_channel():
         assert torch.all(qv.abs().amax(0) == qmax)            # one element per channel hits Qmax
         w1, _ = wl.expert_weights_f32(cfg, 1)
         assert torch.allclose(qv * s[None, :], w1, rtol=0.07, atol=float(s.max()) * 0.51)
+
+
+def test_shared_expert_weights_and_active_mask():
+    cfg = wl.Config("s", "int8", 40, 256, 128, 4, 2, 0.0, 5, shared=1, inactive_ratio=0.3)
+    w = wl.all_weights(cfg)
+    assert w.w1.shape == (5, 256, 256) and w.s2.shape == (5, 256)
+    # the shared expert is drawn like expert index E of the routed recipe
+    q1, q2, s1, s2 = wl.expert_weights(cfg, 4)
+    assert torch.equal(w.w1[4], q1) and torch.equal(w.s1[4], s1)
+    m = wl.active_mask(cfg)
+    assert m.dtype == torch.int8 and m.shape == (40,) and set(m.tolist()) <= {0, 1}
+    assert torch.equal(m, wl.active_mask(cfg)) and 0 < int(m.sum()) < 40
+    assert wl.active_mask(cfg.with_(inactive_ratio=0.0)) is None
