@@ -127,8 +127,8 @@ typedef struct mm_plan {
   int64_t w2_bytes;           /* (E+S) * I * H * elem(usecase) */
   int64_t workspace_bytes;    /* scratch of the three-call path */
   int64_t fused_workspace_bytes; /* scratch of mega_moe (holds the pool too) */
-  uint64_t checksum;          /* guards against a modified plan */
-  int64_t reserved[8];
+  uint64_t checksum;          /* guards against a modified plan (covers every other byte) */
+  int64_t reserved[8];        /* internal choices of the plan (workspace layout); do not modify */
 } mm_plan;
 
 /* Elements: bf16 = 2 bytes, e4m3fn / int8 = 1 byte. */

@@ -26,11 +26,12 @@ int64_t all_experts(const mm_problem& p) { return p.num_experts + p.num_shared_e
 int64_t slots_per_token(const mm_problem& p) { return p.num_topk + p.num_shared_experts; }
 
 uint64_t plan_checksum(const mm_plan* p) {
-  // FNV-1a over every field except the checksum itself
+  // FNV-1a over every byte of the plan except the checksum itself
   const uint8_t* b = reinterpret_cast<const uint8_t*>(p);
-  const size_t n = offsetof(mm_plan, checksum);
+  const size_t skip0 = offsetof(mm_plan, checksum), skip1 = skip0 + sizeof(p->checksum);
   uint64_t h = 1469598103934665603ull;
-  for (size_t i = 0; i < n; ++i) {
+  for (size_t i = 0; i < sizeof(mm_plan); ++i) {
+    if (i >= skip0 && i < skip1) continue;
     h ^= b[i];
     h *= 1099511628211ull;
   }
@@ -38,6 +39,12 @@ uint64_t plan_checksum(const mm_plan* p) {
 }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Choices the plan makes for the workspace layout, kept in its reserved
+// words: [0] the fused kernel's Linear1 reads token rows in place (no pool
+// rows gathered), [1] the largest K split of a tail tile (1: none).
+bool plan_by_token(const mm_plan& pl) { return pl.reserved[0] != 0; }
+int plan_max_split(const mm_plan& pl) { return (int)pl.reserved[1]; }
 
 // ---------------------------------------------------------------- workspace
 struct WsLayout {
@@ -58,20 +65,22 @@ WsLayout ws_layout(const mm_plan& pl) {
   L.a_stage = q ? take(P * p.intermediate_hidden * 4) : -1;
   L.contrib = take(R * p.hidden * (q ? 2 : 4));   // combine slots: bf16 for A8W8, float32 for A16W16
   // partial sums of split tail tiles: one slot per piece in flight
-  L.partials = take((int64_t)kSplitSlots * tile_bm(pl.tile_l1) * tile_bn(pl.tile_l1) * 4);
+  L.partials = plan_max_split(pl) > 1 ? take((int64_t)kSplitSlots * tile_bm(pl.tile_l1) * tile_bn(pl.tile_l1) * 4) : -1;
   L.end = o;
   L.mega_args = take(sizeof(MegaArgs));
   L.counts = take(Et * 4);
   L.offsets = take((Et + 1) * 4);
   L.pool_src = take(P * 4);
   L.route_to_pool = take(R * 4);
-  L.x_pool = take(pl.x_pool_bytes);
-  L.x_pool_scale = take(P * 4);
+  // pool rows only when the fused Linear1 cannot read the token rows in place
+  const bool tok = plan_by_token(pl);
+  L.x_pool = tok ? -1 : take(pl.x_pool_bytes);
+  L.x_pool_scale = tok ? -1 : take(P * 4);
   L.a_pool = take(pl.a_pool_bytes);
   L.a_pool_scale = take(P * 4);
   // A8W8 codes and scales of the T tokens (the fused kernel's Linear1 reads token rows in place)
-  L.x_tok = q ? take(p.num_tokens * p.hidden) : -1;
-  L.x_tok_scale = q ? take(p.num_tokens * 4) : -1;
+  L.x_tok = q && tok ? take(p.num_tokens * p.hidden) : -1;
+  L.x_tok_scale = q && tok ? take(p.num_tokens * 4) : -1;
   L.fused_end = o;
   return L;
 }
@@ -192,24 +201,24 @@ uint32_t barrier_spin_limit() {
   return 1u << 21;
 }
 
-// Largest K split of a tail tile (MM_MAX_SPLIT overrides: 1 turns it off).
-// Only int8 splits by default: its partial sums are exact int32.  With
-// float accumulators a split tile rounds differently from an unsplit one,
-// and which M-block of its expert (so which tile) a route lands in depends
-// on the order in which the dispatch's atomics claim pool rows; unsplit,
-// every route's result depends on its own row alone, so the output is the
-// same on every call and in both paths.  Split only in the compute regime:
-// measured, splitting the last round's tiles makes the 2048 x 4096 layer
-// 2-3% faster and costs the 128-token 7168 x 2048 layers 3-5% (the partial
-// sums add traffic to a step that is already bound by streaming the
-// weights); neutral in between.
-int max_split(const mm_plan& pl) {
+// Largest K split of a tail tile, chosen by the plan (MM_MAX_SPLIT, read
+// when the plan is made, overrides it: 1 turns it off).  Only int8 splits
+// by default: its partial sums are exact int32.  With float accumulators a
+// split tile rounds differently from an unsplit one, and which M-block of
+// its expert (so which tile) a route lands in depends on the order in which
+// the dispatch's atomics claim pool rows; unsplit, every route's result
+// depends on its own row alone, so the output is the same on every call and
+// in both paths.  Split only in the compute regime: measured, splitting the
+// last round's tiles makes the 2048 x 4096 layer 2-3% faster and costs the
+// 128-token 7168 x 2048 layers 3-5% (the partial sums add traffic to a step
+// that is already bound by streaming the weights); neutral in between.
+int choose_max_split(const mm_problem& p) {
   if (const char* v = std::getenv("MM_MAX_SPLIT")) {
     const int n = std::atoi(v);
     if (n >= 1 && n <= 8) return n;
   }
-  if (pl.prob.usecase != MM_A8W8_INT8) return 1;
-  const double expected = (double)(pl.prob.num_tokens * pl.prob.num_topk) / (double)pl.prob.num_experts;
+  if (p.usecase != MM_A8W8_INT8) return 1;
+  const double expected = (double)(p.num_tokens * p.num_topk) / (double)p.num_experts;
   return expected >= 96 ? 8 : 1;
 }
 
@@ -227,17 +236,20 @@ bool fp8_l1_exact(const mm_plan& pl) {
   return pl.prob.intermediate_hidden < 1024;
 }
 
-// Fused kernel: Linear1 reads token rows in place (MM_L1_BY_TOKEN=0 gathers
-// the pool rows instead; a tuning switch).
-bool by_token_enabled() {
+// Fused kernel: Linear1 reads the token rows in place through pool_src when
+// the token matrix fits one buffer descriptor (< 2^31 bytes); otherwise the
+// pool rows are gathered.  MM_L1_BY_TOKEN=0, read when the plan is made,
+// forces the gather (a tuning switch).
+bool choose_by_token(const mm_problem& p) {
   const char* v = std::getenv("MM_L1_BY_TOKEN");
-  return !(v && v[0] == '0');
+  if (v && v[0] == '0') return false;
+  return p.num_tokens * p.hidden * elem_size(p.usecase) < ((int64_t)1 << 31);
 }
 
 void set_split(GemmArgs& g, const mm_plan& pl, const WsLayout& L, void* ws) {
   g.partials = at<uint32_t>(ws, L.partials);
   g.split_flags = at<uint32_t>(ws, L.ctl) + kSplitFlag0;
-  g.max_split = max_split(pl);
+  g.max_split = plan_max_split(pl);
   g.spin_limit = barrier_spin_limit();
 }
 
@@ -423,6 +435,8 @@ mm_status mm_plan_create(const mm_problem* problem, mm_plan* plan) {
   pl.tile_l2 = tile;
   pl.block_m = tile_bm(tile);
   pl.gate_up_group = 32;
+  pl.reserved[0] = choose_by_token(p) ? 1 : 0;
+  pl.reserved[1] = choose_max_split(p);
   const int64_t P = align_up(R + all_experts(p) * (pl.block_m - 1), pl.block_m);
   if (P > ((int64_t)1 << 31) - 1) return MM_ERR_INVALID_ARG;
   pl.pool_rows = P;
@@ -530,8 +544,7 @@ mm_status mega_moe(const mm_plan* plan, const void* x, const int32_t* topk_ids, 
   m.nwaves = dispatch_waves(pl.prob.num_tokens, (int)slots_per_token(pl.prob));
   // Linear1 reads the token rows in place (x, or the token codes) through
   // pool_src when the token matrix fits one buffer descriptor
-  const int64_t tok_bytes = pl.prob.num_tokens * pl.prob.hidden * elem_size(pl.prob.usecase);
-  if (tok_bytes < ((int64_t)1 << 31) && by_token_enabled()) {
+  if (plan_by_token(pl)) {
     m.l1_by_token = 1;
     m.x_tok = q ? at<uint8_t>(workspace, L.x_tok) : nullptr;
     m.x_tok_scale = q ? at<float>(workspace, L.x_tok_scale) : nullptr;
@@ -612,8 +625,8 @@ mm_status mm_read_kernel_clock(const mm_plan* plan, const void* workspace, uint6
 mm_status mm_debug_fused_layout(const mm_plan* plan, const void* workspace, int32_t* offsets_out,
                                 int32_t* pool_src_out, int32_t* route_to_pool_out, void* stream) {
   MM_TRY(check_plan(plan));
-  if (!ok16(workspace) || !ok4(offsets_out) || !ok4(pool_src_out) || !ok4(route_to_pool_out))
-    return MM_ERR_INVALID_ARG;
+  if (!ok4(offsets_out) || !ok4(pool_src_out) || !ok4(route_to_pool_out)) return MM_ERR_INVALID_ARG;
+  if (!ok16(workspace)) return MM_ERR_INVALID_ARG;
   const mm_problem& p = plan->prob;
   const WsLayout L = ws_layout(*plan);
   const uint8_t* ws = static_cast<const uint8_t*>(workspace);

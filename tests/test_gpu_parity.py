@@ -401,11 +401,12 @@ def test_split_tail_tiles(usecase, tile, monkeypatch):
     inp = wl.make_inputs(cfg)
     x, ids, wts = device_inputs(inp)
     monkeypatch.setenv("MM_FORCE_TILE", tile)   # the piece counts above
-    layer = make_layer(inp, "f32")
-    monkeypatch.setenv("MM_MAX_SPLIT", "1")
-    y_one, _ = layer.forward(x, ids, wts)
+    monkeypatch.setenv("MM_MAX_SPLIT", "1")     # read when the plan is made
+    y_one, _ = make_layer(inp, "f32").forward(x, ids, wts)
     y_one = y_one.clone()
     monkeypatch.setenv("MM_MAX_SPLIT", "8")
+    layer = make_layer(inp, "f32")
+    assert layer.plan.workspace_bytes > 0
     log(f"[split] {usecase}, BLOCK_M {64 << int(tile)}: unsplit vs split tail tiles")
     y_f, _ = layer.forward(x, ids, wts)
     y_3, _ = layer.forward_3call(x, ids, wts)
