@@ -272,6 +272,26 @@ mm_status mega_moe(const mm_plan* plan, const void* x, const int32_t* topk_ids,
                    const void* w2, const float* w2_scale, void* y, int32_t* expert_token_nums,
                    void* workspace, uint64_t workspace_bytes, void* stream);
 
+/*
+ * mega_moe_noalloc -- mega_moe for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, semantics and results as mega_moe
+ * (bit for bit), without the workspace argument: the workspace is a static
+ * device array of the library, 96 MiB, one per GPU the library runs on,
+ * held until the process ends.  Allocates nothing and frees nothing.
+ * Plans whose fused_workspace_bytes exceed 96 MiB get MM_ERR_WORKSPACE
+ * (the DeepSeek-V3-shape layer, hidden 7168, intermediate 2048, 32 experts,
+ * top-8, fits up to 128 tokens in every use case).  Every call on a GPU
+ * shares that GPU's array and leaves its contents behind (the call clears
+ * its counters itself): calls that overlap on one GPU, on any streams, race.
+ * mm_read_device_error and mm_debug_fused_layout read this array when
+ * passed a NULL workspace.
+ */
+mm_status mega_moe_noalloc(const mm_plan* plan, const void* x, const int32_t* topk_ids,
+                           const float* topk_weights, const int8_t* x_active_mask,
+                           const void* w1, const float* w1_scale, const void* w2, const float* w2_scale,
+                           void* y, int32_t* expert_token_nums, void* stream);
+
 /* Bits of the device error word. */
 typedef enum mm_device_error {
   MM_DEVERR_NONE = 0,
@@ -288,7 +308,7 @@ typedef enum mm_device_error {
  * *host_out, asynchronously on `stream`: read it after the stream has
  * synchronised.  mega_moe and mm_dispatch_layout clear the word when they
  * start; the two GEMM entry points only add bits to it.  Diagnostics only.
- *   workspace  the workspace passed to that call
+ *   workspace  the workspace passed to that call (NULL: mega_moe_noalloc's)
  *   host_out   host int32, receives an OR of mm_device_error bits
  */
 mm_status mm_read_device_error(const mm_plan* plan, const void* workspace, int32_t* host_out, void* stream);
@@ -316,7 +336,8 @@ mm_status mm_debug_raw_accumulators(const mm_plan* plan, int which, const int32_
  * mega_moe call on `workspace` built inside it (DeepEP notes, sections 1
  * and 3.5: the padded per-expert offsets and the (token, slot) identity of
  * every pool row), asynchronously on `stream`, so that it can be checked
- * like mm_dispatch_layout's outputs.  Diagnostics only.
+ * like mm_dispatch_layout's outputs (workspace NULL: the last
+ * mega_moe_noalloc call's).  Diagnostics only.
  *   offsets_out        device int32 [E+S+1]
  *   pool_src_out       device int32 [P]
  *   route_to_pool_out  device int32 [T*(K+S)]

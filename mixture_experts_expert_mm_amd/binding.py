@@ -59,7 +59,7 @@ class MMPlan(ctypes.Structure):
 
 EXPORTS = [
     "mm_plan_create", "mm_prepare_weights", "mm_dispatch_layout", "mm_grouped_l1_swiglu",
-    "mm_grouped_l2_combine", "mega_moe", "mm_read_device_error", "mm_debug_raw_accumulators",
+    "mm_grouped_l2_combine", "mega_moe", "mega_moe_noalloc", "mm_read_device_error", "mm_debug_raw_accumulators",
     "mm_debug_fused_layout", "mm_read_kernel_clock", "mm_trace_enable", "mm_trace_collect", "mm_kernel_name", "mm_status_string",
 ]
 
@@ -92,6 +92,7 @@ def load() -> ctypes.CDLL:
     lib.mm_grouped_l1_swiglu.argtypes = [P, i32p, i32p, vp, f32p, vp, f32p, vp, f32p, vp, u64, vp]
     lib.mm_grouped_l2_combine.argtypes = [P, i32p, i32p, i32p, i32p, vp, f32p, vp, f32p, f32p, vp, vp, u64, vp]
     lib.mega_moe.argtypes = [P, vp, i32p, f32p, vp, vp, f32p, vp, f32p, vp, i32p, vp, u64, vp]
+    lib.mega_moe_noalloc.argtypes = [P, vp, i32p, f32p, vp, vp, f32p, vp, f32p, vp, i32p, vp]
     lib.mm_read_device_error.argtypes = [P, vp, ctypes.POINTER(ctypes.c_int32), vp]
     lib.mm_debug_raw_accumulators.argtypes = [P, ctypes.c_int, i32p, i32p, vp, vp, i32p, vp, u64, vp]
     lib.mm_debug_fused_layout.argtypes = [P, vp, i32p, i32p, i32p, vp]
@@ -184,6 +185,13 @@ def mega_moe(plan, x, topk_ids, topk_weights, x_active_mask, w1, w1_scale, w2, w
         ctypes.byref(plan), _ptr(x), _ptr(topk_ids), _ptr(topk_weights), _ptr(x_active_mask), _ptr(w1), _ptr(w1_scale),
         _ptr(w2), _ptr(w2_scale), _ptr(y), _ptr(expert_token_nums), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def mega_moe_noalloc(plan, x, topk_ids, topk_weights, x_active_mask, w1, w1_scale, w2, w2_scale, y,
+                     expert_token_nums, stream=None):
+    _check("mega_moe_noalloc", load().mega_moe_noalloc(
+        ctypes.byref(plan), _ptr(x), _ptr(topk_ids), _ptr(topk_weights), _ptr(x_active_mask), _ptr(w1),
+        _ptr(w1_scale), _ptr(w2), _ptr(w2_scale), _ptr(y), _ptr(expert_token_nums), _stream(stream)))
 
 
 def mm_read_device_error(plan, workspace, stream=None) -> int:

@@ -395,6 +395,32 @@ mm_status do_l2(const mm_plan& pl, const int32_t* offsets, const int32_t* counts
 bool ok16(const void* p) { return p && aligned(p, 16); }
 bool ok4(const void* p) { return p && aligned(p, 4); }
 
+// ---------------------------------------------------------------- static scratch
+// The workspace of mega_moe_noalloc: a device array of the library itself,
+// one copy per GPU, held until the process ends.  Host code never passes
+// the array's name to a kernel (on the host it is only a stand-in for the
+// symbol): its device address comes from hipGetSymbolAddress, once per
+// device, with that device current.
+constexpr int64_t kScratchBytes = (int64_t)96 << 20;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+mm_status scratch_of_current_device(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MM_ERR_HIP;
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MM_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -563,8 +589,24 @@ mm_status mega_moe(const mm_plan* plan, const void* x, const int32_t* topk_ids, 
   return MM_OK;
 }
 
+mm_status mega_moe_noalloc(const mm_plan* plan, const void* x, const int32_t* topk_ids, const float* topk_weights,
+                           const int8_t* x_active_mask, const void* w1, const float* w1_scale, const void* w2,
+                           const float* w2_scale, void* y, int32_t* expert_token_nums, void* stream) {
+  MM_TRY(check_plan(plan));
+  if (plan->fused_workspace_bytes > kScratchBytes) return MM_ERR_WORKSPACE;
+  void* ws = nullptr;
+  MM_TRY(scratch_of_current_device(&ws));
+  return mega_moe(plan, x, topk_ids, topk_weights, x_active_mask, w1, w1_scale, w2, w2_scale, y, expert_token_nums,
+                  ws, (uint64_t)kScratchBytes, stream);
+}
+
 mm_status mm_read_device_error(const mm_plan* plan, const void* workspace, int32_t* host_out, void* stream) {
   MM_TRY(check_plan(plan));
+  if (!workspace) {   // the static scratch of mega_moe_noalloc
+    void* ws = nullptr;
+    MM_TRY(scratch_of_current_device(&ws));
+    workspace = ws;
+  }
   if (!ok16(workspace) || !host_out) return MM_ERR_INVALID_ARG;
   const uint8_t* word = static_cast<const uint8_t*>(workspace) + ws_layout(*plan).ctl + 4;
   if (hipMemcpyAsync(host_out, word, 4, hipMemcpyDeviceToHost, static_cast<hipStream_t>(stream)) != hipSuccess)
@@ -626,6 +668,11 @@ mm_status mm_debug_fused_layout(const mm_plan* plan, const void* workspace, int3
                                 int32_t* pool_src_out, int32_t* route_to_pool_out, void* stream) {
   MM_TRY(check_plan(plan));
   if (!ok4(offsets_out) || !ok4(pool_src_out) || !ok4(route_to_pool_out)) return MM_ERR_INVALID_ARG;
+  if (!workspace) {   // the static scratch of mega_moe_noalloc
+    void* ws = nullptr;
+    MM_TRY(scratch_of_current_device(&ws));
+    workspace = ws;
+  }
   if (!ok16(workspace)) return MM_ERR_INVALID_ARG;
   const mm_problem& p = plan->prob;
   const WsLayout L = ws_layout(*plan);
