@@ -38,6 +38,23 @@ in float32, ``q = w / scale`` in float32, then round-half-even and clamp to
 +-127 (int8, Qmax 127) or saturate to +-448 and round to OCP e4m3fn (fp8,
 Qmax 448).  This is input preparation outside the operator, not part of the
 path under test.
+
+The MX use cases (Ascend page, A8W8-FP: element codes with one FLOAT8_E8M0
+scale per output channel and group of 32 along the input dimension; the
+DeepGEMM page's FP8 x FP4 path: FP4 e2m1 weights) draw the weights directly
+as (element code, scale) pairs, stream ``default_rng([seed, 6, e])``:
+
+* ``mxfp8``: codes = torch's float8_e4m3fn cast of N(0,1) * 64 (clipped to
+  +-448, the largest finite e4m3fn value); E8M0 =
+  127 - round(log2(64 * sqrt(fan_in))) + a uniform jitter in {-1, 0, 1};
+* ``mxfp4``: e2m1 magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 drawn with fixed
+  probabilities (``FP4_MAGNITUDE_P``), random sign; E8M0 =
+  127 - round(log2(1.7 * sqrt(fan_in))) + jitter; two codes per byte along
+  the output dimension (even column in the low nibble).
+
+so every weight is about N(0, 1/fan_in) in value.  Shapes: W1 codes
+[E][H][2I] (fp4: [E][H][I] bytes), W2 [E][I][H] (fp4: [E][I][H/2] bytes),
+scales S1 [E][2I][H/32], S2 [E][H][I/32] uint8.
 """
 
 from __future__ import annotations
@@ -49,8 +66,11 @@ from concurrent.futures import ThreadPoolExecutor
 import numpy as np
 import torch
 
-USECASES = ("bf16", "fp8", "int8")
+USECASES = ("bf16", "fp8", "int8", "mxfp8", "mxfp4")
 QMAX = {"fp8": 448.0, "int8": 127.0}
+MX_USECASES = ("mxfp8", "mxfp4")
+# probabilities of the e2m1 magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 in drawn FP4 weights
+FP4_MAGNITUDE_P = (0.16, 0.26, 0.20, 0.13, 0.09, 0.09, 0.05, 0.02)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -182,12 +202,54 @@ def quantize_weight_per_channel(w: torch.Tensor, usecase: str):
     return q, sf
 
 
+def mx_expert_weights(cfg: Config, e: int):
+    """Expert ``e`` of an MX use case: ``(w1, w2, s1, s2)`` as uint8 tensors
+    (codes in the formula layout, fp4 packed two per byte along the output
+    dimension; E8M0 scales per output channel and group of 32)."""
+    rng = np.random.default_rng([cfg.seed, 6, e])
+
+    def codes(k_in, n):
+        if cfg.usecase == "mxfp8":
+            v = np.clip(rng.standard_normal((k_in, n), dtype=np.float32) * np.float32(64.0), -448.0, 448.0)
+            v = torch.from_numpy(v)
+            return v.to(torch.float8_e4m3fn).view(torch.uint8), 64.0
+        mag = rng.choice(8, size=(k_in, n), p=FP4_MAGNITUDE_P).astype(np.uint8)
+        sign = (rng.random((k_in, n)) < 0.5).astype(np.uint8) << 3
+        c = mag | sign
+        packed = (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)
+        return torch.from_numpy(np.ascontiguousarray(packed)), 1.7
+
+    def scales(n, k_in, unit):
+        base = 127 - int(round(np.log2(unit * np.sqrt(k_in))))
+        return torch.from_numpy((base + rng.integers(-1, 2, (n, k_in // 32))).astype(np.uint8))
+
+    w1, u1 = codes(cfg.H, 2 * cfg.I)
+    s1 = scales(2 * cfg.I, cfg.H, u1)
+    w2, u2 = codes(cfg.I, cfg.H)
+    s2 = scales(cfg.H, cfg.I, u2)
+    return w1, w2, s1, s2
+
+
+def unpack_codes(w: torch.Tensor, cfg: Config) -> np.ndarray:
+    """Element codes of MX weights, one per uint8, in the formula layout
+    ``[K_in][N]`` (fp4 nibbles unpacked: even column from the low nibble)."""
+    b = w.view(torch.uint8).numpy()
+    if cfg.usecase != "mxfp4":
+        return b
+    out = np.empty((b.shape[0], 2 * b.shape[1]), dtype=np.uint8)
+    out[:, 0::2] = b & 0xF
+    out[:, 1::2] = b >> 4
+    return out
+
+
 def expert_weights(cfg: Config, e: int):
     """Weights of expert ``e`` in the use case's dtype.
 
     Returns ``(w1, w2, s1, s2)``: ``w1 [H,2I]``, ``w2 [I,H]`` in bf16 / fp8 /
     int8; ``s1 [2I]``, ``s2 [H]`` float32 per-channel scales (``None`` for bf16).
     """
+    if cfg.usecase in MX_USECASES:
+        return mx_expert_weights(cfg, e)
     w1, w2 = expert_weights_f32(cfg, e)
     if cfg.usecase == "bf16":
         return w1.to(torch.bfloat16), w2.to(torch.bfloat16), None, None
@@ -205,13 +267,20 @@ class Weights:
 
 
 def all_weights(cfg: Config) -> Weights:
-    dt = {"bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn, "int8": torch.int8}[cfg.usecase]
     n = cfg.E + cfg.shared
-    w1 = torch.empty((n, cfg.H, 2 * cfg.I), dtype=dt)
-    w2 = torch.empty((n, cfg.I, cfg.H), dtype=dt)
     q = cfg.usecase != "bf16"
-    s1 = torch.empty((n, 2 * cfg.I), dtype=torch.float32) if q else None
-    s2 = torch.empty((n, cfg.H), dtype=torch.float32) if q else None
+    if cfg.usecase in MX_USECASES:
+        half = 2 if cfg.usecase == "mxfp4" else 1
+        w1 = torch.empty((n, cfg.H, 2 * cfg.I // half), dtype=torch.uint8)
+        w2 = torch.empty((n, cfg.I, cfg.H // half), dtype=torch.uint8)
+        s1 = torch.empty((n, 2 * cfg.I, cfg.H // 32), dtype=torch.uint8)
+        s2 = torch.empty((n, cfg.H, cfg.I // 32), dtype=torch.uint8)
+    else:
+        dt = {"bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn, "int8": torch.int8}[cfg.usecase]
+        w1 = torch.empty((n, cfg.H, 2 * cfg.I), dtype=dt)
+        w2 = torch.empty((n, cfg.I, cfg.H), dtype=dt)
+        s1 = torch.empty((n, 2 * cfg.I), dtype=torch.float32) if q else None
+        s2 = torch.empty((n, cfg.H), dtype=torch.float32) if q else None
 
     def one(e):
         a, b, c, d = expert_weights(cfg, e)

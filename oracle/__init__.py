@@ -20,6 +20,13 @@ from .moe_oracle import (  # noqa: F401
     e4m3_decode,
     e4m3_encode,
     e4m3_round,
+    e2m1_decode,
+    e2m1_encode,
+    e2m1_round,
+    elem_decode,
+    mx_quantize,
+    mx_dequantize,
+    MX_WEIGHT_FORMAT,
     silu,
     swiglu,
     quantize_tokens,

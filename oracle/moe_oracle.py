@@ -4,13 +4,16 @@ Sources, cited by page title and section:
 
 * [ASC] "mega_moe" -- Ascend CANN ops-transformer operator page.
   Formula, Conventions, Computation Process (A16W16 non-quantized use case;
-  A8W8-INT Quantization Use Case), Parameters table, Deterministic
-  Computation.
+  A8W8-INT Quantization Use Case; A8W8-FP Quantization Use Case with MX
+  per-group quantisation), Parameters table, Deterministic Computation.
 * [MD]  "05_05 Metadata System" -- DeepEP-v2 notes on DeepGEMM Mega MoE.
   Section 1 (Count -> Prefix Sum -> Scatter), section 3.5 (pool block
   offset), section 5.2 (masked routes).
 * [DG]  "DeepGEMM MegaMoE: Fused Communication and Expert Compute".
-  Section 2 (token identities), section 6 (optional shared experts).
+  Section 1 (FP8 activations x FP4 weights), section 2 (token identities),
+  section 3.3 (the (1, 1, 32) scale recipe), section 4 steps 5-6 (UE8M0
+  block scales, FP8 re-quantisation of the L1 output), section 6 (optional
+  shared experts).
 
 Readings taken where the pages are silent or ambiguous (each one is listed
 with its reason in the design notes of the repository):
@@ -31,7 +34,15 @@ with its reason in the design notes of the repository):
   shared, so its output row is 0;
 * a shared expert ([DG] section 6: an always-local MLP on every token, its
   output in the extra combine slot num_topk, summed with the routed slots)
-  enters with weight 1, after the routed slots.
+  enters with weight 1, after the routed slots;
+* MX per-group quantisation ([ASC] A8W8-FP: groups of 32 along the
+  contraction dimension, a shared exponent stored as FLOAT8_E8M0, elements in
+  the fp8 format) follows the OCP Microscaling definition: shared exponent
+  floor(log2(max|v|)) minus the largest exponent of the element format
+  (8 for e4m3, 2 for e2m1), clamped to the E8M0 range [-127, 127] (an
+  all-zero group takes -127); elements round to nearest even and saturate;
+* the FP8 x FP4 use case ([DG] sections 1 and 4) is the same computation with
+  MX-FP4 (e2m1) weights and MX-FP8 activations.
 """
 
 from __future__ import annotations
@@ -104,6 +115,85 @@ def e4m3_decode(codes) -> np.ndarray:
     val = np.where(eb == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.ldexp(1.0, eb - 7))
     val = np.where((eb == 0xF) & (m == 0x7), np.nan, val)
     return s * val
+
+
+_E2M1_MAX = 6.0
+
+
+def e2m1_round(a) -> np.ndarray:
+    """Value of ``a`` in OCP FP4 e2m1: saturate to +-6, round half-even.
+
+    e2m1 has 2 significant bits, exponent bias 1, smallest normal 1,
+    subnormal quantum 0.5: the magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6.
+    """
+    a = np.clip(np.asarray(a, dtype=np.float64), -_E2M1_MAX, _E2M1_MAX)
+    return _round_to_significand(a, 2, 0)
+
+
+def e2m1_decode(codes) -> np.ndarray:
+    """float64 value of 4-bit e2m1 codes (held one per uint8): bit 3 sign,
+    bits 2-1 exponent, bit 0 mantissa."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64) & 0xF
+    s = np.where(c & 0x8, -1.0, 1.0)
+    eb = (c >> 1) & 0x3
+    m = c & 0x1
+    return s * np.where(eb == 0, m * 0.5, (1.0 + m / 2.0) * np.ldexp(1.0, eb - 1))
+
+
+def e2m1_encode(a) -> np.ndarray:
+    """4-bit code (one per uint8) of ``e2m1_round(a)``; sign bit kept for -0."""
+    a = np.asarray(a, dtype=np.float64)
+    mag = np.abs(e2m1_round(a))
+    table = e2m1_decode(np.arange(8, dtype=np.uint8))          # the 8 magnitudes, ascending
+    code = np.searchsorted(table, mag).astype(np.uint8)        # exact: mag is one of them
+    return (code | (np.signbit(a).astype(np.uint8) << 3)).astype(np.uint8)
+
+
+# --------------------------------------------------------------------------
+# MX per-group quantisation ([ASC] A8W8-FP Quantization Use Case: Q_MX and
+# DQ_MX, group size 32, FLOAT8_E8M0 scales)
+# --------------------------------------------------------------------------
+
+MX_GROUP = 32
+# the exponent of the largest power of two of each element format
+MX_EMAX = {"e4m3": 8, "e2m1": 2}
+
+
+def _elem_encode(v, fmt):
+    return e4m3_encode(v) if fmt == "e4m3" else e2m1_encode(v)
+
+
+def elem_decode(codes, fmt) -> np.ndarray:
+    """float64 values of element codes of format ``fmt`` ("e4m3" or "e2m1")."""
+    return e4m3_decode(codes) if fmt == "e4m3" else e2m1_decode(codes)
+
+
+def mx_quantize(v, fmt: str):
+    """Q_MX along the last axis (a multiple of 32): ``(codes, e8m0)``.
+
+    Per group of 32 values: shared exponent ``X = floor(log2(max|v|)) -
+    MX_EMAX[fmt]`` clamped to [-127, 127] (-127 for an all-zero group), E8M0
+    code ``X + 127``, element codes = ``fmt`` encoding of ``v / 2**X`` (round
+    half-even, saturating).  Division by a power of two is exact.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    n = v.shape[-1]
+    assert n % MX_GROUP == 0
+    g = v.reshape(*v.shape[:-1], n // MX_GROUP, MX_GROUP)
+    amax = np.max(np.abs(g), axis=-1)
+    _, ex = np.frexp(amax)                                   # amax = m * 2**ex, 0.5 <= m < 1
+    x = np.where(amax > 0, ex - 1 - MX_EMAX[fmt], -127)
+    x = np.clip(x, -127, 127).astype(np.int64)
+    codes = _elem_encode(g / np.ldexp(1.0, x)[..., None], fmt)
+    return codes.reshape(v.shape), (x + 127).astype(np.uint8)
+
+
+def mx_dequantize(codes, e8m0, fmt: str) -> np.ndarray:
+    """DQ_MX along the last axis: element value times 2**(e8m0 - 127) of its group."""
+    vals = elem_decode(codes, fmt)
+    n = vals.shape[-1]
+    scale = np.ldexp(1.0, np.asarray(e8m0).astype(np.int64) - 127)
+    return (vals.reshape(*vals.shape[:-1], n // MX_GROUP, MX_GROUP) * scale[..., None]).reshape(vals.shape)
 
 
 # --------------------------------------------------------------------------
@@ -224,6 +314,11 @@ def _e4m3_table() -> np.ndarray:
     return e4m3_decode(np.arange(256, dtype=np.uint8))
 
 
+# MX use cases: activations MX-FP8 (e4m3 elements) in both Linears; the
+# weights' element format
+MX_WEIGHT_FORMAT = {"mxfp8": "e4m3", "mxfp4": "e2m1"}
+
+
 def _expert_f64(expert, e, usecase):
     """Decode expert ``e`` to float64 ``(W1 [H,2I], W2 [I,H], s1, s2)``.
 
@@ -234,6 +329,13 @@ def _expert_f64(expert, e, usecase):
     w1, w2, s1, s2 = expert(e)
     w1 = np.asarray(w1)
     w2 = np.asarray(w2)
+    if usecase in MX_WEIGHT_FORMAT:
+        # codes [K_in, N] (one per uint8) with E8M0 scales [N][K_in / 32]:
+        # per output column, per group of 32 along the contraction dimension
+        fmt = MX_WEIGHT_FORMAT[usecase]
+        w1 = mx_dequantize(w1.view(np.uint8).T, np.asarray(s1), fmt).T
+        w2 = mx_dequantize(w2.view(np.uint8).T, np.asarray(s2), fmt).T
+        return w1, w2, None, None
     if usecase == "fp8":
         table = _e4m3_table()
         w1 = table[w1.view(np.uint8)]
@@ -281,7 +383,12 @@ def moe_forward(x_f32, topk_ids, topk_weights, expert, usecase: str,
     Inputs: ``x_f32`` [T,H] float32 holding the bf16 token values; ``topk_ids``
     [T,K] int; ``topk_weights`` [T,K] float32; ``expert(e)`` returns expert
     ``e``'s weights (bf16 values as float32, int8, or e4m3 bit patterns as
-    uint8) and per-channel scales.  ``tokens`` optionally restricts the
+    uint8) and per-channel scales.  The MX use cases ([ASC] A8W8-FP; "mxfp8":
+    e4m3 weights, "mxfp4": e2m1 weights, [DG] section 1) take the weights as
+    element codes (one per uint8) with E8M0 scales [N][K_in/32], quantise X
+    per token and the SwiGLU output per row with Q_MX in groups of 32 along
+    the contraction dimension (e4m3 elements), and multiply the dequantised
+    values: ``Z = DQ(X^) DQ(W1)``, ``U = SwiGLU(Z)``, ``O = DQ(Q_MX(U)) DQ(W2)``.  ``tokens`` optionally restricts the
     result to those token indices (rows are independent, so each is the same
     as in the full computation).  Returns ``(y float64 [T or len(tokens), H],
     counts)``.  ``activation_clamp`` (None or c >= 0): [ASC] Parameters,
@@ -310,7 +417,11 @@ def moe_forward(x_f32, topk_ids, topk_weights, expert, usecase: str,
     pos = np.full(T, -1, dtype=np.int64)
     pos[tok] = np.arange(len(tok))
 
-    if usecase != "bf16":
+    mx = usecase in MX_WEIGHT_FORMAT
+    if mx:
+        xc, xe = mx_quantize(x[tok].astype(np.float64), "e4m3")
+        xin_sub = mx_dequantize(xc, xe, "e4m3")
+    elif usecase != "bf16":
         _, sx_sub, xin_sub = quantize_tokens(x[tok], usecase)
 
     H = x.shape[1]
@@ -335,6 +446,12 @@ def moe_forward(x_f32, topk_ids, topk_weights, expert, usecase: str,
                 h = np.clip(h, -activation_clamp, activation_clamp)
             a = bf16_round(swiglu(h))
             o = a @ w2
+        elif mx:
+            h = xin_sub[rows] @ w1
+            if activation_clamp is not None:
+                h = np.clip(h, -activation_clamp, activation_clamp)
+            uc, ue = mx_quantize(swiglu(h), "e4m3")
+            o = mx_dequantize(uc, ue, "e4m3") @ w2
         else:
             c = xin_sub[rows] @ w1
             h = (c * s1[None, :]) * sx_sub[rows].astype(np.float64)[:, None]
@@ -365,7 +482,11 @@ def moe_forward_bruteforce(x_f32, topk_ids, topk_weights, expert, usecase: str, 
     g = np.asarray(topk_weights, dtype=np.float64)
     T, K = ids.shape
     H = x.shape[1]
-    if usecase != "bf16":
+    mx = usecase in MX_WEIGHT_FORMAT
+    if mx:
+        xc, xe = mx_quantize(x.astype(np.float64), "e4m3")
+        xq = mx_dequantize(xc, xe, "e4m3")
+    elif usecase != "bf16":
         _, sx, xq = quantize_tokens(x, usecase)
     y = [[0.0] * H for _ in range(T)]
     cache = {}
@@ -389,7 +510,7 @@ def moe_forward_bruteforce(x_f32, topk_ids, topk_weights, expert, usecase: str, 
                 for j in range(H):
                     xv = float(x[i, j]) if usecase == "bf16" else float(xq[i, j])
                     acc += xv * float(w1[j, c])
-                if usecase != "bf16":
+                if usecase != "bf16" and not mx:
                     acc = acc * float(s1[c]) * float(sx[i])
                 if activation_clamp is not None:
                     acc = min(float(activation_clamp), max(-float(activation_clamp), acc))
@@ -400,6 +521,16 @@ def moe_forward_bruteforce(x_f32, topk_ids, topk_weights, expert, usecase: str, 
                 a.append((z / (1.0 + math.exp(-z))) * h[inter + c])
             if usecase == "bf16":
                 a = [float(bf16_round(v)) for v in a]
+                sa = 1.0
+            elif mx:
+                # Q_MX of the row: one E8M0 exponent per group of 32
+                a_new = []
+                for g0 in range(0, inter, MX_GROUP):
+                    grp = a[g0:g0 + MX_GROUP]
+                    amax = max(abs(v) for v in grp)
+                    xexp = -127 if amax == 0 else max(-127, min(127, math.frexp(amax)[1] - 1 - MX_EMAX["e4m3"]))
+                    a_new += [float(e4m3_round(v / 2.0 ** xexp)) * 2.0 ** xexp for v in grp]
+                a = a_new
                 sa = 1.0
             else:
                 qmax = QMAX[usecase]
@@ -412,7 +543,7 @@ def moe_forward_bruteforce(x_f32, topk_ids, topk_weights, expert, usecase: str, 
                 acc = 0.0
                 for c in range(inter):
                     acc += a[c] * float(w2[c, n])
-                if usecase != "bf16":
+                if usecase != "bf16" and not mx:
                     acc = acc * float(s2[n]) * sa
                 y[i][n] += gw * acc
     return np.array(y, dtype=np.float64)

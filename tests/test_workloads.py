@@ -78,3 +78,20 @@ def test_shared_expert_weights_and_active_mask():
     assert m.dtype == torch.int8 and m.shape == (40,) and set(m.tolist()) <= {0, 1}
     assert torch.equal(m, wl.active_mask(cfg)) and 0 < int(m.sum()) < 40
     assert wl.active_mask(cfg.with_(inactive_ratio=0.0)) is None
+
+
+def test_mx_weights_layout_and_scale_of_values():
+    import oracle
+    for uc in ("mxfp8", "mxfp4"):
+        cfg = wl.Config("mx", uc, 8, 512, 256, 3, 2, 0.0, 9, shared=1)
+        w = wl.all_weights(cfg)
+        half = 2 if uc == "mxfp4" else 1
+        assert w.w1.shape == (4, 512, 512 // half) and w.w2.shape == (4, 256, 512 // half)
+        assert w.s1.shape == (4, 512, 16) and w.s2.shape == (4, 512, 8) and w.s1.dtype == torch.uint8
+        codes = wl.unpack_codes(w.w1[0], cfg)
+        assert codes.shape == (512, 512)
+        fmt = oracle.MX_WEIGHT_FORMAT[uc]
+        vals = oracle.mx_dequantize(codes.T, w.s1[0].numpy(), fmt)
+        assert np.all(np.isfinite(vals))
+        rms = np.sqrt(np.mean(vals ** 2))
+        assert 0.5 / np.sqrt(512) < rms < 2.0 / np.sqrt(512), rms
