@@ -83,8 +83,22 @@ typedef enum mm_status {
  *   (per-token for X, per output channel for W, per row for the SwiGLU
  *   output), by the A8W8 formulas with Qmax = 448.
  * A8W8_INT8: symmetric int8 in [-127, 127] with the same scales, Qmax = 127,
- *   exact int32 accumulation. */
-typedef enum mm_usecase { MM_A16W16 = 0, MM_A8W8_FP8 = 1, MM_A8W8_INT8 = 2 } mm_usecase;
+ *   exact int32 accumulation.
+ * MXFP8: the A8W8-FP use case (operator page, A8W8-FP Quantization Use
+ *   Case): e4m3 activations and weights, each group of 32 values along the
+ *   contraction dimension with one FLOAT8_E8M0 scale (MX per-group
+ *   quantisation: shared exponent floor(log2 max|v|) - 8, elements rounded
+ *   to nearest even and saturated); X is quantised per token in Dispatch and
+ *   the SwiGLU output per row in the Linear1 epilogue, both by the library.
+ * MXFP4: the FP8 x FP4 path of the DeepGEMM MegaMoE page (section 1): the
+ *   same MX-FP8 activations with MX-FP4 (e2m1) weights.
+ * The MX use cases take weights as element codes with E8M0 scales
+ * [E+S][N][K_in/32] (per output column, per group of 32 along the input
+ * dimension: S1 [E+S][2I][H/32], S2 [E+S][H][I/32]) and hold at most 512
+ * experts (E + S). */
+typedef enum mm_usecase {
+  MM_A16W16 = 0, MM_A8W8_FP8 = 1, MM_A8W8_INT8 = 2, MM_MXFP8 = 3, MM_MXFP4 = 4
+} mm_usecase;
 
 /* dtype of y: bf16 (the operator's output dtype) or float32 (the same
  * float32 value before its final round-to-nearest-even to bf16). */
@@ -123,7 +137,9 @@ typedef struct mm_plan {
   int64_t pool_rows;          /* P = capacity of the padded pool, a multiple of block_m */
   int64_t x_pool_bytes;       /* P * H * elem(usecase) */
   int64_t a_pool_bytes;       /* P * I * elem(usecase) */
-  int64_t w1_bytes;           /* (E+S) * H * 2I * elem(usecase) (formula and prepared) */
+  int64_t x_pool_scale_bytes; /* A8W8: P * 4 (float32); MX: P * H/32 (E8M0); A16W16: 0 */
+  int64_t a_pool_scale_bytes; /* A8W8: P * 4 (float32); MX: P * I/32 (E8M0); A16W16: 0 */
+  int64_t w1_bytes;           /* (E+S) * H * 2I * elem(usecase) (formula and prepared; e2m1: half a byte) */
   int64_t w2_bytes;           /* (E+S) * I * H * elem(usecase) */
   int64_t workspace_bytes;    /* scratch of the three-call path */
   int64_t fused_workspace_bytes; /* scratch of mega_moe (holds the pool too) */
@@ -131,7 +147,8 @@ typedef struct mm_plan {
   int64_t reserved[8];        /* internal choices of the plan (workspace layout); do not modify */
 } mm_plan;
 
-/* Elements: bf16 = 2 bytes, e4m3fn / int8 = 1 byte. */
+/* Elements: bf16 = 2 bytes, e4m3fn / int8 = 1 byte, e2m1 = half a byte
+ * (two per byte, the even index in the low nibble). */
 
 /*
  * mm_plan_create -- validate a problem and choose BLOCK_M and tiles.
@@ -149,15 +166,17 @@ mm_status mm_plan_create(const mm_problem* problem, mm_plan* plan);
  * mm_prepare_weights -- one-time relayout of the expert weights into the
  * layout the GEMM kernels stream (DeepGEMM MegaMoE page, section 3.2: done
  * once by the caller before repeated launches; not part of the timed path).
- *   w1     device [E+S][H][2I]  formula layout of the operator page (Formula)
- *   w2     device [E+S][I][H]   formula layout
- *   w1_out device [E+S][2I][H] K-contiguous rows; row n of expert e holds the
+ *   w1     device [E+S][H][2I]  formula layout of the operator page (Formula);
+ *                               e2m1: [E+S][H][I] bytes, packed along 2I
+ *   w2     device [E+S][I][H]   formula layout; e2m1: [E+S][I][H/2] bytes
+ *   w1_out device [E+S][2I][H] K-contiguous rows (e2m1: packed along H); row n of expert e holds the
  *                             W1 column c(n) with gate and up columns
  *                             interleaved in groups of g = gate_up_group:
  *                             c(n) = (n/2g)*g + n%g            if n%2g <  g
  *                                    I + (n/2g)*g + n%g - g    otherwise
- *   w2_out device [E+S][H][I] K-contiguous (transposed)
- * Scales stay in formula layout ([E+S][2I] and [E+S][H]).  Buffers must not
+ *   w2_out device [E+S][H][I] K-contiguous (transposed; e2m1: packed along I)
+ * Scales stay in formula layout ([E+S][2I] and [E+S][H], or the MX
+ * [E+S][N][K_in/32] bytes).  Buffers must not
  * overlap.
  */
 mm_status mm_prepare_weights(const mm_plan* plan, const void* w1, const void* w2,
@@ -181,7 +200,9 @@ mm_status mm_prepare_weights(const mm_plan* plan, const void* w1, const void* w2
  *   route_to_pool  device int32 [T*(K+S)] out: pool row of each route, -1 if skipped
  *   x_pool         device [P][H]       out: row p = x_i (bf16) or q_i (A8W8);
  *                                      padding rows are unspecified
- *   x_pool_scale   device f32 [P]      out: s_i of row p (A8W8); may be NULL for A16W16
+ *   x_pool_scale   device, out: s_i of row p, f32 [P] (A8W8), or the E8M0
+ *                                      scales of row p's groups of 32, [P][H/32] (MX);
+ *                                      plan.x_pool_scale_bytes; may be NULL for A16W16
  *   workspace      device, plan.workspace_bytes
  * The order of the rows of one expert inside its pool range is unspecified
  * (the operator page stacks them "in any fixed order").
@@ -190,7 +211,7 @@ mm_status mm_dispatch_layout(const mm_plan* plan, const int32_t* topk_ids, const
                              const void* x,
                              int32_t* expert_counts, int32_t* expert_offsets,
                              int32_t* pool_src, int32_t* route_to_pool,
-                             void* x_pool, float* x_pool_scale,
+                             void* x_pool, void* x_pool_scale,
                              void* workspace, uint64_t workspace_bytes, void* stream);
 
 /*
@@ -202,14 +223,17 @@ mm_status mm_dispatch_layout(const mm_plan* plan, const int32_t* topk_ids, const
  *   expert_offsets, expert_counts  as written by mm_dispatch_layout
  *   x_pool, x_pool_scale           as written by mm_dispatch_layout
  *   w1        device, prepared by mm_prepare_weights
- *   w1_scale  device f32 [E+S][2I] formula order (A8W8), NULL for A16W16
+ *   w1_scale  device f32 [E+S][2I] formula order (A8W8), E8M0 [E+S][2I][H/32]
+ *             (MX), NULL for A16W16
  *   a_pool    device [P][I] out: bf16 A (A16W16) or its int8 / e4m3 codes
- *   a_pool_scale device f32 [P] out: s^A (A8W8), may be NULL for A16W16
+ *   a_pool_scale device out: s^A f32 [P] (A8W8), or A's E8M0 group scales
+ *             [P][I/32] (MX: A = Q_MX(SwiGLU(H)) per row, made in the Linear1
+ *             epilogue); may be NULL for A16W16
  */
 mm_status mm_grouped_l1_swiglu(const mm_plan* plan, const int32_t* expert_offsets,
                                const int32_t* expert_counts, const void* x_pool,
-                               const float* x_pool_scale, const void* w1, const float* w1_scale,
-                               void* a_pool, float* a_pool_scale,
+                               const void* x_pool_scale, const void* w1, const void* w1_scale,
+                               void* a_pool, void* a_pool_scale,
                                void* workspace, uint64_t workspace_bytes, void* stream);
 
 /*
@@ -224,14 +248,14 @@ mm_status mm_grouped_l1_swiglu(const mm_plan* plan, const int32_t* expert_offset
  *   pool_src, route_to_pool        as written by mm_dispatch_layout
  *   a_pool, a_pool_scale           as written by mm_grouped_l1_swiglu
  *   w2        device, prepared by mm_prepare_weights
- *   w2_scale  device f32 [E+S][H] (A8W8), NULL for A16W16
+ *   w2_scale  device f32 [E+S][H] (A8W8), E8M0 [E+S][H][I/32] (MX), NULL for A16W16
  *   topk_weights device f32 [T][K]
  *   y         device [T][H] out, bf16 or f32 per plan.prob.y_dtype
  */
 mm_status mm_grouped_l2_combine(const mm_plan* plan, const int32_t* expert_offsets,
                                 const int32_t* expert_counts, const int32_t* pool_src,
                                 const int32_t* route_to_pool, const void* a_pool,
-                                const float* a_pool_scale, const void* w2, const float* w2_scale,
+                                const void* a_pool_scale, const void* w2, const void* w2_scale,
                                 const float* topk_weights, void* y,
                                 void* workspace, uint64_t workspace_bytes, void* stream);
 
@@ -261,15 +285,15 @@ mm_status mm_grouped_l2_combine(const mm_plan* plan, const int32_t* expert_offse
  *   topk_weights   device f32 [T][K]
  *   x_active_mask  device int8 [T] or NULL
  *   w1, w2         device, prepared by mm_prepare_weights
- *   w1_scale, w2_scale  device f32 (A8W8) or NULL (A16W16)
+ *   w1_scale, w2_scale  device, as for the grouped entry points; NULL for A16W16
  *   y              device [T][H] out (bf16 or f32 per plan)
  *   expert_token_nums device int32 [E] out: N_e of the routed experts
  *   workspace      device, plan.fused_workspace_bytes
  */
 mm_status mega_moe(const mm_plan* plan, const void* x, const int32_t* topk_ids,
                    const float* topk_weights, const int8_t* x_active_mask,
-                   const void* w1, const float* w1_scale,
-                   const void* w2, const float* w2_scale, void* y, int32_t* expert_token_nums,
+                   const void* w1, const void* w1_scale,
+                   const void* w2, const void* w2_scale, void* y, int32_t* expert_token_nums,
                    void* workspace, uint64_t workspace_bytes, void* stream);
 
 /*
@@ -289,7 +313,7 @@ mm_status mega_moe(const mm_plan* plan, const void* x, const int32_t* topk_ids,
  */
 mm_status mega_moe_noalloc(const mm_plan* plan, const void* x, const int32_t* topk_ids,
                            const float* topk_weights, const int8_t* x_active_mask,
-                           const void* w1, const float* w1_scale, const void* w2, const float* w2_scale,
+                           const void* w1, const void* w1_scale, const void* w2, const void* w2_scale,
                            void* y, int32_t* expert_token_nums, void* stream);
 
 /* Bits of the device error word. */

@@ -15,9 +15,9 @@ import torch
 
 from . import _build
 
-MM_A16W16, MM_A8W8_FP8, MM_A8W8_INT8 = 0, 1, 2
+MM_A16W16, MM_A8W8_FP8, MM_A8W8_INT8, MM_MXFP8, MM_MXFP4 = 0, 1, 2, 3, 4
 MM_OUT_BF16, MM_OUT_F32 = 0, 1
-USECASE = {"bf16": MM_A16W16, "fp8": MM_A8W8_FP8, "int8": MM_A8W8_INT8}
+USECASE = {"bf16": MM_A16W16, "fp8": MM_A8W8_FP8, "int8": MM_A8W8_INT8, "mxfp8": MM_MXFP8, "mxfp4": MM_MXFP4}
 KERNEL_IDS = 10
 MM_DEVERR_BAD_EXPERT, MM_DEVERR_BARRIER_TIMEOUT, MM_DEVERR_BAD_OFFSETS = 1, 2, 4
 
@@ -48,6 +48,8 @@ class MMPlan(ctypes.Structure):
         ("pool_rows", ctypes.c_int64),
         ("x_pool_bytes", ctypes.c_int64),
         ("a_pool_bytes", ctypes.c_int64),
+        ("x_pool_scale_bytes", ctypes.c_int64),
+        ("a_pool_scale_bytes", ctypes.c_int64),
         ("w1_bytes", ctypes.c_int64),
         ("w2_bytes", ctypes.c_int64),
         ("workspace_bytes", ctypes.c_int64),

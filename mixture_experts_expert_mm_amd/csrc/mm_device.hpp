@@ -14,7 +14,11 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-enum Usecase : int { UC_BF16 = 0, UC_FP8 = 1, UC_I8 = 2 };
+// UC_MX8: MX-FP8, e4m3 activations and weights with E8M0 scales per 32
+// K-values; UC_MX4: MX-FP8 activations x MX-FP4 (e2m1) weights.
+enum Usecase : int { UC_BF16 = 0, UC_FP8 = 1, UC_I8 = 2, UC_MX8 = 3, UC_MX4 = 4 };
+constexpr bool is_mx(int uc) { return uc == UC_MX8 || uc == UC_MX4; }
+constexpr int kMxGroup = 32;   // K-values per E8M0 scale
 
 constexpr int kWave = 64;
 
@@ -96,6 +100,8 @@ template <int UC> struct Acc;
 template <> struct Acc<UC_BF16> { typedef f32x16 type; };
 template <> struct Acc<UC_FP8> { typedef f32x16 type; };
 template <> struct Acc<UC_I8> { typedef i32x16 type; };
+template <> struct Acc<UC_MX8> { typedef f32x16 type; };
+template <> struct Acc<UC_MX4> { typedef f32x16 type; };
 
 __device__ __forceinline__ void mfma_bf16(f32x16& c, const u32x4& a, const u32x4& b) {
   c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
@@ -111,6 +117,38 @@ __device__ __forceinline__ void mfma_fp8(f32x16& c, const u32x4& a0, const u32x4
   const i32x8 b = __builtin_bit_cast(i32x8, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
   c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
+
+// MX: e4m3 A x (e4m3 or, B_FP4, e2m1) B with one E8M0 scale per K-block of
+// 32: lane half k supplies, in byte OPSEL of its scale word, the scale of
+// K-block k of its A row (sa) and B column (sb).  In an e4m3 operand bytes
+// 0-15 of both lane halves form K-block 0 and bytes 16-31 K-block 1; an
+// e2m1 operand is 16 bytes (32 values, the even K in the low nibble) in b0,
+// lane half k holding K-block k, and the instruction reads only four of its
+// registers.
+template <int OPSEL, bool B_FP4>
+__device__ __forceinline__ void mfma_mx(f32x16& c, const u32x4& a0, const u32x4& a1, const u32x4& b0, const u32x4& b1,
+                                        uint32_t sa, uint32_t sb) {
+  const i32x8 a = __builtin_bit_cast(i32x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+  if constexpr (B_FP4) {
+    const i32x8 b = __builtin_bit_cast(i32x8, __builtin_shufflevector(b0, b0, 0, 1, 2, 3, -1, -1, -1, -1));
+    c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 4, OPSEL, (int)sa, OPSEL, (int)sb);
+  } else {
+    const i32x8 b = __builtin_bit_cast(i32x8, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
+    c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, OPSEL, (int)sa, OPSEL, (int)sb);
+  }
+}
+
+// MX shared exponent of a group of 32 values whose largest magnitude is
+// amax (OCP Microscaling rule): X = floor(log2 amax) - emax of the element
+// format (e4m3: 8), clamped to [-127, 127]; -127 when amax is 0 or below
+// the smallest normal float.  Returns X; the E8M0 code is X + 127 and the
+// element multiplier 2^-X is mx_inv_scale(X), both exact.
+__device__ __forceinline__ int mx_shared_exp_e4m3(float amax) {
+  const int e = (int)((__float_as_uint(amax) >> 23) & 0xffu);   // biased exponent; 0 for 0 and denormals
+  const int x = e - 127 - 8;
+  return x < -127 ? -127 : x;
+}
+__device__ __forceinline__ float mx_inv_scale(int x) { return __uint_as_float((uint32_t)(127 - x) << 23); }
 
 __device__ __forceinline__ float acc_to_f32(float v) { return v; }
 __device__ __forceinline__ float acc_to_f32(int v) { return (float)v; }

@@ -72,6 +72,31 @@ __global__ __launch_bounds__(256) void k_transpose(const T* __restrict__ in, T* 
   }
 }
 
+// e2m1 weights, two per byte: in [E][rows_in][cols_in/2] (packed along the
+// columns) -> out [E][cols_in][rows_in/2] (packed along the rows), with the
+// gate/up interleave c(n) of the output rows when group > 0.  One output
+// byte per thread: values (2b, n) and (2b+1, n), the even one in the low
+// nibble.
+__global__ __launch_bounds__(256) void k_transpose_e2m1(const uint8_t* __restrict__ in, uint8_t* __restrict__ out,
+                                                         int rows_in, int cols_in, int inter, int group) {
+  const int e = blockIdx.z;
+  const int64_t per_e = (int64_t)rows_in * cols_in / 2;
+  const uint8_t* src = in + e * per_e;
+  uint8_t* dstp = out + e * per_e;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;   // output byte of expert e
+  if (idx >= per_e) return;
+  const int n = (int)(idx / (rows_in / 2)), b = (int)(idx % (rows_in / 2));
+  int c = n;
+  if (group > 0) {
+    const int q = n / (2 * group), m = n % (2 * group);
+    c = (m < group) ? q * group + m : inter + q * group + (m - group);
+  }
+  const int r0 = 2 * b, r1 = 2 * b + 1;
+  const uint32_t v0 = (src[(int64_t)r0 * (cols_in / 2) + c / 2] >> ((c & 1) * 4)) & 0xFu;
+  const uint32_t v1 = (src[(int64_t)r1 * (cols_in / 2) + c / 2] >> ((c & 1) * 4)) & 0xFu;
+  dstp[idx] = (uint8_t)(v0 | (v1 << 4));
+}
+
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
@@ -103,6 +128,8 @@ hipError_t launch_gather(const DispatchArgs& a, hipStream_t s) {
   switch (a.usecase) {
     case UC_BF16: hipLaunchKernelGGL(k_gather<UC_BF16>, grid, dim3(256), 0, s, a); break;
     case UC_FP8: hipLaunchKernelGGL(k_gather<UC_FP8>, grid, dim3(256), 0, s, a); break;
+    case UC_MX8:
+    case UC_MX4: hipLaunchKernelGGL(k_gather<UC_MX8>, grid, dim3(256), 0, s, a); break;
     default: hipLaunchKernelGGL(k_gather<UC_I8>, grid, dim3(256), 0, s, a); break;
   }
   return hipGetLastError();
@@ -111,7 +138,11 @@ hipError_t launch_gather(const DispatchArgs& a, hipStream_t s) {
 hipError_t launch_prepare(const void* w1, const void* w2, void* w1o, void* w2o, int E, int H, int I,
                           int esz, int group, hipStream_t s) {
   const dim3 g1((2 * I + 63) / 64, (H + 63) / 64, E), g2((H + 63) / 64, (I + 63) / 64, E);
-  if (esz == 2) {
+  if (esz == 0) {   // e2m1: W1 [E][H][2I] -> [E][2I][H], W2 [E][I][H] -> [E][H][I], nibbles
+    const unsigned b1 = (unsigned)(((int64_t)H * 2 * I / 2 + 255) / 256), b2 = (unsigned)(((int64_t)I * H / 2 + 255) / 256);
+    hipLaunchKernelGGL(k_transpose_e2m1, dim3(b1, 1, E), dim3(256), 0, s, (const uint8_t*)w1, (uint8_t*)w1o, H, 2 * I, I, group);
+    hipLaunchKernelGGL(k_transpose_e2m1, dim3(b2, 1, E), dim3(256), 0, s, (const uint8_t*)w2, (uint8_t*)w2o, I, H, 0, 0);
+  } else if (esz == 2) {
     hipLaunchKernelGGL(k_transpose<uint16_t>, g1, dim3(256), 0, s, (const uint16_t*)w1, (uint16_t*)w1o, H, 2 * I, I, group);
     hipLaunchKernelGGL(k_transpose<uint16_t>, g2, dim3(256), 0, s, (const uint16_t*)w2, (uint16_t*)w2o, I, H, 0, 0);
   } else {

@@ -213,6 +213,22 @@ __device__ __forceinline__ uint2 codes8_of_bf16(const uint4& v, float s) {
   return make_uint2(o[0], o[1]);
 }
 
+// MX-FP8 codes of 8 bf16 activations: e4m3(x * 2^-X), exact scaling by the
+// group's element multiplier inv = 2^-X (saturating at +-448, ties to even).
+__device__ __forceinline__ uint2 mx_codes8_of_bf16(const uint4& v, float inv) {
+  const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+  uint32_t o[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const float f0 = bf16_bits_to_f32(wv[2 * q] & 0xffffu) * inv;
+    const float f1 = bf16_bits_to_f32(wv[2 * q] >> 16) * inv;
+    const float f2 = bf16_bits_to_f32(wv[2 * q + 1] & 0xffffu) * inv;
+    const float f3 = bf16_bits_to_f32(wv[2 * q + 1] >> 16) * inv;
+    o[q] = f32x2_to_e4m3x2(f0, f1) | (f32x2_to_e4m3x2(f2, f3) << 16);
+  }
+  return make_uint2(o[0], o[1]);
+}
+
 __device__ __forceinline__ float amax8_of_bf16(const uint4& v, float m) {
   const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -237,6 +253,34 @@ __device__ __forceinline__ void quant_token_wave(const DispatchArgs& a, int64_t 
   const int nchunk = (int)(a.H / 8);
   const uint4* xr = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + i * a.H);
   uint2* dst = reinterpret_cast<uint2*>(static_cast<uint8_t*>(a.x_pool) + i * a.H);
+  if constexpr (is_mx(UC)) {
+    // Q_MX per group of 32: chunk c (8 values) belongs to group c / 4, the
+    // four chunks of a group sit in four neighbouring lanes (c = j*64 + l)
+    uint8_t* const sc = a.x_pool_mx + i * (a.H / kMxGroup);
+    for (int j0 = 0; j0 < nchunk; j0 += 64 * kTokRegChunks) {
+      uint4 v[kTokRegChunks];
+#pragma unroll
+      for (int j = 0; j < kTokRegChunks; ++j) v[j] = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+      for (int j = 0; j < kTokRegChunks; ++j) {
+        const int c = j0 + j * 64 + l;
+        if (c < nchunk) v[j] = xr[c];
+      }
+#pragma unroll
+      for (int j = 0; j < kTokRegChunks; ++j) {
+        const int c = j0 + j * 64 + l;
+        float m = amax8_of_bf16(v[j], 0.0f);
+        m = fmaxf(m, __shfl_xor(m, 1, 64));
+        m = fmaxf(m, __shfl_xor(m, 2, 64));
+        const int x = mx_shared_exp_e4m3(m);
+        if (c < nchunk) {
+          dst[c] = mx_codes8_of_bf16(v[j], mx_inv_scale(x));
+          if ((l & 3) == 0) sc[c / 4] = (uint8_t)(x + 127);
+        }
+      }
+    }
+    return;
+  }
   const float qmax = (UC == UC_I8) ? 127.0f : 448.0f;
   float m = 0.0f;
   if (nchunk <= 64 * kTokRegChunks) {
@@ -279,7 +323,29 @@ __device__ __forceinline__ void gather_token(const DispatchArgs& a, int64_t i, i
   if (t < nrows) dst[t] = a.route_to_pool[i * a.K + t];
   const int nchunk = (int)(a.H / 8);
   const uint4* xr = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + i * a.H);
-  if constexpr (UC == UC_BF16) {
+  if constexpr (is_mx(UC)) {
+    // Q_MX per group of 32 (four neighbouring threads' chunks), the codes and
+    // E8M0 byte written to each of the token's pool rows
+    __syncthreads();
+    const int gpr = (int)(a.H / kMxGroup);
+    for (int c0 = 0; c0 < nchunk; c0 += NT) {
+      const int c = c0 + t;
+      const uint4 v = c < nchunk ? xr[c] : make_uint4(0u, 0u, 0u, 0u);
+      float m = amax8_of_bf16(v, 0.0f);
+      m = fmaxf(m, __shfl_xor(m, 1, 64));
+      m = fmaxf(m, __shfl_xor(m, 2, 64));
+      const int x = mx_shared_exp_e4m3(m);
+      if (c < nchunk) {
+        const uint2 ov = mx_codes8_of_bf16(v, mx_inv_scale(x));
+        for (int k = 0; k < nrows; ++k) {
+          const int p = dst[k];
+          if (p < 0) continue;
+          reinterpret_cast<uint2*>(static_cast<uint8_t*>(a.x_pool) + (int64_t)p * a.H)[c] = ov;
+          if ((t & 3) == 0) a.x_pool_mx[(int64_t)p * gpr + c / 4] = (uint8_t)(x + 127);
+        }
+      }
+    }
+  } else if constexpr (UC == UC_BF16) {
     __syncthreads();
     for (int c = t; c < nchunk; c += NT) {
       const uint4 v = xr[c];

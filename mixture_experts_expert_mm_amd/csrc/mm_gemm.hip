@@ -8,14 +8,14 @@ template <int UC, int BM, int MODE, bool WIDEN>
 __global__ __launch_bounds__(threads_of<BM>()) __attribute__((amdgpu_waves_per_eu(threads_of<BM>() / 256, threads_of<BM>() / 256)))
 void k_gemm(GemmArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  __shared__ int32_t off_s[kMaxExperts + 1];
-  __shared__ int32_t cnt_s[kMaxExperts];
+  __shared__ int32_t off_s[max_experts<UC>() + 1];
+  __shared__ int32_t cnt_s[max_experts<UC>()];
   gemm_tiles<UC, BM, MODE, WIDEN>(a, lds, off_s, cnt_s);
 }
 
 template <int UC, int BM, int MODE, bool WIDEN>
 static hipError_t launch_one(const GemmArgs& a, int grid, hipStream_t s) {
-  constexpr size_t lds = (size_t)lds_bytes_of<BM>();
+  constexpr size_t lds = (size_t)lds_bytes_of<UC, BM>();
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t err = hipFuncSetAttribute((const void*)k_gemm<UC, BM, MODE, WIDEN>,
@@ -47,6 +47,12 @@ static hipError_t launch_uc(int usecase, int tile, bool exact_l1, const GemmArgs
     case UC_FP8:
       if (MODE == 0 && exact_l1) return launch_bm<UC_FP8, MODE, MODE == 0>(tile, a, grid, s);
       return launch_bm<UC_FP8, MODE>(tile, a, grid, s);
+    case UC_MX8:
+      if (MODE == 0 && exact_l1) return launch_bm<UC_MX8, MODE, MODE == 0>(tile, a, grid, s);
+      return launch_bm<UC_MX8, MODE>(tile, a, grid, s);
+    case UC_MX4:
+      if (MODE == 0 && exact_l1) return launch_bm<UC_MX4, MODE, MODE == 0>(tile, a, grid, s);
+      return launch_bm<UC_MX4, MODE>(tile, a, grid, s);
     default: return launch_bm<UC_I8, MODE>(tile, a, grid, s);
   }
 }

@@ -48,6 +48,23 @@ template <int BM> struct TileShape;
 template <> struct TileShape<64> { static constexpr int WM = 2, WN = 2, BN = 128, S = 6, RB = 128; };
 template <> struct TileShape<128> { static constexpr int WM = 2, WN = 4, BN = 256, S = 3, RB = 128; };
 template <int BM> constexpr int threads_of() { return 64 * TileShape<BM>::WM * TileShape<BM>::WN; }
+// The LDS ring of a use case: A rows of RBA bytes per stage (128 K-values
+// of 1 byte, 64 of bf16), B rows of RBB bytes (64 for e2m1 weights: the same
+// 128 K-values at half a byte each).  The MX use cases also ring one E8M0
+// word per A and B row per stage (the four scales of its 128 K-values), 64
+// rows per wave (BM + BN rows used); the e2m1 ring's smaller stages leave
+// room for more slots.
+template <int UC, int BM> struct Ring {
+  static constexpr int BN = TileShape<BM>::BN;
+  static constexpr int RBA = 128;
+  static constexpr int RBB = UC == UC_MX4 ? 64 : 128;
+  static constexpr int S = UC == UC_MX4 ? (BM == 64 ? 8 : 4) : TileShape<BM>::S;
+  static constexpr int STAGE = BM * RBA + BN * RBB;
+  static constexpr int SCALE_STAGE = is_mx(UC) ? threads_of<BM>() * 4 : 0;
+};
+// Experts the LDS copies of the offsets and counts hold (the MX rings leave
+// room for 512).
+template <int UC> constexpr int max_experts() { return is_mx(UC) ? 512 : 1024; }
 // Per-row data of a tile for its epilogue, two tiles' worth (the next tile's
 // is written while the current one is still being stored): 16 bytes a row.
 struct RowInfo {
@@ -56,8 +73,9 @@ struct RowInfo {
   float rs;        // s^X (Linear1, A8W8) or s^A (Linear2, A8W8) of the row
   float pad;
 };
-template <int BM> constexpr int lds_bytes_of() {
-  return TileShape<BM>::S * (BM + TileShape<BM>::BN) * TileShape<BM>::RB + 2 * BM * (int)sizeof(RowInfo);
+// LDS: the data ring, the row data, the scale ring
+template <int UC, int BM> constexpr int lds_bytes_of() {
+  return Ring<UC, BM>::S * (Ring<UC, BM>::STAGE + Ring<UC, BM>::SCALE_STAGE) + 2 * BM * (int)sizeof(RowInfo);
 }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -110,27 +128,32 @@ __device__ __forceinline__ void vm_barrier() {
 // without a memory access.
 constexpr uint32_t kOffRange = 0x7fff0000u;   // past any A descriptor's range (< 2^31 bytes)
 
-template <int NW, int BM, int STAGE, int S, int RB>
+// A rows take RBA bytes of each K-stage and B rows RBB (half as many for
+// e2m1 weights, so a B group moves twice the rows); instruction i < DA of a
+// wave moves A rows, the others B rows.  Each instruction fills 1 KiB of the
+// stage, so group g lands at byte g*1024 either way.
+template <int NW, int BM, int STAGE, int S, int RBA, int RBB>
 __device__ __forceinline__ void dma_one(uint8_t* lds, const uint8_t* abase, int abytes, const uint8_t* bbase,
-                                        int bbytes, uint32_t voff, int wv, int kbytes, int i, int kb, int kbase,
-                                        bool by_tok, uint32_t voff_a) {
-  constexpr int RPI = 1024 / RB;
-  const bool is_a = i < BM / (RPI * NW);
+                                        int bbytes, uint32_t voff_b, int wv, int kbytes_a, int kbytes_b, int i, int kb,
+                                        int kbase, bool by_tok, uint32_t voff_a) {
+  constexpr int RPIA = 1024 / RBA, RPIB = 1024 / RBB;
+  constexpr int DA = BM / (RPIA * NW);
+  const bool is_a = i < DA;
   const __amdgpu_buffer_rsrc_t rs =
       __builtin_amdgcn_make_buffer_rsrc((void*)(is_a ? abase : bbase), (short)0, is_a ? abytes : bbytes, 0x00020000);
-  const int rows = is_a ? (by_tok ? 0 : RPI * NW * i) : RPI * NW * i - BM;
-  const int soff = __builtin_amdgcn_readfirstlane(rows * kbytes + (kb + kbase) * RB);
+  const int soff = is_a ? __builtin_amdgcn_readfirstlane((by_tok ? 0 : RPIA * NW * i) * kbytes_a + (kb + kbase) * RBA)
+                        : __builtin_amdgcn_readfirstlane(RPIB * NW * (i - DA) * kbytes_b + (kb + kbase) * RBB);
   const int g = wv + NW * i;
-  const uint32_t vo = is_a ? voff_a : voff;
+  const uint32_t vo = is_a ? voff_a : voff_b;
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(lds + (kb % S) * STAGE + g * 1024), 16, vo, soff, 0, 0);
 }
 
 // The fragments of one K-stage held in registers: NQ 16-byte chunks of the
-// wave's MB A blocks and NB B blocks.
-template <int MB, int NB, int NQ>
+// wave's MB A blocks and NQB of its NB B blocks.
+template <int MB, int NB, int NQ, int NQB = NQ>
 struct Frags {
   u32x4 a[MB][NQ];
-  u32x4 b[NB][NQ];
+  u32x4 b[NB][NQB];
 };
 
 // Fragment read r of a stage (r = chunk * (MB + NB) + block; A blocks first),
@@ -154,6 +177,50 @@ __device__ __forceinline__ void read_frag(Frags<MB, NB, NQ>& f, int r, const uin
     if constexpr (NB > 2) if (y == 2) f.b[2][q] = ds_read16<2 * BOFF>(ad);
     if constexpr (NB > 3) if (y == 3) f.b[3][q] = ds_read16<3 * BOFF>(ad);
   }
+}
+
+// Fragment read r of a stage for the MX MFMAs (K = 64 per instruction):
+// phase p = r / RPP reads A chunks 2p, 2p+1 of each A block, then B chunk
+// CPB*p .. CPB*p + CPB-1 of each B block (two e4m3 chunks, or one e2m1
+// chunk: 32 values in 16 bytes).  BOFFA / BOFFB: 32 rows apart.
+template <int BOFFA, int BOFFB, int MB, int NB, int NQ, int NQB>
+__device__ __forceinline__ void read_frag_mx(Frags<MB, NB, NQ, NQB>& f, int r, const uint32_t* aoff,
+                                             const uint32_t* boff, uint32_t so) {
+  constexpr int CPB = NQB / 2;
+  constexpr int RPP = 2 * MB + CPB * NB;
+  const int p = r / RPP, x = r % RPP;
+  if (x < 2 * MB) {
+    const int q = 2 * p + x / MB, i = x % MB;
+    const uint32_t ad = aoff[q] + so;
+    if (i == 0) f.a[0][q] = ds_read16<0>(ad);
+    if constexpr (MB > 1) if (i == 1) f.a[1][q] = ds_read16<BOFFA>(ad);
+    if constexpr (MB > 2) if (i == 2) f.a[2][q] = ds_read16<2 * BOFFA>(ad);
+    if constexpr (MB > 3) if (i == 3) f.a[3][q] = ds_read16<3 * BOFFA>(ad);
+  } else {
+    const int y = x - 2 * MB, q = CPB * p + y / NB, j = y % NB;
+    const uint32_t ad = boff[q] + so;
+    if (j == 0) f.b[0][q] = ds_read16<0>(ad);
+    if constexpr (NB > 1) if (j == 1) f.b[1][q] = ds_read16<BOFFB>(ad);
+    if constexpr (NB > 2) if (j == 2) f.b[2][q] = ds_read16<2 * BOFFB>(ad);
+    if constexpr (NB > 3) if (j == 3) f.b[3][q] = ds_read16<3 * BOFFB>(ad);
+  }
+}
+
+// 16 e4m3 times an MX scale 2^k -> 16 bf16 (exact: e4m3 values times a
+// power of two within the float range are bf16 values)
+__device__ __forceinline__ void widen_e4m3_scaled(const u32x4& w, float s, u32x4& lo, u32x4& hi) {
+#define CVT(x, hi_) __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((x), s, (hi_)))
+  lo = u32x4{CVT(w[0], false), CVT(w[0], true), CVT(w[1], false), CVT(w[1], true)};
+  hi = u32x4{CVT(w[2], false), CVT(w[2], true), CVT(w[3], false), CVT(w[3], true)};
+#undef CVT
+}
+// 32 e2m1 (16 bytes, the even K in the low nibble) times 2^k -> four
+// operands of 8 bf16 in K order (exact)
+__device__ __forceinline__ void widen_e2m1_scaled(const u32x4& w, float s, u32x4* o) {
+#define CVT(x, b_) __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((x), s, (b_)))
+#pragma unroll
+  for (int d = 0; d < 4; ++d) o[d] = u32x4{CVT(w[d], 0), CVT(w[d], 1), CVT(w[d], 2), CVT(w[d], 3)};
+#undef CVT
 }
 
 // 16 e4m3 -> 16 bf16 (exact: every e4m3 value is a bf16 value)
@@ -216,6 +283,10 @@ __device__ __forceinline__ GemmArgs uniform_args(const GemmArgs& in) {
   a.topk_w = uniform_ptr(in.topk_w);
   a.contrib = uniform_ptr(in.contrib);
   a.raw_out = uniform_ptr(in.raw_out);
+  a.a_mx = uniform_ptr(in.a_mx);
+  a.a_mx_rows = (int64_t)uniform_int((int)in.a_mx_rows);   // < 2^31 (checked by the host)
+  a.b_mx = uniform_ptr(in.b_mx);
+  a.out_mx = uniform_ptr(in.out_mx);
   a.err = uniform_ptr(in.err);
   a.E = uniform_int(in.E);
   a.N = uniform_int(in.N);
@@ -245,6 +316,7 @@ struct TileRef {
   const uint8_t* bbase;   // first B row (prepared weights) of the tile
   int kbase, nkl;         // K stages kbase .. kbase + nkl - 1
   uint32_t aoa[2];        // per lane: byte offsets of its A rows' chunks (A read by token)
+  uint32_t sc;            // MX: per lane, byte offset of the scale row it moves (or one past the range)
   int role;               // TileRole: whole tile, or piece 0 (adds the others' partials), or a later piece
   int slot;               // partial slot of a piece (piece 0: the later pieces use slot + 1 ..)
 };
@@ -295,7 +367,7 @@ __device__ __forceinline__ bool poll_flag(uint32_t* p, uint32_t spin_limit) {
 // The expert of a tile is the largest e with (off[e] / BM) * n_tiles <= tile.
 template <int BM>
 __device__ __forceinline__ TileRef resolve_tile(const GemmArgs& a, const int32_t* off_s, const int32_t* cnt_s,
-                                               int tile, int n_tiles, int kbytes) {
+                                               int tile, int n_tiles, int kbytes, int kbytes_b) {
   int lo = 0, hi = a.E;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
@@ -316,37 +388,50 @@ __device__ __forceinline__ TileRef resolve_tile(const GemmArgs& a, const int32_t
   r.n0 = uniform_int(nblk * TileShape<BM>::BN);
   r.valid = uniform_int(min(BM, off_s[lo] + cnt_s[lo] - r.row0));
   r.abase = uniform_ptr(a.a_route ? a.A : a.A + (int64_t)r.row0 * kbytes);
-  r.bbase = uniform_ptr(a.B + ((int64_t)r.e * a.N + r.n0) * kbytes);
+  r.bbase = uniform_ptr(a.B + ((int64_t)r.e * a.N + r.n0) * kbytes_b);
   return r;
 }
 
 template <int UC, int BM, int MODE, bool WIDEN>
 __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, int32_t* off_s, int32_t* cnt_s) {
   const GemmArgs a = uniform_args(args);
-  constexpr int WM = TileShape<BM>::WM, WN = TileShape<BM>::WN, S = TileShape<BM>::S;
+  constexpr bool MX = is_mx(UC), B4 = UC == UC_MX4;
+  // MX on the scaled MX MFMA, or (MXW, Linear1's exact mode) on the bf16
+  // MFMA after widening each e4m3 / e2m1 value times its block scale to bf16
+  constexpr bool MXI = MX && !WIDEN, MXW = MX && WIDEN;
+  constexpr int WM = TileShape<BM>::WM, WN = TileShape<BM>::WN, S = Ring<UC, BM>::S;
   constexpr int NT = threads_of<BM>(), NW = NT / 64;
-  constexpr int BN = TileShape<BM>::BN, RB = TileShape<BM>::RB;
-  constexpr int CH = RB / 16, NQ = CH / 2;                 // chunks per row; per lane and block
-  constexpr int RPI = 1024 / RB;                           // rows per DMA instruction
-  constexpr int RPS = 16 / CH;                             // rows per swizzle step
+  constexpr int BN = TileShape<BM>::BN, RB = Ring<UC, BM>::RBA, RBB = Ring<UC, BM>::RBB;
+  constexpr int CH = RB / 16, NQ = CH / 2;                 // A: chunks per row; per lane and block
+  constexpr int CHB = RBB / 16, NQB = CHB / 2;             // B: the same
+  constexpr int RPI = 1024 / RB, RPIB = 1024 / RBB;        // rows per DMA instruction
+  constexpr int RPS = 16 / CH, RPSB = 16 / CHB;            // rows per swizzle step
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int MB = WTM / 32, NB = WTN / 32;
-  constexpr int ROWS = BM + BN;
-  constexpr int STAGE = ROWS * RB;
-  constexpr int GROUPS = ROWS / RPI;
-  static_assert(GROUPS % NW == 0, "DMA groups must split evenly over the waves");
-  constexpr int D = GROUPS / NW;                           // DMA instructions per wave per stage
-  static_assert((S - 1) * D <= 63, "vmcnt range");
+  constexpr int STAGE = Ring<UC, BM>::STAGE;
+  constexpr int SSTAGE = Ring<UC, BM>::SCALE_STAGE;
+  constexpr int GA = BM / RPI, GB = BN / RPIB, GROUPS = GA + GB;
+  static_assert(GROUPS % NW == 0 && GA % NW == 0, "DMA groups must split evenly over the waves");
+  constexpr int D = GROUPS / NW;                           // data DMA instructions per wave per stage
+  // MX: one scale DMA instruction per wave and stage, 64 rows' E8M0 words:
+  // waves 0 .. BM/64-1 the A rows, the next BN/64 the B rows, the others
+  // none (their loads read zeros into the unused rest of the scale slot).
+  // No lane is masked off, so the step stays free of branches.
+  constexpr int DT = D + (MX ? 1 : 0);                     // DMA instructions per wave per stage
+  static_assert(!MX || (BM % 64 == 0 && BN % 64 == 0 && (BM + BN) / 64 <= NW), "scale rows per wave");
+  static_assert((S - 1) * DT <= 63, "vmcnt range");
   constexpr int ESZ = (UC == UC_BF16) ? 2 : 1;
   constexpr int NFR = MB + NB;                             // fragment reads per chunk index
-  // MFMA phases of a stage: one chunk each, or two for e4m3 MFMAs (K = 64)
-  constexpr int CPP = (UC == UC_FP8 && !WIDEN) ? 2 : 1;
+  // MFMA phases of a stage: one chunk each, or two for e4m3 / MX MFMAs (K = 64)
+  constexpr int CPP = ((UC == UC_FP8 && !WIDEN) || MX) ? 2 : 1;
   constexpr int NPH = NQ / CPP;
   static_assert(NPH >= 2, "a stage needs MFMA phases after its barrier to hide the refill and the reads");
-  constexpr int RPP = NFR * CPP;                           // fragment reads per phase
-  constexpr int MPP = MB * NB * (WIDEN ? 2 : 1);           // MFMAs per phase
+  static_assert(!MX || NPH == 2, "MX phases select scale bytes 0 and 2");
+  constexpr int RPP = MX ? 2 * MB + (NQB / 2) * NB : NFR * CPP;   // fragment reads per phase
+  constexpr int NSR = MX ? MB + NB : 0;                    // scale-word reads per stage (before the fragments)
+  constexpr int MPP = MB * NB * (MXW ? 4 : WIDEN ? 2 : 1); // MFMAs per phase
   // phase 0 may start once only the reads of the later phases are in flight
-  constexpr int P0WAIT = (NQ * NFR - RPP) > 15 ? 15 : (NQ * NFR - RPP);
+  constexpr int P0WAIT = (NPH - 1) * RPP > 15 ? 15 : (NPH - 1) * RPP;
   static_assert(BM % (RPI * NW) == 0, "A rows fill whole DMA instructions");
   static_assert(MODE != 0 || NB % 2 == 0, "Linear1 waves hold whole gate/up pairs");
   typedef typename Acc<UC>::type AccT;
@@ -371,41 +456,79 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
   const bool offsets_ok = __syncthreads_or(bad) == 0;
   if (!offsets_ok && t == 0 && a.err) atomicOr(a.err, (uint32_t)MM_DEVERR_BAD_OFFSETS);
 
-  const int kbytes = a.Kdim * ESZ;
+  const int kbytes = a.Kdim * ESZ;                         // A bytes per row
+  const int kbytes_b = B4 ? a.Kdim / 2 : kbytes;           // B bytes per row
   const int nk = kbytes / RB;
   const int n_tiles = a.N / BN;
   const int total = offsets_ok ? (off_s[a.E] / BM) * n_tiles : 0;
   const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_ptr_t)lds;
   RowInfo* rowinfo = reinterpret_cast<RowInfo*>(lds + S * STAGE);   // [2][BM]
   const uint32_t rowinfo_base = lds_base + (uint32_t)(S * STAGE);
+  // MX scale ring: per slot, BM A words then BN B words
+  uint8_t* const scl = lds + S * STAGE + 2 * BM * (int)sizeof(RowInfo);
+  const uint32_t scl_base = lds_base + (uint32_t)(S * STAGE + 2 * BM * (int)sizeof(RowInfo));
 
   // per-lane LDS addresses of the NQ fragment chunks (stage slot added per
-  // stage); the wave's first rows are a multiple of 16, the swizzle period
-  uint32_t aoff[NQ], boff[NQ];
+  // stage); the wave's first rows are a multiple of 16, the swizzle period.
+  // Chunk q of lane half h is the row's 16-byte chunk NQ*h + q, except for
+  // the MX MFMAs, whose block scales follow the instruction's K layout: in
+  // an e4m3 operand, bytes 0-15 of both lane halves form K-block 0 and bytes
+  // 16-31 K-block 1 (scaled by lane half 0's and 1's scale); in an e2m1
+  // operand each lane half holds one K-block.  So lane half h takes chunks
+  // 2q + h: phase p's blocks are then the stage's MX groups 2p and 2p+1.
+  uint32_t aoff[NQ], boff[NQB];
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
-    const uint32_t cpos = (uint32_t)(((NQ * h + q) ^ ((lr / RPS) % CH)) << 4);
-    aoff[q] = lds_base + (uint32_t)(wm * WTM + lr) * RB + cpos;
-    boff[q] = lds_base + (uint32_t)(BM + wn * WTN + lr) * RB + cpos;
+    const int c = MXI ? 2 * q + h : NQ * h + q;
+    aoff[q] = lds_base + (uint32_t)(wm * WTM + lr) * RB + (uint32_t)((c ^ ((lr / RPS) % CH)) << 4);
   }
+#pragma unroll
+  for (int q = 0; q < NQB; ++q) {
+    const int c = MXI ? 2 * q + h : NQB * h + q;
+    boff[q] = lds_base + (uint32_t)(BM * RB) + (uint32_t)(wn * WTN + lr) * RBB + (uint32_t)((c ^ ((lr / RPSB) % CHB)) << 4);
+  }
+  // MX: the lane's A-row and B-row scale words (slot added per stage)
+  const uint32_t asc_rd = scl_base + (uint32_t)(wm * WTM + lr) * 4;
+  const uint32_t bsc_rd = scl_base + (uint32_t)(BM + wn * WTN + lr) * 4;
   // per-lane byte offset of the DMA rows: group g covers rows RPI*g ..
   // RPI*g + RPI-1, lane l row RPI*g + l/CH, and lands its logical chunk
   // (l%CH) ^ swizzle(row) at position l%CH.  The swizzle of a lane's row is
   // the same in all of a wave's groups g = wv + NW*i: their row offsets
   // differ by RPI*NW*i, a multiple of the swizzle period RPS*CH (needs NW
-  // even when CH = 8).
+  // even when CH = 8).  B rows alike with their own width.
   static_assert((RPI * NW / RPS) % CH == 0, "DMA swizzle must repeat across a wave's groups");
+  static_assert((RPIB * NW / RPSB) % CHB == 0, "DMA swizzle must repeat across a wave's groups");
   const uint32_t vchunk = (uint32_t)(((l % CH) ^ (((RPI * wv + l / CH) / RPS) % CH)) << 4);
   const uint32_t voff = (uint32_t)((RPI * wv + l / CH) * kbytes) + vchunk;
+  const uint32_t vchunk_b = (uint32_t)(((l % CHB) ^ (((RPIB * wv + l / CHB) / RPSB) % CHB)) << 4);
+  const uint32_t voff_b = (uint32_t)((RPIB * wv + l / CHB) * kbytes_b) + vchunk_b;
   // A read by token: the A buffer is the T token rows, each lane's rows come
   // from the route of their pool row (padding rows read token 0, unused)
   const bool by_tok = a.a_route != nullptr;
   constexpr int DA = BM / (RPI * NW);                      // A instructions per wave and stage
   static_assert(DA <= 2, "per-lane A row offsets of at most two instructions");
-  const int abytes = by_tok ? (int)(a.a_rows * kbytes) : BM * kbytes, bbytes = BN * kbytes;
-#define MM_DMA(tr_, i_, kb_)                                                                                    \
-  dma_one<NW, BM, STAGE, S, RB>(lds, (tr_).abase, abytes, (tr_).bbase, bbytes, voff, wv, kbytes, (i_), (kb_), \
-                                (tr_).kbase, by_tok, (tr_).aoa[(i_) < DA ? (i_) : 0])
+  const int abytes = by_tok ? (int)(a.a_rows * kbytes) : BM * kbytes, bbytes = BN * kbytes_b;
+  // MX scale rows: a_mx [a_mx_rows][G], b_mx [E][N][G] bytes, G = Kdim / 32
+  const int gbytes = a.Kdim / kMxGroup;
+  const int asc_bytes = MX ? (int)(a.a_mx_rows * gbytes) : 0;
+  const int bsc_bytes = MX ? a.E * a.N * gbytes : 0;
+  // One DMA instruction x of stage kb of tile tr: x < D data, x = D the
+  // wave's 64 scale rows (lane l: row 64*wv + l of the slot, A rows then B
+  // rows), each lane's word landing at its row's word.
+  const bool scale_a = wv < BM / 64;
+  auto dma_x = [&](const TileRef& tr, int x, int kb) {
+    if (x < D) {
+      dma_one<NW, BM, STAGE, S, RB, RBB>(lds, tr.abase, abytes, tr.bbase, bbytes, voff_b, wv, kbytes, kbytes_b, x, kb,
+                                         tr.kbase, by_tok, tr.aoa[x < DA ? x : 0]);
+    } else if constexpr (MX) {
+      const int soff = __builtin_amdgcn_readfirstlane((kb + tr.kbase) * 4);
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(scale_a ? a.a_mx : a.b_mx), (short)0, scale_a ? asc_bytes : bsc_bytes, 0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(scl + (kb % S) * SSTAGE + 64 * wv * 4), 4, tr.sc, soff,
+                                               0, 0);
+    }
+  };
+#define MM_DMA(tr_, i_, kb_) dma_x((tr_), (i_), (kb_))
 
   // Per-row epilogue data of a tile, thread t holding row t: loaded into
   // registers when the tile's stages go out (the loads that need the route
@@ -421,19 +544,19 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
     RowRegs rr{-1, 0.0f, 1.0f};
     if (t < tr.valid) {
       const int64_t p = (int64_t)tr.row0 + t;
-      if constexpr (MODE == 0 && UC != UC_BF16) {
+      if constexpr (MODE == 0 && UC != UC_BF16 && !MX) {
         if (by_tok) rr.route = gp(a.a_route)[p];
         else rr.rs = gp(a.x_scale)[p];
       }
       if constexpr (MODE == 1) {
         rr.route = gp(a.pool_src)[p];
-        if constexpr (UC != UC_BF16) rr.rs = gp(a.a_scale)[p];
+        if constexpr (UC != UC_BF16 && !MX) rr.rs = gp(a.a_scale)[p];
       }
     }
     return rr;
   };
   auto row_second = [&](RowRegs& rr) {
-    if constexpr (MODE == 0 && UC != UC_BF16) {
+    if constexpr (MODE == 0 && UC != UC_BF16 && !MX) {
       if (by_tok) rr.rs = rr.route >= 0 ? gp(a.x_scale)[rr.route / a.K] : 1.0f;
     }
     if constexpr (MODE == 1) {
@@ -454,7 +577,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
   auto start_first = [&](const TileRef& tr) {
     const RowRegs rr = row_first(tr);
 #pragma unroll
-    for (int x = 0; x < D; ++x) MM_DMA(tr, x, 0);
+    for (int x = 0; x < DT; ++x) MM_DMA(tr, x, 0);
     return rr;
   };
   auto start_rest = [&](const TileRef& tr) {
@@ -462,7 +585,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
     for (int st = 1; st < S; ++st)
       if (st < tr.nkl) {
 #pragma unroll
-        for (int x = 0; x < D; ++x) MM_DMA(tr, x, st);
+        for (int x = 0; x < DT; ++x) MM_DMA(tr, x, st);
       }
   };
   auto start_tile = [&](const TileRef& tr) {
@@ -492,14 +615,14 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
   auto make_item = [&](int j) {
     TileRef r;
     if (j < full) {
-      r = resolve_tile<BM>(a, off_s, cnt_s, t_beg + wgx + j * per_x, n_tiles, kbytes);
+      r = resolve_tile<BM>(a, off_s, cnt_s, t_beg + wgx + j * per_x, n_tiles, kbytes, kbytes_b);
       r.kbase = 0;
       r.nkl = nk;
       r.role = kRoleFull;
       r.slot = 0;
     } else {
       const int p = wgx + (j - full) * per_x, sub = p % sk;
-      r = resolve_tile<BM>(a, off_s, cnt_s, t_beg + full * per_x + p / sk, n_tiles, kbytes);
+      r = resolve_tile<BM>(a, off_s, cnt_s, t_beg + full * per_x + p / sk, n_tiles, kbytes, kbytes_b);
       r.kbase = uniform_int(sub * nk / sk);
       r.nkl = uniform_int((sub + 1) * nk / sk - sub * nk / sk);
       r.role = sk == 1 ? kRoleFull : (sub == 0 ? kRoleReduce : kRoleProduce);
@@ -514,6 +637,33 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
         r.aoa[x] = route >= 0 ? (uint32_t)((route / a.K) * kbytes) + vchunk : kOffRange;
       } else {
         r.aoa[x] = row < r.valid ? voff : kOffRange;
+      }
+    }
+    r.sc = 0;
+    if constexpr (MX) {
+      // A-scale waves: tile row 64*wv + l (its token row when A is read by
+      // token); past the valid rows an offset beyond the range (the word
+      // reads as zero; the row's data is zero too).  B-scale waves: column
+      // n0 + 64*(wv - BM/64) + l in formula order (Linear1's prepared rows
+      // interleave gate and up columns in groups of gate_up_group).  Other
+      // waves: beyond the range.
+      if (scale_a) {
+        const int row = 64 * wv + l;
+        if (by_tok) {
+          const int32_t route = gp(a.a_route)[(int64_t)r.row0 + row];
+          r.sc = route >= 0 ? (uint32_t)((route / a.K) * gbytes) : kOffRange;
+        } else {
+          r.sc = row < r.valid ? (uint32_t)((r.row0 + row) * gbytes) : kOffRange;
+        }
+      } else if (wv < (BM + BN) / 64) {
+        int n = r.n0 + 64 * (wv - BM / 64) + l;
+        if (MODE == 0 && a.gate_up_group > 0) {
+          const int g2 = 2 * a.gate_up_group, qq = n / g2, m = n % g2;
+          n = m < a.gate_up_group ? qq * a.gate_up_group + m : a.I + qq * a.gate_up_group + (m - a.gate_up_group);
+        }
+        r.sc = (uint32_t)(((int64_t)r.e * a.N + n) * gbytes);
+      } else {
+        r.sc = kOffRange;
       }
     }
     return r;
@@ -537,11 +687,97 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
 #pragma unroll
         for (int q = 0; q < 16; ++q) acc[i][j][q] = 0;
 
-    Frags<MB, NB, NQ> f;
+    Frags<MB, NB, NQ, NQB> f;
+    // MX: the scale words of the A rows and B columns of the stage being
+    // computed (shifted so that byte p is the lane's group of phase p) and
+    // of the next stage (being read)
+    uint32_t sa_c[MX ? MB : 1], sb_c[MX ? NB : 1], sa_n[MX ? MB : 1], sb_n[MX ? NB : 1];
+    // MXW: the block scales of phases 0 and 1 as floats (lane half h, phase
+    // p: the stage's K-group 2h + p); a zero E8M0 byte (2^-127, all-zero or
+    // tiny groups) widens as 0
+    float saf[MXW ? MB : 1][2], sbf[MXW ? NB : 1][2];
+    auto read_scales = [&](uint32_t ss) {
+      if constexpr (MX) {
+#pragma unroll
+        for (int i = 0; i < MB; ++i) sa_n[i] = ds_read4<0>(asc_rd + ss + (uint32_t)(i * 32 * 4));
+#pragma unroll
+        for (int j = 0; j < NB; ++j) sb_n[j] = ds_read4<0>(bsc_rd + ss + (uint32_t)(j * 32 * 4));
+      }
+    };
+    // after the wait for the stage's first reads: its scale words.  Lane half
+    // h supplies the scale of K-block h, which in phase p is the stage's
+    // group 2p + h: byte 2p of the word shifted down by 8h bits.
+    auto take_scales = [&]() {
+      if constexpr (MXI) {
+#pragma unroll
+        for (int i = 0; i < MB; ++i) {
+          tie(sa_n[i]);
+          sa_c[i] = sa_n[i] >> (8 * h);
+        }
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          tie(sb_n[j]);
+          sb_c[j] = sb_n[j] >> (8 * h);
+        }
+      } else if constexpr (MXW) {
+#pragma unroll
+        for (int i = 0; i < MB; ++i) {
+          tie(sa_n[i]);
+#pragma unroll
+          for (int p = 0; p < 2; ++p) saf[i][p] = __uint_as_float(((sa_n[i] >> (8 * (2 * h + p))) & 0xffu) << 23);
+        }
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          tie(sb_n[j]);
+#pragma unroll
+          for (int p = 0; p < 2; ++p) sbf[j][p] = __uint_as_float(((sb_n[j] >> (8 * (2 * h + p))) & 0xffu) << 23);
+        }
+      }
+    };
+    // all fragment reads of a stage, slot offset so (scale words first)
+    auto read_stage = [&](uint32_t so) {
+      if constexpr (MX) {
+        read_scales((so / STAGE) * SSTAGE);
+#pragma unroll
+        for (int r = 0; r < NPH * RPP; ++r) read_frag_mx<32 * RB, 32 * RBB>(f, r, aoff, boff, so);
+      } else {
+#pragma unroll
+        for (int r = 0; r < NQ * NFR; ++r) read_frag<32 * RB>(f, r, aoff, boff, so);
+      }
+    };
+    auto read_one = [&](int r, uint32_t so) {
+      if constexpr (MX) read_frag_mx<32 * RB, 32 * RBB>(f, r, aoff, boff, so);
+      else read_frag<32 * RB>(f, r, aoff, boff, so);
+    };
     // MFMA mi of phase p (chunks CPP*p .. CPP*p + CPP-1 of the stage in f)
     u32x4 wa_lo[MB], wa_hi[MB], wb_lo, wb_hi;   // e4m3 -> bf16 widened operands
+    u32x4 wax[MXW ? MB : 1][4], wbx[4];          // MXW: the phase's 32 K-values as four bf16 operands
     auto mfma_at = [&](int p, int mi) {
-      if constexpr (UC == UC_FP8 && !WIDEN) {
+      if constexpr (MXW) {
+        // B block j outer; t: the four 8-value parts of the phase's K range
+        const int j = mi / (4 * MB), i = (mi % (4 * MB)) / 4, t = mi % 4;
+        if (mi == 0) {
+#pragma unroll
+          for (int x = 0; x < MB; ++x) {
+            widen_e4m3_scaled(f.a[x][2 * p], saf[x][p], wax[x][0], wax[x][1]);
+            widen_e4m3_scaled(f.a[x][2 * p + 1], saf[x][p], wax[x][2], wax[x][3]);
+          }
+        }
+        if (mi % (4 * MB) == 0) {
+          if constexpr (B4) {
+            widen_e2m1_scaled(f.b[j][p], sbf[j][p], wbx);
+          } else {
+            widen_e4m3_scaled(f.b[j][2 * p], sbf[j][p], wbx[0], wbx[1]);
+            widen_e4m3_scaled(f.b[j][2 * p + 1], sbf[j][p], wbx[2], wbx[3]);
+          }
+        }
+        mfma_bf16(acc[i][j], wax[i][t], wbx[t]);
+      } else if constexpr (MX) {
+        const int i = mi / NB, j = mi % NB, q0 = 2 * p;
+        const int qb0 = B4 ? p : q0, qb1 = B4 ? p : q0 + 1;
+        if (p == 0) mfma_mx<0, B4>(acc[i][j], f.a[i][q0], f.a[i][q0 + 1], f.b[j][qb0], f.b[j][qb1], sa_c[i], sb_c[j]);
+        else mfma_mx<2, B4>(acc[i][j], f.a[i][q0], f.a[i][q0 + 1], f.b[j][qb0], f.b[j][qb1], sa_c[i], sb_c[j]);
+      } else if constexpr (UC == UC_FP8 && !WIDEN) {
         const int i = mi / NB, j = mi % NB, q0 = 2 * p;
         mfma_fp8(acc[i][j], f.a[i][q0], f.a[i][q0 + 1], f.b[j][q0], f.b[j][q0 + 1]);
       } else if constexpr (WIDEN) {
@@ -560,12 +796,18 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
         else mfma_i8(acc[i][j], f.a[i][p], f.b[j][p]);
       }
     };
-    auto tie_chunks = [&](int c0, int c1) {
+    // the fragment registers of phases p0 .. p1-1 (reads completed)
+    auto tie_phases = [&](int p0, int p1) {
+      constexpr int CPB = NQB / NPH;   // B chunks per phase
 #pragma unroll
       for (int q = 0; q < NQ; ++q) {
-        if (q < c0 || q >= c1) continue;
+        if (q < p0 * CPP || q >= p1 * CPP) continue;
 #pragma unroll
         for (int i = 0; i < MB; ++i) tie(f.a[i][q]);
+      }
+#pragma unroll
+      for (int q = 0; q < NQB; ++q) {
+        if (q < p0 * CPB || q >= p1 * CPB) continue;
 #pragma unroll
         for (int j = 0; j < NB; ++j) tie(f.b[j][q]);
       }
@@ -582,7 +824,8 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
       constexpr bool REFILL = decltype(refill_tag)::value, MORE = decltype(more_tag)::value;
       constexpr int VM = decltype(vm_tag)::value;   // this wave's loads still allowed in flight
       lgkm_wait<P0WAIT>();
-      tie_chunks(0, CPP);
+      take_scales();
+      tie_phases(0, 1);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int mi = 0; mi < MPP; ++mi) mfma_at(0, mi);
@@ -592,9 +835,10 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
       } else {
         lgkm_wait<0>();
       }
-      tie_chunks(CPP, NQ);
+      tie_phases(1, NPH);
       __builtin_amdgcn_sched_barrier(0);
       const uint32_t so = (uint32_t)(((kb + 1) % S) * STAGE);
+      if constexpr (MORE) read_scales((uint32_t)(((kb + 1) % S) * SSTAGE));   // ahead of stage kb+1's fragments
       constexpr int NMR = (NPH - 1) * MPP;   // MFMAs after the barrier: DMA issues spread over them
       int dm = 0;
 #pragma unroll
@@ -605,17 +849,17 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
           mfma_at(p, mi);
           if constexpr (REFILL) {
             const int m = (p - 1) * MPP + mi;
-            const int target = ((m + 1) * D + NMR - 1) / NMR;
+            const int target = ((m + 1) * DT + NMR - 1) / NMR;
 #pragma unroll
-            for (int x = 0; x < D; ++x)
+            for (int x = 0; x < DT; ++x)
               if (x >= dm && x < target) MM_DMA(cur, x, kb + S);
-            dm = target < D ? target : D;
+            dm = target < DT ? target : DT;
           }
           if constexpr (MORE) {
             const int target = ((mi + 1) * RPP + MPP - 1) / MPP;
 #pragma unroll
             for (int r = 0; r < RPP; ++r)
-              if (r >= rd && r < target) read_frag<32 * RB>(f, (p - 1) * RPP + r, aoff, boff, so);
+              if (r >= rd && r < target) read_one((p - 1) * RPP + r, so);
             rd = target < RPP ? target : RPP;
           }
           __builtin_amdgcn_sched_barrier(0);
@@ -623,7 +867,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
       }
       if constexpr (MORE) {
 #pragma unroll
-        for (int r = 0; r < RPP; ++r) read_frag<32 * RB>(f, (NPH - 1) * RPP + r, aoff, boff, so);
+        for (int r = 0; r < RPP; ++r) read_one((NPH - 1) * RPP + r, so);
       }
       __builtin_amdgcn_sched_barrier(0);
     };
@@ -634,21 +878,20 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
     const int nkl = cur.nkl;
     static_for<S>([&](auto cc) {
       constexpr int c = S - 1 - decltype(cc)::value;   // S-1, ..., 0
-      if (min(nkl, S) - 1 == c) vm_barrier<c * D>();
+      if (min(nkl, S) - 1 == c) vm_barrier<c * DT>();
     });
     row_second(rr_cur);
-#pragma unroll
-    for (int r = 0; r < NQ * NFR; ++r) read_frag<32 * RB>(f, r, aoff, boff, 0u);
+    read_stage(0u);
     // Every barrier below has a compile-time DMA count.  At step kb's barrier
     // stage kb+1 must have landed while stages kb+2 .. min(nk-1, kb+S-1) may
     // be in flight; stage kb+S refills while kb + S < nk, and the last S
     // steps drain the ring.
     const std::integral_constant<bool, true> yes;
     const std::integral_constant<bool, false> no;
-    for (int kb = 0; kb < nkl - S; ++kb) step(kb, yes, yes, std::integral_constant<int, (S - 2) * D>{});
+    for (int kb = 0; kb < nkl - S; ++kb) step(kb, yes, yes, std::integral_constant<int, (S - 2) * DT>{});
     static_for<S - 1>([&](auto jj) {
       constexpr int j = S - decltype(jj)::value;   // S, ..., 2 steps before the end
-      if (nkl >= j) step(nkl - j, no, yes, std::integral_constant<int, (j - 2) * D>{});
+      if (nkl >= j) step(nkl - j, no, yes, std::integral_constant<int, (j - 2) * DT>{});
     });
     step(nkl - 1, no, no, std::integral_constant<int, 0>{});
 
@@ -660,19 +903,20 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
     for (int j = 0; j < NB; ++j) {
       cs0[j] = 1.0f;
       cs1[j] = 1.0f;
-      if constexpr (MODE == 0 && UC != UC_BF16) {
+      if constexpr (MODE == 0 && UC != UC_BF16 && !MX) {
         if (j < NB / 2) {
           const int col = cur.n0 / 2 + wn * (WTN / 2) + j * 32 + lr;
           cs0[j] = gp(a.w_scale)[(int64_t)cur.e * 2 * a.I + col];           // gate column
           cs1[j] = gp(a.w_scale)[(int64_t)cur.e * 2 * a.I + a.I + col];     // up column
         }
       }
-      if constexpr (MODE == 1 && UC != UC_BF16) cs0[j] = gp(a.w_scale)[(int64_t)cur.e * a.H + cur.n0 + wn * WTN + j * 32 + lr];
+      if constexpr (MODE == 1 && UC != UC_BF16 && !MX)
+        cs0[j] = gp(a.w_scale)[(int64_t)cur.e * a.H + cur.n0 + wn * WTN + j * 32 + lr];
     }
     // the scales are in registers before the next tile's copies go out (a
     // wait the compiler sees, so it places none later that would also wait
     // for those copies): s_waitcnt vmcnt(0)
-    if constexpr (UC != UC_BF16 && MODE != 2) __builtin_amdgcn_s_waitcnt(0x0F70);
+    if constexpr (UC != UC_BF16 && !MX && MODE != 2) __builtin_amdgcn_s_waitcnt(0x0F70);
     // this tile's row data goes to LDS; every wave is done reading the ring
     row_commit(rr_cur, buf);
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -761,8 +1005,8 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
         // otherwise wait for the next tile's LDS copies first): Linear2 needs
         // the whole entry, A8W8 Linear1 only s^X
         u32x4 ri[MODE == 1 ? 16 : 1];
-        uint32_t sxr[(MODE == 0 && UC != UC_BF16) ? 16 : 1];
-        if constexpr (MODE == 1 || (MODE == 0 && UC != UC_BF16)) {
+        uint32_t sxr[(MODE == 0 && UC != UC_BF16 && !MX) ? 16 : 1];
+        if constexpr (MODE == 1 || (MODE == 0 && UC != UC_BF16 && !MX)) {
 #pragma unroll
           for (int q = 0; q < 16; ++q) {
             const int r = rb + 8 * (q / 4) + (q % 4);
@@ -777,7 +1021,40 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
             else tie(sxr[q]);
           }
         }
-        if constexpr (MODE == 0) {
+        if constexpr (MODE == 0 && MX) {
+          // SwiGLU, then Q_MX of each row's group of 32 A columns: the group
+          // of block j is column lr of the 32 lanes of this lane's half, so
+          // its amax is a maximum over those lanes; exponent
+          // floor(log2 amax) - 8, codes = e4m3(v * 2^-exponent)
+          uint8_t* const obase = static_cast<uint8_t*>(a.a_out) + (int64_t)cur.row0 * a.I + cur.n0 / 2;
+          const int gpr = a.I / kMxGroup;   // scale bytes per row
+          uint8_t* const sbase = a.out_mx + (int64_t)cur.row0 * gpr + cur.n0 / 2 / kMxGroup;
+          int lane_off = rb * a.I + wn * (WTN / 2) + lr;
+          int lane_soff = rb * gpr + (wn * (WTN / 2)) / kMxGroup;   // the lane's first row's scale bytes
+          asm volatile("" : "+v"(lane_off), "+v"(lane_soff));
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            const int r = rb + 8 * (q / 4) + (q % 4);
+#pragma unroll
+            for (int j = 0; j < NB / 2; ++j) {
+              float g = __builtin_amdgcn_fmed3f(acc_to_f32(acc[i][2 * j][q]), -a.clamp, a.clamp);
+              float u = __builtin_amdgcn_fmed3f(acc_to_f32(acc[i][2 * j + 1][q]), -a.clamp, a.clamp);
+              const float v = silu(g) * u;
+              float m = fabsf(v);
+#pragma unroll
+              for (int o = 16; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+              const int x = mx_shared_exp_e4m3(m);
+              const uint32_t code = f32x2_to_e4m3x2(v * mx_inv_scale(x), 0.0f) & 0xffu;
+              if (r < cur.valid) {
+                gp(obase)[lane_off + (8 * (q / 4) + (q % 4)) * a.I + j * 32] = (uint8_t)code;
+                if (lr == 0) gp(sbase)[lane_soff + (8 * (q / 4) + (q % 4)) * gpr + j] = (uint8_t)(x + 127);
+              }
+            }
+            // one row at a time: interleaving the rows' cross-lane maxima would
+            // keep all of them live at once
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        } else if constexpr (MODE == 0) {
           // tile bases are uniform; per-element offsets stay 32-bit (BM*I < 2^31)
           uint16_t* const obase = static_cast<uint16_t*>(a.a_out) + (int64_t)cur.row0 * a.I + cur.n0 / 2;
           float* const sbase = a.a_stage + (int64_t)cur.row0 * a.I + cur.n0 / 2;
@@ -824,8 +1101,9 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
               const uint64_t off = (uint64_t)(uint32_t)route * (uint32_t)a.H + (uint32_t)ncol;
 #pragma unroll
               for (int j = 0; j < NB; ++j) {
-                const float v = acc_to_f32(acc[i][j][q]) * cs0[j];
-                const float o = (UC != UC_BF16) ? (v * rs) * gw : v * gw;
+                // MX: the MFMA applied the block scales; else the per-column one
+                const float v = MX ? acc_to_f32(acc[i][j][q]) : acc_to_f32(acc[i][j][q]) * cs0[j];
+                const float o = (UC != UC_BF16 && !MX) ? (v * rs) * gw : v * gw;
                 if constexpr (UC == UC_BF16) gp(static_cast<float*>(a.contrib))[off + j * 32] = o;
                 else gp(static_cast<uint16_t*>(a.contrib))[off + j * 32] = f32_to_bf16_bits(o);
               }

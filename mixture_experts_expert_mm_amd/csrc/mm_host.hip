@@ -19,7 +19,11 @@ constexpr int64_t kAlign = 256;
 
 inline int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 
-int elem_size(int usecase) { return usecase == MM_A16W16 ? 2 : 1; }
+int elem_size(int usecase) { return usecase == MM_A16W16 ? 2 : 1; }   // activation bytes
+bool mx_usecase(int usecase) { return usecase == MM_MXFP8 || usecase == MM_MXFP4; }
+bool a8w8_usecase(int usecase) { return usecase == MM_A8W8_FP8 || usecase == MM_A8W8_INT8; }
+// weight bytes of n elements (e2m1: two per byte)
+int64_t weight_bytes(int usecase, int64_t n) { return usecase == MM_MXFP4 ? n / 2 : n * elem_size(usecase); }
 
 // experts with weights (routed + shared) and slots per token (top-k + shared)
 int64_t all_experts(const mm_problem& p) { return p.num_experts + p.num_shared_experts; }
@@ -62,7 +66,9 @@ WsLayout ws_layout(const mm_plan& pl) {
   auto take = [&](int64_t bytes) { const int64_t at = o; o = align_up(o + bytes, kAlign); return at; };
   L.ctl = take(kCtlWords * 4);
   L.wave_base = take(dispatch_waves(p.num_tokens, (int)slots_per_token(p)) * Et * 4);
-  L.a_stage = q ? take(P * p.intermediate_hidden * 4) : -1;
+  // float32 SwiGLU output, the input of the A8W8 per-row requantisation (MX
+  // quantises it in the Linear1 epilogue)
+  L.a_stage = a8w8_usecase(p.usecase) ? take(P * p.intermediate_hidden * 4) : -1;
   L.contrib = take(R * p.hidden * (q ? 2 : 4));   // combine slots: bf16 for A8W8, float32 for A16W16
   // partial sums of split tail tiles: one slot per piece in flight
   L.partials = plan_max_split(pl) > 1 ? take((int64_t)kSplitSlots * tile_bm(pl.tile_l1) * tile_bn(pl.tile_l1) * 4) : -1;
@@ -75,12 +81,12 @@ WsLayout ws_layout(const mm_plan& pl) {
   // pool rows only when the fused Linear1 cannot read the token rows in place
   const bool tok = plan_by_token(pl);
   L.x_pool = tok ? -1 : take(pl.x_pool_bytes);
-  L.x_pool_scale = tok ? -1 : take(P * 4);
+  L.x_pool_scale = tok || !q ? -1 : take(pl.x_pool_scale_bytes);
   L.a_pool = take(pl.a_pool_bytes);
-  L.a_pool_scale = take(P * 4);
-  // A8W8 codes and scales of the T tokens (the fused kernel's Linear1 reads token rows in place)
+  L.a_pool_scale = q ? take(pl.a_pool_scale_bytes) : -1;
+  // A8W8 / MX codes and scales of the T tokens (the fused kernel's Linear1 reads token rows in place)
   L.x_tok = q && tok ? take(p.num_tokens * p.hidden) : -1;
-  L.x_tok_scale = q && tok ? take(p.num_tokens * 4) : -1;
+  L.x_tok_scale = q && tok ? take(mx_usecase(p.usecase) ? p.num_tokens * (p.hidden / 32) : p.num_tokens * 4) : -1;
   L.fused_end = o;
   return L;
 }
@@ -162,7 +168,7 @@ mm_status check_plan(const mm_plan* pl) {
 // Argument blocks of each step; the three-call path launches them as
 // separate kernels, mega_moe hands all of them to the fused kernel.
 DispatchArgs dispatch_args(const mm_plan& pl, const int32_t* ids, const int8_t* active, const void* x, int32_t* counts,
-                           int32_t* offsets, int32_t* pool_src, int32_t* r2p, void* x_pool, float* x_pool_scale,
+                           int32_t* offsets, int32_t* pool_src, int32_t* r2p, void* x_pool, void* x_pool_scale,
                            void* ws) {
   const mm_problem& p = pl.prob;
   const WsLayout L = ws_layout(pl);
@@ -175,7 +181,9 @@ DispatchArgs dispatch_args(const mm_plan& pl, const int32_t* ids, const int8_t* 
   d.pool_src = pool_src;
   d.route_to_pool = r2p;
   d.x_pool = x_pool;
-  d.x_pool_scale = x_pool_scale;
+  const bool mx = mx_usecase(p.usecase);
+  d.x_pool_scale = mx ? nullptr : static_cast<float*>(x_pool_scale);
+  d.x_pool_mx = mx ? static_cast<uint8_t*>(x_pool_scale) : nullptr;
   d.wave_base = at<int32_t>(ws, L.wave_base);
   d.err = at<uint32_t>(ws, L.ctl) + 1;
   d.T = p.num_tokens;
@@ -223,16 +231,22 @@ int choose_max_split(const mm_problem& p) {
 }
 
 // e4m3 Linear1 on exact bf16 MFMA (true) or on the e4m3 MFMA (false).  The
-// e4m3 MFMA rounds inside its dot products (~5e-5 of the result's RMS); the
-// row requantisation after SwiGLU can turn that into A code changes, whose
-// effect on a Y element shrinks like 1/sqrt(I): measured max|dY|/rms 8e-3 at
-// I = 2048, but 7e-2 at I = 256, above the 5e-2 bar.  So the e4m3 MFMA for
-// I >= 1024, exact below; MM_FP8_L1=exact|fast overrides (tests, tuning).
+// e4m3 MFMAs round inside their dot products (about 4e-5 of the result's
+// RMS, with unit or any block scales, measured against the exact sum); the
+// requantisation of the SwiGLU output after Linear1 turns that into code
+// changes (0.1-0.2 % of the codes), whose effect on a Y element shrinks like
+// 1/sqrt(I): per-row fp8 measured max|dY|/rms 8e-3 at I = 2048 but 7e-2 at
+// I = 256, MX 5-17e-2 even at I = 2048 (its per-group scales leave each
+// group's largest values in the top binade, where a code step is largest).
+// So: per-row fp8 on the e4m3 MFMA for I >= 1024, exact below; MX always
+// exact (the MX Linear2 keeps the scaled MX MFMA: nothing is quantised after
+// it).  MM_FP8_L1=exact|fast overrides both (tests, tuning).
 bool fp8_l1_exact(const mm_plan& pl) {
   if (const char* v = std::getenv("MM_FP8_L1")) {
     if (std::strcmp(v, "exact") == 0) return true;
     if (std::strcmp(v, "fast") == 0) return false;
   }
+  if (mx_usecase(pl.prob.usecase)) return true;
   return pl.prob.intermediate_hidden < 1024;
 }
 
@@ -254,7 +268,8 @@ void set_split(GemmArgs& g, const mm_plan& pl, const WsLayout& L, void* ws) {
 }
 
 GemmArgs l1_args(const mm_plan& pl, const int32_t* offsets, const int32_t* counts, const void* x_pool,
-                 const float* x_pool_scale, const void* w1, const float* w1_scale, void* a_pool, void* ws) {
+                 const void* x_pool_scale, const void* w1, const void* w1_scale, void* a_pool, void* a_pool_scale,
+                 void* ws) {
   const mm_problem& p = pl.prob;
   const WsLayout L = ws_layout(pl);
   GemmArgs g{};
@@ -274,8 +289,15 @@ GemmArgs l1_args(const mm_plan& pl, const int32_t* offsets, const int32_t* count
   g.clamp = p.clamp_activation ? p.activation_clamp : INFINITY;
   g.routes = p.num_tokens * slots_per_token(p);
   g.err = at<uint32_t>(ws, L.ctl) + 1;
-  g.x_scale = x_pool_scale;
-  g.w_scale = w1_scale;
+  if (mx_usecase(p.usecase)) {
+    g.a_mx = static_cast<const uint8_t*>(x_pool_scale);
+    g.a_mx_rows = pl.pool_rows;
+    g.b_mx = static_cast<const uint8_t*>(w1_scale);
+    g.out_mx = static_cast<uint8_t*>(a_pool_scale);
+  } else {
+    g.x_scale = static_cast<const float*>(x_pool_scale);
+    g.w_scale = static_cast<const float*>(w1_scale);
+  }
   g.a_out = a_pool;
   g.a_stage = at<float>(ws, L.a_stage);
   set_split(g, pl, L, ws);
@@ -285,14 +307,14 @@ GemmArgs l1_args(const mm_plan& pl, const int32_t* offsets, const int32_t* count
   return g;
 }
 
-RequantArgs requant_args(const mm_plan& pl, const GemmArgs& l1, void* a_pool, float* a_pool_scale) {
+RequantArgs requant_args(const mm_plan& pl, const GemmArgs& l1, void* a_pool, void* a_pool_scale) {
   RequantArgs r{};
   r.a_stage = l1.a_stage;
   r.offsets = l1.offsets;
   r.counts = l1.counts;
   r.E = l1.E;
   r.a_pool = a_pool;
-  r.a_scale = a_pool_scale;
+  r.a_scale = static_cast<float*>(a_pool_scale);
   r.P = pl.pool_rows;
   r.I = l1.I;
   r.usecase = pl.prob.usecase;
@@ -300,7 +322,7 @@ RequantArgs requant_args(const mm_plan& pl, const GemmArgs& l1, void* a_pool, fl
 }
 
 GemmArgs l2_args(const mm_plan& pl, const int32_t* offsets, const int32_t* counts, const int32_t* pool_src,
-                 const void* a_pool, const float* a_pool_scale, const void* w2, const float* w2_scale,
+                 const void* a_pool, const void* a_pool_scale, const void* w2, const void* w2_scale,
                  const float* topk_w, void* ws) {
   const mm_problem& p = pl.prob;
   const WsLayout L = ws_layout(pl);
@@ -320,8 +342,14 @@ GemmArgs l2_args(const mm_plan& pl, const int32_t* offsets, const int32_t* count
   g.Kr = (int)p.num_topk;
   g.routes = p.num_tokens * slots_per_token(p);
   g.err = at<uint32_t>(ws, L.ctl) + 1;
-  g.a_scale = a_pool_scale;
-  g.w_scale = w2_scale;
+  if (mx_usecase(p.usecase)) {
+    g.a_mx = static_cast<const uint8_t*>(a_pool_scale);
+    g.a_mx_rows = pl.pool_rows;
+    g.b_mx = static_cast<const uint8_t*>(w2_scale);
+  } else {
+    g.a_scale = static_cast<const float*>(a_pool_scale);
+    g.w_scale = static_cast<const float*>(w2_scale);
+  }
   g.topk_w = topk_w;
   g.contrib = at<uint8_t>(ws, L.contrib);
   set_split(g, pl, L, ws);
@@ -344,7 +372,7 @@ CombineArgs combine_args(const mm_plan& pl, const void* contrib, const int32_t* 
 }
 
 mm_status do_dispatch(const mm_plan& pl, const int32_t* ids, const int8_t* active, const void* x, int32_t* counts,
-                      int32_t* offsets, int32_t* pool_src, int32_t* r2p, void* x_pool, float* x_pool_scale, void* ws,
+                      int32_t* offsets, int32_t* pool_src, int32_t* r2p, void* x_pool, void* x_pool_scale, void* ws,
                       hipStream_t s) {
   const DispatchArgs d = dispatch_args(pl, ids, active, x, counts, offsets, pool_src, r2p, x_pool, x_pool_scale, ws);
   uint32_t* ctl = at<uint32_t>(ws, ws_layout(pl).ctl);
@@ -365,14 +393,14 @@ mm_status clear_split_flags(const GemmArgs& g, hipStream_t s) {
 }
 
 mm_status do_l1(const mm_plan& pl, const int32_t* offsets, const int32_t* counts, const void* x_pool,
-                const float* x_pool_scale, const void* w1, const float* w1_scale, void* a_pool, float* a_pool_scale,
+                const void* x_pool_scale, const void* w1, const void* w1_scale, void* a_pool, void* a_pool_scale,
                 void* ws, hipStream_t s) {
   const mm_problem& p = pl.prob;
-  const GemmArgs g = l1_args(pl, offsets, counts, x_pool, x_pool_scale, w1, w1_scale, a_pool, ws);
+  const GemmArgs g = l1_args(pl, offsets, counts, x_pool, x_pool_scale, w1, w1_scale, a_pool, a_pool_scale, ws);
   const int grid = gemm_grid(pl.tile_l1, pl.pool_rows, g.N, num_cus());
   MM_TRY(clear_split_flags(g, s));
   MM_TRY(run(MM_K_L1, s, [&] { return launch_gemm(0, p.usecase, pl.tile_l1, fp8_l1_exact(pl), g, grid, s); }));
-  if (p.usecase != MM_A16W16) {
+  if (a8w8_usecase(p.usecase)) {
     const RequantArgs r = requant_args(pl, g, a_pool, a_pool_scale);
     MM_TRY(run(MM_K_REQUANT, s, [&] { return launch_requant(r, s); }));
   }
@@ -380,8 +408,8 @@ mm_status do_l1(const mm_plan& pl, const int32_t* offsets, const int32_t* counts
 }
 
 mm_status do_l2(const mm_plan& pl, const int32_t* offsets, const int32_t* counts, const int32_t* pool_src,
-                const int32_t* r2p, const void* a_pool, const float* a_pool_scale, const void* w2,
-                const float* w2_scale, const float* topk_w, void* y, void* ws, hipStream_t s) {
+                const int32_t* r2p, const void* a_pool, const void* a_pool_scale, const void* w2,
+                const void* w2_scale, const float* topk_w, void* y, void* ws, hipStream_t s) {
   const mm_problem& p = pl.prob;
   const GemmArgs g = l2_args(pl, offsets, counts, pool_src, a_pool, a_pool_scale, w2, w2_scale, topk_w, ws);
   const int grid = gemm_grid(pl.tile_l2, pl.pool_rows, g.N, num_cus());
@@ -428,7 +456,7 @@ extern "C" {
 mm_status mm_plan_create(const mm_problem* problem, mm_plan* plan) {
   if (!problem || !plan) return MM_ERR_INVALID_ARG;
   const mm_problem p = *problem;
-  if (p.usecase < MM_A16W16 || p.usecase > MM_A8W8_INT8) return MM_ERR_UNSUPPORTED;
+  if (p.usecase < MM_A16W16 || p.usecase > MM_MXFP4) return MM_ERR_UNSUPPORTED;
   if (p.y_dtype != MM_OUT_BF16 && p.y_dtype != MM_OUT_F32) return MM_ERR_UNSUPPORTED;
   if (p.clamp_activation != 0 && p.clamp_activation != 1) return MM_ERR_INVALID_ARG;
   if (p.clamp_activation && !(p.activation_clamp >= 0.0f)) return MM_ERR_INVALID_ARG;   // negative or NaN
@@ -439,7 +467,7 @@ mm_status mm_plan_create(const mm_problem* problem, mm_plan* plan) {
   if (p.num_experts < 1 || p.num_experts > 1024) return MM_ERR_INVALID_ARG;
   if (p.num_topk < 1 || p.num_topk > 64 || p.num_topk > p.num_experts) return MM_ERR_INVALID_ARG;
   if (p.num_shared_experts < 0 || p.num_shared_experts > 1 || p.reserved0 != 0) return MM_ERR_INVALID_ARG;
-  if (slots_per_token(p) > 64 || all_experts(p) > 1024) return MM_ERR_INVALID_ARG;
+  if (slots_per_token(p) > 64 || all_experts(p) > (mx_usecase(p.usecase) ? 512 : 1024)) return MM_ERR_INVALID_ARG;
   const int64_t R = p.num_tokens * slots_per_token(p);
   if (R > (int64_t)1 << 30) return MM_ERR_INVALID_ARG;
 
@@ -469,8 +497,10 @@ mm_status mm_plan_create(const mm_problem* problem, mm_plan* plan) {
   const int es = elem_size(p.usecase);
   pl.x_pool_bytes = P * p.hidden * es;
   pl.a_pool_bytes = P * p.intermediate_hidden * es;
-  pl.w1_bytes = all_experts(p) * p.hidden * 2 * p.intermediate_hidden * es;
-  pl.w2_bytes = all_experts(p) * p.intermediate_hidden * p.hidden * es;
+  pl.x_pool_scale_bytes = mx_usecase(p.usecase) ? P * (p.hidden / 32) : a8w8_usecase(p.usecase) ? P * 4 : 0;
+  pl.a_pool_scale_bytes = mx_usecase(p.usecase) ? P * (p.intermediate_hidden / 32) : a8w8_usecase(p.usecase) ? P * 4 : 0;
+  pl.w1_bytes = weight_bytes(p.usecase, all_experts(p) * p.hidden * 2 * p.intermediate_hidden);
+  pl.w2_bytes = weight_bytes(p.usecase, all_experts(p) * p.intermediate_hidden * p.hidden);
   const WsLayout L = ws_layout(pl);
   pl.workspace_bytes = L.end;
   pl.fused_workspace_bytes = L.fused_end;
@@ -487,13 +517,13 @@ mm_status mm_prepare_weights(const mm_plan* plan, const void* w1, const void* w2
   hipStream_t s = static_cast<hipStream_t>(stream);
   return run(MM_K_PREPARE, s, [&] {
     return launch_prepare(w1, w2, w1_out, w2_out, (int)all_experts(p), (int)p.hidden, (int)p.intermediate_hidden,
-                          elem_size(p.usecase), plan->gate_up_group, s);
+                          p.usecase == MM_MXFP4 ? 0 : elem_size(p.usecase), plan->gate_up_group, s);
   });
 }
 
 mm_status mm_dispatch_layout(const mm_plan* plan, const int32_t* topk_ids, const int8_t* x_active_mask, const void* x,
                              int32_t* expert_counts, int32_t* expert_offsets, int32_t* pool_src, int32_t* route_to_pool,
-                             void* x_pool, float* x_pool_scale, void* workspace, uint64_t workspace_bytes,
+                             void* x_pool, void* x_pool_scale, void* workspace, uint64_t workspace_bytes,
                              void* stream) {
   MM_TRY(check_plan(plan));
   const bool q = plan->prob.usecase != MM_A16W16;
@@ -507,8 +537,8 @@ mm_status mm_dispatch_layout(const mm_plan* plan, const int32_t* topk_ids, const
 }
 
 mm_status mm_grouped_l1_swiglu(const mm_plan* plan, const int32_t* expert_offsets, const int32_t* expert_counts,
-                               const void* x_pool, const float* x_pool_scale, const void* w1, const float* w1_scale,
-                               void* a_pool, float* a_pool_scale, void* workspace, uint64_t workspace_bytes,
+                               const void* x_pool, const void* x_pool_scale, const void* w1, const void* w1_scale,
+                               void* a_pool, void* a_pool_scale, void* workspace, uint64_t workspace_bytes,
                                void* stream) {
   MM_TRY(check_plan(plan));
   const bool q = plan->prob.usecase != MM_A16W16;
@@ -523,7 +553,7 @@ mm_status mm_grouped_l1_swiglu(const mm_plan* plan, const int32_t* expert_offset
 
 mm_status mm_grouped_l2_combine(const mm_plan* plan, const int32_t* expert_offsets, const int32_t* expert_counts,
                                 const int32_t* pool_src, const int32_t* route_to_pool, const void* a_pool,
-                                const float* a_pool_scale, const void* w2, const float* w2_scale,
+                                const void* a_pool_scale, const void* w2, const void* w2_scale,
                                 const float* topk_weights, void* y, void* workspace, uint64_t workspace_bytes,
                                 void* stream) {
   MM_TRY(check_plan(plan));
@@ -538,8 +568,8 @@ mm_status mm_grouped_l2_combine(const mm_plan* plan, const int32_t* expert_offse
 }
 
 mm_status mega_moe(const mm_plan* plan, const void* x, const int32_t* topk_ids, const float* topk_weights,
-                   const int8_t* x_active_mask, const void* w1, const float* w1_scale, const void* w2,
-                   const float* w2_scale, void* y, int32_t* expert_token_nums, void* workspace,
+                   const int8_t* x_active_mask, const void* w1, const void* w1_scale, const void* w2,
+                   const void* w2_scale, void* y, int32_t* expert_token_nums, void* workspace,
                    uint64_t workspace_bytes, void* stream) {
   MM_TRY(check_plan(plan));
   const bool q = plan->prob.usecase != MM_A16W16;
@@ -555,13 +585,13 @@ mm_status mega_moe(const mm_plan* plan, const void* x, const int32_t* topk_ids, 
   int32_t* pool_src = at<int32_t>(workspace, L.pool_src);
   int32_t* r2p = at<int32_t>(workspace, L.route_to_pool);
   void* x_pool = at<uint8_t>(workspace, L.x_pool);
-  float* xs = q ? at<float>(workspace, L.x_pool_scale) : nullptr;
+  void* xs = q ? at<uint8_t>(workspace, L.x_pool_scale) : nullptr;
   void* a_pool = at<uint8_t>(workspace, L.a_pool);
-  float* as = q ? at<float>(workspace, L.a_pool_scale) : nullptr;
+  void* as = q ? at<uint8_t>(workspace, L.a_pool_scale) : nullptr;
   const mm_plan& pl = *plan;
   MegaArgs m{};
   m.d = dispatch_args(pl, topk_ids, x_active_mask, x, counts, offsets, pool_src, r2p, x_pool, xs, workspace);
-  m.l1 = l1_args(pl, offsets, counts, x_pool, xs, w1, w1_scale, a_pool, workspace);
+  m.l1 = l1_args(pl, offsets, counts, x_pool, xs, w1, w1_scale, a_pool, as, workspace);
   m.rq = requant_args(pl, m.l1, a_pool, as);
   m.l2 = l2_args(pl, offsets, counts, pool_src, a_pool, as, w2, w2_scale, topk_weights, workspace);
   m.counts_out = expert_token_nums;
@@ -573,9 +603,14 @@ mm_status mega_moe(const mm_plan* plan, const void* x, const int32_t* topk_ids, 
   if (plan_by_token(pl)) {
     m.l1_by_token = 1;
     m.x_tok = q ? at<uint8_t>(workspace, L.x_tok) : nullptr;
-    m.x_tok_scale = q ? at<float>(workspace, L.x_tok_scale) : nullptr;
+    m.x_tok_scale = q ? at<uint8_t>(workspace, L.x_tok_scale) : nullptr;
     m.l1.A = static_cast<const uint8_t*>(q ? m.x_tok : x);
-    m.l1.x_scale = m.x_tok_scale;
+    if (mx_usecase(pl.prob.usecase)) {
+      m.l1.a_mx = static_cast<const uint8_t*>(m.x_tok_scale);
+      m.l1.a_mx_rows = pl.prob.num_tokens;
+    } else {
+      m.l1.x_scale = static_cast<const float*>(m.x_tok_scale);
+    }
     m.l1.a_route = pool_src;
     m.l1.a_rows = pl.prob.num_tokens;
     m.l1.group_m = 0;   // token rows are shared K-fold and stay cached: weight reuse order (measured)
@@ -590,8 +625,8 @@ mm_status mega_moe(const mm_plan* plan, const void* x, const int32_t* topk_ids, 
 }
 
 mm_status mega_moe_noalloc(const mm_plan* plan, const void* x, const int32_t* topk_ids, const float* topk_weights,
-                           const int8_t* x_active_mask, const void* w1, const float* w1_scale, const void* w2,
-                           const float* w2_scale, void* y, int32_t* expert_token_nums, void* stream) {
+                           const int8_t* x_active_mask, const void* w1, const void* w1_scale, const void* w2,
+                           const void* w2_scale, void* y, int32_t* expert_token_nums, void* stream) {
   MM_TRY(check_plan(plan));
   if (plan->fused_workspace_bytes > kScratchBytes) return MM_ERR_WORKSPACE;
   void* ws = nullptr;

@@ -29,6 +29,7 @@ struct DispatchArgs {
   int32_t* route_to_pool;    // [T*K]
   void* x_pool;              // [P][H]
   float* x_pool_scale;       // [P] (A8W8)
+  uint8_t* x_pool_mx;        // [P][H/32] E8M0 (MX use cases)
   int32_t* wave_base;        // ws: [waves][E]
   uint32_t* err;             // ws: device error word (mm_device_error bits)
   int64_t T, H, P;
@@ -69,6 +70,13 @@ struct GemmArgs {
   void* contrib;             // [T*K][H] float32 (A16W16) or bf16 (A8W8)
   // debug (mode 2: raw int32 accumulators)
   int32_t* raw_out;
+  // MX use cases: E8M0 scales of the A rows [rows][Kdim/32] (a_mx_rows rows),
+  // of the prepared B rows (formula order, [E][N][Kdim/32]); Linear1 writes
+  // A's codes to a_out and their E8M0 scales to out_mx [P][I/32]
+  const uint8_t* a_mx;
+  int64_t a_mx_rows;
+  const uint8_t* b_mx;
+  uint8_t* out_mx;
   // Linear1 of the fused kernel: A row p of a tile is the token row
   // a_route[p] / K of A (a_rows token rows) instead of pool row p
   const int32_t* a_route;    // [P] route i*K+k of pool row p (-1: padding), or null
@@ -121,8 +129,8 @@ struct MegaArgs {
   int64_t nwaves;            // dispatch waves
   // Linear1 reads the token rows in place (l1.a_route set): A8W8 codes and
   // scales of the T tokens are made here, no pool rows are gathered
-  void* x_tok;               // [T][H] codes (A8W8)
-  float* x_tok_scale;        // [T] (A8W8)
+  void* x_tok;               // [T][H] codes (A8W8, MX)
+  void* x_tok_scale;         // float [T] (A8W8) or E8M0 [T][H/32] (MX)
   int l1_by_token;
   uint32_t spin_limit;       // polls before a grid barrier gives up
   // the routed experts' counts for the caller (expert_token_nums [Er]);
@@ -139,6 +147,7 @@ int mega_grid(int tile, int num_cus);
 hipError_t launch_count(const DispatchArgs& a, hipStream_t s);
 hipError_t launch_scatter(const DispatchArgs& a, hipStream_t s);
 hipError_t launch_gather(const DispatchArgs& a, hipStream_t s);
+// esz: bytes per weight (2, 1), or 0 for e2m1 (two per byte)
 hipError_t launch_prepare(const void* w1, const void* w2, void* w1o, void* w2o, int E, int H, int I,
                           int esz, int group, hipStream_t s);
 // exact_l1: e4m3 Linear1 on bf16 MFMA with exact widening (else on the e4m3 MFMA)

@@ -86,9 +86,9 @@ __device__ __forceinline__ bool grid_barrier(uint32_t* ctl, uint32_t n, uint32_t
   return *ok_lds != 0;
 }
 
-template <int BM>
+template <int UC, int BM>
 constexpr int mega_lds_bytes() {
-  return lds_bytes_of<BM>();
+  return lds_bytes_of<UC, BM>();
 }
 
 template <int UC, int BM, bool WIDEN>
@@ -101,13 +101,14 @@ void k_mega(const MegaArgs* mp) {
   const MegaArgs& m = *mp;
   constexpr int NT = threads_of<BM>(), NW = NT / 64;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  __shared__ int32_t off_s[kMaxExperts + 1];
-  __shared__ int32_t cnt_s[kMaxExperts];
+  constexpr int MAXE = max_experts<UC>();
+  __shared__ int32_t off_s[MAXE + 1];
+  __shared__ int32_t cnt_s[MAXE];
   __shared__ int32_t wsum[NW];
   __shared__ int32_t dst[64];
   __shared__ float red[NW];
   __shared__ int32_t ok;
-  static_assert((kMaxExperts + 1 + (int64_t)NW * kMaxExperts) * 4 <= mega_lds_bytes<BM>(), "dispatch scratch fits");
+  static_assert((MAXE + 1 + (int64_t)NW * MAXE) * 4 <= mega_lds_bytes<UC, BM>(), "dispatch scratch fits");
   int32_t* smem = reinterpret_cast<int32_t*>(lds);
   const int t = threadIdx.x;
   uint32_t* const ctl = m.ctl;
@@ -145,7 +146,8 @@ void k_mega(const MegaArgs* mp) {
     if (m.l1_by_token) {
       DispatchArgs d = m.d;
       d.x_pool = m.x_tok;
-      d.x_pool_scale = m.x_tok_scale;
+      if constexpr (is_mx(UC)) d.x_pool_mx = static_cast<uint8_t*>(m.x_tok_scale);
+      else d.x_pool_scale = static_cast<float*>(m.x_tok_scale);
       // token i to wave i / G of block i % G: a short batch spreads over all CUs
       const int64_t nwv = (int64_t)gridDim.x * NW;
       for (int64_t tok = (int64_t)(t / 64) * gridDim.x + blockIdx.x; tok < d.T; tok += nwv) quant_token_wave<UC>(d, tok);
@@ -181,9 +183,9 @@ void k_mega(const MegaArgs* mp) {
   }
   if (!grid_barrier(ctl, ++nb, spin, bs, &ok)) return;
 
-  if constexpr (UC != UC_BF16) {
+  if constexpr (UC == UC_FP8 || UC == UC_I8) {
     // per-row requantisation of A, one wave per pool row (two rows at a time
-    // when I <= 2048)
+    // when I <= 2048); MX quantised A in the Linear1 epilogue
     const RequantArgs r = m.rq;
     const int64_t used = off_s[r.E], nwv = (int64_t)gridDim.x * NW;
     const int64_t p0 = (int64_t)blockIdx.x * NW + t / 64;
@@ -240,7 +242,7 @@ __global__ __launch_bounds__(256) void k_mega_prep(MegaArgs m, MegaArgs* out) {
 // delays the late workgroups, which the barriers wait for (bounded).
 template <int UC, int BM, bool WIDEN>
 static hipError_t launch_mega_one(const MegaArgs* dev_args, int grid, hipStream_t s) {
-  constexpr size_t lds = (size_t)mega_lds_bytes<BM>();
+  constexpr size_t lds = (size_t)mega_lds_bytes<UC, BM>();
   static int per_cu = -1;
   if (per_cu < 0) {
     hipError_t err = hipFuncSetAttribute((const void*)k_mega<UC, BM, WIDEN>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -275,6 +277,10 @@ hipError_t launch_mega(int usecase, int tile, bool exact_l1, const MegaArgs* dev
     case UC_BF16: return launch_mega_bm<UC_BF16>(tile, dev_args, grid, s);
     case UC_FP8:
       return exact_l1 ? launch_mega_bm<UC_FP8, true>(tile, dev_args, grid, s) : launch_mega_bm<UC_FP8>(tile, dev_args, grid, s);
+    case UC_MX8:
+      return exact_l1 ? launch_mega_bm<UC_MX8, true>(tile, dev_args, grid, s) : launch_mega_bm<UC_MX8>(tile, dev_args, grid, s);
+    case UC_MX4:
+      return exact_l1 ? launch_mega_bm<UC_MX4, true>(tile, dev_args, grid, s) : launch_mega_bm<UC_MX4>(tile, dev_args, grid, s);
     default: return launch_mega_bm<UC_I8>(tile, dev_args, grid, s);
   }
 }

@@ -13,7 +13,9 @@ import torch
 
 from . import binding as B
 
-_DT = {"bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn, "int8": torch.int8}
+_DT = {"bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn, "int8": torch.int8, "mxfp8": torch.uint8,
+       "mxfp4": torch.uint8}
+MX = ("mxfp8", "mxfp4")
 
 
 @dataclasses.dataclass
@@ -44,17 +46,24 @@ class ExpertLayer:
 
     # ---------------------------------------------------------------- weights
     def load_weights(self, w1, w2, s1=None, s2=None, stream=None):
-        """Upload formula-layout weights ([E+S,H,2I], [E+S,I,H]; a shared expert last) and relayout them once."""
+        """Upload formula-layout weights ([E+S,H,2I], [E+S,I,H]; a shared expert last; e2m1 packed two per
+        byte along the last dimension) and relayout them once.  Scales: float32 per output channel (A8W8)
+        or E8M0 bytes [E+S][N][K_in/32] (MX)."""
         dt = _DT[self.usecase]
         w1d = w1.to(self.device).contiguous()
         w2d = w2.to(self.device).contiguous()
         assert w1d.dtype == dt and w2d.dtype == dt
         Et = self.Et
-        assert tuple(w1d.shape) == (Et, self.H, 2 * self.I) and tuple(w2d.shape) == (Et, self.I, self.H)
-        self.w1 = torch.empty((Et, 2 * self.I, self.H), dtype=dt, device=self.device)
-        self.w2 = torch.empty((Et, self.H, self.I), dtype=dt, device=self.device)
+        half = 2 if self.usecase == "mxfp4" else 1
+        assert tuple(w1d.shape) == (Et, self.H, 2 * self.I // half) and tuple(w2d.shape) == (Et, self.I, self.H // half)
+        self.w1 = torch.empty((Et, 2 * self.I, self.H // half), dtype=dt, device=self.device)
+        self.w2 = torch.empty((Et, self.H, self.I // half), dtype=dt, device=self.device)
         B.mm_prepare_weights(self.plan, w1d, w2d, self.w1, self.w2, stream)
-        if self.usecase != "bf16":
+        if self.usecase in MX:
+            assert tuple(s1.shape) == (Et, 2 * self.I, self.H // 32) and tuple(s2.shape) == (Et, self.H, self.I // 32)
+            self.s1 = s1.to(self.device, torch.uint8).contiguous()
+            self.s2 = s2.to(self.device, torch.uint8).contiguous()
+        elif self.usecase != "bf16":
             self.s1 = s1.to(self.device, torch.float32).contiguous()
             self.s2 = s2.to(self.device, torch.float32).contiguous()
         torch.cuda.current_stream(self.device).synchronize() if stream is None else None
@@ -81,10 +90,16 @@ class ExpertLayer:
             pool_src=torch.empty(P, **i32),
             route_to_pool=torch.empty(self.T * self.Ks, **i32),
             x_pool=torch.empty(P * self.H * es, dtype=torch.uint8, device=dev),
-            x_pool_scale=torch.empty(P, dtype=torch.float32, device=dev) if q else None,
+            x_pool_scale=self._scale_buf(self.plan.x_pool_scale_bytes) if q else None,
             a_pool=torch.empty(P * self.I * es, dtype=torch.uint8, device=dev),
-            a_pool_scale=torch.empty(P, dtype=torch.float32, device=dev) if q else None,
+            a_pool_scale=self._scale_buf(self.plan.a_pool_scale_bytes) if q else None,
         )
+
+    def _scale_buf(self, nbytes):
+        """float32 [P] (A8W8) or E8M0 bytes [P][K_in/32] (MX) of a pool."""
+        if self.usecase in MX:
+            return torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+        return torch.empty(nbytes // 4, dtype=torch.float32, device=self.device)
 
     def new_y(self):
         dt = torch.float32 if self.y_dtype in ("f32", "fp32") else torch.bfloat16

@@ -110,6 +110,12 @@ CONFIGS = {
     # as dsv3_bf16
     "dsv3_bf16_t16384": Config("dsv3_bf16_t16384", "bf16", 16384, 7168, 2048, 32, 8, 0.5, 1002),
     "dsv3_bf16_t128": Config("dsv3_bf16_t128", "bf16", 128, 7168, 2048, 32, 8, 0.5, 1002),
+    # the MX use cases (MX-FP8 weights; FP4 weights) on the same layer shape
+    # and routing, at the two token counts
+    "dsv3_mxfp8_t16384": Config("dsv3_mxfp8_t16384", "mxfp8", 16384, 7168, 2048, 32, 8, 0.5, 1005),
+    "dsv3_mxfp8_t128": Config("dsv3_mxfp8_t128", "mxfp8", 128, 7168, 2048, 32, 8, 0.5, 1005),
+    "dsv3_mxfp4_t16384": Config("dsv3_mxfp4_t16384", "mxfp4", 16384, 7168, 2048, 32, 8, 0.5, 1006),
+    "dsv3_mxfp4_t128": Config("dsv3_mxfp4_t128", "mxfp4", 128, 7168, 2048, 32, 8, 0.5, 1006),
 }
 
 

@@ -12,7 +12,7 @@ import oracle
 from mixture_experts_expert_mm_amd import moe
 from mixture_experts_expert_mm_amd import workloads as wl
 
-TOL = {"bf16": 1e-2, "fp8": 5e-2, "int8": 5e-2}
+TOL = {"bf16": 1e-2, "fp8": 5e-2, "int8": 5e-2, "mxfp8": 5e-2, "mxfp4": 5e-2}
 
 
 def log(msg):
@@ -31,6 +31,8 @@ def expert_fn(inp: wl.Inputs):
 
     def expert(e):
         w1, w2 = w.w1[e], w.w2[e]
+        if uc in wl.MX_USECASES:
+            return wl.unpack_codes(w1, inp.cfg), wl.unpack_codes(w2, inp.cfg), w.s1[e].numpy(), w.s2[e].numpy()
         if uc == "fp8":
             w1, w2 = w1.view(torch.uint8), w2.view(torch.uint8)
         elif uc == "bf16":

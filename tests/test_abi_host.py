@@ -42,9 +42,9 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_struct_sizes_match_header():
-    # mm_problem: 5 int64 + 3 int32 + float + 2 int32; mm_plan: problem + 4 int32 + 7 int64 + u64 + 8 int64
+    # mm_problem: 5 int64 + 3 int32 + float + 2 int32; mm_plan: problem + 4 int32 + 9 int64 + u64 + 8 int64
     assert ctypes.sizeof(B.MMProblem) == 64
-    assert ctypes.sizeof(B.MMPlan) == 64 + 16 + 56 + 8 + 64
+    assert ctypes.sizeof(B.MMPlan) == 64 + 16 + 72 + 8 + 64
 
 
 def test_plan_sizes_and_block_m():
@@ -116,6 +116,20 @@ def test_plan_accepts_activation_clamp():
     for c in (None, 0.0, 2.5):
         plan = B.mm_plan_create(64, 256, 128, 8, 2, "bf16", activation_clamp=c)
         assert plan.prob.clamp_activation == (0 if c is None else 1)
+
+
+def test_plan_mx_sizes():
+    _lib()
+    for uc, wdiv in (("mxfp8", 1), ("mxfp4", 2)):
+        p = B.mm_plan_create(4096, 7168, 2048, 32, 8, uc)
+        assert p.x_pool_scale_bytes == p.pool_rows * 7168 // 32
+        assert p.a_pool_scale_bytes == p.pool_rows * 2048 // 32
+        assert p.w1_bytes == 32 * 7168 * 4096 // wdiv and p.w2_bytes == 32 * 2048 * 7168 // wdiv
+    q = B.mm_plan_create(64, 256, 128, 8, 2, "int8")
+    assert q.x_pool_scale_bytes == q.pool_rows * 4 == q.a_pool_scale_bytes
+    assert B.mm_plan_create(64, 256, 128, 8, 2, "bf16").x_pool_scale_bytes == 0
+    with pytest.raises(B.MMError):                         # MX holds at most 512 experts
+        B.mm_plan_create(64, 256, 128, 600, 2, "mxfp8")
 
 
 def test_plan_rejects_unknown_usecase():

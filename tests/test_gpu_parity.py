@@ -53,7 +53,12 @@ def check_dispatch(layer: moe.ExpertLayer, inp: wl.Inputs, im, sample_rows=None)
         rows = np.random.default_rng(0).choice(rows, sample_rows, replace=False)
     tok = psrc[rows] // (c.K + c.shared)
     rows_t = torch.from_numpy(rows).cuda()
-    if c.usecase == "bf16":
+    if c.usecase in wl.MX_USECASES:
+        codes, e8 = oracle.mx_quantize(inp.x.float().numpy()[tok].astype(np.float64), "e4m3")
+        xp = im.x_pool.view(-1, c.H)[rows_t].cpu().numpy()
+        np.testing.assert_array_equal(xp, codes)
+        np.testing.assert_array_equal(im.x_pool_scale.view(-1, c.H // 32)[rows_t].cpu().numpy(), e8)
+    elif c.usecase == "bf16":
         xp = im.x_pool.view(torch.int16).view(-1, c.H)[rows_t].cpu()
         np.testing.assert_array_equal(xp.numpy(), inp.x.view(torch.int16)[torch.from_numpy(tok)].numpy())
     else:
@@ -571,6 +576,127 @@ def test_prepare_weights_layout(usecase):
 
 
 # ---------------------------------------------------------------------------
+# MX use cases (MX-FP8 weights; FP8 x FP4)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("order", ["shuffled", "sorted"])
+def test_mx_quantiser_all_bf16_patterns(order):
+    """Every finite bf16 bit pattern goes through the MX dispatch quantiser
+    (groups of 32 along hidden) once: shuffled, a pattern meets groups of any
+    spread; sorted by magnitude, every pattern sits next to its group's
+    largest.  Codes and E8M0 scales equal the oracle's bit for bit."""
+    bits = np.arange(65536, dtype=np.uint32)
+    f = (bits << 16).view(np.float32)
+    finite = bits[np.isfinite(f)]
+    rng = np.random.default_rng(6)
+    H = 256
+    n = (finite.size + H - 1) // H * H
+    pat = np.concatenate([finite, rng.choice(finite, n - finite.size)])
+    if order == "shuffled":
+        rng.shuffle(pat)
+    else:
+        pat = pat[np.argsort(np.abs((pat << 16).view(np.float32)), kind="stable")]
+    x = torch.from_numpy(pat.astype(np.uint16).view(np.int16).reshape(-1, H)).view(torch.bfloat16)
+    T = x.shape[0]
+    log(f"[mx quantiser] {order} T={T}")
+    layer = moe.ExpertLayer(T, H, 128, 1, 1, "mxfp8", "f32", "cuda")
+    im = layer.new_intermediates()
+    ids = torch.zeros((T, 1), dtype=torch.int32)
+    layer.dispatch(x.cuda(), ids.cuda(), im)
+    torch.cuda.synchronize()
+    codes, e8 = oracle.mx_quantize(x.float().numpy().astype(np.float64), "e4m3")
+    psrc = im.pool_src.cpu().numpy()[:T]
+    np.testing.assert_array_equal(im.x_pool.view(-1, H)[:T].cpu().numpy(), codes[psrc])
+    np.testing.assert_array_equal(im.x_pool_scale.view(-1, H // 32)[:T].cpu().numpy(), e8[psrc])
+
+
+MX_SHAPES = {
+    "mx_bm128": dict(T=256, H=1024, I=1024, E=8, K=4, bias=0.5),    # 128 rows per expert
+    "mx_bm64": dict(T=96, H=1024, I=512, E=16, K=2, bias=1.0),      # 12 rows per expert: BLOCK_M 64
+}
+
+
+@pytest.mark.parametrize("shape", list(MX_SHAPES))
+@pytest.mark.parametrize("usecase", ["mxfp8", "mxfp4"])
+@pytest.mark.parametrize("variant", ["plain", "masked", "shared_active"])
+def test_mx_y_parity(shape, usecase, variant):
+    """MX-FP8 and FP8 x FP4: Y within the fp8 bar against the oracle (which
+    quantises X and the SwiGLU output with Q_MX and multiplies the
+    dequantised values), fused == three-call bit for bit, run-to-run
+    identical, the dispatch metadata and the MX pool rows (codes and E8M0
+    scales) bit-exact; also with masked routes, a shared expert and inactive
+    tokens."""
+    sh = MX_SHAPES[shape]
+    cfg = wl.Config(f"{shape}_{usecase}_{variant}", usecase, sh["T"], sh["H"], sh["I"], sh["E"], sh["K"], sh["bias"],
+                    2025, masked_ratio=0.15 if variant != "plain" else 0.0,
+                    shared=int(variant == "shared_active"), inactive_ratio=0.3 if variant == "shared_active" else 0.0)
+    inp = wl.make_inputs(cfg)
+    log(f"[mx y] {cfg.name}")
+    layer = make_layer(inp, "f32")
+    x, ids, wts = device_inputs(inp)
+    act = device_active(inp)
+    y_f, c_f = layer.forward(x, ids, wts, active=act)
+    y_f = y_f.clone()
+    off, psrc, r2p = (t.cpu().numpy() for t in layer.fused_layout())
+    y_f2, _ = layer.forward(x, ids, wts, active=act)
+    y_3, im = layer.forward_3call(x, ids, wts, active=act)
+    torch.cuda.synchronize()
+    assert layer.device_error(fused=True) == 0 and layer.device_error(fused=False) == 0
+    assert torch.equal(y_f.view(torch.int32), y_f2.view(torch.int32))
+    assert torch.equal(y_f.view(torch.int32), y_3.view(torch.int32))
+    check_dispatch(layer, inp, im)
+    check_layout(inp, layer.plan.block_m, c_f.cpu().numpy(), off, psrc, r2p)
+    err = rel_err(y_f.cpu().double().numpy(), oracle_y(inp))
+    log(f"    max|dY|/rms = {err:.3e}")
+    assert err <= TOL[usecase], err
+
+
+def test_mx_swiglu_quantisation_in_the_linear1_epilogue():
+    """The three-call Linear1 writes A = Q_MX(SwiGLU(H)) per row: its E8M0
+    scales equal the oracle's Q_MX of the SwiGLU of the exact Linear1
+    product for all but a few groups (the MFMA's float32 sums can move an
+    amax across a power of two); in the groups whose scale agrees, at least
+    99 % of the codes agree and no decoded value is more than one e4m3 step
+    (of the group's top binade) from the oracle's."""
+    cfg = wl.Config("mx_a_pool", "mxfp8", 64, 1024, 1024, 4, 2, 0.3, 77)
+    inp = wl.make_inputs(cfg)
+    layer = make_layer(inp, "f32")
+    x, ids, wts = device_inputs(inp)
+    im = layer.new_intermediates()
+    layer.dispatch(x, ids, im)
+    layer.linear1(im)
+    torch.cuda.synchronize()
+    off = im.expert_offsets.cpu().numpy()
+    cnt = im.expert_counts.cpu().numpy()
+    psrc = im.pool_src.cpu().numpy()
+    xc, xe = oracle.mx_quantize(inp.x.float().numpy().astype(np.float64), "e4m3")
+    xin = oracle.mx_dequantize(xc, xe, "e4m3")
+    a_codes = im.a_pool.view(-1, cfg.I).cpu().numpy()
+    a_e8 = im.a_pool_scale.view(-1, cfg.I // 32).cpu().numpy()
+    expert = expert_fn(inp)
+    n_groups = n_same = n_codes = n_codes_same = 0
+    for e in range(cfg.E):
+        rows = np.arange(off[e], off[e] + cnt[e])
+        if rows.size == 0:
+            continue
+        w1 = oracle.mx_dequantize(expert(e)[0].T, expert(e)[2], "e4m3").T
+        u = oracle.swiglu(xin[psrc[rows] // cfg.K] @ w1)
+        uc, ue = oracle.mx_quantize(u, "e4m3")
+        same = ue == a_e8[rows]                                          # [rows, groups]
+        n_groups += ue.size
+        n_same += int(same.sum())
+        gc = a_codes[rows].reshape(rows.size, -1, 32)[same]
+        oc = uc.reshape(rows.size, -1, 32)[same]
+        n_codes += gc.size
+        n_codes_same += int((gc == oc).sum())
+        step = np.ldexp(1.0, ue[same].astype(int) - 127 + 8 - 3)[:, None]   # e4m3 step of the top binade
+        assert np.all(np.abs(oracle.e4m3_decode(gc) - oracle.e4m3_decode(oc)) * np.ldexp(1.0, ue[same].astype(int) - 127)[:, None]
+                      <= step * (1 + 1e-9))
+    log(f"[mx a_pool] E8M0 equal on {n_same} of {n_groups} groups, codes {n_codes_same} of {n_codes}")
+    assert n_same >= 0.99 * n_groups and n_codes_same >= 0.99 * n_codes
+
+
+# ---------------------------------------------------------------------------
 # full-size configurations, in the launch configuration the benchmark times
 # ---------------------------------------------------------------------------
 
@@ -593,7 +719,7 @@ def _tokens_covering_every_m_block(inp, offs, psrc, block_m, extra, seed=11):
 
 
 FULL = ["tiny_bf16", "mid_bf16", "dsv3_bf16", "dsv3_fp8_t128", "dsv3_bf16_t128", "dsv3_fp8_t16384", "dsv3_int8",
-        "dsv3_bf16_t16384"]
+        "dsv3_bf16_t16384", "dsv3_mxfp8_t128", "dsv3_mxfp4_t128", "dsv3_mxfp8_t16384", "dsv3_mxfp4_t16384"]
 
 
 @pytest.mark.parametrize("name", FULL)
