@@ -338,12 +338,15 @@ typedef enum mm_device_error {
 mm_status mm_read_device_error(const mm_plan* plan, const void* workspace, int32_t* host_out, void* stream);
 
 /*
- * mm_debug_raw_accumulators -- the integer GEMM accumulators before any
- * scaling, for checking that the A8W8-INT products are exact (operator
- * page, A8W8-INT: C = Q_e . W1[e] and D = A^int8 . W2[e] in Z_32).
+ * mm_debug_raw_accumulators -- the GEMM accumulators before any scaling:
+ * for A8W8_INT8 the int32 sums, for checking that the products are exact
+ * (operator page, A8W8-INT: C = Q_e . W1[e] and D = A^int8 . W2[e] in Z_32);
+ * for A8W8_FP8 the float32 sums of the e4m3 code products, as int32 bit
+ * patterns, for measuring how far the e4m3 MFMA's sums are from the exact
+ * ones (Linear1 in the mode mega_moe uses: exact bf16 MFMA or e4m3 MFMA).
  * Runs the same mainloop, tile shape and tail-tile K split as the entry
- * points with an epilogue that stores the raw int32 accumulators
- * (A8W8_INT8 plans only).
+ * points with an epilogue that stores the raw accumulators (other use
+ * cases: MM_ERR_UNSUPPORTED).
  *   which = 1: c_out int32 [P][2I], column order of the formula (gate then up),
  *              from x_pool and the prepared w1;
  *   which = 2: c_out int32 [P][H] from a_pool and the prepared w2.

@@ -60,6 +60,7 @@ static hipError_t launch_uc(int usecase, int tile, bool exact_l1, const GemmArgs
 hipError_t launch_gemm(int mode, int usecase, int tile, bool exact_l1, const GemmArgs& a, int grid, hipStream_t s) {
   if (mode == 0) return launch_uc<0>(usecase, tile, exact_l1, a, grid, s);
   if (mode == 1) return launch_uc<1>(usecase, tile, exact_l1, a, grid, s);
+  if (usecase == UC_FP8) return exact_l1 ? launch_bm<UC_FP8, 2, true>(tile, a, grid, s) : launch_bm<UC_FP8, 2>(tile, a, grid, s);
   if (usecase != UC_I8) return hipErrorInvalidValue;
   return launch_bm<UC_I8, 2>(tile, a, grid, s);
 }

@@ -1125,7 +1125,8 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
                 const int qq = n / g2, m = n % g2;
                 col = (m < a.gate_up_group) ? qq * a.gate_up_group + m : a.I + qq * a.gate_up_group + (m - a.gate_up_group);
               }
-              if (r < cur.valid) gp(rbase)[(lane_row + 8 * (q / 4) + (q % 4)) * a.N + col] = acc[i][j][q];
+              // int32 accumulators as they are, float32 ones as their bit patterns
+              if (r < cur.valid) gp(rbase)[(lane_row + 8 * (q / 4) + (q % 4)) * a.N + col] = (int32_t)word_of(acc[i][j][q]);
             }
           }
         }

@@ -260,6 +260,16 @@ bool choose_by_token(const mm_problem& p) {
   return p.num_tokens * p.hidden * elem_size(p.usecase) < ((int64_t)1 << 31);
 }
 
+// M-blocks per tile group of Linear1 / Linear2 (0: a whole expert);
+// MM_GROUP_M1 / MM_GROUP_M2 override (tuning).
+int group_m_of(const char* env, int dflt) {
+  if (const char* v = std::getenv(env)) {
+    const int n = std::atoi(v);
+    if (n >= 0 && n <= 1024) return n;
+  }
+  return dflt;
+}
+
 void set_split(GemmArgs& g, const mm_plan& pl, const WsLayout& L, void* ws) {
   g.partials = at<uint32_t>(ws, L.partials);
   g.split_flags = at<uint32_t>(ws, L.ctl) + kSplitFlag0;
@@ -303,7 +313,7 @@ GemmArgs l1_args(const mm_plan& pl, const int32_t* offsets, const int32_t* count
   set_split(g, pl, L, ws);
   // pool rows are read once per group of N-blocks: group 8 M-blocks (with 4
   // N-blocks per XCD round) to read each activation stage a quarter as often
-  g.group_m = 8;
+  g.group_m = group_m_of("MM_GROUP_M1", 8);
   return g;
 }
 
@@ -353,7 +363,7 @@ GemmArgs l2_args(const mm_plan& pl, const int32_t* offsets, const int32_t* count
   g.topk_w = topk_w;
   g.contrib = at<uint8_t>(ws, L.contrib);
   set_split(g, pl, L, ws);
-  g.group_m = 0;   // measured: grouping slows Linear2 (its weight tiles are re-read per group)
+  g.group_m = group_m_of("MM_GROUP_M2", 0);   // measured: grouping slows Linear2 (its weight tiles are re-read per group)
   return g;
 }
 
@@ -613,7 +623,7 @@ mm_status mega_moe(const mm_plan* plan, const void* x, const int32_t* topk_ids, 
     }
     m.l1.a_route = pool_src;
     m.l1.a_rows = pl.prob.num_tokens;
-    m.l1.group_m = 0;   // token rows are shared K-fold and stay cached: weight reuse order (measured)
+    m.l1.group_m = group_m_of("MM_GROUP_M1", 0);   // token rows are shared K-fold and stay cached: weight reuse order (measured)
   }
   m.spin_limit = barrier_spin_limit();
   MegaArgs* dev_args = at<MegaArgs>(workspace, L.mega_args);
@@ -654,7 +664,7 @@ mm_status mm_debug_raw_accumulators(const mm_plan* plan, int which, const int32_
                                     int32_t* c_out, void* workspace, uint64_t workspace_bytes, void* stream) {
   MM_TRY(check_plan(plan));
   const mm_problem& p = plan->prob;
-  if (p.usecase != MM_A8W8_INT8) return MM_ERR_UNSUPPORTED;
+  if (p.usecase != MM_A8W8_INT8 && p.usecase != MM_A8W8_FP8) return MM_ERR_UNSUPPORTED;
   if ((which != 1 && which != 2) || !ok4(expert_offsets) || !ok4(expert_counts) || !ok16(act_pool) ||
       !ok16(w_prepared) || !ok4(c_out) || !ok16(workspace))
     return MM_ERR_INVALID_ARG;
@@ -687,7 +697,8 @@ mm_status mm_debug_raw_accumulators(const mm_plan* plan, int which, const int32_
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int grid = gemm_grid(tile, plan->pool_rows, g.N, num_cus());
   MM_TRY(clear_split_flags(g, s));
-  return run(which == 1 ? MM_K_L1 : MM_K_L2, s, [&] { return launch_gemm(2, p.usecase, tile, false, g, grid, s); });
+  const bool exact = which == 1 && p.usecase == MM_A8W8_FP8 && fp8_l1_exact(*plan);
+  return run(which == 1 ? MM_K_L1 : MM_K_L2, s, [&] { return launch_gemm(2, p.usecase, tile, exact, g, grid, s); });
 }
 
 mm_status mm_read_kernel_clock(const mm_plan* plan, const void* workspace, uint64_t* host_out, void* stream) {

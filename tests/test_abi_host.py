@@ -162,7 +162,7 @@ def test_entry_points_validate_before_any_hip_call():
                         1 << 40, None) == 1
     # the error word needs a host destination
     assert lib.mm_read_device_error(P, good, None, None) == 1
-    # raw accumulators exist for int8 only, and need a large enough workspace
+    # raw accumulators exist for int8 and fp8 only, and need a large enough workspace
     assert lib.mm_debug_raw_accumulators(P, 1, good, good, good, good, good, good, 1 << 40, None) == 2
     assert lib.mm_debug_raw_accumulators(ctypes.byref(q), 3, good, good, good, good, good, good, 1 << 40, None) == 1
     assert lib.mm_debug_raw_accumulators(ctypes.byref(q), 1, good, good, good, good, good, good, 16, None) == 3

@@ -765,3 +765,39 @@ def test_full_config(name):
     assert err <= TOL[cfg.usecase], err
     del layer
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("mode,bound", [("exact", 1e-6), ("fast", 2e-4)])
+def test_fp8_linear1_accumulator_deviation(mode, bound, monkeypatch):
+    """How far Linear1's float32 sums of e4m3 code products are from the
+    exact sums (numpy float64 of the same codes): the exact mode (bf16 MFMA
+    on exactly widened codes) is float32 rounding only; the e4m3 MFMA rounds
+    inside each instruction, about 4e-5 of the result's RMS (the reason MX
+    and small-I Linear1 default to the exact mode)."""
+    cfg = wl.Config(f"fp8_dev_{mode}", "fp8", 128, 1024, 512, 4, 2, 0.3, 88)
+    inp = wl.make_inputs(cfg)
+    layer = make_layer(inp, "f32")
+    x, ids, wts = device_inputs(inp)
+    im = layer.new_intermediates()
+    layer.dispatch(x, ids, im)
+    monkeypatch.setenv("MM_FP8_L1", mode)
+    P = layer.plan.pool_rows
+    c1 = torch.empty((P, 2 * cfg.I), dtype=torch.int32, device="cuda")
+    B.mm_debug_raw_accumulators(layer.plan, 1, im.expert_offsets, im.expert_counts, im.x_pool, layer.w1, c1,
+                                layer.workspace(False))
+    torch.cuda.synchronize()
+    c1 = c1.view(torch.float32).cpu().numpy().astype(np.float64)
+    offs = im.expert_offsets.cpu().numpy()
+    counts = im.expert_counts.cpu().numpy()
+    xq = oracle.e4m3_decode(im.x_pool.view(-1, cfg.H).cpu().numpy())
+    se = sr = 0.0
+    for e in range(cfg.E):
+        rows = np.arange(offs[e], offs[e] + counts[e])
+        if rows.size == 0:
+            continue
+        ref = xq[rows] @ oracle.e4m3_decode(inp.weights.w1[e].view(torch.uint8).numpy())
+        se += float(((c1[rows] - ref) ** 2).sum())
+        sr += float((ref ** 2).sum())
+    dev = np.sqrt(se / sr)
+    log(f"[fp8 accumulators] {mode}: rms(sum - exact) / rms(exact) = {dev:.3e}")
+    assert dev <= bound, dev
