@@ -13,6 +13,7 @@ typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 // UC_MX8: MX-FP8, e4m3 activations and weights with E8M0 scales per 32
 // K-values; UC_MX4: MX-FP8 activations x MX-FP4 (e2m1) weights.

@@ -31,6 +31,9 @@ template <int UC, int MODE, bool WIDEN = false>
 static hipError_t launch_bm(int tile, const GemmArgs& a, int grid, hipStream_t s) {
   switch (tile) {
     case TILE_M64_N128: return launch_one<UC, 64, MODE, WIDEN>(a, grid, s);
+    case TILE_M256_N256:
+      if constexpr (is_mx(UC)) return hipErrorInvalidValue;   // the plan keeps MX at 128
+      else return launch_one<UC, 256, MODE, WIDEN>(a, grid, s);
     default: return launch_one<UC, 128, MODE, WIDEN>(a, grid, s);
   }
 }

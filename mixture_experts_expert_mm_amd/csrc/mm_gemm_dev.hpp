@@ -38,6 +38,13 @@ constexpr int kMaxExperts = 1024;
 // slots of RB K-bytes per row), one workgroup per CU:
 //  * 128 x 256, eight waves (two per SIMD), three slots of 128 K-bytes (the
 //    LDS holds no more), for the compute regime;
+//  * 256 x 256, four waves (one per SIMD) of 128 x 128, two slots of 64 KiB,
+//    for many rows per expert: per K-stage a wave reads 256 rows for
+//    2 * 128 * 128 products (128 rows for 2 * 64 * 64 at 128 x 256), which
+//    halves the LDS reads, copies and barriers per MFMA.  Its 256
+//    accumulator registers take the whole AGPR file of the wave (one wave
+//    per SIMD has 512 registers); not for the MX use cases (eight scale
+//    rows of 64 per stage, one per wave, need eight waves);
 //  * 64 x 128, four waves (one per SIMD), for the weight-streaming regime
 //    (few rows per expert): narrow tiles make four times as many tiles out
 //    of the same weights, so the last round of tiles leaves fewer CUs idle,
@@ -47,6 +54,7 @@ constexpr int kMaxExperts = 1024;
 template <int BM> struct TileShape;
 template <> struct TileShape<64> { static constexpr int WM = 2, WN = 2, BN = 128, S = 6, RB = 128; };
 template <> struct TileShape<128> { static constexpr int WM = 2, WN = 4, BN = 256, S = 3, RB = 128; };
+template <> struct TileShape<256> { static constexpr int WM = 2, WN = 2, BN = 256, S = 2, RB = 128; };
 template <int BM> constexpr int threads_of() { return 64 * TileShape<BM>::WM * TileShape<BM>::WN; }
 // The LDS ring of a use case: A rows of RBA bytes per stage (128 K-values
 // of 1 byte, 64 of bf16), B rows of RBB bytes (64 for e2m1 weights: the same
@@ -68,9 +76,9 @@ template <int UC> constexpr int max_experts() { return is_mx(UC) ? 512 : 1024; }
 // Per-row data of a tile for its epilogue, two tiles' worth (the next tile's
 // is written while the current one is still being stored): 16 bytes a row.
 struct RowInfo {
-  int32_t route;   // Linear2: route i*K+k of the row (-1: no store)
   float gw;        // Linear2: gate weight G[i,k]
   float rs;        // s^X (Linear1, A8W8) or s^A (Linear2, A8W8) of the row
+  int32_t route;   // Linear2: route i*K+k of the row (-1: no store)
   float pad;
 };
 // LDS: the data ring, the row data, the scale ring
@@ -104,10 +112,26 @@ __device__ __forceinline__ uint32_t ds_read4(uint32_t addr) {
   asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
   return v;
 }
+template <int OFF>
+__device__ __forceinline__ u32x2 ds_read8(uint32_t addr) {
+  u32x2 v;
+  asm volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+  return v;
+}
+// LDS stores outside the compiler's view (for the same reason as the reads)
+template <int OFF>
+__device__ __forceinline__ void ds_write2(uint32_t addr, uint32_t v) {
+  asm volatile("ds_write_b16 %0, %1 offset:%2" ::"v"(addr), "v"(v), "i"(OFF) : "memory");
+}
+template <int OFF>
+__device__ __forceinline__ void ds_write4(uint32_t addr, uint32_t v) {
+  asm volatile("ds_write_b32 %0, %1 offset:%2" ::"v"(addr), "v"(v), "i"(OFF) : "memory");
+}
 template <int N>
 __device__ __forceinline__ void lgkm_wait() { asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N)); }
 __device__ __forceinline__ void tie(uint32_t& v) { asm volatile("" : "+v"(v)); }
 __device__ __forceinline__ void tie(u32x4& v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void tie(u32x2& v) { asm volatile("" : "+v"(v)); }
 // wait until at most VM of this wave's LDS-DMA loads are in flight and all its
 // LDS reads returned, then the workgroup barrier
 template <int VM>
@@ -315,7 +339,7 @@ struct TileRef {
   const uint8_t* abase;   // first A row of the tile
   const uint8_t* bbase;   // first B row (prepared weights) of the tile
   int kbase, nkl;         // K stages kbase .. kbase + nkl - 1
-  uint32_t aoa[2];        // per lane: byte offsets of its A rows' chunks (A read by token)
+  uint32_t aoa[8];        // per lane: byte offsets of its A rows' chunks (A read by token)
   uint32_t sc;            // MX: per lane, byte offset of the scale row it moves (or one past the range)
   int role;               // TileRole: whole tile, or piece 0 (adds the others' partials), or a later piece
   int slot;               // partial slot of a piece (piece 0: the later pieces use slot + 1 ..)
@@ -339,6 +363,10 @@ __device__ __forceinline__ int split_factor(int tail, int G, int nk, int max_spl
   }
   return best;
 }
+
+// Copies issued after MFMA slot g (from 0) when DT copies spread evenly over
+// `slots` MFMAs.
+constexpr int dma_after(int g, int dt, int slots) { return ((g + 1) * dt + slots - 1) / slots < dt ? ((g + 1) * dt + slots - 1) / slots : dt; }
 
 // An accumulator element as a 32-bit word and back.  The element is passed
 // by value: a bit cast applied directly to a vector element expression was
@@ -504,9 +532,9 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
   const uint32_t voff_b = (uint32_t)((RPIB * wv + l / CHB) * kbytes_b) + vchunk_b;
   // A read by token: the A buffer is the T token rows, each lane's rows come
   // from the route of their pool row (padding rows read token 0, unused)
-  const bool by_tok = a.a_route != nullptr;
+  const bool by_tok = MODE == 0 && a.a_route != nullptr;   // only Linear1 reads token rows in place
   constexpr int DA = BM / (RPI * NW);                      // A instructions per wave and stage
-  static_assert(DA <= 2, "per-lane A row offsets of at most two instructions");
+  static_assert(DA <= 8, "per-lane A row offsets of at most eight instructions");
   const int abytes = by_tok ? (int)(a.a_rows * kbytes) : BM * kbytes, bbytes = BN * kbytes_b;
   // MX scale rows: a_mx [a_mx_rows][G], b_mx [E][N][G] bytes, G = Kdim / 32
   const int gbytes = a.Kdim / kMxGroup;
@@ -536,12 +564,38 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
   // written to rowinfo[buf] when the tile's mainloop is done.  No wait for
   // row data holds back the tile's stages.
   static_assert(BM <= NT, "one row per thread");
+  // A8W8: the per-output-channel scales of the lane's columns ride along
+  // (loaded with the row data, before the tile's copies; the epilogue reads
+  // them without a wait)
+  constexpr bool COLS = UC != UC_BF16 && !MX && MODE != 2;
+  constexpr int NCS = COLS ? NB : 1;
   struct RowRegs {
     int32_t route;
     float gw, rs;
+    float cs0[NCS], cs1[NCS];
+  };
+  auto row_blank = [&]() {
+    RowRegs rr;
+    rr.route = -1;
+    rr.gw = 0.0f;
+    rr.rs = 1.0f;
+#pragma unroll
+    for (int j = 0; j < NCS; ++j) rr.cs0[j] = rr.cs1[j] = 1.0f;
+    return rr;
   };
   auto row_first = [&](const TileRef& tr) {
-    RowRegs rr{-1, 0.0f, 1.0f};
+    RowRegs rr = row_blank();
+#pragma unroll
+    for (int j = 0; j < NCS; ++j) {
+      if constexpr (MODE == 0 && COLS) {
+        if (j < NB / 2) {
+          const int col = tr.n0 / 2 + wn * (WTN / 2) + j * 32 + lr;
+          rr.cs0[j] = gp(a.w_scale)[(int64_t)tr.e * 2 * a.I + col];           // gate column
+          rr.cs1[j] = gp(a.w_scale)[(int64_t)tr.e * 2 * a.I + a.I + col];     // up column
+        }
+      }
+      if constexpr (MODE == 1 && COLS) rr.cs0[j] = gp(a.w_scale)[(int64_t)tr.e * a.H + tr.n0 + wn * WTN + j * 32 + lr];
+    }
     if (t < tr.valid) {
       const int64_t p = (int64_t)tr.row0 + t;
       if constexpr (MODE == 0 && UC != UC_BF16 && !MX) {
@@ -556,6 +610,13 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
     return rr;
   };
   auto row_second = [&](RowRegs& rr) {
+    // the tile's first stage has landed, so have the column scales (issued
+    // before it): taken here, at a wait the compiler sees as complete
+#pragma unroll
+    for (int j = 0; j < NCS; ++j) {
+      asm volatile("" : "+v"(rr.cs0[j]));
+      asm volatile("" : "+v"(rr.cs1[j]));
+    }
     if constexpr (MODE == 0 && UC != UC_BF16 && !MX) {
       if (by_tok) rr.rs = rr.route >= 0 ? gp(a.x_scale)[rr.route / a.K] : 1.0f;
     }
@@ -567,7 +628,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
     }
   };
   auto row_commit = [&](const RowRegs& rr, int buf) {
-    if (t < BM) rowinfo[buf * BM + t] = RowInfo{MODE == 1 ? rr.route : -1, rr.gw, rr.rs, 0.0f};
+    if (t < BM) rowinfo[buf * BM + t] = RowInfo{rr.gw, rr.rs, MODE == 1 ? rr.route : -1, 0.0f};
   };
   // The first S stages of tile `tr`, after its row data loads.
   // Between tiles the first stage goes out before the finished tile's
@@ -609,7 +670,10 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
   // the tile's later pieces (in piece order) and runs the epilogue.
   const int n_s = in_grid ? max(0, t_end - t_beg) : 0;
   const int full = n_s / per_x, tail = n_s - full * per_x;
-  const int sk = split_factor(tail, per_x, nk, a.max_split, (int)gridDim.x);
+  // no K split at 256 x 256 (its accumulators fill the register file; a
+  // loop that adds partial sums into them would spill them)
+  constexpr bool CAN_SPLIT = BM != 256;
+  const int sk = CAN_SPLIT ? split_factor(tail, per_x, nk, a.max_split, (int)gridDim.x) : 1;
   const int pieces = tail * sk;
   const int n_items = full + (pieces > wgx ? (pieces - wgx + per_x - 1) / per_x : 0);
   auto make_item = [&](int j) {
@@ -628,16 +692,26 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
       r.role = sk == 1 ? kRoleFull : (sub == 0 ? kRoleReduce : kRoleProduce);
       r.slot = uniform_int(xcd * 2 * per_x + p);
     }
-    r.aoa[0] = r.aoa[1] = 0;
 #pragma unroll
-    for (int x = 0; x < DA; ++x) {
-      const int row = RPI * (wv + NW * x) + l / CH;   // the lane's A row in the tile
-      if (by_tok) {
-        const int32_t route = gp(a.a_route)[(int64_t)r.row0 + row];
-        r.aoa[x] = route >= 0 ? (uint32_t)((route / a.K) * kbytes) + vchunk : kOffRange;
-      } else {
-        r.aoa[x] = row < r.valid ? voff : kOffRange;
+    for (int x = 0; x < 8; ++x) r.aoa[x] = 0;
+    if (by_tok) {
+      // every route load first, then the offsets: one round trip, and no
+      // branch between the loads (a route < 0, a padding row, reads zeros).
+      // The lane id is laundered so that the row addresses are not computed
+      // ahead of the tile loop and kept live through the mainloop.
+      int lm = l;
+      asm volatile("" : "+v"(lm));
+      int32_t route[DA];
+#pragma unroll
+      for (int x = 0; x < DA; ++x) route[x] = gp(a.a_route)[(int64_t)r.row0 + RPI * (wv + NW * x) + lm / CH];
+#pragma unroll
+      for (int x = 0; x < DA; ++x) {
+        const uint32_t tok = (uint32_t)max(route[x], 0) / (uint32_t)a.K;
+        r.aoa[x] = route[x] >= 0 ? tok * (uint32_t)kbytes + vchunk : kOffRange;
       }
+    } else {
+#pragma unroll
+      for (int x = 0; x < DA; ++x) r.aoa[x] = RPI * (wv + NW * x) + l / CH < r.valid ? voff : kOffRange;
     }
     r.sc = 0;
     if constexpr (MX) {
@@ -651,7 +725,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
         const int row = 64 * wv + l;
         if (by_tok) {
           const int32_t route = gp(a.a_route)[(int64_t)r.row0 + row];
-          r.sc = route >= 0 ? (uint32_t)((route / a.K) * gbytes) : kOffRange;
+          r.sc = route >= 0 ? ((uint32_t)max(route, 0) / (uint32_t)a.K) * (uint32_t)gbytes : kOffRange;
         } else {
           r.sc = row < r.valid ? (uint32_t)((r.row0 + row) * gbytes) : kOffRange;
         }
@@ -672,7 +746,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
   int item = 0;
   bool have = item < n_items;
   TileRef cur{};
-  RowRegs rr_cur{-1, 0.0f, 1.0f};
+  RowRegs rr_cur = row_blank();
   int buf = 0;
   if (have) {
     cur = make_item(0);
@@ -814,33 +888,61 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
     };
 
     // One K-stage kb.  Phase 0 runs on fragments read during the previous
-    // stage.  Then a barrier: stage kb+1 has landed for every wave and every
-    // wave is done reading stage kb, so stage kb's slot takes stage kb+S.
-    // Phases 1.. run with those DMA issues and the reads of stage kb+1 spread
-    // between their MFMAs: a phase's fragment registers are read again as
-    // soon as that phase's MFMAs are issued; the last phase's at the end.
-    // Scheduling barriers keep this order.
+    // stage.  In the steady state (a refilling step) a first barrier after
+    // M0 of its MFMAs: every wave is then done reading stage kb (those reads
+    // were issued during the previous step), so stage kb's slot takes stage
+    // kb+S, its copies spread evenly over all the step's later MFMAs (the
+    // copy engine sees a steady demand, and each copy has most of a step to
+    // land).  After phase 0 a barrier: stage kb+1 has landed for every wave
+    // (stage kb+S's first D0 copies may be in flight).  Phases 1.. run with
+    // the other copies and the reads of stage kb+1 spread between their
+    // MFMAs: a phase's fragment registers are read again as soon as that
+    // phase's MFMAs are issued; the last phase's at the end.  Scheduling
+    // barriers keep this order.
+    constexpr int M0 = MPP >= 8 ? MPP / 4 : 1;              // phase-0 MFMAs before the first barrier
+    constexpr int SLOTS = (MPP - M0) + (NPH - 1) * MPP;     // MFMAs the refill spreads over
+    constexpr int D0 = dma_after(MPP - M0 - 1, DT, SLOTS);  // copies issued in phase 0
     auto step = [&](int kb, auto refill_tag, auto more_tag, auto vm_tag) {
       constexpr bool REFILL = decltype(refill_tag)::value, MORE = decltype(more_tag)::value;
-      constexpr int VM = decltype(vm_tag)::value;   // this wave's loads still allowed in flight
+      constexpr int VM = decltype(vm_tag)::value;   // this wave's loads of later stages in flight
+      static_assert(!REFILL || MORE, "a refilling step has a next stage");
       lgkm_wait<P0WAIT>();
       take_scales();
       tie_phases(0, 1);
       __builtin_amdgcn_sched_barrier(0);
+      int dm = 0;
+      if constexpr (REFILL) {
 #pragma unroll
-      for (int mi = 0; mi < MPP; ++mi) mfma_at(0, mi);
-      __builtin_amdgcn_sched_barrier(0);
-      if constexpr (MORE) {
-        vm_barrier<VM>();
+        for (int mi = 0; mi < M0; ++mi) mfma_at(0, mi);
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        tie_phases(1, NPH);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int mi = M0; mi < MPP; ++mi) {
+          mfma_at(0, mi);
+          const int target = dma_after(mi - M0, DT, SLOTS);
+#pragma unroll
+          for (int x = 0; x < DT; ++x)
+            if (x >= dm && x < target) MM_DMA(cur, x, kb + S);
+          dm = target;
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        vm_barrier<VM + D0>();
       } else {
-        lgkm_wait<0>();
+#pragma unroll
+        for (int mi = 0; mi < MPP; ++mi) mfma_at(0, mi);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (MORE) {
+          vm_barrier<VM>();
+        } else {
+          lgkm_wait<0>();
+        }
+        tie_phases(1, NPH);
       }
-      tie_phases(1, NPH);
       __builtin_amdgcn_sched_barrier(0);
       const uint32_t so = (uint32_t)(((kb + 1) % S) * STAGE);
       if constexpr (MORE) read_scales((uint32_t)(((kb + 1) % S) * SSTAGE));   // ahead of stage kb+1's fragments
-      constexpr int NMR = (NPH - 1) * MPP;   // MFMAs after the barrier: DMA issues spread over them
-      int dm = 0;
 #pragma unroll
       for (int p = 1; p < NPH; ++p) {
         int rd = 0;
@@ -848,12 +950,11 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
         for (int mi = 0; mi < MPP; ++mi) {
           mfma_at(p, mi);
           if constexpr (REFILL) {
-            const int m = (p - 1) * MPP + mi;
-            const int target = ((m + 1) * DT + NMR - 1) / NMR;
+            const int target = dma_after((MPP - M0) + (p - 1) * MPP + mi, DT, SLOTS);
 #pragma unroll
             for (int x = 0; x < DT; ++x)
               if (x >= dm && x < target) MM_DMA(cur, x, kb + S);
-            dm = target < DT ? target : DT;
+            dm = target;
           }
           if constexpr (MORE) {
             const int target = ((mi + 1) * RPP + MPP - 1) / MPP;
@@ -896,39 +997,18 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
     step(nkl - 1, no, no, std::integral_constant<int, 0>{});
 
     // ------------------------------------------------ next tile, epilogue
-    // per-column scales (A8W8) of this wave's columns, loaded before the next
-    // tile's copies so that waiting for them does not wait for those
-    float cs0[NB], cs1[NB];
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      cs0[j] = 1.0f;
-      cs1[j] = 1.0f;
-      if constexpr (MODE == 0 && UC != UC_BF16 && !MX) {
-        if (j < NB / 2) {
-          const int col = cur.n0 / 2 + wn * (WTN / 2) + j * 32 + lr;
-          cs0[j] = gp(a.w_scale)[(int64_t)cur.e * 2 * a.I + col];           // gate column
-          cs1[j] = gp(a.w_scale)[(int64_t)cur.e * 2 * a.I + a.I + col];     // up column
-        }
-      }
-      if constexpr (MODE == 1 && UC != UC_BF16 && !MX)
-        cs0[j] = gp(a.w_scale)[(int64_t)cur.e * a.H + cur.n0 + wn * WTN + j * 32 + lr];
-    }
-    // the scales are in registers before the next tile's copies go out (a
-    // wait the compiler sees, so it places none later that would also wait
-    // for those copies): s_waitcnt vmcnt(0)
-    if constexpr (UC != UC_BF16 && !MX && MODE != 2) __builtin_amdgcn_s_waitcnt(0x0F70);
     // this tile's row data goes to LDS; every wave is done reading the ring
     row_commit(rr_cur, buf);
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     const int nitem = item + 1;
     const bool nhave = nitem < n_items;
     TileRef nxt{};
-    RowRegs rr_nxt{-1, 0.0f, 1.0f};
+    RowRegs rr_nxt = row_blank();
     // A K piece of a split tile: a later piece hands its partial sums to
     // piece 0 through its slot and moves on; piece 0 adds them in piece
     // order.  Both finish this exchange before the next item's stages go out
     // (the waits for the exchange would otherwise wait for those too).
-    if (cur.role != kRoleFull) {
+    if (CAN_SPLIT && cur.role != kRoleFull) {
       // Slots [slot, slot + sk) as one buffer.  Only rows below the tile's
       // valid count are exchanged: word group v of block (i, j) holds rows
       // rb0 + 32i + 8v .. + 3 of one column; a group past the valid rows gets
@@ -992,27 +1072,52 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
             __hip_atomic_store(&a.split_flags[cur.slot + q], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
-    // the next item's first stages go out now, ahead of this tile's epilogue
+    // The next item's first stage goes out now, ahead of this tile's
+    // epilogue, where the epilogue keeps its values in registers.  At
+    // 256 x 256 the accumulators fill the register file and the epilogue
+    // reloads spilled values, and each reload waits for every load in
+    // flight: there the next item's stages all go out after the epilogue.
+    constexpr bool EARLY_FIRST = BM != 256;
+    // Epilogue staging (Linear1 without MX, Linear2): one 32-row block of a
+    // wave's outputs at a time, OESZ bytes an element, rows OPITCH bytes
+    // apart (padded so that the two lane halves, 4 rows apart, write other
+    // banks), in the ring slots the next item's copies leave alone.
+    constexpr int OESZ = MODE == 1 ? (UC == UC_BF16 ? 4 : 2) : (UC == UC_BF16 ? 2 : 4);
+    constexpr int OCOLS = MODE == 1 ? WTN : WTN / 2;           // output columns of a wave
+    constexpr int OPITCH = OCOLS * OESZ + (OESZ == 4 ? 32 : 16);
+    constexpr int OREG = 32 * OPITCH;                           // one wave's staging bytes
+    constexpr int CPR = OCOLS * OESZ / 16;                      // 16-byte pieces per staged row
+    constexpr int CPL = 32 * CPR / 64;                          // pieces per lane
+    constexpr bool STAGED = MODE == 1 || (MODE == 0 && !MX);
+    static_assert(!STAGED || ((EARLY_FIRST ? STAGE : 0) + NW * OREG <= S * STAGE && 64 % CPR == 0 && CPL >= 1),
+                  "epilogue staging fits the free ring slots");
+    const uint32_t stg_base = lds_base + (uint32_t)(EARLY_FIRST ? STAGE : 0);
     if (nhave) {
       nxt = make_item(nitem);
-      rr_nxt = start_first(nxt);
+      if (EARLY_FIRST) rr_nxt = start_first(nxt);
     }
     if (cur.role != kRoleProduce) {   // a later piece has no epilogue
+      // The lane's coordinates again, from a lane id the compiler cannot
+      // trace: nothing the epilogue derives from them is computed ahead of
+      // the tile loop and kept live (or spilled) through the mainloop.
+      int le = l;
+      asm volatile("" : "+v"(le));
+      const int h = le / 32, lr = le % 32;
 #pragma unroll
       for (int i = 0; i < MB; ++i) {
         const int rb = wm * WTM + i * 32 + 4 * h;   // this lane's rows: rb + 8*(q/4) + q%4
         // row data of the 16 rows, read outside the compiler's view (it would
         // otherwise wait for the next tile's LDS copies first): Linear2 needs
         // the whole entry, A8W8 Linear1 only s^X
-        u32x4 ri[MODE == 1 ? 16 : 1];
+        u32x2 ri[MODE == 1 ? 16 : 1];   // Linear2: G[i,k] and s^A of the row
         uint32_t sxr[(MODE == 0 && UC != UC_BF16 && !MX) ? 16 : 1];
         if constexpr (MODE == 1 || (MODE == 0 && UC != UC_BF16 && !MX)) {
 #pragma unroll
           for (int q = 0; q < 16; ++q) {
             const int r = rb + 8 * (q / 4) + (q % 4);
             const uint32_t ad = rowinfo_base + (uint32_t)((buf * BM + r) * (int)sizeof(RowInfo));
-            if constexpr (MODE == 1) ri[q] = ds_read16<0>(ad);
-            else sxr[q] = ds_read4<8>(ad);
+            if constexpr (MODE == 1) ri[q] = ds_read8<0>(ad);
+            else sxr[q] = ds_read4<4>(ad);
           }
           lgkm_wait<0>();
 #pragma unroll
@@ -1054,58 +1159,89 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
             // keep all of them live at once
             __builtin_amdgcn_sched_barrier(0);
           }
-        } else if constexpr (MODE == 0) {
-          // tile bases are uniform; per-element offsets stay 32-bit (BM*I < 2^31)
-          uint16_t* const obase = static_cast<uint16_t*>(a.a_out) + (int64_t)cur.row0 * a.I + cur.n0 / 2;
-          float* const sbase = a.a_stage + (int64_t)cur.row0 * a.I + cur.n0 / 2;
-          // the lane's first row offset, laundered so that the compiler does not
-          // hoist the 16 per-row offsets out of the tile loop (they would stay
-          // live through the mainloop)
-          int lane_off = rb * a.I + wn * (WTN / 2) + lr;
-          asm volatile("" : "+v"(lane_off));
+        } else if constexpr (MODE == 0 || MODE == 1) {
+          // The wave's 32-row block i goes through LDS: each lane writes its
+          // 16 rows x NB column values (one column per lane, the MFMA
+          // layout), then reads back 16-byte pieces of rows and stores them
+          // whole (8 bf16 or 4 float32 a lane and instruction instead of one
+          // element).
+          const uint32_t wst = stg_base + (uint32_t)(wv * OREG);   // this wave's staging block
+          const uint32_t wlane = wst + (uint32_t)((4 * h) * OPITCH + lr * OESZ);
 #pragma unroll
           for (int q = 0; q < 16; ++q) {
-            const int r = rb + 8 * (q / 4) + (q % 4);
 #pragma unroll
-            for (int j = 0; j < NB / 2; ++j) {
-              const int oc = lane_off + (8 * (q / 4) + (q % 4)) * a.I + j * 32;
-              float g = acc_to_f32(acc[i][2 * j][q]);
-              float u = acc_to_f32(acc[i][2 * j + 1][q]);
-              if constexpr (UC != UC_BF16) {
-                const float sx = __uint_as_float(sxr[q]);
-                g = (g * cs0[j]) * sx;
-                u = (u * cs1[j]) * sx;
+            for (int j = 0; j < OCOLS / 32; ++j) {
+              float o;
+              if constexpr (MODE == 0) {
+                // SwiGLU of the gate column (block 2j) and its up partner (2j+1)
+                float g = acc_to_f32(acc[i][2 * j][q]);
+                float u = acc_to_f32(acc[i][2 * j + 1][q]);
+                if constexpr (UC != UC_BF16) {
+                  const float sx = __uint_as_float(sxr[q]);
+                  g = (g * rr_cur.cs0[j]) * sx;
+                  u = (u * rr_cur.cs1[j]) * sx;
+                }
+                // the operator's activation_clamp (+inf: none; identity on finite H)
+                g = __builtin_amdgcn_fmed3f(g, -a.clamp, a.clamp);
+                u = __builtin_amdgcn_fmed3f(u, -a.clamp, a.clamp);
+                o = silu(g) * u;
+              } else {
+                // contribution of route i*K+k: ((D * s^W2) * s^A) * G[i,k]
+                // (MX: the MFMA applied the block scales; A16W16: D * G)
+                const float gw = __uint_as_float(ri[q][0]);
+                const float rs = __uint_as_float(ri[q][1]);
+                float v = acc_to_f32(acc[i][j][q]);
+                if constexpr (COLS) v *= rr_cur.cs0[j];
+                o = (UC != UC_BF16 && !MX) ? (v * rs) * gw : v * gw;
               }
-              // the operator's activation_clamp (+inf: none; identity on finite H)
-              g = __builtin_amdgcn_fmed3f(g, -a.clamp, a.clamp);
-              u = __builtin_amdgcn_fmed3f(u, -a.clamp, a.clamp);
-              const float v = silu(g) * u;
-              if (r < cur.valid) {
-                if constexpr (UC == UC_BF16) gp(obase)[oc] = f32_to_bf16_bits(v);
-                else gp(sbase)[oc] = v;
-              }
+              const uint32_t ad = wlane + (uint32_t)((8 * (q / 4) + (q % 4)) * OPITCH + j * 32 * OESZ);
+              if constexpr (OESZ == 2) ds_write2<0>(ad, f32_to_bf16_bits(o));
+              else ds_write4<0>(ad, __float_as_uint(o));
             }
           }
-        } else if constexpr (MODE == 1) {
-          // contribution of route i*K+k: ((D * s^W2) * s^A) * G[i,k].  Row
-          // outer, so that a row's slot offset (one 32 x 32 -> 64-bit
-          // multiply) serves all of the lane's columns in it and one mask
-          // covers them.
-          const int ncol = cur.n0 + wn * WTN + lr;
+          lgkm_wait<0>();
+          // read back: lane le takes 16-byte piece ch of staged rows
+          // le / CPR + (64 / CPR) * k
+          const int ch = le % CPR, r0 = le / CPR;
+          u32x4 pv[CPL];
+          uint32_t prt[MODE == 1 ? CPL : 1];
 #pragma unroll
-          for (int q = 0; q < 16; ++q) {
-            const int32_t route = (int32_t)ri[q][0];
-            const float gw = __uint_as_float(ri[q][1]);
-            const float rs = __uint_as_float(ri[q][2]);
-            if (route >= 0) {
-              const uint64_t off = (uint64_t)(uint32_t)route * (uint32_t)a.H + (uint32_t)ncol;
+          for (int k = 0; k < CPL; ++k) {
+            const int row = r0 + (64 / CPR) * k;
+            pv[k] = ds_read16<0>(wst + (uint32_t)(row * OPITCH + ch * 16));
+            if constexpr (MODE == 1)
+              prt[k] = ds_read4<8>(rowinfo_base + (uint32_t)((buf * BM + wm * WTM + i * 32 + row) * (int)sizeof(RowInfo)));
+          }
+          lgkm_wait<0>();
 #pragma unroll
-              for (int j = 0; j < NB; ++j) {
-                // MX: the MFMA applied the block scales; else the per-column one
-                const float v = MX ? acc_to_f32(acc[i][j][q]) : acc_to_f32(acc[i][j][q]) * cs0[j];
-                const float o = (UC != UC_BF16 && !MX) ? (v * rs) * gw : v * gw;
-                if constexpr (UC == UC_BF16) gp(static_cast<float*>(a.contrib))[off + j * 32] = o;
-                else gp(static_cast<uint16_t*>(a.contrib))[off + j * 32] = f32_to_bf16_bits(o);
+          for (int k = 0; k < CPL; ++k) {
+            tie(pv[k]);
+            if constexpr (MODE == 1) tie(prt[k]);
+          }
+          if constexpr (MODE == 0) {
+            // the tile's rows of A as one buffer whose range ends at its last
+            // valid row: stores to rows past it are dropped without a branch
+            // (offsets stay 32-bit: BLOCK_M * I * 4 < 2^31)
+            uint8_t* const obase =
+                (UC == UC_BF16 ? static_cast<uint8_t*>(a.a_out) : reinterpret_cast<uint8_t*>(a.a_stage)) +
+                ((int64_t)cur.row0 * a.I + cur.n0 / 2) * OESZ;
+            const __amdgpu_buffer_rsrc_t ors =
+                __builtin_amdgcn_make_buffer_rsrc(obase, (short)0, cur.valid * a.I * OESZ, 0x00020000);
+#pragma unroll
+            for (int k = 0; k < CPL; ++k) {
+              const int row = wm * WTM + i * 32 + r0 + (64 / CPR) * k;
+              __builtin_amdgcn_raw_buffer_store_b128(pv[k], ors, (row * a.I + wn * (WTN / 2)) * OESZ + ch * 16, 0, 0);
+            }
+          } else {
+            // each row into its route's combine slot (rows without a route: none)
+#pragma unroll
+            for (int k = 0; k < CPL; ++k) {
+              const int32_t route = (int32_t)prt[k];
+              if (route >= 0) {
+                uint8_t* const dst = static_cast<uint8_t*>(a.contrib) +
+                                     ((uint64_t)(uint32_t)route * (uint32_t)a.H + (uint32_t)(cur.n0 + wn * WTN)) * OESZ +
+                                     ch * 16;
+                *gp(reinterpret_cast<u32x4*>(dst)) = pv[k];
               }
             }
           }
@@ -1132,7 +1268,13 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
         }
       }
     }
-    if (nhave) start_rest(nxt);
+    // every wave is done reading its staging block before the copies
+    // overwrite the slots
+    if constexpr (STAGED) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (nhave) {
+      if (!EARLY_FIRST) rr_nxt = start_first(nxt);
+      start_rest(nxt);
+    }
     item = nitem;
     have = nhave;
     cur = nxt;

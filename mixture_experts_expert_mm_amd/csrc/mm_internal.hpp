@@ -41,9 +41,10 @@ struct DispatchArgs {
 enum TileCfg : int {
   TILE_M64_N128 = 0,   // weight-streaming regime: few rows per expert
   TILE_M128_N256 = 1,  // compute regime
-  TILE_COUNT = 2
+  TILE_M256_N256 = 2,  // compute regime, many rows per expert
+  TILE_COUNT = 3
 };
-inline int tile_bm(int t) { return t == TILE_M64_N128 ? 64 : 128; }
+inline int tile_bm(int t) { return t == TILE_M64_N128 ? 64 : t == TILE_M128_N256 ? 128 : 256; }
 inline int tile_bn(int t) { return t == TILE_M64_N128 ? 128 : 256; }
 
 struct GemmArgs {

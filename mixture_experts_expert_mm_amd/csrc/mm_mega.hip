@@ -184,13 +184,15 @@ void k_mega(const MegaArgs* mp) {
   if (!grid_barrier(ctl, ++nb, spin, bs, &ok)) return;
 
   if constexpr (UC == UC_FP8 || UC == UC_I8) {
-    // per-row requantisation of A, one wave per pool row (two rows at a time
-    // when I <= 2048); MX quantised A in the Linear1 epilogue
+    // per-row requantisation of A, one wave per pool row (two rows at a
+    // time when I <= 2048, four with four waves per CU: the same loads in
+    // flight per CU); MX quantised A in the Linear1 epilogue
     const RequantArgs r = m.rq;
     const int64_t used = off_s[r.E], nwv = (int64_t)gridDim.x * NW;
     const int64_t p0 = (int64_t)blockIdx.x * NW + t / 64;
+    constexpr int RU = NW >= 8 ? 2 : 4;
     if (r.I <= 2048) {
-      for (int64_t p = p0; p < used; p += 2 * nwv) requant_rows<UC, 2, 4>(r, p, nwv, off_s, cnt_s);
+      for (int64_t p = p0; p < used; p += RU * nwv) requant_rows<UC, RU, 4>(r, p, nwv, off_s, cnt_s);
     } else {
       for (int64_t p = p0; p < used; p += nwv) requant_rows<UC, 1>(r, p, 0, off_s, cnt_s);
     }
@@ -205,10 +207,11 @@ void k_mega(const MegaArgs* mp) {
   if (!grid_barrier(ctl, ++nb, spin, bs, &ok)) return;
 
   // combine: 8 columns of one token per item; two items per thread at a time
-  // with bf16 slots (A8W8), one with float32 slots
+  // with bf16 slots (A8W8), one with float32 slots; twice that with four
+  // waves per CU (the same loads in flight per CU)
   const CombineArgs c = m.cb;
   const int64_t work = c.T * (c.H / 8), stride = (int64_t)gridDim.x * NT;
-  constexpr int CU = UC == UC_BF16 ? 1 : 2;
+  constexpr int CU = (UC == UC_BF16 ? 1 : 2) * (NW >= 8 ? 1 : 2);
   for (int64_t idx = (int64_t)blockIdx.x * NT + t; idx < work; idx += CU * stride)
     combine_items<CU, UC != UC_BF16>(c, idx, stride, work);
   __syncthreads();
@@ -262,7 +265,13 @@ static hipError_t launch_mega_one(const MegaArgs* dev_args, int grid, hipStream_
 
 template <int UC, bool WIDEN = false>
 static hipError_t launch_mega_bm(int tile, const MegaArgs* a, int grid, hipStream_t s) {
-  return tile == TILE_M64_N128 ? launch_mega_one<UC, 64, WIDEN>(a, grid, s) : launch_mega_one<UC, 128, WIDEN>(a, grid, s);
+  switch (tile) {
+    case TILE_M64_N128: return launch_mega_one<UC, 64, WIDEN>(a, grid, s);
+    case TILE_M256_N256:
+      if constexpr (is_mx(UC)) return hipErrorInvalidValue;   // the plan keeps MX at 128
+      else return launch_mega_one<UC, 256, WIDEN>(a, grid, s);
+    default: return launch_mega_one<UC, 128, WIDEN>(a, grid, s);
+  }
 }
 
 hipError_t launch_mega_prep(const MegaArgs& a, MegaArgs* dev_args, hipStream_t s) {

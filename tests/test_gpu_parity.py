@@ -32,7 +32,11 @@ SMALL = {
     "bm32": dict(T=20, H=256, I=128, E=16, K=2, bias=0.5),
     "bm64": dict(T=200, H=512, I=256, E=24, K=2, bias=2.0),
     "bm128": dict(T=333, H=768, I=384, E=6, K=3, bias=0.5),
+    # BLOCK_M 256 (forced): ~300 rows per expert, one full and one ragged
+    # M-block each, 3 x 2 and 3 x 3 tiles of 256 x 256
+    "bm256": dict(T=600, H=768, I=384, E=4, K=2, bias=0.5),
 }
+FORCED_TILE = {"bm256": "2"}   # MM_FORCE_TILE of shapes whose tile the plan would not choose
 
 
 def small_cfg(shape: str, usecase: str, **kw) -> wl.Config:
@@ -87,7 +91,9 @@ def test_dispatch_metadata_full_configs(name):
 
 @pytest.mark.parametrize("shape", list(SMALL))
 @pytest.mark.parametrize("usecase", ["bf16", "fp8", "int8"])
-def test_dispatch_small_masked(shape, usecase):
+def test_dispatch_small_masked(shape, usecase, monkeypatch):
+    if shape in FORCED_TILE:
+        monkeypatch.setenv("MM_FORCE_TILE", FORCED_TILE[shape])
     cfg = small_cfg(shape, usecase, masked_ratio=0.2)
     log(f"[dispatch masked] {cfg.name}")
     inp = wl.make_inputs(cfg)
@@ -132,7 +138,9 @@ def test_activation_quantiser_all_bf16_patterns(usecase):
 @pytest.mark.parametrize("shape", list(SMALL))
 @pytest.mark.parametrize("usecase", ["bf16", "fp8", "int8"])
 @pytest.mark.parametrize("masked", [0.0, 0.25])
-def test_y_parity_small(shape, usecase, masked):
+def test_y_parity_small(shape, usecase, masked, monkeypatch):
+    if shape in FORCED_TILE:
+        monkeypatch.setenv("MM_FORCE_TILE", FORCED_TILE[shape])
     cfg = small_cfg(shape, usecase, masked_ratio=masked)
     log(f"[y small] {cfg.name} masked={masked}")
     inp = wl.make_inputs(cfg)
@@ -166,15 +174,18 @@ def test_tiny_config_all_elements():
 # exact integer accumulators (A8W8-INT)
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("shape", ["bm64", "split128", "split64"])
+@pytest.mark.parametrize("shape", ["bm64", "bm256", "split128", "split64"])
 def test_int8_accumulators_exact(shape, monkeypatch):
     """int32 accumulators before any scaling equal numpy's int64 products on
-    every valid row.  bm64: the 64 x 128 tile, no split.  split128 / split64:
-    256 routes per expert, so the tail tiles of both GEMMs are split along K
-    (BLOCK_M 128: Linear1 in up to 4 pieces, Linear2 in 2; BLOCK_M 64 forced:
-    more pieces) and piece 0 adds the others' partial sums."""
-    if shape == "bm64":
-        cfg = small_cfg("bm64", "int8")
+    every valid row.  bm64: the 64 x 128 tile, no split; bm256: the 256 x 256
+    tile (forced).  split128 / split64: 256 routes per expert, so the tail
+    tiles of both GEMMs are split along K (BLOCK_M 128: Linear1 in up to 4
+    pieces, Linear2 in 2; BLOCK_M 64 forced: more pieces) and piece 0 adds
+    the others' partial sums."""
+    if shape in ("bm64", "bm256"):
+        if shape in FORCED_TILE:
+            monkeypatch.setenv("MM_FORCE_TILE", FORCED_TILE[shape])
+        cfg = small_cfg(shape, "int8")
     else:
         cfg = wl.Config(f"{shape}_int8", "int8", 512, 2048, 1024, 8, 4, 0.3, 61)
         if shape == "split64":
