@@ -279,7 +279,10 @@ mm_status mm_grouped_l2_combine(const mm_plan* plan, const int32_t* expert_offse
  * wait (about a second), the barrier gives up: the call has already
  * returned MM_OK, y is then unspecified, and only the error word
  * (MM_DEVERR_BARRIER_TIMEOUT) reports it.  Callers that share the GPU with
- * long-running concurrent kernels must read the error word.
+ * long-running concurrent kernels must read the error word, or make the plan
+ * with the environment variable MM_COOPERATIVE=1 set: the fused kernel is
+ * then launched cooperatively, so the runtime starts it only once the whole
+ * grid can be resident (some microseconds more per call).
  *   x              device bf16 [T][H]
  *   topk_ids       device int32 [T][K]
  *   topk_weights   device f32 [T][K]

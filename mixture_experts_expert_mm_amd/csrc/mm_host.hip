@@ -49,6 +49,8 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 // rows gathered), [1] the largest K split of a tail tile (1: none).
 bool plan_by_token(const mm_plan& pl) { return pl.reserved[0] != 0; }
 int plan_max_split(const mm_plan& pl) { return (int)pl.reserved[1]; }
+// [2] the fused kernel's launch: cooperative (1) or ordinary (0)
+bool plan_cooperative(const mm_plan& pl) { return pl.reserved[2] != 0; }
 
 // ---------------------------------------------------------------- workspace
 struct WsLayout {
@@ -505,6 +507,8 @@ mm_status mm_plan_create(const mm_problem* problem, mm_plan* plan) {
   pl.gate_up_group = 32;
   pl.reserved[0] = choose_by_token(p) ? 1 : 0;
   pl.reserved[1] = choose_max_split(p);
+  // MM_COOPERATIVE=1 when the plan is made: launch the fused kernel cooperatively
+  if (const char* v = std::getenv("MM_COOPERATIVE")) pl.reserved[2] = std::atoi(v) == 1 ? 1 : 0;
   const int64_t P = align_up(R + all_experts(p) * (pl.block_m - 1), pl.block_m);
   if (P > ((int64_t)1 << 31) - 1) return MM_ERR_INVALID_ARG;
   pl.pool_rows = P;
@@ -633,7 +637,8 @@ mm_status mega_moe(const mm_plan* plan, const void* x, const int32_t* topk_ids, 
   MegaArgs* dev_args = at<MegaArgs>(workspace, L.mega_args);
   MM_TRY(run(MM_K_ZERO, s, [&] { return launch_mega_prep(m, dev_args, s); }));
   MM_TRY(run(MM_K_MEGA, s, [&] {
-    return launch_mega(pl.prob.usecase, pl.tile_l1, fp8_l1_exact(pl), dev_args, mega_grid(pl.tile_l1, num_cus()), s);
+    return launch_mega(pl.prob.usecase, pl.tile_l1, fp8_l1_exact(pl), dev_args, mega_grid(pl.tile_l1, num_cus()),
+                       plan_cooperative(pl), s);
   }));
   return MM_OK;
 }

@@ -143,7 +143,8 @@ struct MegaArgs {
 // clears counts[0..E) and ctl words [ctl_first, ctl_first + ctl_n)
 hipError_t launch_zero(int32_t* counts, int E, uint32_t* ctl, int ctl_first, int ctl_n, hipStream_t s);
 hipError_t launch_mega_prep(const MegaArgs& a, MegaArgs* dev_args, hipStream_t s);
-hipError_t launch_mega(int usecase, int tile, bool exact_l1, const MegaArgs* dev_args, int grid, hipStream_t s);
+hipError_t launch_mega(int usecase, int tile, bool exact_l1, const MegaArgs* dev_args, int grid, bool coop,
+                       hipStream_t s);
 int mega_grid(int tile, int num_cus);
 hipError_t launch_count(const DispatchArgs& a, hipStream_t s);
 hipError_t launch_scatter(const DispatchArgs& a, hipStream_t s);

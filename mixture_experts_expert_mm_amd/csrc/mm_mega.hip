@@ -239,12 +239,13 @@ __global__ __launch_bounds__(256) void k_mega_prep(MegaArgs m, MegaArgs* out) {
 
 // The grid barriers need every workgroup of the grid resident at once.  The
 // grid is one workgroup per CU and the kernel's LDS use admits one per CU,
-// which the occupancy query confirms here; the launch is an ordinary one (a
-// cooperative launch guarantees the same on an idle device but costs tens of
-// microseconds more per call).  Work of other streams that holds CUs only
-// delays the late workgroups, which the barriers wait for (bounded).
+// which the occupancy query confirms here.  By default the launch is an
+// ordinary one: work of other streams that holds CUs only delays the late
+// workgroups, which the barriers wait for (bounded).  A plan made with
+// MM_COOPERATIVE=1 launches cooperatively: the runtime then starts the grid
+// only once all of it can be resident, at some microseconds per call.
 template <int UC, int BM, bool WIDEN>
-static hipError_t launch_mega_one(const MegaArgs* dev_args, int grid, hipStream_t s) {
+static hipError_t launch_mega_one(const MegaArgs* dev_args, int grid, bool cooperative, hipStream_t s) {
   constexpr size_t lds = (size_t)mega_lds_bytes<UC, BM>();
   static int per_cu = -1;
   if (per_cu < 0) {
@@ -259,18 +260,25 @@ static hipError_t launch_mega_one(const MegaArgs* dev_args, int grid, hipStream_
   if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return hipErrorInvalidDevice;
   if (per_cu < 1 || grid > per_cu * cus) return hipErrorCooperativeLaunchTooLarge;
+  if (cooperative) {
+    // the runtime starts the grid only when all of it can be resident
+    const MegaArgs* arg = dev_args;
+    void* params[] = {(void*)&arg};
+    return hipLaunchCooperativeKernel((const void*)k_mega<UC, BM, WIDEN>, dim3(grid), dim3(threads_of<BM>()), params,
+                                      (unsigned)lds, s);
+  }
   hipLaunchKernelGGL((k_mega<UC, BM, WIDEN>), dim3(grid), dim3(threads_of<BM>()), lds, s, dev_args);
   return hipGetLastError();
 }
 
 template <int UC, bool WIDEN = false>
-static hipError_t launch_mega_bm(int tile, const MegaArgs* a, int grid, hipStream_t s) {
+static hipError_t launch_mega_bm(int tile, const MegaArgs* a, int grid, bool coop, hipStream_t s) {
   switch (tile) {
-    case TILE_M64_N128: return launch_mega_one<UC, 64, WIDEN>(a, grid, s);
+    case TILE_M64_N128: return launch_mega_one<UC, 64, WIDEN>(a, grid, coop, s);
     case TILE_M256_N256:
       if constexpr (is_mx(UC)) return hipErrorInvalidValue;   // the plan keeps MX at 128
-      else return launch_mega_one<UC, 256, WIDEN>(a, grid, s);
-    default: return launch_mega_one<UC, 128, WIDEN>(a, grid, s);
+      else return launch_mega_one<UC, 256, WIDEN>(a, grid, coop, s);
+    default: return launch_mega_one<UC, 128, WIDEN>(a, grid, coop, s);
   }
 }
 
@@ -281,16 +289,20 @@ hipError_t launch_mega_prep(const MegaArgs& a, MegaArgs* dev_args, hipStream_t s
   return hipGetLastError();
 }
 
-hipError_t launch_mega(int usecase, int tile, bool exact_l1, const MegaArgs* dev_args, int grid, hipStream_t s) {
+hipError_t launch_mega(int usecase, int tile, bool exact_l1, const MegaArgs* dev_args, int grid, bool coop,
+                       hipStream_t s) {
   switch (usecase) {
-    case UC_BF16: return launch_mega_bm<UC_BF16>(tile, dev_args, grid, s);
+    case UC_BF16: return launch_mega_bm<UC_BF16>(tile, dev_args, grid, coop, s);
     case UC_FP8:
-      return exact_l1 ? launch_mega_bm<UC_FP8, true>(tile, dev_args, grid, s) : launch_mega_bm<UC_FP8>(tile, dev_args, grid, s);
+      return exact_l1 ? launch_mega_bm<UC_FP8, true>(tile, dev_args, grid, coop, s)
+                      : launch_mega_bm<UC_FP8>(tile, dev_args, grid, coop, s);
     case UC_MX8:
-      return exact_l1 ? launch_mega_bm<UC_MX8, true>(tile, dev_args, grid, s) : launch_mega_bm<UC_MX8>(tile, dev_args, grid, s);
+      return exact_l1 ? launch_mega_bm<UC_MX8, true>(tile, dev_args, grid, coop, s)
+                      : launch_mega_bm<UC_MX8>(tile, dev_args, grid, coop, s);
     case UC_MX4:
-      return exact_l1 ? launch_mega_bm<UC_MX4, true>(tile, dev_args, grid, s) : launch_mega_bm<UC_MX4>(tile, dev_args, grid, s);
-    default: return launch_mega_bm<UC_I8>(tile, dev_args, grid, s);
+      return exact_l1 ? launch_mega_bm<UC_MX4, true>(tile, dev_args, grid, coop, s)
+                      : launch_mega_bm<UC_MX4>(tile, dev_args, grid, coop, s);
+    default: return launch_mega_bm<UC_I8>(tile, dev_args, grid, coop, s);
   }
 }
 

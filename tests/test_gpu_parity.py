@@ -305,6 +305,27 @@ def test_fused_equals_three_call_and_is_deterministic(usecase):
     assert layer.device_error(fused=True) == 0 and layer.device_error(fused=False) == 0
 
 
+@pytest.mark.parametrize("shape,usecase", [("bm128", "bf16"), ("bm128", "fp8"), ("bm256", "int8")])
+def test_cooperative_launch_equals_ordinary(shape, usecase, monkeypatch):
+    """A plan made with MM_COOPERATIVE=1 launches the fused kernel
+    cooperatively; the results are those of the ordinary launch, bit for bit."""
+    if shape in FORCED_TILE:
+        monkeypatch.setenv("MM_FORCE_TILE", FORCED_TILE[shape])
+    cfg = small_cfg(shape, usecase)
+    inp = wl.make_inputs(cfg)
+    x, ids, wts = device_inputs(inp)
+    ordinary = make_layer(inp, "f32")
+    y0, c0 = ordinary.forward(x, ids, wts)
+    monkeypatch.setenv("MM_COOPERATIVE", "1")
+    coop = make_layer(inp, "f32")
+    assert coop.plan.reserved[2] == 1 and ordinary.plan.reserved[2] == 0
+    y1, c1 = coop.forward(x, ids, wts)
+    torch.cuda.synchronize()
+    assert coop.device_error() == 0
+    assert torch.equal(y0.view(torch.int32), y1.view(torch.int32))
+    assert torch.equal(c0, c1)
+
+
 @pytest.mark.parametrize("usecase", ["bf16", "fp8"])
 @pytest.mark.parametrize("T,E,block_m", [(1024, 32, 128), (1025, 32, 128), (512, 256, 64), (513, 256, 64)])
 def test_fused_one_block_dispatch_boundary(T, E, block_m, usecase):
