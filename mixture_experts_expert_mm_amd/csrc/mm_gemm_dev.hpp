@@ -392,22 +392,26 @@ __device__ __forceinline__ bool poll_flag(uint32_t* p, uint32_t spin_limit) {
 // expert at a time and per K-stage read 8 activation and 4 weight stages
 // (the fewest bytes for 32 tiles when activation rows come from the pool);
 // without groups they read one weight stage and up to 32 activation stages.
-// The expert of a tile is the largest e with (off[e] / BM) * n_tiles <= tile.
+// Tiles are counted inside an XCD's slice of M-blocks [mb_beg, mb_end): an
+// expert's M-blocks clipped to the slice, times the N-blocks.  The expert of
+// a tile is the largest e with (clip(off[e] / BM) - mb_beg) * n_tiles <= tile.
 template <int BM>
 __device__ __forceinline__ TileRef resolve_tile(const GemmArgs& a, const int32_t* off_s, const int32_t* cnt_s,
-                                               int tile, int n_tiles, int kbytes, int kbytes_b) {
+                                               int tile, int n_tiles, int kbytes, int kbytes_b, int mb_beg,
+                                               int mb_end) {
+  auto first_mb = [&](int e) { return min(max(off_s[e] / BM, mb_beg), mb_end); };
   int lo = 0, hi = a.E;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if ((off_s[mid] / BM) * n_tiles <= tile) lo = mid; else hi = mid;
+    if ((first_mb(mid) - mb_beg) * n_tiles <= tile) lo = mid; else hi = mid;
   }
   // every field is wave-uniform; saying so keeps them in scalar registers
   // (a tile base the compiler cannot prove uniform would turn each buffer
   // load into a loop over lanes)
   TileRef r;
   r.e = uniform_int(lo);
-  const int mb0 = off_s[lo] / BM, nmb = (off_s[lo + 1] - off_s[lo]) / BM;
-  const int local = tile - mb0 * n_tiles;
+  const int mb0 = first_mb(lo), nmb = first_mb(lo + 1) - mb0;
+  const int local = tile - (mb0 - mb_beg) * n_tiles;
   const int GM = a.group_m > 0 ? a.group_m : nmb;   // M-blocks per group (0: the whole expert)
   const int g = local / (GM * n_tiles), gm = min(GM, nmb - g * GM);
   const int idx = local - g * GM * n_tiles;
@@ -488,7 +492,6 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
   const int kbytes_b = B4 ? a.Kdim / 2 : kbytes;           // B bytes per row
   const int nk = kbytes / RB;
   const int n_tiles = a.N / BN;
-  const int total = offsets_ok ? (off_s[a.E] / BM) * n_tiles : 0;
   const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_ptr_t)lds;
   RowInfo* rowinfo = reinterpret_cast<RowInfo*>(lds + S * STAGE);   // [2][BM]
   const uint32_t rowinfo_base = lds_base + (uint32_t)(S * STAGE);
@@ -547,7 +550,9 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
   auto dma_x = [&](const TileRef& tr, int x, int kb) {
     if (x < D) {
       dma_one<NW, BM, STAGE, S, RB, RBB>(lds, tr.abase, abytes, tr.bbase, bbytes, voff_b, wv, kbytes, kbytes_b, x, kb,
-                                         tr.kbase, by_tok, tr.aoa[x < DA ? x : 0]);
+                                         tr.kbase, by_tok,
+                                         by_tok ? tr.aoa[x < DA ? x : 0]
+                                                : (RPI * (wv + NW * x) + l / CH < tr.valid ? voff : kOffRange));
     } else if constexpr (MX) {
       const int soff = __builtin_amdgcn_readfirstlane((kb + tr.kbase) * 4);
       const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
@@ -572,7 +577,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
   struct RowRegs {
     int32_t route;
     float gw, rs;
-    float cs0[NCS], cs1[NCS];
+    float cs0[NCS], cs1[MODE == 0 ? NCS : 1];   // cs1: Linear1's up columns
   };
   auto row_blank = [&]() {
     RowRegs rr;
@@ -580,7 +585,9 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
     rr.gw = 0.0f;
     rr.rs = 1.0f;
 #pragma unroll
-    for (int j = 0; j < NCS; ++j) rr.cs0[j] = rr.cs1[j] = 1.0f;
+    for (int j = 0; j < NCS; ++j) rr.cs0[j] = 1.0f;
+#pragma unroll
+    for (int j = 0; j < (MODE == 0 ? NCS : 1); ++j) rr.cs1[j] = 1.0f;
     return rr;
   };
   auto row_first = [&](const TileRef& tr) {
@@ -613,9 +620,10 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
     // the tile's first stage has landed, so have the column scales (issued
     // before it): taken here, at a wait the compiler sees as complete
 #pragma unroll
-    for (int j = 0; j < NCS; ++j) {
-      asm volatile("" : "+v"(rr.cs0[j]));
-      asm volatile("" : "+v"(rr.cs1[j]));
+    for (int j = 0; j < NCS; ++j) asm volatile("" : "+v"(rr.cs0[j]));
+    if constexpr (MODE == 0) {
+#pragma unroll
+      for (int j = 0; j < NCS; ++j) asm volatile("" : "+v"(rr.cs1[j]));
     }
     if constexpr (MODE == 0 && UC != UC_BF16 && !MX) {
       if (by_tok) rr.rs = rr.route >= 0 ? gp(a.x_scale)[rr.route / a.K] : 1.0f;
@@ -655,12 +663,16 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
     return rr;
   };
 
-  // Workgroup w runs on XCD w % 8 (round-robin dispatch); each XCD walks its
-  // own contiguous slice of the tile list so the sharing happens inside one L2.
+  // Workgroup w runs on XCD w % 8 (round-robin dispatch); each XCD walks the
+  // tiles of its own contiguous slice of M-blocks, all their N-blocks, so the
+  // sharing happens inside one L2 and every tile of an M-block runs on the
+  // same XCD (measured: bf16 16K tokens 1.5% faster than equal tile counts).
   const int nxcd = gridDim.x >= 8 ? 8 : 1;
   const int xcd = blockIdx.x % nxcd, wgx = blockIdx.x / nxcd, per_x = gridDim.x / nxcd;
-  const int slice = (total + nxcd - 1) / nxcd;
-  const int t_beg = xcd * slice, t_end = min(total, t_beg + slice);
+  const int n_mb = offsets_ok ? off_s[a.E] / BM : 0;
+  const int mb_slice = (n_mb + nxcd - 1) / nxcd;
+  const int mb_beg = min(n_mb, xcd * mb_slice), mb_end = min(n_mb, mb_beg + mb_slice);
+  const int t_beg = 0, t_end = (mb_end - mb_beg) * n_tiles;
   const bool in_grid = (int)blockIdx.x < per_x * nxcd;   // a tail beyond a multiple of 8 stays idle
 
   // Work list of this workgroup: the slice's full rounds of tiles round
@@ -679,14 +691,15 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
   auto make_item = [&](int j) {
     TileRef r;
     if (j < full) {
-      r = resolve_tile<BM>(a, off_s, cnt_s, t_beg + wgx + j * per_x, n_tiles, kbytes, kbytes_b);
+      r = resolve_tile<BM>(a, off_s, cnt_s, t_beg + wgx + j * per_x, n_tiles, kbytes, kbytes_b, mb_beg, mb_end);
       r.kbase = 0;
       r.nkl = nk;
       r.role = kRoleFull;
       r.slot = 0;
     } else {
       const int p = wgx + (j - full) * per_x, sub = p % sk;
-      r = resolve_tile<BM>(a, off_s, cnt_s, t_beg + full * per_x + p / sk, n_tiles, kbytes, kbytes_b);
+      r = resolve_tile<BM>(a, off_s, cnt_s, t_beg + full * per_x + p / sk, n_tiles, kbytes, kbytes_b, mb_beg,
+                           mb_end);
       r.kbase = uniform_int(sub * nk / sk);
       r.nkl = uniform_int((sub + 1) * nk / sk - sub * nk / sk);
       r.role = sk == 1 ? kRoleFull : (sub == 0 ? kRoleReduce : kRoleProduce);
@@ -709,10 +722,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
         const uint32_t tok = (uint32_t)max(route[x], 0) / (uint32_t)a.K;
         r.aoa[x] = route[x] >= 0 ? tok * (uint32_t)kbytes + vchunk : kOffRange;
       }
-    } else {
-#pragma unroll
-      for (int x = 0; x < DA; ++x) r.aoa[x] = RPI * (wv + NW * x) + l / CH < r.valid ? voff : kOffRange;
-    }
+    }   // (pool rows: the offsets follow from the valid count when the copies go out)
     r.sc = 0;
     if constexpr (MX) {
       // A-scale waves: tile row 64*wv + l (its token row when A is read by
