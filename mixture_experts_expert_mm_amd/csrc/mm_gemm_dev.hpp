@@ -1397,6 +1397,82 @@ __device__ __forceinline__ void requant_rows(const RequantArgs& a, int64_t p0, i
   }
 }
 
+// The fused kernel's requantisation with four waves per CU (one per SIMD):
+// rows p0 + k * pstride below `used`, RU at a time, the next RU rows' loads
+// issued before this batch's maxima, codes and stores, so that a wave alone
+// on its SIMD keeps loads in flight while it computes.  Each load and store
+// is a buffer access whose descriptor covers its row only when the row is
+// live (padding rows and rows past `used`: no memory access, loads read 0),
+// so every batch issues the same instructions and the waits between them
+// have fixed counts.  The same arithmetic as requant_rows (bit for bit).
+// I <= 2048: four chunks of 8 values per lane.
+template <int UC, int RU>
+__device__ __forceinline__ void requant_stream(const RequantArgs& a, int64_t p0, int64_t pstride, int64_t used,
+                                               const int32_t* off_s, const int32_t* cnt_s) {
+  constexpr int RC = 4;
+  if (p0 >= used) return;
+  const int l = lane_id();
+  const int nch = a.I / 8;
+  const float qmax = (UC == UC_I8) ? 127.0f : 448.0f;
+  float4 buf[2][RU][2 * RC];
+  bool live[2][RU];
+  auto row_rsrc = [&](const void* base, int64_t p, int64_t elem_bytes, bool on) {
+    const uint8_t* b = static_cast<const uint8_t*>(base) + (on ? p : 0) * elem_bytes;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)uniform_ptr(b), (short)0, on ? (int)elem_bytes : 0, 0x00020000);
+  };
+  auto load = [&](auto bt, int64_t p) {
+    constexpr int b = decltype(bt)::value;
+#pragma unroll
+    for (int u = 0; u < RU; ++u) {
+      const int64_t pu = p + u * pstride;
+      live[b][u] = requant_row_live(a, pu, off_s, cnt_s);
+      const __amdgpu_buffer_rsrc_t rs = row_rsrc(a.a_stage, pu, (int64_t)a.I * 4, live[b][u]);
+#pragma unroll
+      for (int j = 0; j < RC; ++j) {
+        const int c = j * 64 + l;
+        const int off = c < nch ? c * 32 : (int)kOffRange;
+        buf[b][u][2 * j] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+        buf[b][u][2 * j + 1] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16, 0, 0));
+      }
+    }
+  };
+  auto process = [&](auto bt, int64_t p) {
+    constexpr int b = decltype(bt)::value;
+#pragma unroll
+    for (int u = 0; u < RU; ++u) {
+      float m = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 2 * RC; ++j) m = amax4(buf[b][u][j], m);
+      const float sc = fmaxf(wave_max(m) / qmax, 1e-8f);
+      const int64_t pu = p + u * pstride;
+      const __amdgpu_buffer_rsrc_t ro = row_rsrc(a.a_pool, pu, a.I, live[b][u]);
+#pragma unroll
+      for (int j = 0; j < RC; ++j) {
+        const int c = j * 64 + l;
+        const uint2 q = requant_codes8<UC>(buf[b][u][2 * j], buf[b][u][2 * j + 1], sc);
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{q.x, q.y}, ro, c < nch ? c * 8 : (int)kOffRange, 0, 0);
+      }
+      const __amdgpu_buffer_rsrc_t rsc = row_rsrc(a.a_scale, pu, 4, live[b][u]);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), rsc, l == 0 ? 0 : (int)kOffRange, 0, 0);
+    }
+  };
+  const std::integral_constant<int, 0> b0;
+  const std::integral_constant<int, 1> b1;
+  const int64_t step = (int64_t)RU * pstride;
+  int64_t p = p0;
+  load(b0, p);
+  for (;;) {
+    load(b1, p + step);   // the next batch (past `used`: nothing is read)
+    process(b0, p);
+    p += step;
+    if (p >= used) break;
+    load(b0, p + step);
+    process(b1, p);
+    p += step;
+    if (p >= used) break;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Token Combine: y_i = sum_{k=0..K-1} slot[i*K+k] in slot order, float32;
 // masked routes (route_to_pool < 0) contribute nothing.  One thread makes 8

@@ -185,14 +185,17 @@ void k_mega(const MegaArgs* mp) {
 
   if constexpr (UC == UC_FP8 || UC == UC_I8) {
     // per-row requantisation of A, one wave per pool row (two rows at a
-    // time when I <= 2048, four with four waves per CU: the same loads in
-    // flight per CU); MX quantised A in the Linear1 epilogue
+    // time when I <= 2048; with four waves per CU, two rows while the next
+    // two load); MX quantised A in the Linear1 epilogue
     const RequantArgs r = m.rq;
     const int64_t used = off_s[r.E], nwv = (int64_t)gridDim.x * NW;
     const int64_t p0 = (int64_t)blockIdx.x * NW + t / 64;
-    constexpr int RU = NW >= 8 ? 2 : 4;
     if (r.I <= 2048) {
-      for (int64_t p = p0; p < used; p += RU * nwv) requant_rows<UC, RU, 4>(r, p, nwv, off_s, cnt_s);
+      if constexpr (NW >= 8) {
+        for (int64_t p = p0; p < used; p += 2 * nwv) requant_rows<UC, 2, 4>(r, p, nwv, off_s, cnt_s);
+      } else {
+        requant_stream<UC, 2>(r, p0, nwv, used, off_s, cnt_s);   // one wave per SIMD: loads ahead of the math
+      }
     } else {
       for (int64_t p = p0; p < used; p += nwv) requant_rows<UC, 1>(r, p, 0, off_s, cnt_s);
     }
