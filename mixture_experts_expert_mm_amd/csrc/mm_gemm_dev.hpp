@@ -124,6 +124,10 @@ __device__ __forceinline__ void ds_write2(uint32_t addr, uint32_t v) {
   asm volatile("ds_write_b16 %0, %1 offset:%2" ::"v"(addr), "v"(v), "i"(OFF) : "memory");
 }
 template <int OFF>
+__device__ __forceinline__ void ds_write2hi(uint32_t addr, uint32_t v) {   // bits 16-31 of v
+  asm volatile("ds_write_b16_d16_hi %0, %1 offset:%2" ::"v"(addr), "v"(v), "i"(OFF) : "memory");
+}
+template <int OFF>
 __device__ __forceinline__ void ds_write4(uint32_t addr, uint32_t v) {
   asm volatile("ds_write_b32 %0, %1 offset:%2" ::"v"(addr), "v"(v), "i"(OFF) : "memory");
 }
@@ -547,6 +551,10 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
   // wave's 64 scale rows (lane l: row 64*wv + l of the slot, A rows then B
   // rows), each lane's word landing at its row's word.
   const bool scale_a = wv < BM / 64;
+  // (each field read on its own: a select between the two fields' addresses
+  // would put a copy of the arguments in scratch memory)
+  const void* const scale_src = scale_a ? (const void*)uniform_ptr(a.a_mx) : (const void*)uniform_ptr(a.b_mx);
+  const int scale_bytes = uniform_int(scale_a ? asc_bytes : bsc_bytes);
   auto dma_x = [&](const TileRef& tr, int x, int kb) {
     if (x < D) {
       dma_one<NW, BM, STAGE, S, RB, RBB>(lds, tr.abase, abytes, tr.bbase, bbytes, voff_b, wv, kbytes, kbytes_b, x, kb,
@@ -555,8 +563,8 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
                                                 : (RPI * (wv + NW * x) + l / CH < tr.valid ? voff : kOffRange));
     } else if constexpr (MX) {
       const int soff = __builtin_amdgcn_readfirstlane((kb + tr.kbase) * 4);
-      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(scale_a ? a.a_mx : a.b_mx), (short)0, scale_a ? asc_bytes : bsc_bytes, 0x00020000);
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc((void*)scale_src, (short)0, scale_bytes, 0x00020000);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(scl + (kb % S) * SSTAGE + 64 * wv * 4), 4, tr.sc, soff,
                                                0, 0);
     }
@@ -1122,13 +1130,12 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
         u32x2 ri[MODE == 1 ? 16 : 1];   // Linear2: G[i,k] and s^A of the row
         uint32_t sxr[(MODE == 0 && UC != UC_BF16 && !MX) ? 16 : 1];
         if constexpr (MODE == 1 || (MODE == 0 && UC != UC_BF16 && !MX)) {
-#pragma unroll
-          for (int q = 0; q < 16; ++q) {
-            const int r = rb + 8 * (q / 4) + (q % 4);
-            const uint32_t ad = rowinfo_base + (uint32_t)((buf * BM + r) * (int)sizeof(RowInfo));
-            if constexpr (MODE == 1) ri[q] = ds_read8<0>(ad);
-            else sxr[q] = ds_read4<4>(ad);
-          }
+          const uint32_t ad = rowinfo_base + (uint32_t)((buf * BM + rb) * (int)sizeof(RowInfo));
+          static_for<16>([&](auto qc) {
+            constexpr int q = qc, OFF = (8 * (q / 4) + (q % 4)) * (int)sizeof(RowInfo);
+            if constexpr (MODE == 1) ri[q] = ds_read8<OFF>(ad);
+            else sxr[q] = ds_read4<OFF + 4>(ad);
+          });
           lgkm_wait<0>();
 #pragma unroll
           for (int q = 0; q < 16; ++q) {
@@ -1177,51 +1184,65 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
           // element).
           const uint32_t wst = stg_base + (uint32_t)(wv * OREG);   // this wave's staging block
           const uint32_t wlane = wst + (uint32_t)((4 * h) * OPITCH + lr * OESZ);
-#pragma unroll
-          for (int q = 0; q < 16; ++q) {
-#pragma unroll
-            for (int j = 0; j < OCOLS / 32; ++j) {
-              float o;
-              if constexpr (MODE == 0) {
-                // SwiGLU of the gate column (block 2j) and its up partner (2j+1)
-                float g = acc_to_f32(acc[i][2 * j][q]);
-                float u = acc_to_f32(acc[i][2 * j + 1][q]);
-                if constexpr (UC != UC_BF16) {
-                  const float sx = __uint_as_float(sxr[q]);
-                  g = (g * rr_cur.cs0[j]) * sx;
-                  u = (u * rr_cur.cs1[j]) * sx;
-                }
-                // the operator's activation_clamp (+inf: none; identity on finite H)
-                g = __builtin_amdgcn_fmed3f(g, -a.clamp, a.clamp);
-                u = __builtin_amdgcn_fmed3f(u, -a.clamp, a.clamp);
-                o = silu(g) * u;
-              } else {
-                // contribution of route i*K+k: ((D * s^W2) * s^A) * G[i,k]
-                // (MX: the MFMA applied the block scales; A16W16: D * G)
-                const float gw = __uint_as_float(ri[q][0]);
-                const float rs = __uint_as_float(ri[q][1]);
-                float v = acc_to_f32(acc[i][j][q]);
-                if constexpr (COLS) v *= rr_cur.cs0[j];
-                o = (UC != UC_BF16 && !MX) ? (v * rs) * gw : v * gw;
+          // output value of accumulator q of column block j (constant q, j)
+          auto value = [&](const int q, const int j) -> float {
+            float o;
+            if constexpr (MODE == 0) {
+              // SwiGLU of the gate column (block 2j) and its up partner (2j+1)
+              float g = acc_to_f32(acc[i][2 * j][q]);
+              float u = acc_to_f32(acc[i][2 * j + 1][q]);
+              if constexpr (UC != UC_BF16) {
+                const float sx = __uint_as_float(sxr[q]);
+                g = (g * rr_cur.cs0[j]) * sx;
+                u = (u * rr_cur.cs1[j]) * sx;
               }
-              const uint32_t ad = wlane + (uint32_t)((8 * (q / 4) + (q % 4)) * OPITCH + j * 32 * OESZ);
-              if constexpr (OESZ == 2) ds_write2<0>(ad, f32_to_bf16_bits(o));
-              else ds_write4<0>(ad, __float_as_uint(o));
+              // the operator's activation_clamp (+inf: none; identity on finite H)
+              g = __builtin_amdgcn_fmed3f(g, -a.clamp, a.clamp);
+              u = __builtin_amdgcn_fmed3f(u, -a.clamp, a.clamp);
+              o = silu(g) * u;
+            } else {
+              // contribution of route i*K+k: ((D * s^W2) * s^A) * G[i,k]
+              // (MX: the MFMA applied the block scales; A16W16: D * G)
+              const float gw = __uint_as_float(ri[q][0]);
+              const float rs = __uint_as_float(ri[q][1]);
+              float v = acc_to_f32(acc[i][j][q]);
+              if constexpr (COLS) v *= rr_cur.cs0[j];
+              o = (UC != UC_BF16 && !MX) ? (v * rs) * gw : v * gw;
             }
-          }
+            return o;
+          };
+          // rows q and q + 1 (q even) are adjacent: bf16 pairs share one
+          // conversion, the high half stored by ds_write_b16_d16_hi; the
+          // offsets are the instructions' immediates
+          static_for<8>([&](auto qp) {
+            constexpr int q = 2 * qp;
+            static_for<OCOLS / 32>([&](auto jc) {
+              constexpr int j = jc, OFF = (8 * (q / 4) + (q % 4)) * OPITCH + j * 32 * OESZ;
+              static_assert(OFF + OPITCH < 65536, "LDS offsets fit the immediate");
+              const float o0 = value(q, j), o1 = value(q + 1, j);
+              if constexpr (OESZ == 2) {
+                const uint32_t pk = pack_bf16x2(o0, o1);
+                ds_write2<OFF>(wlane, pk);
+                ds_write2hi<OFF + OPITCH>(wlane, pk);
+              } else {
+                ds_write4<OFF>(wlane, __float_as_uint(o0));
+                ds_write4<OFF + OPITCH>(wlane, __float_as_uint(o1));
+              }
+            });
+          });
           lgkm_wait<0>();
           // read back: lane le takes 16-byte piece ch of staged rows
           // le / CPR + (64 / CPR) * k
           const int ch = le % CPR, r0 = le / CPR;
           u32x4 pv[CPL];
           uint32_t prt[MODE == 1 ? CPL : 1];
-#pragma unroll
-          for (int k = 0; k < CPL; ++k) {
-            const int row = r0 + (64 / CPR) * k;
-            pv[k] = ds_read16<0>(wst + (uint32_t)(row * OPITCH + ch * 16));
-            if constexpr (MODE == 1)
-              prt[k] = ds_read4<8>(rowinfo_base + (uint32_t)((buf * BM + wm * WTM + i * 32 + row) * (int)sizeof(RowInfo)));
-          }
+          const uint32_t rd = wst + (uint32_t)(r0 * OPITCH + ch * 16);
+          const uint32_t rdi = rowinfo_base + (uint32_t)((buf * BM + wm * WTM + i * 32 + r0) * (int)sizeof(RowInfo));
+          static_for<CPL>([&](auto kc) {
+            constexpr int k = kc;
+            pv[k] = ds_read16<(64 / CPR) * k * OPITCH>(rd);
+            if constexpr (MODE == 1) prt[k] = ds_read4<8 + (64 / CPR) * k * (int)sizeof(RowInfo)>(rdi);
+          });
           lgkm_wait<0>();
 #pragma unroll
           for (int k = 0; k < CPL; ++k) {
@@ -1416,9 +1437,12 @@ __device__ __forceinline__ void requant_stream(const RequantArgs& a, int64_t p0,
   const float qmax = (UC == UC_I8) ? 127.0f : 448.0f;
   float4 buf[2][RU][2 * RC];
   bool live[2][RU];
+  // (the row is the wave's: its base and range go to scalar registers, or
+  // the compiler would loop over the lanes for each access)
   auto row_rsrc = [&](const void* base, int64_t p, int64_t elem_bytes, bool on) {
     const uint8_t* b = static_cast<const uint8_t*>(base) + (on ? p : 0) * elem_bytes;
-    return __builtin_amdgcn_make_buffer_rsrc((void*)uniform_ptr(b), (short)0, on ? (int)elem_bytes : 0, 0x00020000);
+    return __builtin_amdgcn_make_buffer_rsrc((void*)uniform_ptr(b), (short)0,
+                                             uniform_int(on ? (int)elem_bytes : 0), 0x00020000);
   };
   auto load = [&](auto bt, int64_t p) {
     constexpr int b = decltype(bt)::value;
@@ -1579,6 +1603,151 @@ __device__ __forceinline__ void combine_items(const CombineArgs& a, int64_t idx0
       *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.y) + tok[u] * a.H + col[u]) = o;
     }
   }
+}
+
+// Token Combine of the fused kernel through LDS: the slot rows arrive by
+// LDS-DMA (no registers hold loads in flight, so a workgroup of few waves
+// still keeps three units of 8 slot-row segments in flight), then each thread
+// sums its columns in slot order exactly as combine_items does (masked
+// routes add nothing) and stores them.  A unit is one token's columns
+// [seg * NT * CPT, +NT * CPT) of its K <= 8 slots (slots past K and columns
+// past H are loaded beyond the descriptors' ranges: zeros, no memory
+// access), plus the token's route_to_pool entries, which every wave loads
+// into its own corner.  Thread t reads only the bytes its own wave loaded, so
+// the waves need no barrier; the waits are fixed vmcnt counts (every unit
+// issues the same copies and stores per wave, out-of-range ones included).
+template <int NT, bool BF16>
+struct CombineLds {
+  static constexpr int NW = NT / 64, CPT = BF16 ? 8 : 4, ESZ = BF16 ? 2 : 4;
+  static constexpr int KMAX = 8;
+  static constexpr int SLOT_BYTES = NT * 16;                   // one slot row segment
+  static constexpr int UNIT = KMAX * SLOT_BYTES + NW * 256;   // + the waves' route_to_pool corners
+  static constexpr int NBUF = NT <= 256 ? 3 : 2;
+  static constexpr int BYTES = NBUF * UNIT;
+  static constexpr int DT = KMAX + 1;                          // DMA instructions per wave and unit
+  static constexpr int YS = BF16 ? 2 : 1;                      // y stores per wave and unit
+};
+
+template <int NT, bool BF16>
+__device__ __forceinline__ void combine_lds(const CombineArgs& a, uint8_t* lds) {
+  typedef CombineLds<NT, BF16> C;
+  constexpr int NW = C::NW, CPT = C::CPT, ESZ = C::ESZ, NBUF = C::NBUF, DT = C::DT, YS = C::YS;
+  const int t = threadIdx.x, l = t % 64;
+  const int wv = __builtin_amdgcn_readfirstlane(t / 64);
+  const int K = a.K, H = a.H;
+  const int SEG = NT * CPT;
+  const int nseg = (H + SEG - 1) / SEG;
+  const int64_t units = a.T * nseg, G = gridDim.x;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_ptr_t)lds;
+  const int ysz = a.y_f32 ? 4 : 2;
+  // unit j's copies into buffer b (past the last unit: every copy beyond range)
+  auto issue = [&](int64_t j, int b) {
+    const bool on = j < units;
+    const int64_t i = on ? j / nseg : 0;
+    const int seg = on ? (int)(j % nseg) : 0;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)uniform_ptr(static_cast<const uint8_t*>(a.contrib) + i * K * (int64_t)H * ESZ), (short)0,
+        on ? K * H * ESZ : 0, 0x00020000);
+    const int col = seg * SEG + (wv * 64 + l) * CPT;
+    uint8_t* const ub = lds + b * C::UNIT;
+#pragma unroll
+    for (int k = 0; k < C::KMAX; ++k) {
+      const int off = (k < K && col < H) ? (k * H + col) * ESZ : (int)kOffRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(ub + k * C::SLOT_BYTES + wv * 1024), 16, off, 0, 0, 0);
+    }
+    const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)uniform_ptr(reinterpret_cast<const uint8_t*>(a.route_to_pool) + i * K * 4), (short)0, on ? K * 4 : 0,
+        0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lds_ptr_t)(ub + C::KMAX * C::SLOT_BYTES + wv * 256), 4, l * 4, 0, 0,
+                                             0);
+  };
+  // sum and store unit j from buffer b; VM: this wave's later copies and
+  // stores still allowed in flight when unit j's copies have landed
+  auto finish = [&](int64_t j, int b, auto vm_tag) {
+    constexpr int VM = decltype(vm_tag)::value;
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(VM) : "memory");
+    const int64_t i = j / nseg;
+    const int seg = (int)(j % nseg);
+    const uint32_t ub = lds_base + (uint32_t)(b * C::UNIT);
+    uint32_t pi[C::KMAX];
+    u32x4 v[C::KMAX];
+#pragma unroll
+    for (int k = 0; k < C::KMAX; ++k) pi[k] = ds_read4<0>(ub + (uint32_t)(C::KMAX * C::SLOT_BYTES + wv * 256 + k * 4));
+#pragma unroll
+    for (int k = 0; k < C::KMAX; ++k) v[k] = ds_read16<0>(ub + (uint32_t)(k * C::SLOT_BYTES + t * 16));
+    lgkm_wait<0>();
+    float acc[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < C::KMAX; ++k) {
+      tie(pi[k]);
+      tie(v[k]);
+      if (k < K && (int32_t)pi[k] >= 0) {
+        if constexpr (BF16) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            acc[2 * q] += bf16_bits_to_f32(v[k][q] & 0xffffu);
+            acc[2 * q + 1] += bf16_bits_to_f32(v[k][q] >> 16);
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[q] += __uint_as_float(v[k][q]);
+        }
+      }
+    }
+    const int col = seg * SEG + t * CPT;
+    const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)uniform_ptr(static_cast<uint8_t*>(a.y) + i * (int64_t)H * ysz), (short)0, H * ysz, 0x00020000);
+    const int yo = col < H ? col * ysz : (int)kOffRange;
+    if constexpr (BF16) {
+      if (a.y_f32) {
+        __builtin_amdgcn_raw_buffer_store_b128(
+            u32x4{__float_as_uint(acc[0]), __float_as_uint(acc[1]), __float_as_uint(acc[2]), __float_as_uint(acc[3])},
+            ry, yo, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(
+            u32x4{__float_as_uint(acc[4]), __float_as_uint(acc[5]), __float_as_uint(acc[6]), __float_as_uint(acc[7])},
+            ry, yo == (int)kOffRange ? yo : yo + 16, 0, 0);
+      } else {
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                                                     pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])},
+                                               ry, yo, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, ry, (int)kOffRange, 0, 0);   // keeps YS fixed
+      }
+    } else {
+      if (a.y_f32)
+        __builtin_amdgcn_raw_buffer_store_b128(
+            u32x4{__float_as_uint(acc[0]), __float_as_uint(acc[1]), __float_as_uint(acc[2]), __float_as_uint(acc[3])},
+            ry, yo, 0, 0);
+      else
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])}, ry, yo,
+                                              0, 0);
+    }
+  };
+  const int64_t j0 = blockIdx.x;
+  if (j0 >= units) return;
+  // copies of the first NBUF - 1 units, then per unit: the copies of the
+  // unit NBUF - 1 ahead, then the wait for this unit's (the first units see
+  // fewer later stores, so their counts are their own).  Copies past the
+  // last unit still write zeros into LDS: every exit waits for them.
+#pragma unroll
+  for (int b = 0; b < NBUF - 1; ++b) issue(j0 + b * G, b);
+  int64_t j = j0;
+  issue(j + (NBUF - 1) * G, NBUF - 1);
+  finish(j, 0, std::integral_constant<int, (NBUF - 1) * DT>{});
+  j += G;
+  if (j < units) {
+    issue(j + (NBUF - 1) * G, 0);
+    finish(j, 1, std::integral_constant<int, (NBUF - 1) * DT + YS>{});
+    j += G;
+    int b = 2 % NBUF;
+    for (; j < units; j += G) {
+      issue(j + (NBUF - 1) * G, (b + NBUF - 1) % NBUF);
+      finish(j, b, std::integral_constant<int, (NBUF - 1) * (DT + YS)>{});
+      b = (b + 1) % NBUF;
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 }  // namespace mm

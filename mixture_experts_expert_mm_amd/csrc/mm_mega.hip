@@ -209,14 +209,20 @@ void k_mega(const MegaArgs* mp) {
   }
   if (!grid_barrier(ctl, ++nb, spin, bs, &ok)) return;
 
-  // combine: 8 columns of one token per item; two items per thread at a time
-  // with bf16 slots (A8W8), one with float32 slots; twice that with four
-  // waves per CU (the same loads in flight per CU)
+  // combine: up to 8 slots a token through LDS (the ring is free now);
+  // otherwise 8 columns of one token per item, two items per thread at a
+  // time with bf16 slots (A8W8), one with float32 slots, twice that with
+  // four waves per CU (the same loads in flight per CU)
   const CombineArgs c = m.cb;
-  const int64_t work = c.T * (c.H / 8), stride = (int64_t)gridDim.x * NT;
-  constexpr int CU = (UC == UC_BF16 ? 1 : 2) * (NW >= 8 ? 1 : 2);
-  for (int64_t idx = (int64_t)blockIdx.x * NT + t; idx < work; idx += CU * stride)
-    combine_items<CU, UC != UC_BF16>(c, idx, stride, work);
+  static_assert(CombineLds<NT, UC != UC_BF16>::BYTES <= mega_lds_bytes<UC, BM>(), "combine buffers fit the ring");
+  if (c.K <= CombineLds<NT, UC != UC_BF16>::KMAX) {
+    combine_lds<NT, UC != UC_BF16>(c, lds);
+  } else {
+    const int64_t work = c.T * (c.H / 8), stride = (int64_t)gridDim.x * NT;
+    constexpr int CU = (UC == UC_BF16 ? 1 : 2) * (NW >= 8 ? 1 : 2);
+    for (int64_t idx = (int64_t)blockIdx.x * NT + t; idx < work; idx += CU * stride)
+      combine_items<CU, UC != UC_BF16>(c, idx, stride, work);
+  }
   __syncthreads();
   if (blockIdx.x == 0 && t == 0) {
     uint64_t* clk = reinterpret_cast<uint64_t*>(ctl + kClockWord0);

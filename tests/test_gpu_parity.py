@@ -398,6 +398,33 @@ def test_fused_deterministic_with_experts_of_several_m_blocks(usecase):
     assert torch.equal(y_a.view(torch.int32), y_3.view(torch.int32))
 
 
+@pytest.mark.parametrize("usecase", ["bf16", "fp8", "int8", "mxfp8"])
+@pytest.mark.parametrize("y_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("K,shared", [(8, 0), (7, 1), (8, 1)])
+@pytest.mark.parametrize("T", [40, 300])
+def test_fused_combine_slot_counts(usecase, y_dtype, K, shared, T):
+    """The fused kernel's Token Combine takes up to 8 slots a token through
+    LDS and more (top-8 plus a shared expert) through registers.  Masked
+    routes, a hidden size that ends inside a column segment, 64-row and
+    128-row tiles (T = 40 and 300): fused == three-call bit for bit, and
+    the float32 Y within the oracle tolerance (the bar is set on float32
+    output; bf16 output adds its own rounding)."""
+    cfg = wl.Config(f"combine_{usecase}", usecase, T, 1280, 256, 16, K, 0.5, 77, masked_ratio=0.2, shared=shared)
+    inp = wl.make_inputs(cfg)
+    log(f"[combine] {usecase} y={y_dtype} T={T} K={K} shared={shared}")
+    layer = make_layer(inp, y_dtype)
+    x, ids, wts = device_inputs(inp)
+    y_f, _ = layer.forward(x, ids, wts)
+    y_f = y_f.clone()
+    y_3, _ = layer.forward_3call(x, ids, wts)
+    torch.cuda.synchronize()
+    assert layer.device_error(fused=True) == 0 and layer.device_error(fused=False) == 0
+    assert torch.equal(y_f.view(torch.int16), y_3.view(torch.int16))
+    if y_dtype == "f32":
+        err = rel_err(y_f.cpu().double().numpy(), oracle_y(inp))
+        assert err <= TOL[usecase], err
+
+
 @pytest.mark.parametrize("usecase", ["bf16", "fp8", "int8"])
 @pytest.mark.parametrize("shape", ["max_hidden", "max_intermediate"])
 def test_largest_hidden_and_intermediate(shape, usecase):
