@@ -1106,7 +1106,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
     constexpr int OREG = 32 * OPITCH;                           // one wave's staging bytes
     constexpr int CPR = OCOLS * OESZ / 16;                      // 16-byte pieces per staged row
     constexpr int CPL = 32 * CPR / 64;                          // pieces per lane
-    constexpr bool STAGED = MODE == 1 || (MODE == 0 && !MX);
+    constexpr bool STAGED = MODE == 0 || MODE == 1;
     static_assert(!STAGED || ((EARLY_FIRST ? STAGE : 0) + NW * OREG <= S * STAGE && 64 % CPR == 0 && CPL >= 1),
                   "epilogue staging fits the free ring slots");
     const uint32_t stg_base = lds_base + (uint32_t)(EARLY_FIRST ? STAGE : 0);
@@ -1144,38 +1144,57 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
           }
         }
         if constexpr (MODE == 0 && MX) {
-          // SwiGLU, then Q_MX of each row's group of 32 A columns: the group
-          // of block j is column lr of the 32 lanes of this lane's half, so
-          // its amax is a maximum over those lanes; exponent
-          // floor(log2 amax) - 8, codes = e4m3(v * 2^-exponent)
-          uint8_t* const obase = static_cast<uint8_t*>(a.a_out) + (int64_t)cur.row0 * a.I + cur.n0 / 2;
-          const int gpr = a.I / kMxGroup;   // scale bytes per row
-          uint8_t* const sbase = a.out_mx + (int64_t)cur.row0 * gpr + cur.n0 / 2 / kMxGroup;
-          int lane_off = rb * a.I + wn * (WTN / 2) + lr;
-          int lane_soff = rb * gpr + (wn * (WTN / 2)) / kMxGroup;   // the lane's first row's scale bytes
-          asm volatile("" : "+v"(lane_off), "+v"(lane_soff));
+          // SwiGLU into LDS (float32, the MFMA layout: one column per lane),
+          // then Q_MX of each row's group of 32 A columns (the wave's 32
+          // output columns) from a lane pair: lanes 2r and 2r+1 take row r,
+          // 16 columns each; the group's amax is the larger of the two
+          // halves' maxima; exponent floor(log2 amax) - 8, codes
+          // e4m3(v * 2^-exponent), 16 codes a lane in one store
+          static_assert(OCOLS == kMxGroup && OESZ == 4, "one MX group of A columns per wave and row");
+          const uint32_t wst = stg_base + (uint32_t)(wv * OREG);
+          const uint32_t wlane = wst + (uint32_t)((4 * h) * OPITCH + lr * 4);
+          static_for<16>([&](auto qc) {
+            constexpr int q = qc, OFF = (8 * (q / 4) + (q % 4)) * OPITCH;
+            const float g = __builtin_amdgcn_fmed3f(acc_to_f32(acc[i][0][q]), -a.clamp, a.clamp);
+            const float u = __builtin_amdgcn_fmed3f(acc_to_f32(acc[i][1][q]), -a.clamp, a.clamp);
+            ds_write4<OFF>(wlane, __float_as_uint(silu(g) * u));
+          });
+          lgkm_wait<0>();
+          const int row = le / 2, half = le % 2;
+          u32x4 w[4];
+          const uint32_t rd = wst + (uint32_t)(row * OPITCH + half * 64);
+          static_for<4>([&](auto kc) {
+            constexpr int k = kc;
+            w[k] = ds_read16<16 * k>(rd);
+          });
+          lgkm_wait<0>();
+          float m = 0.0f;
 #pragma unroll
-          for (int q = 0; q < 16; ++q) {
-            const int r = rb + 8 * (q / 4) + (q % 4);
+          for (int k = 0; k < 4; ++k) {
+            tie(w[k]);
 #pragma unroll
-            for (int j = 0; j < NB / 2; ++j) {
-              float g = __builtin_amdgcn_fmed3f(acc_to_f32(acc[i][2 * j][q]), -a.clamp, a.clamp);
-              float u = __builtin_amdgcn_fmed3f(acc_to_f32(acc[i][2 * j + 1][q]), -a.clamp, a.clamp);
-              const float v = silu(g) * u;
-              float m = fabsf(v);
-#pragma unroll
-              for (int o = 16; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-              const int x = mx_shared_exp_e4m3(m);
-              const uint32_t code = f32x2_to_e4m3x2(v * mx_inv_scale(x), 0.0f) & 0xffu;
-              if (r < cur.valid) {
-                gp(obase)[lane_off + (8 * (q / 4) + (q % 4)) * a.I + j * 32] = (uint8_t)code;
-                if (lr == 0) gp(sbase)[lane_soff + (8 * (q / 4) + (q % 4)) * gpr + j] = (uint8_t)(x + 127);
-              }
-            }
-            // one row at a time: interleaving the rows' cross-lane maxima would
-            // keep all of them live at once
-            __builtin_amdgcn_sched_barrier(0);
+            for (int c = 0; c < 4; ++c) m = fmaxf(m, fabsf(__uint_as_float(w[k][c])));
           }
+          m = fmaxf(m, __shfl_xor(m, 1, 64));
+          const int x = mx_shared_exp_e4m3(m);
+          const float inv = mx_inv_scale(x);
+          u32x4 codes;
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            codes[k] = f32x2_to_e4m3x2(__uint_as_float(w[k][0]) * inv, __uint_as_float(w[k][1]) * inv) |
+                       (f32x2_to_e4m3x2(__uint_as_float(w[k][2]) * inv, __uint_as_float(w[k][3]) * inv) << 16);
+          // the tile's rows as buffers whose ranges end at its last valid
+          // row: stores to rows past it are dropped without a branch
+          const int gpr = a.I / kMxGroup;   // scale bytes per row
+          const int trow = wm * WTM + i * 32 + row;
+          const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
+              static_cast<uint8_t*>(a.a_out) + (int64_t)cur.row0 * a.I + cur.n0 / 2, (short)0, cur.valid * a.I,
+              0x00020000);
+          const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+              a.out_mx + (int64_t)cur.row0 * gpr + cur.n0 / 2 / kMxGroup, (short)0, cur.valid * gpr, 0x00020000);
+          __builtin_amdgcn_raw_buffer_store_b128(codes, ors, trow * a.I + wn * kMxGroup + half * 16, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(x + 127), srs, half == 0 ? trow * gpr + wn : (int)kOffRange,
+                                               0, 0);
         } else if constexpr (MODE == 0 || MODE == 1) {
           // The wave's 32-row block i goes through LDS: each lane writes its
           // 16 rows x NB column values (one column per lane, the MFMA
