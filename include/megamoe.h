@@ -282,7 +282,11 @@ mm_status mm_grouped_l2_combine(const mm_plan* plan, const int32_t* expert_offse
  * long-running concurrent kernels must read the error word, or make the plan
  * with the environment variable MM_COOPERATIVE=1 set: the fused kernel is
  * then launched cooperatively, so the runtime starts it only once the whole
- * grid can be resident (some microseconds more per call).
+ * grid can be resident (some microseconds more per call).  A plan made with
+ * MM_DEP=1 set replaces the barriers between Linear1, the requantisation and
+ * Linear2 by per-M-block completion counters (same results, bit for bit;
+ * off by default: not faster on the measured layers).  Its waits are bounded
+ * the same way and report the same error bit.
  *   x              device bf16 [T][H]
  *   topk_ids       device int32 [T][K]
  *   topk_weights   device f32 [T][K]

@@ -328,6 +328,9 @@ __device__ __forceinline__ GemmArgs uniform_args(const GemmArgs& in) {
   a.a_route = uniform_ptr(in.a_route);
   a.a_rows = (int64_t)uniform_int((int)in.a_rows);   // < 2^31 (checked by the host)
   a.partials = uniform_ptr(in.partials);
+  a.dep_done = uniform_ptr(in.dep_done);
+  a.dep_wait = uniform_ptr(in.dep_wait);
+  a.dep_target = (uint32_t)uniform_int((int)in.dep_target);
   a.split_flags = uniform_ptr(in.split_flags);
   a.max_split = uniform_int(in.max_split);
   a.clamp = __builtin_bit_cast(float, uniform_int(__builtin_bit_cast(int, in.clamp)));
@@ -761,6 +764,34 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
     return r;
   };
 
+  // Dependency schedule of the fused kernel.  Linear2: before the first
+  // copy of a tile of M-block b, wait until dep_wait[b] >= dep_target; one
+  // wave-wide load reads the counters of 64 blocks, and blocks seen complete
+  // are not polled again.  Linear1: a tile counts for its M-block once its
+  // stores are complete (pend_mb, below).
+  int dw_base = 0, pend_mb = -1;
+  uint64_t dw_mask = 0;
+  auto dep_ready = [&](int mb) {
+    if constexpr (MODE != 1) return;
+    if (a.dep_wait == nullptr || dw_base == 0x40000000) return;
+    if (mb >= dw_base && mb < dw_base + 64 && ((dw_mask >> (mb - dw_base)) & 1u)) return;
+    if (mb < dw_base || mb >= dw_base + 64) dw_base = mb;
+    uint32_t polls = 0;
+    for (;;) {
+      const int q = dw_base + l;
+      const uint32_t v = q < n_mb ? __hip_atomic_load(a.dep_wait + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+      dw_mask = __ballot(v >= a.dep_target);
+      if ((dw_mask >> (mb - dw_base)) & 1u) break;
+      if (++polls > a.spin_limit) {   // gives up: flagged, and no later wait of this wave polls
+        if (l == 0 && a.err) atomicOr(a.err, (uint32_t)MM_DEVERR_BARRIER_TIMEOUT);
+        dw_base = 0x40000000;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    asm volatile("" ::: "memory");
+  };
+
   int item = 0;
   bool have = item < n_items;
   TileRef cur{};
@@ -768,6 +799,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
   int buf = 0;
   if (have) {
     cur = make_item(0);
+    dep_ready(cur.row0 / BM);
     rr_cur = start_tile(cur);
   }
   while (have) {
@@ -1017,7 +1049,18 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
     // ------------------------------------------------ next tile, epilogue
     // this tile's row data goes to LDS; every wave is done reading the ring
     row_commit(rr_cur, buf);
+    // (a one-stage tile's wait did not cover the stores of the tile before:
+    // with the dependency schedule they are waited for here)
+    if (MODE == 0 && a.dep_done != nullptr && cur.nkl < 2) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // Every wave has waited for this tile's last stage, so the stores of the
+    // tile before it, issued earlier, are complete: that tile counts for its
+    // M-block now (in-order completion of vector memory operations)
+    if (MODE == 0 && a.dep_done != nullptr) {
+      if (t == 0 && pend_mb >= 0)
+        __hip_atomic_fetch_add(a.dep_done + pend_mb, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      pend_mb = cur.role != kRoleProduce ? cur.row0 / BM : -1;
+    }
     const int nitem = item + 1;
     const bool nhave = nitem < n_items;
     TileRef nxt{};
@@ -1112,7 +1155,10 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
     const uint32_t stg_base = lds_base + (uint32_t)(EARLY_FIRST ? STAGE : 0);
     if (nhave) {
       nxt = make_item(nitem);
-      if (EARLY_FIRST) rr_nxt = start_first(nxt);
+      if (EARLY_FIRST) {
+        dep_ready(nxt.row0 / BM);
+        rr_nxt = start_first(nxt);
+      }
     }
     if (cur.role != kRoleProduce) {   // a later piece has no epilogue
       // The lane's coordinates again, from a lane id the compiler cannot
@@ -1322,7 +1368,10 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
     // overwrite the slots
     if constexpr (STAGED) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     if (nhave) {
-      if (!EARLY_FIRST) rr_nxt = start_first(nxt);
+      if (!EARLY_FIRST) {
+        dep_ready(nxt.row0 / BM);
+        rr_nxt = start_first(nxt);
+      }
       start_rest(nxt);
     }
     item = nitem;
@@ -1334,6 +1383,8 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
 #undef MM_DMA
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
   __syncthreads();   // the block is done with LDS
+  if (MODE == 0 && a.dep_done != nullptr && t == 0 && pend_mb >= 0)
+    __hip_atomic_fetch_add(a.dep_done + pend_mb, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------------------
@@ -1514,6 +1565,127 @@ __device__ __forceinline__ void requant_stream(const RequantArgs& a, int64_t p0,
     p += step;
     if (p >= used) break;
   }
+}
+
+// The fused kernel's requantisation under its dependency schedule: the rows
+// of this workgroup's XCD slice (the M-blocks its Linear1 and Linear2 tiles
+// cover, as gemm_tiles cuts them), wave wx of the slice's WX waves taking
+// rows wx, wx + WX, ..., two at a time with the next two rows' loads in
+// flight (as requant_stream, the same arithmetic).  A row is loaded once all
+// Linear1 tiles of its M-block are counted (dep_l1[b] >= l1_target); every
+// row of the slice (padding rows too) counts once in dep_rq[b] when its
+// stores are complete: two batches later, when the loads of a batch issued
+// after them have landed (in-order completion), or at the end.  I <= 2048.
+template <int UC, int BM, int NW>
+__device__ __forceinline__ void requant_dep(const RequantArgs& a, const int32_t* off_s, const int32_t* cnt_s,
+                                            const uint32_t* dep_l1, uint32_t l1_target, uint32_t* dep_rq,
+                                            uint32_t spin_limit, uint32_t* err) {
+  constexpr int RC = 4, RU = 2;
+  constexpr int nxcd = 8;
+  const int xcd = blockIdx.x % nxcd, per_x = gridDim.x / nxcd;
+  if ((int)blockIdx.x >= per_x * nxcd) return;
+  const int n_mb = off_s[a.E] / BM;
+  const int mb_slice = (n_mb + nxcd - 1) / nxcd;
+  const int mb_beg = min(n_mb, xcd * mb_slice), mb_end = min(n_mb, mb_beg + mb_slice);
+  const int64_t WX = (int64_t)per_x * NW, step = RU * WX;
+  const int64_t wx = (int64_t)(blockIdx.x / nxcd) * NW + __builtin_amdgcn_readfirstlane((int)threadIdx.x / 64);
+  const int64_t r_beg = (int64_t)mb_beg * BM + wx, r_end = (int64_t)mb_end * BM;
+  const int64_t nbat = r_end > r_beg ? (r_end - r_beg + step - 1) / step : 0;
+  if (nbat == 0) return;
+  const int l = lane_id();
+  const int nch = a.I / 8;
+  const float qmax = (UC == UC_I8) ? 127.0f : 448.0f;
+  float4 buf[2][RU][2 * RC];
+  bool live[2][RU];
+  int dw_base = 0;
+  uint64_t dw_mask = 0;
+  auto l1_ready = [&](int mb) {
+    if (dw_base == 0x40000000) return;
+    if (mb >= dw_base && mb < dw_base + 64 && ((dw_mask >> (mb - dw_base)) & 1u)) return;
+    if (mb < dw_base || mb >= dw_base + 64) dw_base = mb;
+    uint32_t polls = 0;
+    for (;;) {
+      const int q = dw_base + l;
+      const uint32_t v = q < n_mb ? __hip_atomic_load(dep_l1 + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+      dw_mask = __ballot(v >= l1_target);
+      if ((dw_mask >> (mb - dw_base)) & 1u) break;
+      if (++polls > spin_limit) {   // gives up: flagged, and no later wait of this wave polls
+        if (l == 0 && err) atomicOr(err, (uint32_t)MM_DEVERR_BARRIER_TIMEOUT);
+        dw_base = 0x40000000;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    asm volatile("" ::: "memory");
+  };
+  auto row_rsrc = [&](const void* base, int64_t p, int64_t elem_bytes, bool on) {
+    const uint8_t* b = static_cast<const uint8_t*>(base) + (on ? p : 0) * elem_bytes;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)uniform_ptr(b), (short)0,
+                                             uniform_int(on ? (int)elem_bytes : 0), 0x00020000);
+  };
+  auto load = [&](auto bt, int64_t j) {
+    constexpr int b = decltype(bt)::value;
+#pragma unroll
+    for (int u = 0; u < RU; ++u) {
+      const int64_t pu = r_beg + j * step + u * WX;
+      const bool in = pu < r_end;
+      if (in) l1_ready((int)(pu / BM));
+      live[b][u] = in && requant_row_live(a, pu, off_s, cnt_s);
+      const __amdgpu_buffer_rsrc_t rs = row_rsrc(a.a_stage, pu, (int64_t)a.I * 4, live[b][u]);
+#pragma unroll
+      for (int c8 = 0; c8 < RC; ++c8) {
+        const int c = c8 * 64 + l;
+        const int off = c < nch ? c * 32 : (int)kOffRange;
+        buf[b][u][2 * c8] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+        buf[b][u][2 * c8 + 1] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16, 0, 0));
+      }
+    }
+  };
+  auto process = [&](auto bt, int64_t j) {
+    constexpr int b = decltype(bt)::value;
+#pragma unroll
+    for (int u = 0; u < RU; ++u) {
+      float m = 0.0f;
+#pragma unroll
+      for (int c8 = 0; c8 < 2 * RC; ++c8) m = amax4(buf[b][u][c8], m);
+      const float sc = fmaxf(wave_max(m) / qmax, 1e-8f);
+      const int64_t pu = r_beg + j * step + u * WX;
+      const __amdgpu_buffer_rsrc_t ro = row_rsrc(a.a_pool, pu, a.I, live[b][u]);
+#pragma unroll
+      for (int c8 = 0; c8 < RC; ++c8) {
+        const int c = c8 * 64 + l;
+        const uint2 q = requant_codes8<UC>(buf[b][u][2 * c8], buf[b][u][2 * c8 + 1], sc);
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{q.x, q.y}, ro, c < nch ? c * 8 : (int)kOffRange, 0, 0);
+      }
+      const __amdgpu_buffer_rsrc_t rsc = row_rsrc(a.a_scale, pu, 4, live[b][u]);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), rsc, l == 0 ? 0 : (int)kOffRange, 0, 0);
+    }
+  };
+  auto publish = [&](int64_t j) {
+    asm volatile("" ::: "memory");
+    if (j < 0 || j >= nbat || l != 0) return;
+#pragma unroll
+    for (int u = 0; u < RU; ++u) {
+      const int64_t pu = r_beg + j * step + u * WX;
+      if (pu < r_end) __hip_atomic_fetch_add(dep_rq + pu / BM, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  };
+  const std::integral_constant<int, 0> b0;
+  const std::integral_constant<int, 1> b1;
+  load(b0, 0);
+  for (int64_t j = 0;;) {
+    load(b1, j + 1);   // the next batch (past the slice: nothing is read)
+    process(b0, j);
+    publish(j - 2);
+    if (++j >= nbat) break;
+    load(b0, j + 1);
+    process(b1, j);
+    publish(j - 2);
+    if (++j >= nbat) break;
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  publish(nbat - 2);
+  publish(nbat - 1);
 }
 
 // ---------------------------------------------------------------------------

@@ -88,6 +88,13 @@ struct GemmArgs {
   int max_split;             // largest K split of a tail tile (<= 1: none)
   float clamp;               // Linear1: H clamped to [-clamp, clamp] before SwiGLU (+inf: none)
   uint32_t spin_limit;       // polls before a wait for a partial gives up
+  // The fused kernel's dependency schedule (null: none).  Linear1 adds one
+  // to dep_done[b] for each finished tile of M-block b, once its stores are
+  // complete; Linear2 waits for dep_wait[b] >= dep_target before the first
+  // copy of a tile of M-block b.
+  uint32_t* dep_done;
+  const uint32_t* dep_wait;
+  uint32_t dep_target;
 };
 
 struct RequantArgs {
@@ -137,6 +144,13 @@ struct MegaArgs {
   // the routed experts' counts for the caller (expert_token_nums [Er]);
   // d.counts is the workspace's own [E] array (shared experts included)
   int32_t* counts_out;
+  // counters of the dependency schedule, cleared by the pre-pass: per
+  // M-block finished Linear1 tiles [0, dep_blocks), then requantised rows
+  // [dep_blocks, 2 * dep_blocks)
+  uint32_t* dep;
+  int64_t dep_blocks;
+  int no_dep;                // 1: grid barriers instead of the dependency schedule
+  int pad_;
 };
 
 // launchers (return hipError_t of the launch)

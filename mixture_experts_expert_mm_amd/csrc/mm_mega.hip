@@ -52,6 +52,13 @@ __device__ __forceinline__ bool poll_until(uint32_t* p, uint32_t target, uint32_
 __device__ __forceinline__ void barrier_register(uint32_t* ctl, BarState& bs) {
   bs = BarState{xcc_id(), 0u, 0u};
   if (threadIdx.x == 0) {
+    // ctl[3] != 0: some workgroup does not run on XCD blockIdx % 8, so the
+    // GEMMs' per-XCD slices do not share an L2 and the dependency schedule
+    // is off (grid barriers between the phases instead)
+    if (gridDim.x % 8 != 0 || blockIdx.x % 8 != bs.xcd) {
+      __hip_atomic_fetch_or(&ctl[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    }
     __hip_atomic_fetch_add(&ctl[32 + bs.xcd], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_fetch_add(&ctl[2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -154,6 +161,18 @@ void k_mega(const MegaArgs* mp) {
     }
   }
   if (!grid_barrier(ctl, ++nb, spin, bs, &ok)) return;
+  // Dependency schedule (every workgroup reads the same word, so all take
+  // the same barriers): with each workgroup on XCD blockIdx % 8, the tiles
+  // of an M-block, its requantisation and its Linear2 tiles all run on one
+  // XCD, which shares one L2.  Linear1 counts finished tiles per M-block,
+  // the requantisation waits for them and counts rows, Linear2 waits for
+  // those: no grid barrier between Linear1, the requantisation and Linear2.
+  // Completion is published once the stores are complete (in L2); consumers
+  // poll with device-scope loads and read the data through L2 (this kernel
+  // has not read those lines before, so no stale copies sit in L1).
+  constexpr bool kA8W8 = UC == UC_FP8 || UC == UC_I8;
+  const bool dep = !m.no_dep && gridDim.x >= 8 && (!kA8W8 || m.rq.I <= 2048) &&
+                   __hip_atomic_load(&ctl[3], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u;
   // the counts are final: the routed experts' ones go to the caller
   if (blockIdx.x == 0)
     for (int e = t; e < m.d.Er; e += NT) m.counts_out[e] = m.d.counts[e];
@@ -177,34 +196,46 @@ void k_mega(const MegaArgs* mp) {
   }
 
   // Linear1 + SwiGLU (gemm_tiles leaves the offsets and counts in off_s / cnt_s)
+  constexpr int BN = TileShape<BM>::BN;
   {
-    const GemmArgs g = m.l1;
+    GemmArgs g = m.l1;
+    if (dep) g.dep_done = m.dep;
     gemm_tiles<UC, BM, 0, WIDEN>(g, lds, off_s, cnt_s);
   }
-  if (!grid_barrier(ctl, ++nb, spin, bs, &ok)) return;
+  if (!dep && !grid_barrier(ctl, ++nb, spin, bs, &ok)) return;
 
-  if constexpr (UC == UC_FP8 || UC == UC_I8) {
-    // per-row requantisation of A, one wave per pool row (two rows at a
-    // time when I <= 2048; with four waves per CU, two rows while the next
-    // two load); MX quantised A in the Linear1 epilogue
-    const RequantArgs r = m.rq;
-    const int64_t used = off_s[r.E], nwv = (int64_t)gridDim.x * NW;
-    const int64_t p0 = (int64_t)blockIdx.x * NW + t / 64;
-    if (r.I <= 2048) {
-      if constexpr (NW >= 8) {
-        for (int64_t p = p0; p < used; p += 2 * nwv) requant_rows<UC, 2, 4>(r, p, nwv, off_s, cnt_s);
-      } else {
-        requant_stream<UC, 2>(r, p0, nwv, used, off_s, cnt_s);   // one wave per SIMD: loads ahead of the math
-      }
+  if constexpr (kA8W8) {
+    if (dep) {
+      requant_dep<UC, BM, NW>(m.rq, off_s, cnt_s, m.dep, (uint32_t)(m.l1.N / BN), m.dep + m.dep_blocks, spin,
+                              m.l1.err);
+      __syncthreads();   // (gemm_tiles rewrites off_s / cnt_s, with the same values)
     } else {
-      for (int64_t p = p0; p < used; p += nwv) requant_rows<UC, 1>(r, p, 0, off_s, cnt_s);
+      // per-row requantisation of A, one wave per pool row (two rows at a
+      // time when I <= 2048; with four waves per CU, two rows while the next
+      // two load); MX quantised A in the Linear1 epilogue
+      const RequantArgs r = m.rq;
+      const int64_t used = off_s[r.E], nwv = (int64_t)gridDim.x * NW;
+      const int64_t p0 = (int64_t)blockIdx.x * NW + t / 64;
+      if (r.I <= 2048) {
+        if constexpr (NW >= 8) {
+          for (int64_t p = p0; p < used; p += 2 * nwv) requant_rows<UC, 2, 4>(r, p, nwv, off_s, cnt_s);
+        } else {
+          requant_stream<UC, 2>(r, p0, nwv, used, off_s, cnt_s);   // one wave per SIMD: loads ahead of the math
+        }
+      } else {
+        for (int64_t p = p0; p < used; p += nwv) requant_rows<UC, 1>(r, p, 0, off_s, cnt_s);
+      }
+      if (!grid_barrier(ctl, ++nb, spin, bs, &ok)) return;
     }
-    if (!grid_barrier(ctl, ++nb, spin, bs, &ok)) return;
   }
 
   // Linear2 + gate weight into the combine slots
   {
-    const GemmArgs g = m.l2;
+    GemmArgs g = m.l2;
+    if (dep) {
+      g.dep_wait = kA8W8 ? m.dep + m.dep_blocks : m.dep;
+      g.dep_target = kA8W8 ? (uint32_t)BM : (uint32_t)(m.l1.N / BN);
+    }
     gemm_tiles<UC, BM, 1, false>(g, lds, off_s, cnt_s);
   }
   if (!grid_barrier(ctl, ++nb, spin, bs, &ok)) return;
@@ -238,6 +269,7 @@ __global__ __launch_bounds__(256) void k_mega_prep(MegaArgs m, MegaArgs* out) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t j = i; j < m.d.E; j += stride) m.d.counts[j] = 0;
   for (int64_t j = i; j < kCtlWords; j += stride) m.ctl[j] = 0u;
+  for (int64_t j = i; j < 2 * m.dep_blocks; j += stride) m.dep[j] = 0u;
   constexpr int words = (int)(sizeof(MegaArgs) / 4);
   static_assert(sizeof(MegaArgs) % 4 == 0, "argument block copies as words");
   if (blockIdx.x == 0) {

@@ -326,6 +326,34 @@ def test_cooperative_launch_equals_ordinary(shape, usecase, monkeypatch):
     assert torch.equal(c0, c1)
 
 
+@pytest.mark.parametrize("shape,usecase", [("bm64", "fp8"), ("bm128", "bf16"), ("bm128", "fp8"), ("bm128", "int8"),
+                                           ("bm128", "mxfp8"), ("bm256", "bf16"), ("bm256", "fp8"), ("bm256", "int8")])
+def test_dependency_schedule_equals_barriers(shape, usecase, monkeypatch):
+    """The fused kernel's per-M-block dependency schedule (Linear1, the
+    requantisation and Linear2 without grid barriers between them) gives
+    the results of the barrier schedule (the default) and of the three-call
+    path, bit for bit; masked routes and a shared expert."""
+    if shape in FORCED_TILE:
+        monkeypatch.setenv("MM_FORCE_TILE", FORCED_TILE[shape])
+    cfg = small_cfg(shape, usecase, masked_ratio=0.1, shared=1)
+    inp = wl.make_inputs(cfg)
+    x, ids, wts = device_inputs(inp)
+    log(f"[dependency schedule] {cfg.name}")
+    bar = make_layer(inp, "f32")
+    monkeypatch.setenv("MM_DEP", "1")
+    dep = make_layer(inp, "f32")
+    assert dep.plan.reserved[3] == 1 and bar.plan.reserved[3] == 0
+    y_dep, c_dep = dep.forward(x, ids, wts)
+    y_dep = y_dep.clone()
+    y_3, _ = dep.forward_3call(x, ids, wts)
+    y_bar, c_bar = bar.forward(x, ids, wts)
+    torch.cuda.synchronize()
+    assert dep.device_error(fused=True) == 0 and bar.device_error(fused=True) == 0
+    assert torch.equal(y_dep.view(torch.int32), y_bar.view(torch.int32))
+    assert torch.equal(y_dep.view(torch.int32), y_3.view(torch.int32))
+    assert torch.equal(c_dep, c_bar)
+
+
 @pytest.mark.parametrize("usecase", ["bf16", "fp8"])
 @pytest.mark.parametrize("T,E,block_m", [(1024, 32, 128), (1025, 32, 128), (512, 256, 64), (513, 256, 64)])
 def test_fused_one_block_dispatch_boundary(T, E, block_m, usecase):
