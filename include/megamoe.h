@@ -286,7 +286,10 @@ mm_status mm_grouped_l2_combine(const mm_plan* plan, const int32_t* expert_offse
  * MM_DEP=1 set replaces the barriers between Linear1, the requantisation and
  * Linear2 by per-M-block completion counters (same results, bit for bit;
  * off by default: not faster on the measured layers).  Its waits are bounded
- * the same way and report the same error bit.
+ * the same way and report the same error bit.  The GEMM tiles of the fused
+ * kernel are claimed from per-XCD counters (faster workgroups and XCDs take
+ * more tiles; same results); MM_STATIC_TILES=1 at plan time restores a fixed
+ * round robin.
  *   x              device bf16 [T][H]
  *   topk_ids       device int32 [T][K]
  *   topk_weights   device f32 [T][K]

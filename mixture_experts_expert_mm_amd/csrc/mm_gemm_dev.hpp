@@ -331,6 +331,8 @@ __device__ __forceinline__ GemmArgs uniform_args(const GemmArgs& in) {
   a.dep_done = uniform_ptr(in.dep_done);
   a.dep_wait = uniform_ptr(in.dep_wait);
   a.dep_target = (uint32_t)uniform_int((int)in.dep_target);
+  a.claim = uniform_ptr(in.claim);
+  a.steal = uniform_int(in.steal);
   a.split_flags = uniform_ptr(in.split_flags);
   a.max_split = uniform_int(in.max_split);
   a.clamp = __builtin_bit_cast(float, uniform_int(__builtin_bit_cast(int, in.clamp)));
@@ -696,13 +698,47 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
   // no K split at 256 x 256 (its accumulators fill the register file; a
   // loop that adds partial sums into them would spill them)
   constexpr bool CAN_SPLIT = BM != 256;
-  const int sk = CAN_SPLIT ? split_factor(tail, per_x, nk, a.max_split, (int)gridDim.x) : 1;
+  // Dynamic tiles (the fused kernel, a.claim set; smaller tiles only with
+  // at least 8 tiles per workgroup, where the last round matters little):
+  // the workgroups of an XCD take the slice's tiles in order from a counter
+  // of their XCD, each claiming its next tile when it starts the current
+  // one, so a workgroup that runs faster takes more tiles.  A workgroup
+  // whose XCD's slice is exhausted goes on claiming from the next XCDs'
+  // counters (a.steal), so a faster XCD takes tiles of a slower one.  Item j
+  // of XCD x is tile j of x's slice, whole (no K split).
+  const bool dyn = a.claim != nullptr && in_grid && (BM == 256 || n_s >= 8 * per_x);
+  const int sk = CAN_SPLIT && !dyn ? split_factor(tail, per_x, nk, a.max_split, (int)gridDim.x) : 1;
   const int pieces = tail * sk;
   const int n_items = full + (pieces > wgx ? (pieces - wgx + per_x - 1) / per_x : 0);
+  __shared__ int32_t claim_s[2];
+  int cx = xcd, cx_beg = mb_beg, cx_end = mb_end, cx_ns = n_s;   // the XCD whose tiles are being claimed
+  auto set_cx = [&](int x) {
+    cx = x;
+    cx_beg = min(n_mb, x * mb_slice);
+    cx_end = min(n_mb, cx_beg + mb_slice);
+    cx_ns = (cx_end - cx_beg) * n_tiles;
+  };
+  // thread 0: the claim v of XCD x, moved on to the next XCDs while their
+  // slices are exhausted; into claim_s (x = -1: none left)
+  auto settle_claim = [&](uint32_t v) {
+    int x = cx, left = a.steal ? nxcd - 1 : 0;
+    const auto ns_of = [&](int y) {
+      const int b = min(n_mb, y * mb_slice);
+      return (min(n_mb, b + mb_slice) - b) * n_tiles;
+    };
+    while ((int)v >= ns_of(x) && left > 0) {
+      x = (x + 1) % nxcd;
+      --left;
+      v = __hip_atomic_fetch_add(a.claim + x, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    claim_s[0] = (int)v;
+    claim_s[1] = (int)v < ns_of(x) ? x : -1;
+  };
   auto make_item = [&](int j) {
     TileRef r;
-    if (j < full) {
-      r = resolve_tile<BM>(a, off_s, cnt_s, t_beg + wgx + j * per_x, n_tiles, kbytes, kbytes_b, mb_beg, mb_end);
+    if (dyn || j < full) {
+      r = resolve_tile<BM>(a, off_s, cnt_s, t_beg + (dyn ? j : wgx + j * per_x), n_tiles, kbytes, kbytes_b,
+                           dyn ? cx_beg : mb_beg, dyn ? cx_end : mb_end);
       r.kbase = 0;
       r.nkl = nk;
       r.role = kRoleFull;
@@ -794,15 +830,29 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
 
   int item = 0;
   bool have = item < n_items;
+  if (dyn) {
+    if (t == 0) settle_claim(__hip_atomic_fetch_add(a.claim + xcd, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    __syncthreads();
+    item = __builtin_amdgcn_readfirstlane(claim_s[0]);
+    const int x = __builtin_amdgcn_readfirstlane(claim_s[1]);
+    have = x >= 0;
+    if (have) set_cx(x);
+  }
   TileRef cur{};
   RowRegs rr_cur = row_blank();
   int buf = 0;
   if (have) {
-    cur = make_item(0);
+    cur = make_item(item);
     dep_ready(cur.row0 / BM);
     rr_cur = start_tile(cur);
   }
+  // thread 0: the claim for the item after this one, made when this item
+  // starts (at 256 x 256, whose next item is settled after the epilogue,
+  // when its epilogue starts: nothing held through the main loop)
+  uint32_t claim_v = 0;
   while (have) {
+    if (BM != 256 && dyn && t == 0)
+      claim_v = __hip_atomic_fetch_add(a.claim + cx, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     AccT acc[MB][NB];
 #pragma unroll
     for (int i = 0; i < MB; ++i)
@@ -1049,6 +1099,9 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
     // ------------------------------------------------ next tile, epilogue
     // this tile's row data goes to LDS; every wave is done reading the ring
     row_commit(rr_cur, buf);
+    // dynamic tiles with the next tile's first stage ahead of the epilogue:
+    // the next item is settled here (after the epilogue at 256 x 256)
+    if (BM != 256 && dyn && t == 0) settle_claim(claim_v);
     // (a one-stage tile's wait did not cover the stores of the tile before:
     // with the dependency schedule they are waited for here)
     if (MODE == 0 && a.dep_done != nullptr && cur.nkl < 2) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -1061,9 +1114,19 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
         __hip_atomic_fetch_add(a.dep_done + pend_mb, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       pend_mb = cur.role != kRoleProduce ? cur.row0 / BM : -1;
     }
-    const int nitem = item + 1;
-    const bool nhave = nitem < n_items;
+    int nitem = item + 1;
+    bool nhave = !dyn && nitem < n_items;   // dynamic tiles: known after the row-data barrier, or the epilogue
     TileRef nxt{};
+    bool early_dyn = false;   // the next dynamic item's TileRef is made here (not after the epilogue)
+    if (BM == 256 && dyn && t == 0)
+      claim_v = __hip_atomic_fetch_add(a.claim + cx, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (BM != 256 && dyn) {
+      nitem = __builtin_amdgcn_readfirstlane(claim_s[0]);
+      const int x = __builtin_amdgcn_readfirstlane(claim_s[1]);
+      nhave = x >= 0;
+      if (nhave) set_cx(x);
+      early_dyn = true;
+    }
     RowRegs rr_nxt = row_blank();
     // A K piece of a split tile: a later piece hands its partial sums to
     // piece 0 through its slot and moves on; piece 0 adds them in piece
@@ -1366,7 +1429,18 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& args, uint8_t* lds, i
     }
     // every wave is done reading its staging block before the copies
     // overwrite the slots
+    if (BM == 256 && dyn && t == 0) settle_claim(claim_v);
     if constexpr (STAGED) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else if (dyn) __syncthreads();
+    if (dyn && !early_dyn) {
+      nitem = __builtin_amdgcn_readfirstlane(claim_s[0]);
+      const int x = __builtin_amdgcn_readfirstlane(claim_s[1]);
+      nhave = x >= 0;
+      if (nhave) {
+        set_cx(x);
+        nxt = make_item(nitem);
+      }
+    }
     if (nhave) {
       if (!EARLY_FIRST) {
         dep_ready(nxt.row0 / BM);

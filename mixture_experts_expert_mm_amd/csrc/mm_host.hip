@@ -53,6 +53,9 @@ int plan_max_split(const mm_plan& pl) { return (int)pl.reserved[1]; }
 bool plan_cooperative(const mm_plan& pl) { return pl.reserved[2] != 0; }
 // [3] the fused kernel's dependency schedule: on where it applies (1) or off (0)
 bool plan_dep(const mm_plan& pl) { return pl.reserved[3] != 0; }
+// [4] the fused kernel's 256 x 256 tiles: static round robin (1) or claimed
+// from per-XCD counters (0)
+bool plan_static_tiles(const mm_plan& pl) { return pl.reserved[4] != 0; }
 
 // ---------------------------------------------------------------- workspace
 struct WsLayout {
@@ -92,7 +95,7 @@ WsLayout ws_layout(const mm_plan& pl) {
   L.x_tok = q && tok ? take(p.num_tokens * p.hidden) : -1;
   L.x_tok_scale = q && tok ? take(mx_usecase(p.usecase) ? p.num_tokens * (p.hidden / 32) : p.num_tokens * 4) : -1;
   // the fused kernel's per-M-block counters (its dependency schedule)
-  L.dep = take(2 * (P / pl.block_m) * 4);
+  L.dep = take((2 * (P / pl.block_m) + 16) * 4);
   L.fused_end = o;
   return L;
 }
@@ -518,6 +521,8 @@ mm_status mm_plan_create(const mm_problem* problem, mm_plan* plan) {
   // counters.  Off by default: measured slower for A8W8 (6.12 vs 5.99 ms at
   // 16K fp8 tokens, 0.372 vs 0.340 ms at 128), no faster for bf16 and MX.
   if (const char* v = std::getenv("MM_DEP")) pl.reserved[3] = std::atoi(v) == 1 ? 1 : 0;
+  // MM_STATIC_TILES=1 when the plan is made: no per-XCD tile counters
+  if (const char* v = std::getenv("MM_STATIC_TILES")) pl.reserved[4] = std::atoi(v) == 1 ? 1 : 0;
   const int64_t P = align_up(R + all_experts(p) * (pl.block_m - 1), pl.block_m);
   if (P > ((int64_t)1 << 31) - 1) return MM_ERR_INVALID_ARG;
   pl.pool_rows = P;
@@ -646,6 +651,7 @@ mm_status mega_moe(const mm_plan* plan, const void* x, const int32_t* topk_ids, 
   m.dep = at<uint32_t>(workspace, L.dep);
   m.dep_blocks = pl.pool_rows / pl.block_m;
   m.no_dep = plan_dep(pl) ? 0 : 1;
+  m.static_tiles = plan_static_tiles(pl) ? 1 : 0;
   MegaArgs* dev_args = at<MegaArgs>(workspace, L.mega_args);
   MM_TRY(run(MM_K_ZERO, s, [&] { return launch_mega_prep(m, dev_args, s); }));
   MM_TRY(run(MM_K_MEGA, s, [&] {

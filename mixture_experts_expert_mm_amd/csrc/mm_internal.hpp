@@ -95,6 +95,10 @@ struct GemmArgs {
   uint32_t* dep_done;
   const uint32_t* dep_wait;
   uint32_t dep_target;
+  // the fused kernel's per-XCD tile counters [8], zero at the start (null:
+  // each workgroup takes every G-th tile of its XCD's slice)
+  uint32_t* claim;
+  int steal;                 // with claim: take other XCDs' tiles once this XCD's are done
 };
 
 struct RequantArgs {
@@ -146,11 +150,12 @@ struct MegaArgs {
   int32_t* counts_out;
   // counters of the dependency schedule, cleared by the pre-pass: per
   // M-block finished Linear1 tiles [0, dep_blocks), then requantised rows
-  // [dep_blocks, 2 * dep_blocks)
+  // [dep_blocks, 2 * dep_blocks), then the tile counters of Linear1 and
+  // Linear2 (8 each)
   uint32_t* dep;
   int64_t dep_blocks;
   int no_dep;                // 1: grid barriers instead of the dependency schedule
-  int pad_;
+  int static_tiles;          // 1: no tile counters (each workgroup every G-th tile)
 };
 
 // launchers (return hipError_t of the launch)

@@ -200,6 +200,8 @@ void k_mega(const MegaArgs* mp) {
   {
     GemmArgs g = m.l1;
     if (dep) g.dep_done = m.dep;
+    if (!m.static_tiles) g.claim = m.dep + 2 * m.dep_blocks;
+    g.steal = !dep && m.static_tiles == 0;   // the dependency schedule needs every tile on its own XCD
     gemm_tiles<UC, BM, 0, WIDEN>(g, lds, off_s, cnt_s);
   }
   if (!dep && !grid_barrier(ctl, ++nb, spin, bs, &ok)) return;
@@ -232,6 +234,8 @@ void k_mega(const MegaArgs* mp) {
   // Linear2 + gate weight into the combine slots
   {
     GemmArgs g = m.l2;
+    if (!m.static_tiles) g.claim = m.dep + 2 * m.dep_blocks + 8;
+    g.steal = !dep && m.static_tiles == 0;
     if (dep) {
       g.dep_wait = kA8W8 ? m.dep + m.dep_blocks : m.dep;
       g.dep_target = kA8W8 ? (uint32_t)BM : (uint32_t)(m.l1.N / BN);
@@ -269,7 +273,7 @@ __global__ __launch_bounds__(256) void k_mega_prep(MegaArgs m, MegaArgs* out) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t j = i; j < m.d.E; j += stride) m.d.counts[j] = 0;
   for (int64_t j = i; j < kCtlWords; j += stride) m.ctl[j] = 0u;
-  for (int64_t j = i; j < 2 * m.dep_blocks; j += stride) m.dep[j] = 0u;
+  for (int64_t j = i; j < 2 * m.dep_blocks + 16; j += stride) m.dep[j] = 0u;
   constexpr int words = (int)(sizeof(MegaArgs) / 4);
   static_assert(sizeof(MegaArgs) % 4 == 0, "argument block copies as words");
   if (blockIdx.x == 0) {

@@ -326,6 +326,38 @@ def test_cooperative_launch_equals_ordinary(shape, usecase, monkeypatch):
     assert torch.equal(c0, c1)
 
 
+@pytest.mark.parametrize("case", ["bm256_bf16", "bm256_fp8", "bm256_int8", "bm128_fp8", "bm128_mxfp8"])
+def test_tile_claiming_equals_static_tiles(case, monkeypatch):
+    """The fused kernel's tiles claimed from per-XCD counters, other XCDs'
+    tiles taken once a slice is done (the default at 256 x 256, and with at
+    least 8 tiles per workgroup at 128 x 256), give the results of the static
+    round robin (a plan made with MM_STATIC_TILES=1) and of the three-call
+    path, bit for bit."""
+    shape, usecase = case.split("_")
+    if shape == "bm256":
+        monkeypatch.setenv("MM_FORCE_TILE", "2")
+        cfg = small_cfg("bm256", usecase, masked_ratio=0.1)
+    else:   # 32 M-blocks per XCD slice x 8 Linear1 tiles: claimed at 128 x 256 too
+        monkeypatch.setenv("MM_FORCE_TILE", "1")
+        cfg = wl.Config(f"claim_{usecase}", usecase, 8192, 256, 1024, 8, 4, 0.5, 5, masked_ratio=0.1)
+    inp = wl.make_inputs(cfg)
+    x, ids, wts = device_inputs(inp)
+    log(f"[tile claiming] {cfg.name}")
+    dyn = make_layer(inp, "f32")
+    y_dyn, c_dyn = dyn.forward(x, ids, wts)
+    y_dyn = y_dyn.clone()
+    y_3, _ = dyn.forward_3call(x, ids, wts)
+    monkeypatch.setenv("MM_STATIC_TILES", "1")
+    sta = make_layer(inp, "f32")
+    assert sta.plan.reserved[4] == 1 and dyn.plan.reserved[4] == 0
+    y_sta, c_sta = sta.forward(x, ids, wts)
+    torch.cuda.synchronize()
+    assert dyn.device_error(fused=True) == 0 and sta.device_error(fused=True) == 0
+    assert torch.equal(y_dyn.view(torch.int32), y_sta.view(torch.int32))
+    assert torch.equal(y_dyn.view(torch.int32), y_3.view(torch.int32))
+    assert torch.equal(c_dyn, c_sta)
+
+
 @pytest.mark.parametrize("shape,usecase", [("bm64", "fp8"), ("bm128", "bf16"), ("bm128", "fp8"), ("bm128", "int8"),
                                            ("bm128", "mxfp8"), ("bm256", "bf16"), ("bm256", "fp8"), ("bm256", "int8")])
 def test_dependency_schedule_equals_barriers(shape, usecase, monkeypatch):
