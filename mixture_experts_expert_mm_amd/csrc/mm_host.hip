@@ -497,11 +497,12 @@ mm_status mm_plan_create(const mm_problem* problem, mm_plan* plan) {
   // Measured on the 7168 x 2048, 32-expert, top-8 layer: BLOCK_M 64 is 6-9%
   // faster at 16 rows per expert, 128 is 4-5% faster at 32 rows and 16% / 31%
   // faster at 128 / 256 rows (fewer passes over each expert's weights).
-  // 256 x 256 from 2048 rows per expert on (measured on the same layer:
-  // 3-6% faster at 2048 and 4096 rows, even at 1024, 2% slower at 512); not
-  // for the MX use cases (their scale copies need eight waves).
+  // 256 x 256 from 1024 rows per expert on (measured on the same layer:
+  // 3-6% faster at 2048 and 4096 rows; at 1024 rows, with the fused
+  // kernel's tiles claimed across XCDs, 3.02 vs 3.13 ms for bf16); not for
+  // the MX use cases (their scale copies need eight waves).
   const double expected = (double)R / (double)p.num_experts;
-  int tile = expected < 24 ? TILE_M64_N128 : expected < 2048 ? TILE_M128_N256 : TILE_M256_N256;
+  int tile = expected < 24 ? TILE_M64_N128 : expected < 1024 ? TILE_M128_N256 : TILE_M256_N256;
   // tuning override: MM_FORCE_TILE=<0..2> selects BLOCK_M 64/128/256
   if (const char* f = std::getenv("MM_FORCE_TILE")) {
     const int v = std::atoi(f);

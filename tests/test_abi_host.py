@@ -49,8 +49,9 @@ def test_struct_sizes_match_header():
 
 def test_plan_sizes_and_block_m():
     _lib()
-    p = B.mm_plan_create(4096, 7168, 2048, 32, 8, "bf16")
-    assert p.block_m == 128
+    p = B.mm_plan_create(4096, 7168, 2048, 32, 8, "bf16")   # 1024 rows per expert: 256 x 256
+    assert p.block_m == 256
+    assert B.mm_plan_create(2048, 7168, 2048, 32, 8, "bf16").block_m == 128   # 512 rows per expert
     R = 4096 * 8
     assert p.pool_rows % p.block_m == 0
     assert p.pool_rows >= R + 32 * (p.block_m - 1)
